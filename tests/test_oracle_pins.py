@@ -1,0 +1,306 @@
+"""Pins of the CPU oracle against things other than itself.
+
+* E2M1: the OCP MX FP4 table (tests/golden/e2m1_ocp_mx_fp4.txt).
+* E4M3: torch's float8_e4m3fn decoder for all 256 bytes, the OCP FP8
+  landmarks (tests/golden/e4m3_ocp_fp8_special.txt), and torch's
+  round-to-nearest-even cast for the encoder below the saturation point.
+* bf16: torch's bfloat16 decoder.
+* Quantiser: hand-worked cases (tests/golden/quantiser_worked_cases.txt) and
+  the nearest-value invariants on random N(0, 0.02) matrices.
+* GEMM: exact rational brute force (Python fractions over the golden/torch
+  tables), a closed form, one-hot reconstruction, zero scales.
+* A set of deliberately broken oracles (mistakes planted on the CPU) must
+  fail these pins, which shows they can catch a dropped term, a swapped
+  nibble order, a transposed operand or a wrong block index.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+
+pytestmark = pytest.mark.filterwarnings("ignore")
+
+
+# ---- golden tables ----------------------------------------------------------
+
+def _golden_e2m1(golden_dir):
+    vals = {}
+    with open(os.path.join(golden_dir, "e2m1_ocp_mx_fp4.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            c, v = line.split()
+            vals[int(c, 16)] = float(v)
+    assert len(vals) == 16
+    return vals
+
+
+def _torch_e4m3_table():
+    b = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    return b.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _torch_bf16(bits):
+    return torch.from_numpy(np.asarray(bits, np.uint16).view(np.int16)).view(
+        torch.bfloat16).to(torch.float64).numpy()
+
+
+# ---- element decoders -------------------------------------------------------
+
+def test_e2m1_all_16_codes(oracle_mod, golden_dir):
+    g = _golden_e2m1(golden_dir)
+    for c in range(16):
+        v = oracle_mod.e2m1_value(c)
+        assert v == g[c], (c, v, g[c])
+        assert math.copysign(1.0, v) == math.copysign(1.0, g[c])
+
+
+def test_e4m3_all_256_bytes_match_torch(oracle_mod):
+    ref = _torch_e4m3_table()
+    for b in range(256):
+        v = oracle_mod.e4m3_value(b)
+        if math.isnan(ref[b]):
+            assert math.isnan(v), b
+        else:
+            assert v == ref[b], (b, v, ref[b])
+            assert math.copysign(1.0, v) == math.copysign(1.0, ref[b])
+
+
+def test_e4m3_landmarks(oracle_mod, golden_dir):
+    with open(os.path.join(golden_dir, "e4m3_ocp_fp8_special.txt")) as f:
+        rows = [l.split() for l in f if l.strip() and not l.startswith("#")]
+    assert len(rows) >= 10
+    for b, v in rows:
+        got = oracle_mod.e4m3_value(int(b, 16))
+        if v == "nan":
+            assert math.isnan(got)
+        else:
+            assert got == float(v), (b, got, v)
+    finite_nonneg = [b for b in range(128) if not math.isnan(oracle_mod.e4m3_value(b))]
+    assert len(finite_nonneg) == 127
+
+
+def test_bf16_decode_matches_torch(oracle_mod):
+    rng = np.random.default_rng(0)
+    bits = np.concatenate([rng.integers(0, 65536, 4000), [0, 0x8000, 0x3F80, 0x0001, 0x7F7F]])
+    bits = bits[((bits >> 7) & 0xFF) != 0xFF]  # finite patterns
+    ref = _torch_bf16(bits.astype(np.uint16))
+    for b, r in zip(bits, ref):
+        assert oracle_mod.bf16_value(int(b)) == r
+
+
+# ---- element encoders -------------------------------------------------------
+
+def test_e4m3_encoder_matches_torch_rne_below_saturation(oracle_mod):
+    table = _torch_e4m3_table()
+    finite = sorted(set(float(table[b]) for b in range(127)))
+    xs = list(finite)
+    xs += [(a + b) / 2 for a, b in zip(finite[:-1], finite[1:])]      # every tie point
+    xs += [np.nextafter(np.float32(x), np.float32(0)) for x in xs if x > 0]
+    xs += [np.nextafter(np.float32(x), np.float32(1e9)) for x in xs]
+    rng = np.random.default_rng(1)
+    xs += list(rng.uniform(0, 464, 3000)) + list(np.exp(rng.uniform(-12, 6, 3000)))
+    xs = np.array([x for x in xs if 0 <= x < 464], dtype=np.float32)
+    ref = torch.from_numpy(xs).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    for x, r in zip(xs, ref):
+        assert oracle_mod.e4m3_encode(float(x)) == int(r), (float(x), int(r))
+
+
+def test_e4m3_encoder_saturates(oracle_mod):
+    for x in [448.0, 463.9, 464.0, 470.0, 1e6, float("inf")]:
+        assert oracle_mod.e4m3_encode(x) == 0x7E
+
+
+def test_e2m1_encoder_nearest_ties_to_even(oracle_mod, golden_dir):
+    g = _golden_e2m1(golden_dir)
+    mags = [g[c] for c in range(8)]
+    ties = {0.25: 0, 0.75: 2, 1.25: 2, 1.75: 4, 2.5: 4, 3.5: 6, 5.0: 6}
+    for x, c in ties.items():
+        assert oracle_mod.e2m1_encode(x) == c
+        assert oracle_mod.e2m1_encode(-x) == c | 8
+    rng = np.random.default_rng(2)
+    for x in np.concatenate([rng.uniform(-8, 8, 4000), np.linspace(-7, 7, 2801)]):
+        x = float(np.float32(x))
+        c = oracle_mod.e2m1_encode(x)
+        assert (c >> 3) == (1 if math.copysign(1, x) < 0 else 0)
+        best = min(abs(m - abs(x)) for m in mags)
+        assert abs(mags[c & 7] - abs(x)) == best, (x, c)
+    assert oracle_mod.e2m1_encode(100.0) == 7 and oracle_mod.e2m1_encode(-7.0) == 15
+
+
+# ---- quantiser --------------------------------------------------------------
+
+def _worked_cases(golden_dir):
+    rows = []
+    with open(os.path.join(golden_dir, "quantiser_worked_cases.txt")) as f:
+        for line in f:
+            if not line.startswith("row"):
+                continue
+            head, scale, codes = line.split("|")
+            w = [float(v) for v in head.split(":")[1].split()]
+            rows.append((w, int(scale.split(":")[1], 16),
+                         [int(c, 16) for c in codes.split(":")[1].split()]))
+    return rows
+
+
+def test_quantiser_worked_cases(oracle_mod, golden_dir):
+    rows = _worked_cases(golden_dir)
+    W = np.array([r[0] for r in rows], np.float32)
+    codes, scales, t = oracle_mod.quantize(W)
+    assert t == 1.0
+    for i, (_, sc, cs) in enumerate(rows):
+        assert scales[i, 0] == sc, (i, scales[i, 0], sc)
+        got = []
+        for byte in codes[i]:
+            got += [int(byte) & 15, int(byte) >> 4]
+        assert got == cs, (i, got, cs)
+
+
+def test_quantiser_invariants_random(oracle_mod, golden_dir):
+    g = _golden_e2m1(golden_dir)
+    e4 = _torch_e4m3_table()
+    W = synth.weights(0, 7, 24, 256)
+    codes, scales, t = oracle_mod.quantize(W)
+    amax = float(np.max(np.abs(W)))
+    assert t == float(np.float32(amax) / np.float32(2688.0))
+    for n in range(W.shape[0]):
+        for b in range(W.shape[1] // 16):
+            blk = W[n, 16 * b:16 * b + 16]
+            s = np.float32(np.float32(np.max(np.abs(blk))) / np.float32(6.0)) / np.float32(t)
+            ref_sc = int(torch.tensor([float(s)], dtype=torch.float32).to(
+                torch.float8_e4m3fn).view(torch.uint8)[0])
+            assert scales[n, b] == ref_sc
+            d = np.float32(e4[ref_sc]) * np.float32(t)
+            for i in range(16):
+                byte = codes[n, 8 * b + i // 2]
+                c = (byte >> 4) if (i & 1) else (byte & 15)
+                x = np.float32(blk[i]) / d
+                err = abs(abs(g[c]) - abs(float(x)))
+                assert err == min(abs(g[m] - abs(float(x))) for m in range(8))
+
+
+def test_quantiser_zero_tensor(oracle_mod):
+    codes, scales, t = oracle_mod.quantize(np.zeros((3, 32), np.float32))
+    assert t == 0.0 and not codes.any() and not scales.any()
+
+
+# ---- GEMM -------------------------------------------------------------------
+
+def _exact(act_bits, codes, scales, t, golden_dir):
+    """Exact rational y and S from the golden E2M1 table and torch's E4M3 and
+    bf16 decoders."""
+    g = _golden_e2m1(golden_dir)
+    e4 = _torch_e4m3_table()
+    a = _torch_bf16(act_bits)
+    M, K = act_bits.shape
+    N = codes.shape[0]
+    tq = Fraction(float(t))
+    y = [[Fraction(0)] * N for _ in range(M)]
+    S = [[Fraction(0)] * N for _ in range(M)]
+    for n in range(N):
+        for k in range(K):
+            byte = int(codes[n, k // 2])
+            c = (byte >> 4) if (k & 1) else (byte & 15)
+            w = Fraction(g[c]) * Fraction(float(e4[int(scales[n, k // 16])])) * tq
+            for m in range(M):
+                p = Fraction(float(a[m, k])) * w
+                y[m][n] += p
+                S[m][n] += abs(p)
+    return y, S
+
+
+def _random_case(seed, M, K, N):
+    codes, scales = synth.random_planes(seed, 1, N, K)
+    act = synth.activations(seed, 2, M, K)
+    t = float(np.float32(np.random.default_rng(seed).uniform(1e-5, 2.0)))
+    return act, codes, scales, t
+
+
+def _check_brute_force(gemm, golden_dir, seeds=range(6)):
+    shapes = [(1, 16, 1), (3, 32, 5), (8, 64, 8), (5, 48, 7), (2, 64, 3), (8, 16, 2)]
+    for seed, (M, K, N) in zip(seeds, shapes):
+        act, codes, scales, t = _random_case(seed, M, K, N)
+        y, S = gemm(act, codes, scales, t)
+        ey, eS = _exact(act, codes, scales, t, golden_dir)
+        for m in range(M):
+            for n in range(N):
+                bound = float(eS[m][n]) * K * 2.0 ** -52 + 1e-300
+                if abs(Fraction(float(y[m, n])) - ey[m][n]) > Fraction(bound):
+                    return False
+                if abs(float(S[m, n]) - float(eS[m][n])) > bound:
+                    return False
+    return True
+
+
+def test_gemm_brute_force_fractions(oracle_mod, golden_dir):
+    assert _check_brute_force(lambda *a: oracle_mod.gemm(*a, threads=2), golden_dir)
+
+
+def test_gemm_closed_form_constant(oracle_mod, golden_dir):
+    g = _golden_e2m1(golden_dir)
+    e4 = _torch_e4m3_table()
+    K, N = 256, 4
+    one = synth._to_bf16_bits(np.ones((1, K), np.float32))
+    for c, s, t in [(7, 0x7E, 0.25), (1, 0x01, 1.0), (0xB, 0x3A, 3.0e-5), (2, 0x38, 1.0)]:
+        codes = np.full((N, K // 2), c | (c << 4), np.uint8)
+        scales = np.full((N, K // 16), s, np.uint8)
+        y, S = oracle_mod.gemm(one, codes, scales, np.float32(t))
+        exact = K * g[c] * float(e4[s]) * float(np.float32(t))
+        assert np.all(y == exact), (c, s, y[0, 0], exact)
+        assert np.all(S == abs(exact))
+
+
+def test_gemm_one_hot_reconstructs_weights(oracle_mod, golden_dir):
+    g = _golden_e2m1(golden_dir)
+    e4 = _torch_e4m3_table()
+    K, N = 64, 6
+    codes, scales = synth.random_planes(3, 4, N, K)
+    t = float(np.float32(0.0123))
+    eye = synth._to_bf16_bits(np.eye(K, dtype=np.float32))
+    y, _ = oracle_mod.gemm(eye, codes, scales, t)
+    for k in range(K):
+        for n in range(N):
+            byte = int(codes[n, k // 2])
+            c = (byte >> 4) if (k & 1) else (byte & 15)
+            assert y[k, n] == g[c] * float(e4[scales[n, k // 16]]) * t
+
+
+def test_gemm_zero_scales_give_zero(oracle_mod):
+    codes, _ = synth.random_planes(5, 6, 4, 128)
+    act = synth.activations(5, 7, 3, 128)
+    y, S = oracle_mod.gemm(act, codes, np.zeros((4, 8), np.uint8), 0.5)
+    assert not y.any() and not S.any()
+
+
+# ---- planted mistakes must be caught ----------------------------------------
+
+def _swap_nibbles(codes):
+    return ((codes >> 4) | (codes << 4)).astype(np.uint8)
+
+
+MUTANTS = {
+    # low/high nibble order exchanged
+    "nibble_order": lambda o, a, c, s, t: o.gemm(a, _swap_nibbles(c), s, t),
+    # tensor scale dropped
+    "no_tensor_scale": lambda o, a, c, s, t: o.gemm(a, c, s, 1.0),
+    # block index off by one (scales shifted along K)
+    "block_shift": lambda o, a, c, s, t: o.gemm(a, c, np.roll(s, 1, axis=1), t),
+    # the last activation column dropped
+    "dropped_term": lambda o, a, c, s, t: o.gemm(
+        np.concatenate([a[:, :-1], np.zeros((a.shape[0], 1), np.uint16)], 1), c, s, t),
+    # activations reversed along K (a transposed / mis-indexed operand)
+    "reversed_k": lambda o, a, c, s, t: o.gemm(np.ascontiguousarray(a[:, ::-1]), c, s, t),
+    # sign bit of the E2M1 code ignored
+    "sign_ignored": lambda o, a, c, s, t: o.gemm(a, (c & 0x77).astype(np.uint8), s, t),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistakes_fail_brute_force(oracle_mod, golden_dir, name):
+    mutant = MUTANTS[name]
+    assert not _check_brute_force(lambda a, c, s, t: mutant(oracle_mod, a, c, s, t), golden_dir)
