@@ -1,0 +1,186 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 weight-streaming GEMM library.
+ *
+ * What the library computes
+ *   The decode round of "Ignis" (README, "What sets it apart", "The decode
+ *   round"; and "Why ignis", tile "One round for every lane"): one pass over
+ *   weights stored in NVFP4 serves every decode lane at once, so the round is
+ *   bound by the bandwidth of streaming the weights.  The body format is the
+ *   one "Models and artifacts" gives in "The artifact": 4-bit floating point
+ *   with one scale per 16 values, read by the kernels as stored.
+ *
+ *     y[m][n] = tensor_scale * sum_k bf16(a[m][k]) * E2M1(code[n][k])
+ *                                   * E4M3(scale[n][k/16])
+ *
+ *   for M lanes (rows of activations), K inputs and N outputs.  E2M1 is the
+ *   OCP MX FP4 element, E4M3 the OCP FP8 "FN" type (max 448), tensor_scale an
+ *   fp32 per-matrix factor.  Products are exact; sums are in fp32.
+ *
+ * Canonical weight planes (the format as produced by a quantiser)
+ *   codes  : uint8 [N][K/2]; byte j of row n holds k = 2j in bits 0..3 and
+ *            k = 2j+1 in bits 4..7.
+ *   scales : uint8 [N][K/16]; one E4M3 byte per block of 16 consecutive k.
+ *   Kernels read a packed permutation of these planes made once by
+ *   nvfp4_pack (no conversion at load beyond that permutation).
+ *
+ * Conventions for every entry point
+ *   - Pointers named *_dev are device pointers (e.g. from hipMalloc or a torch
+ *     CUDA tensor); the caller owns all device memory.  The library allocates
+ *     no device memory except the graph objects of a round plan.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *     Every launch is asynchronous on that stream; no entry point synchronises
+ *     except nvfp4_round_create (graph capture) and nvfp4_quantize (none: the
+ *     tensor scale stays on the device).
+ *   - Return value: NVFP4_OK or an error code.  On error nothing was launched
+ *     and nvfp4_last_error() (thread-local) names the offending parameter.
+ *     No entry point aborts, exits or throws.
+ *   - NaN/Inf activations, NaN scale bytes (0x7F, 0xFF) and negative scales
+ *     are outside the contract and are not checked.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum nvfp4_status {
+    NVFP4_OK = 0,
+    NVFP4_EINVAL = 1,       /* a parameter is invalid (named by nvfp4_last_error) */
+    NVFP4_EUNSUPPORTED = 2, /* a legal request outside what this plan/build supports */
+    NVFP4_EHIP = 3,         /* the HIP runtime returned an error (message carried) */
+    NVFP4_ESTATE = 4        /* misuse of a handle (destroyed, wrong plan) */
+};
+
+enum nvfp4_out_dtype { NVFP4_OUT_F32 = 0, NVFP4_OUT_BF16 = 1 };
+
+/* Largest number of lanes (activation rows) the decode kernel serves in one
+ * weight pass; larger M goes to the prefill kernel. */
+#define NVFP4_DECODE_MAX_M 8
+
+/* ---- status ----------------------------------------------------------------- */
+
+/* Static text of a status code. */
+const char* nvfp4_status_string(int status);
+/* Thread-local text of the last error raised on this thread ("" if none). */
+const char* nvfp4_last_error(void);
+/* Library version as an integer (major*10000 + minor*100 + patch). */
+int nvfp4_version(void);
+
+/* ---- packed layout ----------------------------------------------------------- */
+
+/* Bytes of the packed code / scale planes for a K x N weight matrix.  They
+ * include padding of K to a multiple of 128 and of N to a multiple of 16
+ * (padding is zero codes and zero scales).  Return 0 for invalid K or N
+ * (K % 16 != 0, K < 16, N < 1). */
+size_t nvfp4_packed_code_bytes(int K, int N);
+size_t nvfp4_packed_scale_bytes(int K, int N);
+
+/* Permute canonical planes into the packed gfx950 layout (a bijection on the
+ * non-padding bytes, bit-exact).  codes_dev: [N][K/2], scales_dev: [N][K/16];
+ * outputs sized by the two functions above, 16-byte aligned.  Inputs and
+ * outputs must not overlap. */
+int nvfp4_pack(const uint8_t* codes_dev, const uint8_t* scales_dev, int K, int N,
+               uint8_t* codes_packed_dev, uint8_t* scales_packed_dev, void* stream);
+
+/* Inverse of nvfp4_pack (for tests and export). */
+int nvfp4_unpack(const uint8_t* codes_packed_dev, const uint8_t* scales_packed_dev, int K,
+                 int N, uint8_t* codes_dev, uint8_t* scales_dev, void* stream);
+
+/* ---- quantiser ----------------------------------------------------------------- */
+
+/* Quantise fp32 weights w_dev [N][K] (row-major, K % 16 == 0) to canonical
+ * NVFP4 planes: tensor scale t = amax/(6*448); block scale = (block amax/6)/t
+ * rounded to E4M3 (nearest-even, saturating at 448); each value w/(E4M3*t)
+ * rounded to E2M1 (nearest-even, saturating at 6, sign kept; a block whose
+ * decoded scale is 0 gets +0 codes).  All arithmetic fp32, round to nearest
+ * even.  Writes codes_dev [N][K/2], scales_dev [N][K/16] and the fp32 tensor
+ * scale to *tensor_scale_dev (device memory).  workspace_dev: at least
+ * nvfp4_quantize_workspace_bytes() bytes, any content. */
+size_t nvfp4_quantize_workspace_bytes(void);
+int nvfp4_quantize(const float* w_dev, int K, int N, uint8_t* codes_dev, uint8_t* scales_dev,
+                   float* tensor_scale_dev, void* workspace_dev, void* stream);
+
+/* ---- GEMM plan --------------------------------------------------------------------- */
+
+typedef struct nvfp4_gemm_plan* nvfp4_gemm;
+
+/* Optional kernel configuration for nvfp4_gemm_create_ex; 0 fields mean
+ * "choose automatically". */
+typedef struct nvfp4_gemm_config {
+    int split_k;      /* decode: number of K slices (workgroups per column group) */
+    int waves;        /* decode: waves per workgroup (column tiles of 16 per workgroup) */
+    int reserved[6];
+} nvfp4_gemm_config;
+
+/* Create a plan for GEMMs of shape (M <= max_M) x K x N with the given output
+ * dtype.  Validates K % 16 == 0, K >= 16, N >= 1, max_M >= 1, out_dtype.
+ * *workspace_bytes receives the device workspace every run of this plan
+ * needs (may be 0).  The workspace must be zero-filled before its first use
+ * (nvfp4_workspace_clear or any zero fill); every run leaves it zeroed again.
+ * No device memory is allocated. */
+int nvfp4_gemm_create(nvfp4_gemm* plan, int max_M, int K, int N, int out_dtype,
+                      size_t* workspace_bytes);
+int nvfp4_gemm_create_ex(nvfp4_gemm* plan, int max_M, int K, int N, int out_dtype,
+                         const nvfp4_gemm_config* config, size_t* workspace_bytes);
+void nvfp4_gemm_destroy(nvfp4_gemm plan);
+
+/* Run out[m][n] = tensor_scale * sum_k act[m][k] * w[n][k] for m < M.
+ *   codes_dev, scales_dev : packed planes (nvfp4_pack) of the K x N matrix
+ *   act_dev               : bf16 bits [M][K] row-major, 16-byte aligned
+ *   out_dev               : [M][N] row-major, fp32 or bf16 (plan's dtype;
+ *                           bf16 is round-to-nearest-even of the fp32 result)
+ *   workspace_dev         : the plan's workspace (16-byte aligned), or NULL
+ *                           if the plan needs none
+ * (K, N) must equal the plan's, 1 <= M <= max_M.  M <= 8 uses the decode
+ * kernel (one pass over the weights for all M rows); larger M uses the bf16
+ * MFMA prefill kernel.  Asynchronous; no synchronisation. */
+int nvfp4_gemm_run(nvfp4_gemm plan, int M, int K, int N, const uint8_t* codes_dev,
+                   const uint8_t* scales_dev, float tensor_scale, const uint16_t* act_dev,
+                   void* out_dev, void* workspace_dev, void* stream);
+
+/* Zero a workspace with a fill kernel (safe inside graph capture). */
+int nvfp4_workspace_clear(void* workspace_dev, size_t bytes, void* stream);
+
+/* ---- decode round ---------------------------------------------------------------------- */
+
+/* One matrix of a round.  act_dev holds max_M rows of K bf16 values, out_dev
+ * max_M rows of N outputs. */
+typedef struct nvfp4_layer {
+    int K, N;
+    const uint8_t* codes_dev;  /* packed */
+    const uint8_t* scales_dev; /* packed */
+    float tensor_scale;
+    const uint16_t* act_dev;
+    void* out_dev;
+    int out_dtype;
+} nvfp4_layer;
+
+typedef struct nvfp4_round_plan* nvfp4_round;
+
+/* Workspace a round over these layers needs (the maximum over its matrices;
+ * the matrices run in stream order and reuse it). */
+int nvfp4_round_workspace_bytes(const nvfp4_layer* layers, int n_layers, int max_M,
+                                size_t* workspace_bytes);
+
+/* Capture one HIP graph per width M = 1..max_M (max_M <= 8), each running
+ * the n_layers GEMMs in list order on one stream, as the reference engine
+ * replays one graph per batch width.  The layer array is copied; the device
+ * buffers it names must stay valid while the plan lives.  The workspace is
+ * zeroed on `stream` before capture.  Synchronises `stream`. */
+int nvfp4_round_create(nvfp4_round* plan, const nvfp4_layer* layers, int n_layers, int max_M,
+                       void* workspace_dev, size_t workspace_bytes, void* stream);
+/* Replay the graph of width M (1..max_M) on `stream`. */
+int nvfp4_round_run(nvfp4_round plan, int M, void* stream);
+/* Number of kernel nodes in the graph of width M (0 on error). */
+int nvfp4_round_graph_nodes(nvfp4_round plan, int M);
+void nvfp4_round_destroy(nvfp4_round plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

@@ -1,0 +1,89 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/nvfp4.h"
+
+namespace nvfp4 {
+
+// ---- packed layout -----------------------------------------------------------
+// A weight matrix is cut into column tiles of 16 outputs (one MFMA column
+// block) and K superblocks of 512 values.  One (tile, superblock) holds:
+//   codes : 4 KiB = [kb 0..3][lane 0..63][16 bytes]; lane l (column l%16, K
+//           octet g = l/16) holds, for MFMA step s = 0..3, the 4 canonical code
+//           bytes of k = sb*512 + kb*128 + 32*s + 8*g .. +7 at bytes 4s..4s+3.
+//   scales: 512 B = [column 0..15][half p 0..1][kb 0..3][step s 0..3]: the
+//           E4M3 byte of block (sb*512 + kb*128 + 32*s + 16*p) / 16.
+// Tiles are stored column-tile major, superblocks ascending within a tile, so
+// one wave streams one contiguous range per column tile.
+constexpr int kTileN = 16;
+constexpr int kSuperK = 512;
+constexpr int kCodeBytesPerSuper = kTileN * kSuperK / 2;     // 4096
+constexpr int kScaleBytesPerSuper = kTileN * kSuperK / 16;   // 512
+
+inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+inline int padded_k(int K) { return round_up(K, kSuperK); }
+inline int padded_n(int N) { return round_up(N, kTileN); }
+
+// ---- errors --------------------------------------------------------------------
+int set_error(int status, const char* fmt, ...);
+void clear_error();
+int hip_fail(hipError_t e, const char* what);
+
+#define NVFP4_HIP(call)                                           \
+    do {                                                          \
+        hipError_t e_ = (call);                                   \
+        if (e_ != hipSuccess) return ::nvfp4::hip_fail(e_, #call); \
+    } while (0)
+
+// ---- plans ---------------------------------------------------------------------
+struct DecodeConfig {
+    int waves;          // column tiles (waves) per workgroup
+    int splits;         // K slices
+    int sb_per_split;   // superblocks per K slice
+    int n_groups;       // column groups of `waves` tiles
+    int grid;           // workgroups launched (n_groups padded to 8, times splits)
+    size_t ws_bytes;    // partial sums + counters
+    size_t counter_off; // byte offset of the counters in the workspace
+    int lds_bytes;
+};
+
+struct PrefillConfig {
+    int enabled;
+    size_t ws_bytes;
+};
+
+}  // namespace nvfp4
+
+struct nvfp4_gemm_plan {
+    uint32_t magic;
+    int max_M, K, N, out_dtype;
+    int Kp, Np;
+    nvfp4::DecodeConfig dec;
+    nvfp4::PrefillConfig pre;
+    size_t ws_bytes;
+};
+
+namespace nvfp4 {
+constexpr uint32_t kGemmMagic = 0x4E564634u;  // "NVF4"
+constexpr uint32_t kRoundMagic = 0x524F4E44u;
+
+int make_decode_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, DecodeConfig* out);
+int make_prefill_config(int max_M, int K, int N, PrefillConfig* out);
+
+// Launchers (no validation: callers validated).  Return NVFP4_OK or EHIP.
+int launch_decode(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
+                  float ts, const uint16_t* act, void* out, void* ws, hipStream_t s);
+int launch_prefill(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
+                   float ts, const uint16_t* act, void* out, void* ws, hipStream_t s);
+int launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+
+// Shared validation of a GEMM run against its plan.
+int validate_run(const nvfp4_gemm_plan* p, int M, int K, int N, const void* codes,
+                 const void* scales, const void* act, const void* out, const void* ws);
+int run_gemm(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
+             float ts, const uint16_t* act, void* out, void* ws, hipStream_t s);
+}  // namespace nvfp4

@@ -1,0 +1,172 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol,
+sizes its packed planes, and refuses invalid requests (naming the parameter)
+before it makes any HIP call, so none of this needs a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import nvfp4_weight_streaming_amd as nv
+    if not os.path.exists(nv.LIB_PATH):
+        from nvfp4_weight_streaming_amd import build as b
+        b.build()
+    nv.lib()
+    return nv
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree(nv):
+    declared = _declared_functions()
+    assert len(declared) >= 15
+    assert sorted(nv.EXPORTS) == declared
+
+
+def test_library_exports_every_declared_symbol(nv):
+    L = ctypes.CDLL(nv.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(nv):
+    assert nv.status_string(nv.OK) == "ok"
+    assert nv.status_string(nv.EINVAL) == "invalid argument"
+    assert nv.status_string(99) == "unknown status"
+    assert nv.lib().nvfp4_version() >= 100
+
+
+@pytest.mark.parametrize("K,N", [(256, 512), (5120, 5120), (5120, 7168), (6144, 5120),
+                                 (5120, 34816), (17408, 5120), (5120, 152064), (48, 17)])
+def test_packed_sizes(nv, K, N):
+    Kp = -(-K // 512) * 512
+    Np = -(-N // 16) * 16
+    assert nv.nvfp4_packed_code_bytes(K, N) == Np * Kp // 2
+    assert nv.nvfp4_packed_scale_bytes(K, N) == Np * Kp // 16
+
+
+@pytest.mark.parametrize("K,N", [(0, 16), (8, 16), (24, 16), (16, 0), (-16, 4)])
+def test_packed_sizes_invalid(nv, K, N):
+    assert nv.nvfp4_packed_code_bytes(K, N) == 0
+    assert nv.nvfp4_packed_scale_bytes(K, N) == 0
+
+
+@pytest.mark.parametrize("args,word", [
+    ((8, 24, 16, 0), "K"), ((8, 0, 16, 0), "K"), ((8, 256, 0, 0), "N"),
+    ((0, 256, 16, 0), "max_M"), ((8, 256, 16, 7), "out_dtype")])
+def test_gemm_create_rejects(nv, args, word):
+    with pytest.raises(nv.Nvfp4Error) as e:
+        nv.nvfp4_gemm_create(*args)
+    assert e.value.status == nv.EINVAL
+    assert e.value.message.startswith(word)
+
+
+def test_gemm_create_null_outputs(nv):
+    L = nv.lib()
+    ws = ctypes.c_size_t()
+    assert L.nvfp4_gemm_create(None, 8, 256, 16, 0, ctypes.byref(ws)) == nv.EINVAL
+    assert "plan" in nv.last_error()
+    h = ctypes.c_void_p()
+    assert L.nvfp4_gemm_create(ctypes.byref(h), 8, 256, 16, 0, None) == nv.EINVAL
+    assert "workspace_bytes" in nv.last_error()
+
+
+def test_gemm_config_validation(nv):
+    with pytest.raises(nv.Nvfp4Error) as e:
+        nv.nvfp4_gemm_create(8, 5120, 5120, 1, split_k=0, waves=3)
+    assert "waves" in e.value.message
+    plan, ws = nv.nvfp4_gemm_create(8, 5120, 5120, 1, split_k=5, waves=8)
+    assert ws > 0
+    nv.nvfp4_gemm_destroy(plan)
+    plan, ws = nv.nvfp4_gemm_create(8, 2560, 5120, 1, split_k=1, waves=4)
+    assert ws == 0  # no K split: no partials, no counters
+    nv.nvfp4_gemm_destroy(plan)
+    # one workgroup stages at most 5 x 512 values of K, so K = 5120 needs 2 slices
+    plan, ws = nv.nvfp4_gemm_create(8, 5120, 5120, 1, split_k=1, waves=4)
+    assert ws > 0
+    nv.nvfp4_gemm_destroy(plan)
+
+
+def test_workspace_sizes_for_round_shapes(nv):
+    for K, N in [(5120, 7168), (6144, 5120), (5120, 34816), (17408, 5120), (5120, 152064)]:
+        plan, ws = nv.nvfp4_gemm_create(8, K, N, 1)
+        assert ws % 256 == 0
+        nv.nvfp4_gemm_destroy(plan)
+
+
+FAKE = 1 << 20  # a 16-byte-aligned non-null address; never dereferenced
+
+
+@pytest.mark.parametrize("kw,word,status", [
+    (dict(M=0), "M", 1), (dict(M=9), "M", 1), (dict(K=512), "K", 1), (dict(N=64), "N", 1),
+    (dict(codes=None), "codes", 1), (dict(scales=None), "scales", 1), (dict(act=None), "act", 1),
+    (dict(out=None), "out", 1), (dict(codes=FAKE + 4), "codes", 1),
+    (dict(act=FAKE + 8), "act", 1), (dict(out=FAKE + 2), "out", 1),
+    (dict(workspace=None), "workspace", 1), (dict(workspace=FAKE + 4), "workspace", 1)])
+def test_gemm_run_validates_before_any_gpu_call(nv, kw, word, status):
+    plan, ws = nv.nvfp4_gemm_create(8, 5120, 5120, 1)
+    assert ws > 0
+    args = dict(M=4, K=5120, N=5120, codes=FAKE, scales=FAKE, act=FAKE, out=FAKE,
+                workspace=FAKE)
+    args.update(kw)
+    try:
+        with pytest.raises(nv.Nvfp4Error) as e:
+            nv.nvfp4_gemm_run(plan, args["M"], args["K"], args["N"], args["codes"],
+                              args["scales"], 1.0, args["act"], args["out"], args["workspace"],
+                              stream=0)
+        assert e.value.status == status
+        assert e.value.message.startswith(word)
+    finally:
+        nv.nvfp4_gemm_destroy(plan)
+
+
+def test_gemm_run_bad_handle(nv):
+    L = nv.lib()
+    assert L.nvfp4_gemm_run(None, 1, 256, 16, FAKE, FAKE, ctypes.c_float(1.0), FAKE, FAKE,
+                            None, None) == nv.ESTATE
+    assert "plan" in nv.last_error()
+
+
+def test_pack_and_quantize_validate(nv):
+    L = nv.lib()
+    assert L.nvfp4_pack(FAKE, FAKE, 24, 16, FAKE, FAKE, None) == nv.EINVAL
+    assert nv.last_error().startswith("K")
+    assert L.nvfp4_pack(None, FAKE, 32, 16, FAKE, FAKE, None) == nv.EINVAL
+    assert nv.last_error().startswith("codes")
+    assert L.nvfp4_pack(FAKE, FAKE, 32, 16, FAKE + 8, FAKE, None) == nv.EINVAL
+    assert L.nvfp4_unpack(FAKE, FAKE, 32, 0, FAKE, FAKE, None) == nv.EINVAL
+    assert nv.last_error().startswith("N")
+    assert L.nvfp4_quantize(FAKE, 20, 4, FAKE, FAKE, FAKE, FAKE, None) == nv.EINVAL
+    assert nv.last_error().startswith("K")
+    assert L.nvfp4_quantize(FAKE, 32, 4, FAKE, FAKE, FAKE, None, None) == nv.EINVAL
+    assert nv.last_error().startswith("workspace")
+    assert nv.nvfp4_quantize_workspace_bytes() >= 4
+
+
+def test_round_validation(nv):
+    good = dict(K=256, N=32, codes=FAKE, scales=FAKE, tensor_scale=1.0, act=FAKE, out=FAKE,
+                out_dtype=1)
+    assert nv.nvfp4_round_workspace_bytes([good] * 3, 8) >= 0
+    for bad, word in [(dict(K=20), "layers[1].K"), (dict(N=0), "layers[1].N"),
+                      (dict(act=None), "layers[1]"), (dict(out_dtype=5), "layers[1].out_dtype"),
+                      (dict(codes=FAKE + 1), "layers[1]")]:
+        layers = [good, dict(good, **bad), good]
+        with pytest.raises(nv.Nvfp4Error) as e:
+            nv.nvfp4_round_workspace_bytes(layers, 8)
+        assert e.value.message.startswith(word), e.value.message
+    with pytest.raises(nv.Nvfp4Error) as e:
+        nv.nvfp4_round_workspace_bytes([good], 9)
+    assert e.value.message.startswith("max_M")
+    L = nv.lib()
+    assert L.nvfp4_round_run(None, 1, None) == nv.ESTATE
+    assert nv.nvfp4_round_graph_nodes(None, 1) == 0

@@ -1,0 +1,250 @@
+"""GPU parity of the pack, quantise and GEMM kernels against the CPU oracle.
+
+Every input comes from the seeded generator (synth); expected values come
+only from the oracle.  Integer work (pack, quantiser codes) is compared
+bit-exactly; GEMM outputs within |err| <= 2^-16 * sum|a*w| per element (plus
+the final rounding allowance for bf16 outputs)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import bf16_bits, check, dev, dev_bf16, host, pack, require_gpu, run
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nv():
+    return require_gpu()
+
+
+# ---- pack ---------------------------------------------------------------------
+
+@pytest.mark.parametrize("K,N", [(16, 1), (48, 17), (512, 16), (1040, 100), (2576, 33),
+                                 (5120, 48)])
+def test_pack_unpack_roundtrip_bit_exact(nv, K, N):
+    import torch
+    codes, scales = synth.random_planes(11, K + N, N, K)
+    cd, sd = dev(codes), dev(scales)
+    pw = pack(nv, cd, sd, K, N, 1.0)
+    pc = host(pw.codes)
+    ps = host(pw.scales)
+    # a permutation plus zero padding: byte histograms match
+    hc = np.bincount(codes.ravel(), minlength=256)
+    hc[0] += pc.size - codes.size
+    assert np.array_equal(np.bincount(pc, minlength=256), hc)
+    hs = np.bincount(scales.ravel(), minlength=256)
+    hs[0] += ps.size - scales.size
+    assert np.array_equal(np.bincount(ps, minlength=256), hs)
+    c2 = torch.full_like(cd, 0xAB)
+    s2 = torch.full_like(sd, 0xAB)
+    nv.nvfp4_unpack(pw.codes, pw.scales, K, N, c2, s2)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(c2), codes)
+    assert np.array_equal(host(s2), scales)
+
+
+# ---- quantiser ----------------------------------------------------------------
+
+def _gpu_quantize(nv, W):
+    import torch
+    N, K = W.shape
+    w = dev(W.astype(np.float32))
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((N, K // 16), dtype=torch.uint8, device="cuda")
+    ts = torch.empty(1, dtype=torch.float32, device="cuda")
+    ws = torch.empty(nv.nvfp4_quantize_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    nv.nvfp4_quantize(w, K, N, codes, scales, ts, ws)
+    torch.cuda.synchronize()
+    return host(codes), host(scales), float(host(ts)[0])
+
+
+def _quantiser_cases():
+    rng = np.random.default_rng(5)
+    special = synth.weights(3, 9, 40, 64)
+    special[0, :16] = 0.0                                   # zero block
+    special[1, :16] = special[1, :16] * 1e-6                # block scale rounds to 0 / subnormal
+    special[2, 16:32] = special[2, 16:32] * 1e-3
+    special[3, :] = -0.0                                    # negative zeros
+    special[4, 5] = 3.0                                     # a large value sets the tensor scale
+    special[5, :16] = np.float32(6.375)                     # scale midpoint tie
+    special[6, 32:48] = rng.uniform(-1e-4, 1e-4, 16)
+    return [
+        ("tiny_config", synth.weights(0, 0, 512, 256)),
+        ("special", special),
+        ("wide", synth.weights(0, 5, 64, 5120)),
+    ]
+
+
+@pytest.mark.parametrize("case", [c[0] for c in _quantiser_cases()])
+def test_quantiser_bit_exact(nv, case):
+    W = dict(_quantiser_cases())[case]
+    c_ref, s_ref, t_ref = oracle.quantize(W)
+    c, s, t = _gpu_quantize(nv, W)
+    assert t == t_ref
+    assert np.array_equal(s, s_ref)
+    assert np.array_equal(c, c_ref)
+
+
+def test_quantiser_worked_cases(nv, golden_dir):
+    import os
+    rows = []
+    for line in open(os.path.join(golden_dir, "quantiser_worked_cases.txt")):
+        if line.startswith("row"):
+            head, sc, cs = line.split("|")
+            rows.append(([float(v) for v in head.split(":")[1].split()], int(sc.split(":")[1], 16),
+                         [int(x, 16) for x in cs.split(":")[1].split()]))
+    W = np.array([r[0] for r in rows], np.float32)
+    c, s, t = _gpu_quantize(nv, W)
+    assert t == 1.0
+    for i, (_, sc, cs) in enumerate(rows):
+        assert s[i, 0] == sc
+        got = []
+        for byte in c[i]:
+            got += [int(byte) & 15, int(byte) >> 4]
+        assert got == cs, (i, got, cs)
+
+
+# ---- GEMM -----------------------------------------------------------------------
+
+def test_tiny_config_full_parity(nv):
+    """M=1, K=256, N=512, fp32 out, seed 0; the GPU quantises and packs."""
+    W = synth.weights(0, 0, 512, 256)
+    c_ref, s_ref, t_ref = oracle.quantize(W)
+    c, s, t = _gpu_quantize(nv, W)
+    assert t == t_ref and np.array_equal(c, c_ref) and np.array_equal(s, s_ref)
+    act = synth.activations(0, 0, 1, 256)
+    pw = pack(nv, dev(c), dev(s), 256, 512, t)
+    out, _ = run(nv, pw, dev_bf16(act), nv.OUT_F32)
+    y, S = oracle.gemm(act, c_ref, s_ref, t_ref)
+    check(out, y, S, bf16=False, what="tiny")
+
+
+def test_one_hot_reconstructs_every_weight_exactly(nv):
+    """Lane m of call i carries a one-hot activation at k = 8 i + m: every
+    output equals one dequantised weight exactly, so the sweep reads the whole
+    matrix back through the kernel and checks the packed layout and every
+    index bit-exactly.  t is a power of two so w*t is exact in fp32."""
+    K, N = 1040, 37
+    codes, scales = synth.random_planes(21, 3, N, K)
+    t = 2.0 ** -7
+    pw = pack(nv, dev(codes), dev(scales), K, N, t)
+    wref = oracle.dequantize(codes, scales, t)  # [N][K] fp64, exact
+    eye = np.zeros((K, K), np.float32)
+    np.fill_diagonal(eye, 1.0)
+    bits = synth._to_bf16_bits(eye)
+    g = nv.Gemm(8, K, N, nv.OUT_F32)
+    import torch
+    got = np.zeros((K, N))
+    for k0 in range(0, K, 8):
+        out = torch.full((8, N), float("nan"), device="cuda")
+        g(pw, dev_bf16(bits[k0:k0 + 8]), out)
+        got[k0:k0 + 8] = host(out)
+    assert np.array_equal(got, wref.T)
+
+
+@pytest.mark.parametrize("c,s,t", [(7, 0x7E, 0.25), (1, 0x01, 1.0), (0xB, 0x3A, 2.0 ** -20),
+                                   (2, 0x38, 1.0)])
+def test_closed_form_constant_weights(nv, c, s, t):
+    K, N, M = 2048, 48, 8
+    codes = np.full((N, K // 2), c | (c << 4), np.uint8)
+    scales = np.full((N, K // 16), s, np.uint8)
+    pw = pack(nv, dev(codes), dev(scales), K, N, t)
+    one = synth._to_bf16_bits(np.ones((M, K), np.float32))
+    out, _ = run(nv, pw, dev_bf16(one), nv.OUT_F32)
+    exact = K * oracle.e2m1_value(c) * oracle.e4m3_value(s) * t
+    assert np.all(host(out) == exact)
+
+
+def test_zero_scales_give_zero(nv):
+    K, N = 512, 32
+    codes, _ = synth.random_planes(4, 4, N, K)
+    pw = pack(nv, dev(codes), dev(np.zeros((N, K // 16), np.uint8)), K, N, 1.0)
+    out, _ = run(nv, pw, dev_bf16(synth.activations(4, 4, 8, K)), nv.OUT_F32)
+    assert np.all(host(out) == 0.0)
+
+
+RAGGED = [(1, 16, 1), (3, 48, 17), (8, 512, 16), (5, 1040, 100), (8, 2576, 33),
+          (2, 5136, 515), (7, 12288, 40), (4, 256, 512), (6, 3072, 7)]
+
+
+@pytest.mark.parametrize("M,K,N", RAGGED)
+@pytest.mark.parametrize("bf16", [False, True])
+def test_random_planes_ragged(nv, M, K, N, bf16):
+    """Every code and every finite scale byte (subnormal ones included),
+    shapes with ragged K and N tails."""
+    codes, scales = synth.random_planes(M * 7 + K, N, N, K)
+    t = float(np.float32(np.random.default_rng(K + N).uniform(1e-4, 1e-2)))
+    act = synth.activations(M + K, N, M, K)
+    pw = pack(nv, dev(codes), dev(scales), K, N, t)
+    out, _ = run(nv, pw, dev_bf16(act), nv.OUT_BF16 if bf16 else nv.OUT_F32)
+    y, S = oracle.gemm(act, codes, scales, t)
+    check(out, y, S, bf16=bf16, what="ragged %r" % ((M, K, N),))
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 8])
+def test_projection_5120_full(nv, M):
+    """The single-projection config: M lanes, K = N = 5120, quantised
+    N(0, 0.02) weights, bf16 out; plus an fp32 plan checked to the strict bound."""
+    K = N = 5120
+    W = synth.weights(0, 100, N, K)
+    c_ref, s_ref, t_ref = oracle.quantize(W)
+    c, s, t = _gpu_quantize(nv, W)
+    assert t == t_ref and np.array_equal(c, c_ref) and np.array_equal(s, s_ref)
+    act = synth.activations(0, 100, M, K)
+    pw = pack(nv, dev(c), dev(s), K, N, t)
+    y, S = oracle.gemm(act, c_ref, s_ref, t_ref)
+    out, _ = run(nv, pw, dev_bf16(act), nv.OUT_BF16)
+    check(out, y, S, bf16=True, what="projection bf16 M=%d" % M)
+    out32, _ = run(nv, pw, dev_bf16(act), nv.OUT_F32)
+    check(out32, y, S, bf16=False, what="projection f32 M=%d" % M)
+
+
+@pytest.mark.parametrize("split_k,waves", [(1, 4), (2, 2), (3, 8), (7, 4), (12, 2), (12, 8)])
+def test_split_configurations_agree_and_are_deterministic(nv, split_k, waves):
+    M, K, N = 8, 6144, 1000
+    codes, scales = synth.random_planes(8, 8, N, K)
+    t = 3.0e-4
+    act = synth.activations(8, 8, M, K)
+    pw = pack(nv, dev(codes), dev(scales), K, N, t)
+    y, S = oracle.gemm(act, codes, scales, t)
+    out1, g = run(nv, pw, dev_bf16(act), nv.OUT_F32, split_k=split_k, waves=waves)
+    check(out1, y, S, bf16=False, what="split %d waves %d" % (split_k, waves))
+    import torch
+    out2 = torch.full_like(out1, float("nan"))
+    for _ in range(3):  # the workspace counters must reset themselves
+        g(pw, dev_bf16(act), out2)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out1).view(np.uint32), host(out2).view(np.uint32))
+
+
+@pytest.mark.parametrize("M", [9, 20])
+def test_more_than_eight_lanes(nv, M):
+    K, N = 512, 64
+    codes, scales = synth.random_planes(9, M, N, K)
+    act = synth.activations(9, M, M, K)
+    pw = pack(nv, dev(codes), dev(scales), K, N, 0.01)
+    out, _ = run(nv, pw, dev_bf16(act), nv.OUT_F32)
+    y, S = oracle.gemm(act, codes, scales, 0.01)
+    check(out, y, S, bf16=False, what="M=%d" % M)
+
+
+def test_m_below_plan_max_and_bf16_rounding(nv):
+    """A plan for 8 lanes run with fewer; bf16 out equals RNE of the fp32 out."""
+    import torch
+    K, N = 2048, 300
+    codes, scales = synth.random_planes(12, 12, N, K)
+    act = synth.activations(12, 12, 8, K)
+    pw = pack(nv, dev(codes), dev(scales), K, N, 0.003)
+    g32 = nv.Gemm(8, K, N, nv.OUT_F32)
+    g16 = nv.Gemm(8, K, N, nv.OUT_BF16)
+    for M in (1, 3, 8):
+        o32 = torch.full((M, N), float("nan"), device="cuda")
+        o16 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+        g32(pw, dev_bf16(act[:M]), o32)
+        g16(pw, dev_bf16(act[:M]), o16)
+        torch.cuda.synchronize()
+        assert np.array_equal(bf16_bits(o16), bf16_bits(o32.to(torch.bfloat16)))
+        y, S = oracle.gemm(act[:M], codes, scales, 0.003)
+        check(o32, y, S, bf16=False, what="M=%d of 8" % M)
