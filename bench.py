@@ -1,0 +1,276 @@
+"""Benchmark of the NVFP4 weight-streaming decode round on one MI355X.
+
+One step = one replay of the 27B-class decode round: 64 layers x {qkv
+5120x7168, o 6144x5120, gate_up 5120x34816, down 17408x5120} (K x N), every
+matrix streamed once for M lanes, captured in one HIP graph per width.  The
+headline runs M = 8 lanes; the same run also times widths 1..8.
+
+Prints one JSON line (rank 0):
+  value        = algorithmic bytes of the round (NVFP4 weights + bf16
+                 activations in + bf16 outputs) / device time per round, GB/s
+  roofline     = the decode kernel's achieved GB/s per launch (HIP events
+                 around individual launches of the same matrices) against the
+                 MI355X HBM peak of 8 TB/s
+  cpu_baseline = the CPU oracle timed on the host's cores on a bounded sample
+                 of the same workload (see cpu_baseline() below)
+
+Inputs are synthetic (seeded N(0, 0.02) fp32 weights quantised on the GPU,
+N(0, 1) bf16 activations) and resident in HBM before the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+LAYERS = 64
+ROUND_SHAPES = (("qkv", 5120, 7168), ("o", 6144, 5120), ("gate_up", 5120, 34816),
+                ("down", 17408, 5120))
+METRIC = "NVFP4 decode GEMM GB/s & % HBM peak at M=1..8; 27B-class round ms"
+
+
+def weight_bytes(K, N):
+    return K * N // 2 + K * N // 16
+
+
+def round_bytes(M, layers=LAYERS):
+    """Algorithmic bytes of one round: weights once, activations in and bf16
+    outputs once."""
+    b = 0
+    for _, K, N in ROUND_SHAPES:
+        b += weight_bytes(K, N) + M * K * 2 + M * N * 2
+    return b * layers
+
+
+def build_round(nv, seed=0, layers=LAYERS, max_M=8, log=None):
+    """Generate, quantise and pack every matrix of the round on the GPU.
+    Returns (round spec list, buffers kept alive, tensor scales)."""
+    import torch
+    import synth
+    specs, keep = [], []
+    total = sum(nv.nvfp4_packed_code_bytes(K, N) + nv.nvfp4_packed_scale_bytes(K, N)
+                for _, K, N in ROUND_SHAPES) * layers
+    arena = torch.empty(total, dtype=torch.uint8, device="cuda")
+    keep.append(arena)
+    off = 0
+    qws = torch.empty(nv.nvfp4_quantize_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    ts_dev = torch.empty(layers * len(ROUND_SHAPES), dtype=torch.float32, device="cuda")
+    t0 = time.time()
+    for layer in range(layers):
+        for j, (name, K, N) in enumerate(ROUND_SHAPES):
+            idx = layer * len(ROUND_SHAPES) + j
+            w = synth.weights_device(seed, synth.stream_id(layer, name), N, K)
+            codes = torch.empty((N, K // 2), dtype=torch.uint8, device="cuda")
+            scales = torch.empty((N, K // 16), dtype=torch.uint8, device="cuda")
+            nv.nvfp4_quantize(w, K, N, codes, scales, ts_dev[idx:idx + 1], qws)
+            cb, sb = nv.nvfp4_packed_code_bytes(K, N), nv.nvfp4_packed_scale_bytes(K, N)
+            cpk = arena[off:off + cb]
+            spk = arena[off + cb:off + cb + sb]
+            off += cb + sb
+            nv.nvfp4_pack(codes, scales, K, N, cpk, spk)
+            del w, codes, scales
+            act = synth.activations_device(seed, synth.stream_id(layer, name), max_M, K)
+            out = torch.empty((max_M, N), dtype=torch.bfloat16, device="cuda")
+            keep += [act, out]
+            specs.append(dict(K=K, N=N, codes=cpk, scales=spk, tensor_scale=0.0, act=act,
+                              out=out, out_dtype=nv.OUT_BF16, name=name, layer=layer))
+        if log and layer % 16 == 15:
+            torch.cuda.synchronize()
+            log("  built layers 0..%d (%.1f s)" % (layer, time.time() - t0))
+    ts = ts_dev.cpu().tolist()
+    for s, t in zip(specs, ts):
+        s["tensor_scale"] = t
+    torch.cuda.synchronize()
+    return specs, keep
+
+
+def cpu_baseline(rows=None, lanes=8, threads=None):
+    """The CPU oracle, as it stands, on a bounded sample of the round: the
+    first `rows` output columns of each of layer 0's four matrices, M = 8
+    lanes.  Quantisation of the sample (with the oracle's quantiser) is not
+    timed; the oracle GEMM is.  Returns (GB/s of NVFP4 weights processed,
+    threads, sample description, seconds)."""
+    import numpy as np
+    import oracle
+    import synth
+    if threads is None:
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    if rows is None:
+        rows = int(os.environ.get("NVFP4_CPU_SAMPLE_ROWS", "1024"))
+    oracle.build()
+    work = []
+    for name, K, N in ROUND_SHAPES:
+        W = synth.weights(0, synth.stream_id(0, name), rows, K)
+        codes, scales, t = oracle.quantize(W)
+        act = synth.activations(0, synth.stream_id(0, name), lanes, K)
+        work.append((K, codes, scales, t, act))
+    t0 = time.perf_counter()
+    nbytes = 0
+    for K, codes, scales, t, act in work:
+        oracle.gemm(act, codes, scales, t, threads=threads)
+        nbytes += weight_bytes(K, rows)
+    dt = time.perf_counter() - t0
+    desc = ("oracle GEMM (fp64, exact dequantisation) on the first %d output columns of each "
+            "of layer 0's qkv/o/gate_up/down matrices, M=%d lanes; %d weight bytes in %.2f s"
+            % (rows, lanes, nbytes, dt))
+    return nbytes / dt / 1e9, threads, desc, dt
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=LAYERS)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quiet", action="store_true")
+    args = ap.parse_args()
+
+    def log(msg):
+        if not args.quiet:
+            print(msg, file=sys.stderr, flush=True)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the decode round "
+              "of one card); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import nvfp4_weight_streaming_amd as nv
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    nv.lib()
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()  # default priority
+    log("building the round (%d layers) ..." % args.layers)
+    with torch.cuda.stream(stream):
+        specs, keep = build_round(nv, layers=args.layers, log=log)
+        ws_bytes = nv.nvfp4_round_workspace_bytes(specs, 8)
+        ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+        plan = nv.nvfp4_round_create(specs, 8, ws, ws_bytes, stream)
+    torch.cuda.synchronize()
+    nodes = nv.nvfp4_round_graph_nodes(plan, 8)
+    log("round graph: %d kernel nodes per width" % nodes)
+
+    def time_round(M, steps, warmup):
+        for _ in range(warmup):
+            nv.nvfp4_round_run(plan, M, stream)
+        stream.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            nv.nvfp4_round_run(plan, M, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps  # ms per round
+
+    # Headline: M = 8 lanes.
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    ms8 = time_round(8, args.steps, args.warmup)
+    wall = time.perf_counter() - t_wall0
+    bytes8 = round_bytes(8, args.layers)
+    gbs8 = bytes8 / (ms8 * 1e-3) / 1e9
+    log("M=8: %.3f ms per round, %.1f GB/s (%.1f%% of 8 TB/s)" % (ms8, gbs8, 100 * gbs8 / HBM_PEAK_GBS))
+
+    sweep = {}
+    for M in range(1, 9):
+        ms = ms8 if M == 8 else time_round(M, max(5, args.steps // 2), 2)
+        gbs = round_bytes(M, args.layers) / (ms * 1e-3) / 1e9
+        sweep[str(M)] = {"round_ms": round(ms, 4), "GB_s": round(gbs, 1),
+                         "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        log("M=%d: %.3f ms, %.1f GB/s" % (M, ms, gbs))
+
+    # Roofline of the decode kernel: the same matrices launched one at a time
+    # with HIP events around each launch, on the stream they run on.
+    plans = {}
+    for _, K, N in ROUND_SHAPES:
+        plans[(K, N)] = nv.Gemm(8, K, N, nv.OUT_BF16)
+    dur, nbytes = [], []
+    reps = 2
+    with torch.cuda.stream(stream):
+        for r in range(reps + 1):
+            evs = []
+            for s in specs:
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                g = plans[(s["K"], s["N"])]
+                nv.nvfp4_gemm_run(g.plan, 8, s["K"], s["N"], s["codes"], s["scales"],
+                                  s["tensor_scale"], s["act"], s["out"], g.workspace, stream)
+                b.record(stream)
+                evs.append((a, b, s))
+            torch.cuda.synchronize()
+            if r == 0:
+                continue  # warm-up pass
+            for a, b, s in evs:
+                dur.append(a.elapsed_time(b) * 1e-3)
+                nbytes.append(weight_bytes(s["K"], s["N"]) + 8 * s["K"] * 2 + 8 * s["N"] * 2)
+    avg_dur = sum(dur) / len(dur)
+    avg_bytes = sum(nbytes) / len(nbytes)
+    achieved = avg_bytes / avg_dur / 1e9
+    log("decode kernel: %.2f us average launch, %.0f bytes average, %.1f GB/s"
+        % (avg_dur * 1e6, avg_bytes, achieved))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        v, thr, desc, dt = cpu_baseline()
+        cpu = {"value": round(v, 5), "unit": "GB/s", "cores": thr, "kind": "oracle",
+               "sample": desc}
+        log("cpu baseline: %.4f GB/s on %d threads (%.1f s)" % (v, thr, dt))
+
+    nv.nvfp4_round_destroy(plan)
+    line = {
+        "metric": METRIC,
+        "value": round(gbs8, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms8, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "27B-class dense decode round: %d layers x {qkv 5120x7168, o 6144x5120, "
+                        "gate_up 5120x34816, down 17408x5120} (K x N), NVFP4 weights "
+                        "(E2M1 + E4M3 per 16 + fp32 per tensor), bf16 activations and outputs, "
+                        "one hipGraph replay per round" % args.layers,
+            "lanes": 8,
+            "round_weight_bytes": sum(weight_bytes(K, N) for _, K, N in ROUND_SHAPES) * args.layers,
+            "round_bytes_m8": bytes8,
+            "graph_kernel_nodes": nodes,
+            "parallelism": "single GPU",
+        },
+        "frac_hbm_peak": round(gbs8 / HBM_PEAK_GBS, 4),
+        "round_sweep": sweep,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "nvfp4::decode_kernel<4, true> (bf16 out), M=8, the round's matrices",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "avg_launch_us": round(avg_dur * 1e6, 3),
+            "avg_algorithmic_bytes": round(avg_bytes),
+            "traffic": None,
+        },
+        "cpu_baseline": cpu,
+        "timed_wall_s": round(wall, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -73,7 +73,7 @@ int nvfp4_version(void);
 /* ---- packed layout ----------------------------------------------------------- */
 
 /* Bytes of the packed code / scale planes for a K x N weight matrix.  They
- * include padding of K to a multiple of 128 and of N to a multiple of 16
+ * include padding of K to a multiple of 512 and of N to a multiple of 16
  * (padding is zero codes and zero scales).  Return 0 for invalid K or N
  * (K % 16 != 0, K < 16, N < 1). */
 size_t nvfp4_packed_code_bytes(int K, int N);
@@ -112,15 +112,20 @@ typedef struct nvfp4_gemm_plan* nvfp4_gemm;
  * "choose automatically". */
 typedef struct nvfp4_gemm_config {
     int split_k;      /* decode: number of K slices (workgroups per column group) */
-    int waves;        /* decode: waves per workgroup (column tiles of 16 per workgroup) */
-    int reserved[6];
+    int waves;        /* decode: waves per workgroup (column tiles of 16), 4 or 8 */
+    int chunks;       /* decode: K values per slice in units of 512, 1..4 (when
+                         split_k is 0) */
+    int reserved[5];
 } nvfp4_gemm_config;
 
 /* Create a plan for GEMMs of shape (M <= max_M) x K x N with the given output
  * dtype.  Validates K % 16 == 0, K >= 16, N >= 1, max_M >= 1, out_dtype.
  * *workspace_bytes receives the device workspace every run of this plan
  * needs (may be 0).  The workspace must be zero-filled before its first use
- * (nvfp4_workspace_clear or any zero fill); every run leaves it zeroed again.
+ * (nvfp4_workspace_clear or any zero fill); every run leaves its counter
+ * region zeroed again.  A workspace belongs to one plan: runs of different
+ * plans (or overlapping runs of one plan on different streams) must not share
+ * it -- a round plan lays out one workspace for all of its matrices itself.
  * No device memory is allocated. */
 int nvfp4_gemm_create(nvfp4_gemm* plan, int max_M, int K, int N, int out_dtype,
                       size_t* workspace_bytes);

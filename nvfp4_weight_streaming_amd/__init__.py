@@ -46,8 +46,8 @@ _STATUS = {OK: "ok", EINVAL: "EINVAL", EUNSUPPORTED: "EUNSUPPORTED", EHIP: "EHIP
 
 
 class GemmConfig(ctypes.Structure):
-    _fields_ = [("split_k", ctypes.c_int), ("waves", ctypes.c_int),
-                ("reserved", ctypes.c_int * 6)]
+    _fields_ = [("split_k", ctypes.c_int), ("waves", ctypes.c_int), ("chunks", ctypes.c_int),
+                ("reserved", ctypes.c_int * 5)]
 
 
 class Layer(ctypes.Structure):
@@ -159,12 +159,12 @@ def nvfp4_quantize(w, K, N, codes, scales, tensor_scale, workspace, stream=None)
                                 _ptr(workspace), _stream(stream)))
 
 
-def nvfp4_gemm_create(max_M, K, N, out_dtype, split_k=0, waves=0):
+def nvfp4_gemm_create(max_M, K, N, out_dtype, split_k=0, waves=0, chunks=0):
     """Returns (plan handle, workspace bytes)."""
     h = ctypes.c_void_p()
     ws = ctypes.c_size_t()
-    if split_k or waves:
-        cfg = GemmConfig(split_k, waves)
+    if split_k or waves or chunks:
+        cfg = GemmConfig(split_k, waves, chunks)
         _check(lib().nvfp4_gemm_create_ex(ctypes.byref(h), max_M, K, N, out_dtype,
                                           ctypes.byref(cfg), ctypes.byref(ws)))
     else:
@@ -271,9 +271,11 @@ class PackedWeight:
 class Gemm:
     """A plan plus its workspace: ``Gemm(max_M, K, N, out_dtype)(w, act, out)``."""
 
-    def __init__(self, max_M, K, N, out_dtype=OUT_BF16, split_k=0, waves=0, device="cuda"):
+    def __init__(self, max_M, K, N, out_dtype=OUT_BF16, split_k=0, waves=0, chunks=0,
+                 device="cuda"):
         import torch
-        self.plan, self.ws_bytes = nvfp4_gemm_create(max_M, K, N, out_dtype, split_k, waves)
+        self.plan, self.ws_bytes = nvfp4_gemm_create(max_M, K, N, out_dtype, split_k, waves,
+                                                     chunks)
         self.K, self.N, self.max_M, self.out_dtype = K, N, max_M, out_dtype
         self.workspace = None
         if self.ws_bytes:

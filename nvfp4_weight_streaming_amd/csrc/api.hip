@@ -83,9 +83,10 @@ int validate_run(const nvfp4_gemm_plan* p, int M, int K, int N, const void* code
 }
 
 int run_gemm(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
-             float ts, const uint16_t* act, void* out, void* ws, hipStream_t s) {
+             float ts, const uint16_t* act, void* out, void* ws, size_t partial_off,
+             hipStream_t s) {
     if (M <= NVFP4_DECODE_MAX_M || !p->pre.enabled)
-        return launch_decode(p, M, codes, scales, ts, act, out, ws, s);
+        return launch_decode(p, M, codes, scales, ts, act, out, ws, partial_off, s);
     return launch_prefill(p, M, codes, scales, ts, act, out, ws, s);
 }
 
@@ -170,7 +171,7 @@ int nvfp4_gemm_run(nvfp4_gemm plan, int M, int K, int N, const uint8_t* codes_de
     int st = validate_run(plan, M, K, N, codes_dev, scales_dev, act_dev, out_dev, workspace_dev);
     if (st != NVFP4_OK) return st;
     return run_gemm(plan, M, codes_dev, scales_dev, tensor_scale, act_dev, out_dev,
-                    workspace_dev, (hipStream_t)stream);
+                    workspace_dev, plan->dec.counter_bytes, (hipStream_t)stream);
 }
 
 int nvfp4_workspace_clear(void* workspace_dev, size_t bytes, void* stream) {

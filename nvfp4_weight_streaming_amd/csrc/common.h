@@ -42,13 +42,16 @@ int hip_fail(hipError_t e, const char* what);
 // ---- plans ---------------------------------------------------------------------
 struct DecodeConfig {
     int waves;          // column tiles (waves) per workgroup
+    int chunks;         // superblocks of 512 k per K slice (loaded up front per wave)
     int splits;         // K slices
-    int sb_per_split;   // superblocks per K slice
     int n_groups;       // column groups of `waves` tiles
     int grid;           // workgroups launched (n_groups padded to 8, times splits)
-    size_t ws_bytes;    // partial sums + counters
-    size_t counter_off; // byte offset of the counters in the workspace
-    int lds_bytes;
+    // Workspace layout: [counters: counter_bytes][partial sums: partial_bytes].
+    // Counters come first so that, when several plans share one workspace (a
+    // round), no plan's partial sums ever overlap any plan's counters.
+    size_t counter_bytes;
+    size_t partial_bytes;
+    size_t ws_bytes;    // counter_bytes + partial_bytes
 };
 
 struct PrefillConfig {
@@ -75,8 +78,11 @@ int make_decode_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, De
 int make_prefill_config(int max_M, int K, int N, PrefillConfig* out);
 
 // Launchers (no validation: callers validated).  Return NVFP4_OK or EHIP.
+// ws: the workspace; partial_off: byte offset of the partial sums in it (the
+// plan's own counter_bytes, or a larger value shared by the plans of a round).
 int launch_decode(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
-                  float ts, const uint16_t* act, void* out, void* ws, hipStream_t s);
+                  float ts, const uint16_t* act, void* out, void* ws, size_t partial_off,
+                  hipStream_t s);
 int launch_prefill(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
                    float ts, const uint16_t* act, void* out, void* ws, hipStream_t s);
 int launch_fill_zero(void* p, size_t bytes, hipStream_t s);
@@ -85,5 +91,6 @@ int launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 int validate_run(const nvfp4_gemm_plan* p, int M, int K, int N, const void* codes,
                  const void* scales, const void* act, const void* out, const void* ws);
 int run_gemm(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
-             float ts, const uint16_t* act, void* out, void* ws, hipStream_t s);
+             float ts, const uint16_t* act, void* out, void* ws, size_t partial_off,
+             hipStream_t s);
 }  // namespace nvfp4

@@ -36,7 +36,7 @@ typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 constexpr int kLdsPad = 8;         // bf16 elements of padding per LDS row
-constexpr int kMaxSlice = 5 * kSuperK;  // largest K slice one workgroup stages
+constexpr int kMaxChunks = 4;  // superblocks of 512 k per wave (all loaded up front)
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
     uint32_t u = __float_as_uint(x);
@@ -111,120 +111,144 @@ __device__ __forceinline__ void chunk_steps(float (&acc)[4], const Chunk& x, con
     kb_steps(acc, x.c[3], x.s.w, a + 384);
 }
 
-template <int WAVES, bool BF16>
+// One workgroup = WAVES column tiles (one per wave) x one K slice of up to
+// NCH superblocks.  Every load a wave will need is issued before it computes
+// anything: first its share of the activation slice, then all of its weight
+// chunks; the activations are written to LDS as soon as they land (in-order
+// completion counting lets the weights stay in flight), and the MFMA work on
+// chunk c waits only for chunk c.
+template <int WAVES, int NCH, bool BF16>
 __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
     const uint4* __restrict__ codes, const uint4* __restrict__ scales,
     const uint16_t* __restrict__ act, void* __restrict__ out, float* __restrict__ partial,
-    unsigned int* __restrict__ counters, float ts, int M, int K, int N, int nsb,
-    int sb_per_split, int splits, int n_groups, int n_tiles) {
-    extern __shared__ uint4 lds_raw[];
-    __shared__ int s_last;
+    unsigned int* __restrict__ counters, float ts, int M, int K, int N, int nsb, int splits,
+    int n_groups, int n_tiles) {
+    constexpr int kThreads = WAVES * 64;
+    constexpr int kStride = NCH * kSuperK + kLdsPad;          // LDS row, bf16 elements
+    constexpr int kVecs = 9 * NCH * (kSuperK / 8);            // 8 rows + zero row, 16 B each
+    constexpr int kVecPerThread = (kVecs + kThreads - 1) / kThreads;
     constexpr int kCols = WAVES * kTileN;
+    __shared__ __attribute__((aligned(16))) __bf16 lds[9 * kStride];
+    __shared__ int s_last;
 
     const int b = blockIdx.x;
     const int xcd = b & 7, q = b >> 3;
     const int ng = (q / splits) * 8 + xcd;
     const int split = q - (q / splits) * splits;
     if (ng >= n_groups) return;  // whole workgroup: padding of the column groups to 8
-    const int sb0 = split * sb_per_split;
-    const int sb1 = min(sb0 + sb_per_split, nsb);
-    const int klen = (sb1 - sb0) * kSuperK;
-    const int stride = klen + kLdsPad;
+    const int sb0 = split * NCH;
+    const int nch = min(NCH, nsb - sb0);  // superblocks in this slice (>= 1)
     const int k0 = sb0 * kSuperK;
-    __bf16* lds = (__bf16*)lds_raw;  // rows 0..M-1: activations; row M: zeros
+    const int row_vecs = nch * (kSuperK / 8);
 
+    // 1. This thread's share of the activation slice (rows 0..7 and the zero
+    //    row 8).  Loads are unconditional with clamped addresses; rows >= M,
+    //    k >= K and the zero row are replaced by zeros when stored.
+    uint4 av[kVecPerThread];
+#pragma unroll
+    for (int i = 0; i < kVecPerThread; ++i) {
+        const int idx = threadIdx.x + i * kThreads;
+        const int r = idx / row_vecs, oct = idx - r * row_vecs;
+        const int m = min(r, M - 1);
+        const int k = min(k0 + 8 * oct, K - 8);
+        av[i] = *(const uint4*)(act + (size_t)m * K + k);
+    }
+
+    // 2. All weight chunks of this wave's column tile and K slice.
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int nt = ng * WAVES + wave;
+    const int nt = min(ng * WAVES + wave, n_tiles - 1);
     const int col = lane & 15, g = lane >> 4;
-    const bool active = nt < n_tiles;
-    const uint4* cp = codes + ((size_t)(active ? nt : 0) * nsb + sb0) * 256 + lane;
-    const uint4* sp = scales + ((size_t)(active ? nt : 0) * nsb + sb0) * 32 + col * 2 + (g >> 1);
-    // The first superblock's weights do not depend on the activations: issue
-    // their loads before staging.
-    Chunk A, B;
-    if (active) load_chunk(A, cp, sp);
+    const uint4* cp = codes + ((size_t)nt * nsb + sb0) * 256 + lane;
+    const uint4* sp = scales + ((size_t)nt * nsb + sb0) * 32 + col * 2 + (g >> 1);
+    Chunk w[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int cc = min(c, nch - 1);  // a short slice re-reads its last chunk (cache hit)
+        load_chunk(w[c], cp + 256 * cc, sp + 32 * cc);
+    }
 
-    // Stage this K slice of the activations (and one zero row) in LDS.
-    const int noct = klen / 8;
-    for (int idx = threadIdx.x; idx < (M + 1) * noct; idx += WAVES * 64) {
-        int r = idx / noct, oct = idx - r * noct;
-        int k = k0 + 8 * oct;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (r < M && k < K) v = *(const uint4*)(act + (size_t)r * K + k);
-        *(uint4*)(lds + r * stride + 8 * oct) = v;
+    // 3. Activations to LDS.
+#pragma unroll
+    for (int i = 0; i < kVecPerThread; ++i) {
+        const int idx = threadIdx.x + i * kThreads;
+        const int r = idx / row_vecs, oct = idx - r * row_vecs;
+        if (r < 9) {
+            const int k = k0 + 8 * oct;
+            const bool keep = r < M && k < K;
+            uint4 v = av[i];
+            v.x = keep ? v.x : 0u;
+            v.y = keep ? v.y : 0u;
+            v.z = keep ? v.z : 0u;
+            v.w = keep ? v.w : 0u;
+            *(uint4*)(lds + r * kStride + 8 * oct) = v;
+        }
     }
     __syncthreads();
 
+    // 4. MFMA over the slice.  A-operand row of this lane: activation row
+    //    `col` for its block half (col < 8 pairs with octets 0,1; col >= 8
+    //    with octets 2,3), else the zero row.
+    const int m = col & 7;
+    const bool live = ((col >> 3) == (g >> 1)) && (m < M);
+    const __bf16* ap = lds + (live ? m : 8) * kStride + 8 * g;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    if (active) {
-        // A-operand row of this lane: activation row `col` for its block half
-        // (col < 8 pairs with octets 0,1; col >= 8 with octets 2,3), else zeros.
-        const int m = col & 7;
-        const bool live = ((col >> 3) == (g >> 1)) && (m < M);
-        const __bf16* ap = lds + (live ? m : M) * stride + 8 * g;
-        // Ping-pong over superblocks: the next one's loads are in flight while
-        // this one computes.  The prefetch is unconditional (on the last
-        // superblock it re-reads the current one, which the caches serve) so
-        // the compiler can count outstanding loads exactly.
-        int left = sb1 - sb0;  // superblocks still to compute, A loaded
-        while (true) {
-            int nx = left > 1 ? 1 : 0;
-            load_chunk(B, cp + 256 * nx, sp + 32 * nx);
-            chunk_steps(acc, A, ap);
-            if (--left == 0) break;
-            cp += 256;
-            sp += 32;
-            ap += kSuperK;
-            nx = left > 1 ? 1 : 0;
-            load_chunk(A, cp + 256 * nx, sp + 32 * nx);
-            chunk_steps(acc, B, ap);
-            if (--left == 0) break;
-            cp += 256;
-            sp += 32;
-            ap += kSuperK;
-        }
-    }
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+        if (c < nch) chunk_steps(acc, w[c], ap + c * kSuperK);
+
     // Lanes g and g+2 hold the same (row, column) for the two block halves.
+#pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] += __shfl_xor(acc[j], 32, 64);
+    const bool mine = lane < 32 && ng * WAVES + wave < n_tiles;
 
     if (splits == 1) {
-        if (lane < 32 && nt < n_tiles) {
+        if (mine) {
             const int n = nt * kTileN + col;
+#pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int m = 4 * g + j;
-                if (m < M && n < N) store_out<BF16>(out, (size_t)m * N + n, acc[j] * ts);
+                const int mm = 4 * g + j;
+                if (mm < M && n < N) store_out<BF16>(out, (size_t)mm * N + n, acc[j] * ts);
             }
         }
         return;
     }
 
-    // Split K: publish this slice's partial sums, the last slice reduces.
+    // Split K.  The slices of one column group run on one XCD (blockIdx % 8).
+    // Partial sums are written with agent-coherent (write-through) stores and
+    // read back with agent-coherent loads, so the hand-off needs only the
+    // store-completion wait before the counter increment -- no write-back of
+    // the whole L2, which an agent-scope fence would cost every workgroup.
     float* pbase = partial + (size_t)(ng * splits + split) * 8 * kCols;
-    if (lane < 32 && nt < n_tiles) {
+    if (mine) {
+#pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int m = 4 * g + j;
-            if (m < M) pbase[m * kCols + wave * kTileN + col] = acc[j];
+            const int mm = 4 * g + j;
+            if (mm < M)
+                __hip_atomic_store(pbase + mm * kCols + wave * kTileN + col, acc[j],
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    __threadfence();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0) {
-        unsigned int old = atomicAdd(&counters[ng], 1u);
+        const unsigned int old =
+            __hip_atomic_fetch_add(&counters[ng], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (old == (unsigned int)(splits - 1));
     }
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
     const float* gbase = partial + (size_t)ng * splits * 8 * kCols;
-    for (int idx = threadIdx.x; idx < M * kCols; idx += WAVES * 64) {
-        const int m = idx / kCols, c = idx - m * kCols;
+    for (int idx = threadIdx.x; idx < M * kCols; idx += kThreads) {
+        const int mm = idx / kCols, c = idx - mm * kCols;
         const int n = ng * kCols + c;
         float sum = 0.f;
-        for (int sp = 0; sp < splits; ++sp)
-            sum += __builtin_nontemporal_load(gbase + (size_t)(sp * 8 + m) * kCols + c);
-        if (n < N) store_out<BF16>(out, (size_t)m * N + n, sum * ts);
+        for (int sp2 = 0; sp2 < splits; ++sp2)
+            sum += __hip_atomic_load(gbase + (size_t)(sp2 * 8 + mm) * kCols + c, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+        if (n < N) store_out<BF16>(out, (size_t)mm * N + n, sum * ts);
     }
-    if (threadIdx.x == 0) counters[ng] = 0u;  // leave the workspace zeroed
+    if (threadIdx.x == 0)  // leave the counter zeroed for the next run
+        __hip_atomic_store(&counters[ng], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---- plan ----------------------------------------------------------------------
@@ -232,70 +256,84 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
 int make_decode_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, DecodeConfig* d) {
     (void)max_M;
     int waves = (cfg && cfg->waves) ? cfg->waves : 4;
-    if (waves != 2 && waves != 4 && waves != 8)
-        return set_error(NVFP4_EINVAL, "config.waves: %d is not 2, 4 or 8", waves);
+    if (waves != 4 && waves != 8)
+        return set_error(NVFP4_EINVAL, "config.waves: %d is not 4 or 8", waves);
     const int n_tiles = padded_n(N) / kTileN;
     const int nsb = padded_k(K) / kSuperK;
     const int n_groups = (n_tiles + waves - 1) / waves;
     const int ng8 = round_up(n_groups, 8);
-    const int max_sb = kMaxSlice / kSuperK;
-    int splits;
+    int chunks;
     if (cfg && cfg->split_k) {
         if (cfg->split_k < 1) return set_error(NVFP4_EINVAL, "config.split_k: %d < 1", cfg->split_k);
-        splits = cfg->split_k < nsb ? cfg->split_k : nsb;
+        int sk = cfg->split_k < nsb ? cfg->split_k : nsb;
+        chunks = (nsb + sk - 1) / sk;
+        if (chunks > kMaxChunks)
+            return set_error(NVFP4_EINVAL, "config.split_k: %d leaves %d superblocks of 512 per "
+                             "slice, more than %d", cfg->split_k, chunks, kMaxChunks);
+    } else if (cfg && cfg->chunks) {
+        if (cfg->chunks < 1 || cfg->chunks > kMaxChunks)
+            return set_error(NVFP4_EINVAL, "config.chunks: %d outside [1, %d]", cfg->chunks, kMaxChunks);
+        chunks = cfg->chunks < nsb ? cfg->chunks : nsb;
     } else {
-        // Aim for about four workgroups per CU (256 CUs).
-        splits = (1024 + ng8 - 1) / ng8;
-        if (splits > nsb) splits = nsb;
-        if (splits < 1) splits = 1;
+        // The largest slice (fewest partial sums) that still gives about
+        // 1024 workgroups (four per CU on 256 CUs).
+        chunks = kMaxChunks < nsb ? kMaxChunks : nsb;
+        while (chunks > 1 && (long)ng8 * ((nsb + chunks - 1) / chunks) < 1024) --chunks;
     }
-    int sb_per = (nsb + splits - 1) / splits;
-    if (sb_per > max_sb) sb_per = max_sb;
-    splits = (nsb + sb_per - 1) / sb_per;
+    const int splits = (nsb + chunks - 1) / chunks;
     d->waves = waves;
+    d->chunks = chunks;
     d->splits = splits;
-    d->sb_per_split = sb_per;
     d->n_groups = n_groups;
     d->grid = ng8 * splits;
-    d->lds_bytes = (NVFP4_DECODE_MAX_M + 1) * (sb_per * kSuperK + kLdsPad) * 2;
     if (splits > 1) {
-        size_t part = (size_t)ng8 * splits * 8 * waves * kTileN * sizeof(float);
-        d->counter_off = (part + 255) / 256 * 256;
-        d->ws_bytes = d->counter_off + ((size_t)ng8 * sizeof(unsigned int) + 255) / 256 * 256;
+        d->counter_bytes = ((size_t)ng8 * sizeof(unsigned int) + 255) / 256 * 256;
+        d->partial_bytes = (size_t)ng8 * splits * 8 * waves * kTileN * sizeof(float);
     } else {
-        d->counter_off = 0;
-        d->ws_bytes = 0;
+        d->counter_bytes = 0;
+        d->partial_bytes = 0;
     }
+    d->ws_bytes = d->counter_bytes + d->partial_bytes;
     return NVFP4_OK;
 }
 
-template <int WAVES, bool BF16>
+template <int WAVES, int NCH, bool BF16>
 static int launch_t(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
-                    float ts, const uint16_t* act, void* out, void* ws, hipStream_t s) {
+                    float ts, const uint16_t* act, void* out, void* ws, size_t partial_off,
+                    hipStream_t s) {
     const DecodeConfig& d = p->dec;
-    const int lds = (M + 1) * (d.sb_per_split * kSuperK + kLdsPad) * 2;
-    float* partial = (float*)ws;
-    unsigned int* counters = ws ? (unsigned int*)((char*)ws + d.counter_off) : nullptr;
-    hipLaunchKernelGGL((decode_kernel<WAVES, BF16>), dim3(d.grid), dim3(WAVES * 64), lds, s,
+    unsigned int* counters = (unsigned int*)ws;
+    float* partial = ws ? (float*)((char*)ws + partial_off) : nullptr;
+    hipLaunchKernelGGL((decode_kernel<WAVES, NCH, BF16>), dim3(d.grid), dim3(WAVES * 64), 0, s,
                        (const uint4*)codes, (const uint4*)scales, act, out, partial, counters, ts,
-                       M, p->K, p->N, p->Kp / kSuperK, d.sb_per_split, d.splits, d.n_groups,
-                       p->Np / kTileN);
+                       M, p->K, p->N, p->Kp / kSuperK, d.splits, d.n_groups, p->Np / kTileN);
     NVFP4_HIP(hipGetLastError());
     return NVFP4_OK;
 }
 
-template <bool BF16>
-static int launch_w(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
-                    float ts, const uint16_t* act, void* out, void* ws, hipStream_t s) {
-    switch (p->dec.waves) {
-        case 2: return launch_t<2, BF16>(p, M, codes, scales, ts, act, out, ws, s);
-        case 4: return launch_t<4, BF16>(p, M, codes, scales, ts, act, out, ws, s);
-        default: return launch_t<8, BF16>(p, M, codes, scales, ts, act, out, ws, s);
+template <int WAVES, bool BF16>
+static int launch_c(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
+                    float ts, const uint16_t* act, void* out, void* ws, size_t po,
+                    hipStream_t s) {
+    switch (p->dec.chunks) {
+        case 1: return launch_t<WAVES, 1, BF16>(p, M, codes, scales, ts, act, out, ws, po, s);
+        case 2: return launch_t<WAVES, 2, BF16>(p, M, codes, scales, ts, act, out, ws, po, s);
+        case 3: return launch_t<WAVES, 3, BF16>(p, M, codes, scales, ts, act, out, ws, po, s);
+        default: return launch_t<WAVES, 4, BF16>(p, M, codes, scales, ts, act, out, ws, po, s);
     }
 }
 
+template <bool BF16>
+static int launch_w(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
+                    float ts, const uint16_t* act, void* out, void* ws, size_t po,
+                    hipStream_t s) {
+    if (p->dec.waves == 8) return launch_c<8, BF16>(p, M, codes, scales, ts, act, out, ws, po, s);
+    return launch_c<4, BF16>(p, M, codes, scales, ts, act, out, ws, po, s);
+}
+
 int launch_decode(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
-                  float ts, const uint16_t* act, void* out, void* ws, hipStream_t s) {
+                  float ts, const uint16_t* act, void* out, void* ws, size_t partial_off,
+                  hipStream_t s) {
     const size_t esz = p->out_dtype == NVFP4_OUT_BF16 ? 2 : 4;
     // Rows beyond 8 (when no prefill kernel applies) run as further weight passes.
     for (int m0 = 0; m0 < M; m0 += NVFP4_DECODE_MAX_M) {
@@ -303,8 +341,8 @@ int launch_decode(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const u
         const uint16_t* a = act + (size_t)m0 * p->K;
         void* o = (char*)out + (size_t)m0 * p->N * esz;
         int st = p->out_dtype == NVFP4_OUT_BF16
-                     ? launch_w<true>(p, mm, codes, scales, ts, a, o, ws, s)
-                     : launch_w<false>(p, mm, codes, scales, ts, a, o, ws, s);
+                     ? launch_w<true>(p, mm, codes, scales, ts, a, o, ws, partial_off, s)
+                     : launch_w<false>(p, mm, codes, scales, ts, a, o, ws, partial_off, s);
         if (st) return st;
     }
     return NVFP4_OK;

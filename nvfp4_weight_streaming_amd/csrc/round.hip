@@ -18,6 +18,7 @@ struct nvfp4_round_plan {
     std::vector<nvfp4_gemm_plan*> plans;
     void* ws;
     size_t ws_bytes;
+    size_t partial_off;  // shared offset of the partial sums (after every plan's counters)
     hipGraph_t graph[NVFP4_DECODE_MAX_M];
     hipGraphExec_t exec[NVFP4_DECODE_MAX_M];
     int nodes[NVFP4_DECODE_MAX_M];
@@ -61,22 +62,35 @@ using namespace nvfp4;
 
 extern "C" {
 
+// Workspace of a round: one counter region at the start, sized for the plan
+// with the most counters, then one partial-sum region sized for the largest.
+static int round_layout(const nvfp4_layer* layers, int n_layers, int max_M, size_t* counters,
+                        size_t* partials) {
+    size_t mc = 0, mp = 0;
+    for (int i = 0; i < n_layers; ++i) {
+        nvfp4_gemm p;
+        size_t b = 0;
+        int st = nvfp4_gemm_create(&p, max_M, layers[i].K, layers[i].N, layers[i].out_dtype, &b);
+        if (st) return st;
+        if (p->dec.counter_bytes > mc) mc = p->dec.counter_bytes;
+        if (p->dec.partial_bytes > mp) mp = p->dec.partial_bytes;
+        nvfp4_gemm_destroy(p);
+    }
+    *counters = mc;
+    *partials = mp;
+    return NVFP4_OK;
+}
+
 int nvfp4_round_workspace_bytes(const nvfp4_layer* layers, int n_layers, int max_M,
                                 size_t* workspace_bytes) {
     clear_error();
     int st = validate_layers(layers, n_layers, max_M);
     if (st) return st;
     if (!workspace_bytes) return set_error(NVFP4_EINVAL, "workspace_bytes: NULL");
-    size_t mx = 0;
-    for (int i = 0; i < n_layers; ++i) {
-        nvfp4_gemm p;
-        size_t b = 0;
-        st = nvfp4_gemm_create(&p, max_M, layers[i].K, layers[i].N, layers[i].out_dtype, &b);
-        if (st) return st;
-        nvfp4_gemm_destroy(p);
-        if (b > mx) mx = b;
-    }
-    *workspace_bytes = mx;
+    size_t c = 0, p = 0;
+    st = round_layout(layers, n_layers, max_M, &c, &p);
+    if (st) return st;
+    *workspace_bytes = c + p;
     return NVFP4_OK;
 }
 
@@ -87,9 +101,10 @@ int nvfp4_round_create(nvfp4_round* plan, const nvfp4_layer* layers, int n_layer
     *plan = nullptr;
     int st = validate_layers(layers, n_layers, max_M);
     if (st) return st;
-    size_t need = 0;
-    st = nvfp4_round_workspace_bytes(layers, n_layers, max_M, &need);
+    size_t need_c = 0, need_p = 0;
+    st = round_layout(layers, n_layers, max_M, &need_c, &need_p);
     if (st) return st;
+    const size_t need = need_c + need_p;
     if (workspace_bytes < need)
         return set_error(NVFP4_EINVAL, "workspace_bytes: %zu < %zu needed", workspace_bytes, need);
     if (need && !workspace) return set_error(NVFP4_EINVAL, "workspace: NULL");
@@ -102,6 +117,7 @@ int nvfp4_round_create(nvfp4_round* plan, const nvfp4_layer* layers, int n_layer
     r->layers.assign(layers, layers + n_layers);
     r->ws = workspace;
     r->ws_bytes = workspace_bytes;
+    r->partial_off = need_c;
     for (int i = 0; i < n_layers; ++i) {
         nvfp4_gemm p = nullptr;
         size_t b = 0;
@@ -138,7 +154,7 @@ int nvfp4_round_create(nvfp4_round* plan, const nvfp4_layer* layers, int n_layer
         for (int i = 0; i < n_layers && !lst; ++i) {
             const nvfp4_layer& l = r->layers[i];
             lst = run_gemm(r->plans[i], M, l.codes_dev, l.scales_dev, l.tensor_scale, l.act_dev,
-                           l.out_dev, workspace, cap);
+                           l.out_dev, workspace, r->partial_off, cap);
         }
         hipGraph_t g = nullptr;
         e = hipStreamEndCapture(cap, &g);

@@ -88,11 +88,18 @@ def test_gemm_config_validation(nv):
     plan, ws = nv.nvfp4_gemm_create(8, 5120, 5120, 1, split_k=5, waves=8)
     assert ws > 0
     nv.nvfp4_gemm_destroy(plan)
-    plan, ws = nv.nvfp4_gemm_create(8, 2560, 5120, 1, split_k=1, waves=4)
+    plan, ws = nv.nvfp4_gemm_create(8, 2048, 5120, 1, split_k=1, waves=4)
     assert ws == 0  # no K split: no partials, no counters
     nv.nvfp4_gemm_destroy(plan)
-    # one workgroup stages at most 5 x 512 values of K, so K = 5120 needs 2 slices
-    plan, ws = nv.nvfp4_gemm_create(8, 5120, 5120, 1, split_k=1, waves=4)
+    # a workgroup holds at most 4 x 512 values of K, so K = 5120 needs 3 slices
+    with pytest.raises(nv.Nvfp4Error) as e:
+        nv.nvfp4_gemm_create(8, 5120, 5120, 1, split_k=1)
+    assert e.value.message.startswith("config.split_k")
+    for bad in (0 - 1, 5):
+        with pytest.raises(nv.Nvfp4Error) as e:
+            nv.nvfp4_gemm_create(8, 5120, 5120, 1, chunks=bad)
+        assert e.value.message.startswith("config.chunks")
+    plan, ws = nv.nvfp4_gemm_create(8, 5120, 5120, 1, chunks=4)
     assert ws > 0
     nv.nvfp4_gemm_destroy(plan)
 

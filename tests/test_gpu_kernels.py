@@ -201,22 +201,34 @@ def test_projection_5120_full(nv, M):
     check(out32, y, S, bf16=False, what="projection f32 M=%d" % M)
 
 
-@pytest.mark.parametrize("split_k,waves", [(1, 4), (2, 2), (3, 8), (7, 4), (12, 2), (12, 8)])
-def test_split_configurations_agree_and_are_deterministic(nv, split_k, waves):
+@pytest.mark.parametrize("chunks", [1, 2, 3, 4])
+@pytest.mark.parametrize("waves", [4, 8])
+def test_split_configurations_agree_and_are_deterministic(nv, chunks, waves):
     M, K, N = 8, 6144, 1000
     codes, scales = synth.random_planes(8, 8, N, K)
     t = 3.0e-4
     act = synth.activations(8, 8, M, K)
     pw = pack(nv, dev(codes), dev(scales), K, N, t)
     y, S = oracle.gemm(act, codes, scales, t)
-    out1, g = run(nv, pw, dev_bf16(act), nv.OUT_F32, split_k=split_k, waves=waves)
-    check(out1, y, S, bf16=False, what="split %d waves %d" % (split_k, waves))
+    out1, g = run(nv, pw, dev_bf16(act), nv.OUT_F32, chunks=chunks, waves=waves)
+    check(out1, y, S, bf16=False, what="chunks %d waves %d" % (chunks, waves))
     import torch
     out2 = torch.full_like(out1, float("nan"))
     for _ in range(3):  # the workspace counters must reset themselves
         g(pw, dev_bf16(act), out2)
     torch.cuda.synchronize()
     assert np.array_equal(host(out1).view(np.uint32), host(out2).view(np.uint32))
+
+
+@pytest.mark.parametrize("M,K,N", [(8, 1536, 4096), (3, 2048, 64), (8, 17408, 40)])
+def test_single_slice_and_long_k(nv, M, K, N):
+    """No K split (K <= 2048: one slice per column group) and the longest K."""
+    codes, scales = synth.random_planes(M, K, N, K)
+    act = synth.activations(M, K, M, K)
+    pw = pack(nv, dev(codes), dev(scales), K, N, 0.002)
+    out, _ = run(nv, pw, dev_bf16(act), nv.OUT_F32)
+    y, S = oracle.gemm(act, codes, scales, 0.002)
+    check(out, y, S, bf16=False, what="%r" % ((M, K, N),))
 
 
 @pytest.mark.parametrize("M", [9, 20])
