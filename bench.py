@@ -8,9 +8,9 @@ headline runs M = 8 lanes; the same run also times widths 1..8.
 Prints one JSON line (rank 0):
   value        = algorithmic bytes of the round (NVFP4 weights + bf16
                  activations in + bf16 outputs) / device time per round, GB/s
-  roofline     = the decode kernel's achieved GB/s per launch (HIP events
-                 around individual launches of the same matrices) against the
-                 MI355X HBM peak of 8 TB/s
+  roofline     = the decode kernel: average algorithmic bytes per launch over
+                 the round's matrices / average launch duration (HIP events
+                 around each launch) against the MI355X HBM peak of 8 TB/s
   cpu_baseline = the CPU oracle timed on the host's cores on a bounded sample
                  of the same workload (see cpu_baseline() below)
 
@@ -130,6 +130,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=LAYERS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="also run one plain 1 GiB device copy (for scaling memory counters)")
     ap.add_argument("--quiet", action="store_true")
     args = ap.parse_args()
 
@@ -150,76 +152,108 @@ def main():
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()  # default priority
     log("building the round (%d layers) ..." % args.layers)
+    plans, wss = {}, []
     with torch.cuda.stream(stream):
         specs, keep = build_round(nv, layers=args.layers, log=log)
-        ws_bytes = nv.nvfp4_round_workspace_bytes(specs, 8)
-        ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
-        plan = nv.nvfp4_round_create(specs, 8, ws, ws_bytes, stream)
+        for mode in (nv.ROUND_PERSISTENT, nv.ROUND_PER_MATRIX):
+            ws_bytes = nv.nvfp4_round_workspace_bytes(specs, 8, mode=mode)
+            ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+            wss.append(ws)
+            plans[mode] = nv.nvfp4_round_create(specs, 8, ws, ws_bytes, stream, mode=mode)
     torch.cuda.synchronize()
-    nodes = nv.nvfp4_round_graph_nodes(plan, 8)
-    log("round graph: %d kernel nodes per width" % nodes)
+    nodes = {m: nv.nvfp4_round_graph_nodes(p, 8) for m, p in plans.items()}
+    log("round graphs: persistent %d node(s), per-matrix %d nodes per width"
+        % (nodes[nv.ROUND_PERSISTENT], nodes[nv.ROUND_PER_MATRIX]))
 
-    def time_round(M, steps, warmup):
+    def time_round(plan, M, steps, warmup):
+        """Mean device time per replay (ms): one HIP event pair around each
+        replay, all on the stream the graph runs on."""
         for _ in range(warmup):
             nv.nvfp4_round_run(plan, M, stream)
         stream.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
+        evs = []
         for _ in range(steps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
             nv.nvfp4_round_run(plan, M, stream)
-        e1.record(stream)
+            b.record(stream)
+            evs.append((a, b))
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps  # ms per round
+        return sum(a.elapsed_time(b) for a, b in evs) / steps
 
-    # Headline: M = 8 lanes.
+    headline = plans[nv.ROUND_PER_MATRIX]
+    persistent = plans[nv.ROUND_PERSISTENT]
+    # Headline: M = 8 lanes, the default round (one graph of per-matrix decode
+    # kernels).  The timed region is the K replays bracketed by device
+    # synchronisation.
+    for _ in range(args.warmup):
+        nv.nvfp4_round_run(headline, 8, stream)
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
-    ms8 = time_round(8, args.steps, args.warmup)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        nv.nvfp4_round_run(headline, 8, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
+    ms8 = e0.elapsed_time(e1) / args.steps
     bytes8 = round_bytes(8, args.layers)
     gbs8 = bytes8 / (ms8 * 1e-3) / 1e9
-    log("M=8: %.3f ms per round, %.1f GB/s (%.1f%% of 8 TB/s)" % (ms8, gbs8, 100 * gbs8 / HBM_PEAK_GBS))
+    log("M=8 round: %.3f ms, %.1f GB/s (%.1f%% of 8 TB/s)" % (ms8, gbs8, 100 * gbs8 / HBM_PEAK_GBS))
 
-    sweep = {}
+    sweep, sweep_ps = {}, {}
     for M in range(1, 9):
-        ms = ms8 if M == 8 else time_round(M, max(5, args.steps // 2), 2)
-        gbs = round_bytes(M, args.layers) / (ms * 1e-3) / 1e9
-        sweep[str(M)] = {"round_ms": round(ms, 4), "GB_s": round(gbs, 1),
-                         "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
-        log("M=%d: %.3f ms, %.1f GB/s" % (M, ms, gbs))
+        for mode, tab in ((nv.ROUND_PER_MATRIX, sweep), (nv.ROUND_PERSISTENT, sweep_ps)):
+            ms = time_round(plans[mode], M, max(5, args.steps // 2), 2)
+            gbs = round_bytes(M, args.layers) / (ms * 1e-3) / 1e9
+            tab[str(M)] = {"round_ms": round(ms, 4), "GB_s": round(gbs, 1),
+                           "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        log("M=%d: per-matrix graph %.3f ms (%.1f GB/s), persistent %.3f ms"
+            % (M, sweep[str(M)]["round_ms"], sweep[str(M)]["GB_s"], sweep_ps[str(M)]["round_ms"]))
+    flags = nv.nvfp4_round_status(persistent)
+    assert flags == 0, "persistent round wait timed out (flags %d)" % flags
 
-    # Roofline of the decode kernel: the same matrices launched one at a time
-    # with HIP events around each launch, on the stream they run on.
-    plans = {}
+    # Roofline of the dominant kernel, the decode kernel (one launch per
+    # matrix): the same matrices launched one at a time with HIP events around
+    # each launch, on the stream they run on.
+    gplans = {}
     for _, K, N in ROUND_SHAPES:
-        plans[(K, N)] = nv.Gemm(8, K, N, nv.OUT_BF16)
+        gplans[(K, N)] = nv.Gemm(8, K, N, nv.OUT_BF16)
     dur, nbytes = [], []
-    reps = 2
     with torch.cuda.stream(stream):
-        for r in range(reps + 1):
+        for r in range(3):
             evs = []
-            for s in specs:
+            for sp in specs:
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)
                 a.record(stream)
-                g = plans[(s["K"], s["N"])]
-                nv.nvfp4_gemm_run(g.plan, 8, s["K"], s["N"], s["codes"], s["scales"],
-                                  s["tensor_scale"], s["act"], s["out"], g.workspace, stream)
+                g = gplans[(sp["K"], sp["N"])]
+                nv.nvfp4_gemm_run(g.plan, 8, sp["K"], sp["N"], sp["codes"], sp["scales"],
+                                  sp["tensor_scale"], sp["act"], sp["out"], g.workspace, stream)
                 b.record(stream)
-                evs.append((a, b, s))
+                evs.append((a, b, sp))
             torch.cuda.synchronize()
             if r == 0:
                 continue  # warm-up pass
-            for a, b, s in evs:
+            for a, b, sp in evs:
                 dur.append(a.elapsed_time(b) * 1e-3)
-                nbytes.append(weight_bytes(s["K"], s["N"]) + 8 * s["K"] * 2 + 8 * s["N"] * 2)
-    avg_dur = sum(dur) / len(dur)
+                nbytes.append(weight_bytes(sp["K"], sp["N"]) + 8 * sp["K"] * 2 + 8 * sp["N"] * 2)
+    dk_us = sum(dur) / len(dur) * 1e6
     avg_bytes = sum(nbytes) / len(nbytes)
-    achieved = avg_bytes / avg_dur / 1e9
+    achieved = avg_bytes / (dk_us * 1e-6) / 1e9
     log("decode kernel: %.2f us average launch, %.0f bytes average, %.1f GB/s"
-        % (avg_dur * 1e6, avg_bytes, achieved))
+        % (dk_us, avg_bytes, achieved))
+
+    if args.calibration_copy:
+        # A plain copy kernel of known size: 1 GiB read, 1 GiB written.
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -228,7 +262,8 @@ def main():
                "sample": desc}
         log("cpu baseline: %.4f GB/s on %d threads (%.1f s)" % (v, thr, dt))
 
-    nv.nvfp4_round_destroy(plan)
+    for p in plans.values():
+        nv.nvfp4_round_destroy(p)
     line = {
         "metric": METRIC,
         "value": round(gbs8, 2),
@@ -246,24 +281,28 @@ def main():
             "workload": "27B-class dense decode round: %d layers x {qkv 5120x7168, o 6144x5120, "
                         "gate_up 5120x34816, down 17408x5120} (K x N), NVFP4 weights "
                         "(E2M1 + E4M3 per 16 + fp32 per tensor), bf16 activations and outputs, "
-                        "one hipGraph replay per round" % args.layers,
+                        "M=8 lanes, one hipGraph replay per round (one decode kernel per matrix)"
+                        % args.layers,
             "lanes": 8,
             "round_weight_bytes": sum(weight_bytes(K, N) for _, K, N in ROUND_SHAPES) * args.layers,
             "round_bytes_m8": bytes8,
-            "graph_kernel_nodes": nodes,
+            "graph_kernel_nodes": nodes[nv.ROUND_PER_MATRIX],
             "parallelism": "single GPU",
         },
         "frac_hbm_peak": round(gbs8 / HBM_PEAK_GBS, 4),
+        "round_ms_m1_to_m8": {k: v["round_ms"] for k, v in sweep.items()},
         "round_sweep": sweep,
+        "round_sweep_persistent_kernel": sweep_ps,
         "roofline": {
             "bound": "hbm",
-            "kernel": "nvfp4::decode_kernel<4, true> (bf16 out), M=8, the round's matrices",
+            "kernel": "nvfp4::decode_kernel<WAVES, CHUNKS, true> (split-K decode, bf16 out), M=8",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "avg_launch_us": round(avg_dur * 1e6, 3),
-            "avg_algorithmic_bytes": round(avg_bytes),
+            "avg_launch_us": round(dk_us, 3),
+            "avg_algorithmic_bytes_per_launch": round(avg_bytes),
+            "launches_per_round": 4 * args.layers,
             "traffic": None,
         },
         "cpu_baseline": cpu,

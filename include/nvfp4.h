@@ -108,18 +108,31 @@ int nvfp4_quantize(const float* w_dev, int K, int N, uint8_t* codes_dev, uint8_t
 
 typedef struct nvfp4_gemm_plan* nvfp4_gemm;
 
+/* Decode kernels (M <= 8). */
+enum nvfp4_kernel {
+    NVFP4_KERNEL_AUTO = 0,
+    NVFP4_KERNEL_STREAM = 1, /* full-K column groups, per-wave weight ring */
+    NVFP4_KERNEL_SPLITK = 2  /* K split over workgroups, last one reduces (default) */
+};
+
 /* Optional kernel configuration for nvfp4_gemm_create_ex; 0 fields mean
  * "choose automatically". */
 typedef struct nvfp4_gemm_config {
-    int split_k;      /* decode: number of K slices (workgroups per column group) */
-    int waves;        /* decode: waves per workgroup (column tiles of 16), 4 or 8 */
-    int chunks;       /* decode: K values per slice in units of 512, 1..4 (when
-                         split_k is 0) */
-    int reserved[5];
+    int split_k; /* SPLITK: number of K slices (workgroups per column group) */
+    int waves;   /* SPLITK: waves per workgroup (column tiles of 16), 4 or 8 */
+    int chunks;  /* SPLITK: K values per slice in units of 512, 1..4 (when
+                    split_k is 0) */
+    int kernel;  /* nvfp4_kernel */
+    int tiles;   /* STREAM: column tiles of 16 per workgroup, 2, 4 or 8 */
+    int reserved[3];
 } nvfp4_gemm_config;
 
 /* Create a plan for GEMMs of shape (M <= max_M) x K x N with the given output
  * dtype.  Validates K % 16 == 0, K >= 16, N >= 1, max_M >= 1, out_dtype.
+ * The first plan made on a device also runs a one-off check of the device's
+ * workgroup-to-XCD dispatch order (one tiny kernel and a synchronisation);
+ * split-K plans use the cheaper in-L2 hand-off of partial sums only if it
+ * holds.
  * *workspace_bytes receives the device workspace every run of this plan
  * needs (may be 0).  The workspace must be zero-filled before its first use
  * (nvfp4_workspace_clear or any zero fill); every run leaves its counter
@@ -166,18 +179,49 @@ typedef struct nvfp4_layer {
 
 typedef struct nvfp4_round_plan* nvfp4_round;
 
-/* Workspace a round over these layers needs (the maximum over its matrices;
- * the matrices run in stream order and reuse it). */
+/* Forms of a round (see nvfp4_round_create_ex). */
+enum nvfp4_round_mode {
+    NVFP4_ROUND_PERSISTENT = 0, /* one persistent kernel walks every matrix */
+    NVFP4_ROUND_PER_MATRIX = 1  /* one decode kernel per matrix */
+};
+
+/* Workspace a round over these layers needs in the given form (the default
+ * form is NVFP4_ROUND_PER_MATRIX). */
 int nvfp4_round_workspace_bytes(const nvfp4_layer* layers, int n_layers, int max_M,
                                 size_t* workspace_bytes);
+int nvfp4_round_workspace_bytes_ex(const nvfp4_layer* layers, int n_layers, int max_M, int mode,
+                                   size_t* workspace_bytes);
 
-/* Capture one HIP graph per width M = 1..max_M (max_M <= 8), each running
- * the n_layers GEMMs in list order on one stream, as the reference engine
- * replays one graph per batch width.  The layer array is copied; the device
- * buffers it names must stay valid while the plan lives.  The workspace is
- * zeroed on `stream` before capture.  Synchronises `stream`. */
+/* Capture one HIP graph per width M = 1..max_M (max_M <= 8), each running the
+ * n_layers GEMMs in list order, as the reference engine replays one graph per
+ * batch width.  Matrix i+1 starts computing only once every output of matrix
+ * i is written (the order of a forward pass in which each matrix consumes the
+ * previous one's result).
+ *   PER_MATRIX : the graph holds one decode kernel launch per matrix.
+ *   PERSISTENT : the graph holds one kernel whose resident workgroups walk
+ *                every matrix; the next matrix's weights are fetched while the
+ *                previous matrix finishes (no launch boundary between them).
+ *                Outputs are written with device-coherent stores.  Its waits
+ *                are bounded: a wait that times out raises a flag read by
+ *                nvfp4_round_status (the results are then not valid).  The
+ *                grid assumes it has the device to itself while it runs.
+ * The layer array is copied; the device buffers it names must stay valid
+ * while the plan lives.  The workspace (nvfp4_round_workspace_bytes_ex
+ * bytes, 16-byte aligned) is zeroed and written here, then owned by the plan
+ * until it is destroyed.  Synchronises `stream`.  nvfp4_round_create is the
+ * PER_MATRIX form (measured faster on MI355X for the 27B-class round). */
 int nvfp4_round_create(nvfp4_round* plan, const nvfp4_layer* layers, int n_layers, int max_M,
                        void* workspace_dev, size_t workspace_bytes, void* stream);
+int nvfp4_round_create_ex(nvfp4_round* plan, const nvfp4_layer* layers, int n_layers, int max_M,
+                          int mode, void* workspace_dev, size_t workspace_bytes, void* stream);
+/* Error flags raised by the replays since the last call (bit 0: a wait timed
+ * out), then cleared; after a time-out the plan's counters are also re-zeroed
+ * so later replays are valid again.  Synchronises the device.  Always 0 for
+ * PER_MATRIX. */
+int nvfp4_round_status(nvfp4_round plan, unsigned int* flags);
+/* Bound on the polling rounds of each wait of a PERSISTENT round (default
+ * 2^16, tens of milliseconds).  Synchronises the device. */
+int nvfp4_round_set_spin_limit(nvfp4_round plan, unsigned int limit);
 /* Replay the graph of width M (1..max_M) on `stream`. */
 int nvfp4_round_run(nvfp4_round plan, int M, void* stream);
 /* Number of kernel nodes in the graph of width M (0 on error). */

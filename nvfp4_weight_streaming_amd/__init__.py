@@ -29,9 +29,11 @@ EXPORTS = (
     "nvfp4_quantize_workspace_bytes", "nvfp4_quantize",
     "nvfp4_gemm_create", "nvfp4_gemm_create_ex", "nvfp4_gemm_destroy", "nvfp4_gemm_run",
     "nvfp4_workspace_clear",
-    "nvfp4_round_workspace_bytes", "nvfp4_round_create", "nvfp4_round_run",
-    "nvfp4_round_graph_nodes", "nvfp4_round_destroy",
+    "nvfp4_round_workspace_bytes", "nvfp4_round_workspace_bytes_ex", "nvfp4_round_create",
+    "nvfp4_round_create_ex", "nvfp4_round_status", "nvfp4_round_set_spin_limit",
+    "nvfp4_round_run", "nvfp4_round_graph_nodes", "nvfp4_round_destroy",
 )
+ROUND_PERSISTENT, ROUND_PER_MATRIX = 0, 1
 
 
 class Nvfp4Error(RuntimeError):
@@ -47,7 +49,10 @@ _STATUS = {OK: "ok", EINVAL: "EINVAL", EUNSUPPORTED: "EUNSUPPORTED", EHIP: "EHIP
 
 class GemmConfig(ctypes.Structure):
     _fields_ = [("split_k", ctypes.c_int), ("waves", ctypes.c_int), ("chunks", ctypes.c_int),
-                ("reserved", ctypes.c_int * 5)]
+                ("kernel", ctypes.c_int), ("tiles", ctypes.c_int), ("reserved", ctypes.c_int * 3)]
+
+
+KERNEL_AUTO, KERNEL_STREAM, KERNEL_SPLITK = 0, 1, 2
 
 
 class Layer(ctypes.Structure):
@@ -90,7 +95,11 @@ def lib():
         L.nvfp4_gemm_run.argtypes = [vp, i, i, i, vp, vp, c.c_float, vp, vp, vp, vp]
         L.nvfp4_workspace_clear.argtypes = [vp, sz, vp]
         L.nvfp4_round_workspace_bytes.argtypes = [c.POINTER(Layer), i, i, c.POINTER(sz)]
+        L.nvfp4_round_workspace_bytes_ex.argtypes = [c.POINTER(Layer), i, i, i, c.POINTER(sz)]
         L.nvfp4_round_create.argtypes = [c.POINTER(vp), c.POINTER(Layer), i, i, vp, sz, vp]
+        L.nvfp4_round_create_ex.argtypes = [c.POINTER(vp), c.POINTER(Layer), i, i, i, vp, sz, vp]
+        L.nvfp4_round_status.argtypes = [vp, c.POINTER(c.c_uint)]
+        L.nvfp4_round_set_spin_limit.argtypes = [vp, c.c_uint]
         L.nvfp4_round_run.argtypes = [vp, i, vp]
         L.nvfp4_round_graph_nodes.argtypes = [vp, i]
         L.nvfp4_round_destroy.argtypes = [vp]
@@ -159,12 +168,12 @@ def nvfp4_quantize(w, K, N, codes, scales, tensor_scale, workspace, stream=None)
                                 _ptr(workspace), _stream(stream)))
 
 
-def nvfp4_gemm_create(max_M, K, N, out_dtype, split_k=0, waves=0, chunks=0):
+def nvfp4_gemm_create(max_M, K, N, out_dtype, split_k=0, waves=0, chunks=0, kernel=0, tiles=0):
     """Returns (plan handle, workspace bytes)."""
     h = ctypes.c_void_p()
     ws = ctypes.c_size_t()
-    if split_k or waves or chunks:
-        cfg = GemmConfig(split_k, waves, chunks)
+    if split_k or waves or chunks or kernel or tiles:
+        cfg = GemmConfig(split_k, waves, chunks, kernel, tiles)
         _check(lib().nvfp4_gemm_create_ex(ctypes.byref(h), max_M, K, N, out_dtype,
                                           ctypes.byref(cfg), ctypes.byref(ws)))
     else:
@@ -197,18 +206,37 @@ def _layers(layers):
     return arr
 
 
-def nvfp4_round_workspace_bytes(layers, max_M) -> int:
+def nvfp4_round_workspace_bytes(layers, max_M, mode=None) -> int:
     ws = ctypes.c_size_t()
-    _check(lib().nvfp4_round_workspace_bytes(_layers(layers), len(layers), max_M,
-                                             ctypes.byref(ws)))
+    if mode is None:
+        _check(lib().nvfp4_round_workspace_bytes(_layers(layers), len(layers), max_M,
+                                                 ctypes.byref(ws)))
+    else:
+        _check(lib().nvfp4_round_workspace_bytes_ex(_layers(layers), len(layers), max_M, mode,
+                                                    ctypes.byref(ws)))
     return ws.value
 
 
-def nvfp4_round_create(layers, max_M, workspace, workspace_bytes, stream=None):
+def nvfp4_round_create(layers, max_M, workspace, workspace_bytes, stream=None, mode=None):
     h = ctypes.c_void_p()
-    _check(lib().nvfp4_round_create(ctypes.byref(h), _layers(layers), len(layers), max_M,
-                                    _ptr(workspace), workspace_bytes, _stream(stream)))
+    if mode is None:
+        _check(lib().nvfp4_round_create(ctypes.byref(h), _layers(layers), len(layers), max_M,
+                                        _ptr(workspace), workspace_bytes, _stream(stream)))
+    else:
+        _check(lib().nvfp4_round_create_ex(ctypes.byref(h), _layers(layers), len(layers), max_M,
+                                           mode, _ptr(workspace), workspace_bytes,
+                                           _stream(stream)))
     return h.value
+
+
+def nvfp4_round_status(plan) -> int:
+    f = ctypes.c_uint()
+    _check(lib().nvfp4_round_status(plan, ctypes.byref(f)))
+    return f.value
+
+
+def nvfp4_round_set_spin_limit(plan, limit: int):
+    _check(lib().nvfp4_round_set_spin_limit(plan, limit))
 
 
 def nvfp4_round_run(plan, M, stream=None):
@@ -271,11 +299,11 @@ class PackedWeight:
 class Gemm:
     """A plan plus its workspace: ``Gemm(max_M, K, N, out_dtype)(w, act, out)``."""
 
-    def __init__(self, max_M, K, N, out_dtype=OUT_BF16, split_k=0, waves=0, chunks=0,
-                 device="cuda"):
+    def __init__(self, max_M, K, N, out_dtype=OUT_BF16, split_k=0, waves=0, chunks=0, kernel=0,
+                 tiles=0, device="cuda"):
         import torch
         self.plan, self.ws_bytes = nvfp4_gemm_create(max_M, K, N, out_dtype, split_k, waves,
-                                                     chunks)
+                                                     chunks, kernel, tiles)
         self.K, self.N, self.max_M, self.out_dtype = K, N, max_M, out_dtype
         self.workspace = None
         if self.ws_bytes:

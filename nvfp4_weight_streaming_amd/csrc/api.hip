@@ -85,8 +85,20 @@ int validate_run(const nvfp4_gemm_plan* p, int M, int K, int N, const void* code
 int run_gemm(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
              float ts, const uint16_t* act, void* out, void* ws, size_t partial_off,
              hipStream_t s) {
-    if (M <= NVFP4_DECODE_MAX_M || !p->pre.enabled)
-        return launch_decode(p, M, codes, scales, ts, act, out, ws, partial_off, s);
+    if (M > NVFP4_DECODE_MAX_M && p->pre.enabled)
+        return launch_prefill(p, M, codes, scales, ts, act, out, ws, s);
+    if (p->str.enabled) {
+        // Rows beyond 8 (when no prefill kernel applies) run as further passes.
+        const size_t esz = p->out_dtype == NVFP4_OUT_BF16 ? 2 : 4;
+        for (int m0 = 0; m0 < M; m0 += NVFP4_DECODE_MAX_M) {
+            const int mm = M - m0 < NVFP4_DECODE_MAX_M ? M - m0 : NVFP4_DECODE_MAX_M;
+            int st = stream_launch_gemm(p, mm, codes, scales, ts, act + (size_t)m0 * p->K,
+                                        (char*)out + (size_t)m0 * p->N * esz, s);
+            if (st) return st;
+        }
+        return NVFP4_OK;
+    }
+    return launch_decode(p, M, codes, scales, ts, act, out, ws, partial_off, s);
     return launch_prefill(p, M, codes, scales, ts, act, out, ws, s);
 }
 
@@ -134,14 +146,24 @@ static int create_plan(nvfp4_gemm* plan, int max_M, int K, int N, int out_dtype,
     p->out_dtype = out_dtype;
     p->Kp = padded_k(K);
     p->Np = padded_n(N);
-    int st = make_decode_config(K, N, max_M, cfg, &p->dec);
-    if (st == NVFP4_OK) st = make_prefill_config(max_M, K, N, &p->pre);
+    const int kernel = cfg ? cfg->kernel : NVFP4_KERNEL_AUTO;
+    int st = NVFP4_OK;
+    if (kernel < NVFP4_KERNEL_AUTO || kernel > NVFP4_KERNEL_SPLITK)
+        st = set_error(NVFP4_EINVAL, "config.kernel: %d is not AUTO, STREAM or SPLITK", kernel);
+    const int tiles = cfg ? cfg->tiles : 0;
+    if (!st && tiles != 0 && tiles != 2 && tiles != 4 && tiles != 8)
+        st = set_error(NVFP4_EINVAL, "config.tiles: %d is not 2, 4 or 8", tiles);
+    p->str.enabled = kernel == NVFP4_KERNEL_STREAM;
+    p->str.tiles = tiles;
+    if (!st) st = make_decode_config(K, N, max_M, cfg, &p->dec);
+    if (!st) st = make_prefill_config(max_M, K, N, &p->pre);
     if (st != NVFP4_OK) {
         p->magic = 0;
         delete p;
         return st;
     }
-    p->ws_bytes = p->dec.ws_bytes > p->pre.ws_bytes ? p->dec.ws_bytes : p->pre.ws_bytes;
+    const size_t dec_ws = p->str.enabled ? 0 : p->dec.ws_bytes;
+    p->ws_bytes = dec_ws > p->pre.ws_bytes ? dec_ws : p->pre.ws_bytes;
     *workspace_bytes = p->ws_bytes;
     *plan = p;
     return NVFP4_OK;

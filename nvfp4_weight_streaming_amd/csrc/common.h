@@ -46,12 +46,19 @@ struct DecodeConfig {
     int splits;         // K slices
     int n_groups;       // column groups of `waves` tiles
     int grid;           // workgroups launched (n_groups padded to 8, times splits)
+    int l2_local;       // split-K partials stay in one XCD's L2 (mapping verified)
     // Workspace layout: [counters: counter_bytes][partial sums: partial_bytes].
     // Counters come first so that, when several plans share one workspace (a
     // round), no plan's partial sums ever overlap any plan's counters.
     size_t counter_bytes;
     size_t partial_bytes;
     size_t ws_bytes;    // counter_bytes + partial_bytes
+};
+
+struct StreamDesc;
+struct StreamConfig {
+    int enabled;  // the streaming kernel serves M <= 8
+    int tiles;    // forced column tiles per workgroup (0: by shape)
 };
 
 struct PrefillConfig {
@@ -66,6 +73,7 @@ struct nvfp4_gemm_plan {
     int max_M, K, N, out_dtype;
     int Kp, Np;
     nvfp4::DecodeConfig dec;
+    nvfp4::StreamConfig str;
     nvfp4::PrefillConfig pre;
     size_t ws_bytes;
 };
@@ -86,6 +94,24 @@ int launch_decode(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const u
 int launch_prefill(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
                    float ts, const uint16_t* act, void* out, void* ws, hipStream_t s);
 int launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+
+// Streaming kernel (stream.hip).
+void stream_fill_desc(StreamDesc* d, int K, int N, const void* codes, const void* scales,
+                      const uint16_t* act, void* out, float ts, int out_dtype, int T_override);
+int stream_launch_gemm(const nvfp4_gemm_plan* p, int M, const uint8_t* codes,
+                       const uint8_t* scales, float ts, const uint16_t* act, void* out,
+                       hipStream_t s);
+int stream_round_grid(int* grid);
+// Persistent round: writes the descriptors (with the task rotation for `grid`)
+// into the workspace.  Layout, in bytes.
+struct StreamRoundLayout {
+    size_t done_off, status_off, desc_off, flags_off, total;
+};
+size_t stream_round_layout(int n, StreamRoundLayout* out);
+int stream_round_write_descs(const nvfp4_layer* L, int n, int grid, void* ws,
+                             const StreamRoundLayout& lay, hipStream_t s);
+int stream_launch_round(int n, int M, int grid, void* ws, const StreamRoundLayout& lay,
+                        hipStream_t s);
 
 // Shared validation of a GEMM run against its plan.
 int validate_run(const nvfp4_gemm_plan* p, int M, int K, int N, const void* codes,

@@ -27,89 +27,9 @@
 // group (an atomic counter) adds them in split order, so results are
 // deterministic.  Workgroups of one column group are placed on one XCD
 // (blockIdx % 8 selects the XCD), so their partials meet in one L2.
-#include "common.h"
+#include "decode_device.h"
 
 namespace nvfp4 {
-
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
-
-constexpr int kLdsPad = 8;         // bf16 elements of padding per LDS row
-constexpr int kMaxChunks = 4;  // superblocks of 512 k per wave (all loaded up front)
-
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
-    uint32_t u = __float_as_uint(x);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
-    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-}
-
-template <bool BF16>
-__device__ __forceinline__ void store_out(void* out, size_t idx, float v) {
-    if (BF16)
-        ((uint16_t*)out)[idx] = f32_to_bf16_rne(v);
-    else
-        ((float*)out)[idx] = v;
-}
-
-// 8 E2M1 codes (4 bytes, low nibble first) -> 8 bf16 values in k order.
-__device__ __forceinline__ bf16x8 e2m1x8_to_bf16(uint32_t w) {
-    bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
-    bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
-    bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2);
-    bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
-    return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
-
-// The packed bytes one wave streams per 512-k superblock: 4 code chunks (16 B
-// per lane each, 4 MFMA steps apiece) and one 16-byte scale word per lane.
-struct Chunk {
-    uint4 c[4];
-    uint4 s;
-};
-
-__device__ __forceinline__ void load_chunk(Chunk& x, const uint4* cp, const uint4* sp) {
-    x.c[0] = cp[0];
-    x.c[1] = cp[64];
-    x.c[2] = cp[128];
-    x.c[3] = cp[192];
-    x.s = sp[0];
-}
-
-__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
-    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
-
-// 128 k: four independent MFMAs (one per 32-k step), then the block scales.
-// a: this lane's A-operand pointer for the first step of the 128.
-__device__ __forceinline__ void kb_steps(float (&acc)[4], const uint4& cw, uint32_t sw,
-                                         const __bf16* a) {
-    f32x4 r[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        const bf16x8 av = *(const bf16x8*)(a + 32 * s);
-        const bf16x8 bv = e2m1x8_to_bf16(word(cw, s));
-        r[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-    }
-    const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 0);
-    const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 1);
-    const float s2 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 2);
-    const float s3 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 3);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        acc[j] = __builtin_fmaf(s0, r[0][j], acc[j]);
-        acc[j] = __builtin_fmaf(s1, r[1][j], acc[j]);
-        acc[j] = __builtin_fmaf(s2, r[2][j], acc[j]);
-        acc[j] = __builtin_fmaf(s3, r[3][j], acc[j]);
-    }
-}
-
-__device__ __forceinline__ void chunk_steps(float (&acc)[4], const Chunk& x, const __bf16* a) {
-    kb_steps(acc, x.c[0], x.s.x, a);
-    kb_steps(acc, x.c[1], x.s.y, a + 128);
-    kb_steps(acc, x.c[2], x.s.z, a + 256);
-    kb_steps(acc, x.c[3], x.s.w, a + 384);
-}
 
 // One workgroup = WAVES column tiles (one per wave) x one K slice of up to
 // NCH superblocks.  Every load a wave will need is issued before it computes
@@ -122,11 +42,9 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
     const uint4* __restrict__ codes, const uint4* __restrict__ scales,
     const uint16_t* __restrict__ act, void* __restrict__ out, float* __restrict__ partial,
     unsigned int* __restrict__ counters, float ts, int M, int K, int N, int nsb, int splits,
-    int n_groups, int n_tiles) {
+    int n_groups, int n_tiles, int l2_local) {
     constexpr int kThreads = WAVES * 64;
     constexpr int kStride = NCH * kSuperK + kLdsPad;          // LDS row, bf16 elements
-    constexpr int kVecs = 9 * NCH * (kSuperK / 8);            // 8 rows + zero row, 16 B each
-    constexpr int kVecPerThread = (kVecs + kThreads - 1) / kThreads;
     constexpr int kCols = WAVES * kTileN;
     __shared__ __attribute__((aligned(16))) __bf16 lds[9 * kStride];
     __shared__ int s_last;
@@ -139,20 +57,10 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
     const int sb0 = split * NCH;
     const int nch = min(NCH, nsb - sb0);  // superblocks in this slice (>= 1)
     const int k0 = sb0 * kSuperK;
-    const int row_vecs = nch * (kSuperK / 8);
 
-    // 1. This thread's share of the activation slice (rows 0..7 and the zero
-    //    row 8).  Loads are unconditional with clamped addresses; rows >= M,
-    //    k >= K and the zero row are replaced by zeros when stored.
-    uint4 av[kVecPerThread];
-#pragma unroll
-    for (int i = 0; i < kVecPerThread; ++i) {
-        const int idx = threadIdx.x + i * kThreads;
-        const int r = idx / row_vecs, oct = idx - r * row_vecs;
-        const int m = min(r, M - 1);
-        const int k = min(k0 + 8 * oct, K - 8);
-        av[i] = *(const uint4*)(act + (size_t)m * K + k);
-    }
+    // 1. This thread's share of the activation slice.
+    ActStage<kThreads, NCH, kStride> stage;
+    stage.load(act, M, K, k0, nch);
 
     // 2. All weight chunks of this wave's column tile and K slice.
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -168,21 +76,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
     }
 
     // 3. Activations to LDS.
-#pragma unroll
-    for (int i = 0; i < kVecPerThread; ++i) {
-        const int idx = threadIdx.x + i * kThreads;
-        const int r = idx / row_vecs, oct = idx - r * row_vecs;
-        if (r < 9) {
-            const int k = k0 + 8 * oct;
-            const bool keep = r < M && k < K;
-            uint4 v = av[i];
-            v.x = keep ? v.x : 0u;
-            v.y = keep ? v.y : 0u;
-            v.z = keep ? v.z : 0u;
-            v.w = keep ? v.w : 0u;
-            *(uint4*)(lds + r * kStride + 8 * oct) = v;
-        }
-    }
+    stage.store(lds, M, K, k0, nch);
     __syncthreads();
 
     // 4. MFMA over the slice.  A-operand row of this lane: activation row
@@ -213,19 +107,25 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
         return;
     }
 
-    // Split K.  The slices of one column group run on one XCD (blockIdx % 8).
-    // Partial sums are written with agent-coherent (write-through) stores and
-    // read back with agent-coherent loads, so the hand-off needs only the
-    // store-completion wait before the counter increment -- no write-back of
-    // the whole L2, which an agent-scope fence would cost every workgroup.
+    // Split K.  The slices of one column group run on one XCD (blockIdx % 8
+    // selects it, verified when the plan is made: l2_local), so their
+    // partial sums meet in that XCD's L2: plain stores, a wait for their
+    // completion, then the counter increment.  Without the verified mapping
+    // the partials go through device-coherent (write-through) stores and
+    // loads instead.  Either way the hand-off needs no agent-scope fence,
+    // whose write-back of the whole L2 would cost every workgroup.
     float* pbase = partial + (size_t)(ng * splits + split) * 8 * kCols;
     if (mine) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int mm = 4 * g + j;
-            if (mm < M)
-                __hip_atomic_store(pbase + mm * kCols + wave * kTileN + col, acc[j],
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (mm < M) {
+                float* dst = pbase + mm * kCols + wave * kTileN + col;
+                if (l2_local)
+                    *dst = acc[j];
+                else
+                    __hip_atomic_store(dst, acc[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -241,25 +141,68 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
     for (int idx = threadIdx.x; idx < M * kCols; idx += kThreads) {
         const int mm = idx / kCols, c = idx - mm * kCols;
         const int n = ng * kCols + c;
-        float sum = 0.f;
-        for (int sp2 = 0; sp2 < splits; ++sp2)
-            sum += __hip_atomic_load(gbase + (size_t)(sp2 * 8 + mm) * kCols + c, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
+        const float sum = sum_partials<kCols>(gbase, splits, mm, c, l2_local);
         if (n < N) store_out<BF16>(out, (size_t)mm * N + n, sum * ts);
     }
     if (threadIdx.x == 0)  // leave the counter zeroed for the next run
         __hip_atomic_store(&counters[ng], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---- XCD mapping check -----------------------------------------------------------
+
+// Workgroups are dispatched to the 8 XCDs round-robin (workgroup b on XCD
+// b % 8); the split-K hand-off relies on it to keep partial sums in one L2.
+// Checked once per device by reading each workgroup's XCC_ID register.
+constexpr int kProbeBlocks = 64;
+__device__ unsigned int g_xcc_probe[kProbeBlocks];
+
+__global__ void xcc_probe_kernel() {
+    unsigned int v;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+    if (threadIdx.x == 0) g_xcc_probe[blockIdx.x] = v & 0xFu;
+}
+
+static int xcd_mapping_verified() {
+    static int cached[64];
+    static bool init = false;
+    if (!init) {
+        for (int& c : cached) c = -1;
+        init = true;
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    if (cached[dev] >= 0) return cached[dev];
+    unsigned int h[kProbeBlocks];
+    int ok = 0;
+    hipLaunchKernelGGL(xcc_probe_kernel, dim3(kProbeBlocks), dim3(64), 0, 0);
+    if (hipGetLastError() == hipSuccess && hipDeviceSynchronize() == hipSuccess &&
+        hipMemcpyFromSymbol(h, HIP_SYMBOL(g_xcc_probe), sizeof(h), 0, hipMemcpyDeviceToHost) ==
+            hipSuccess) {
+        ok = 1;
+        for (int b = 0; b < kProbeBlocks; ++b)
+            if (h[b] != (unsigned int)(b % 8)) ok = 0;
+    }
+    (void)hipGetLastError();
+    cached[dev] = ok;
+    return ok;
+}
+
 // ---- plan ----------------------------------------------------------------------
 
 int make_decode_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, DecodeConfig* d) {
     (void)max_M;
-    int waves = (cfg && cfg->waves) ? cfg->waves : 4;
-    if (waves != 4 && waves != 8)
-        return set_error(NVFP4_EINVAL, "config.waves: %d is not 4 or 8", waves);
     const int n_tiles = padded_n(N) / kTileN;
     const int nsb = padded_k(K) / kSuperK;
+    // Defaults measured on MI355X over the round's shapes (K = 5120..17408,
+    // N = 5120..152064): 2 superblocks per slice and 4 waves per workgroup,
+    // except very long K (>= 16384), where 3 superblocks and 8 waves win.
+    const bool long_k = nsb >= 32;
+    int waves = (cfg && cfg->waves) ? cfg->waves : (long_k ? 8 : 4);
+    if (waves != 4 && waves != 8)
+        return set_error(NVFP4_EINVAL, "config.waves: %d is not 4 or 8", waves);
     const int n_groups = (n_tiles + waves - 1) / waves;
     const int ng8 = round_up(n_groups, 8);
     int chunks;
@@ -275,12 +218,11 @@ int make_decode_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, De
             return set_error(NVFP4_EINVAL, "config.chunks: %d outside [1, %d]", cfg->chunks, kMaxChunks);
         chunks = cfg->chunks < nsb ? cfg->chunks : nsb;
     } else {
-        // The largest slice (fewest partial sums) that still gives about
-        // 1024 workgroups (four per CU on 256 CUs).
-        chunks = kMaxChunks < nsb ? kMaxChunks : nsb;
-        while (chunks > 1 && (long)ng8 * ((nsb + chunks - 1) / chunks) < 1024) --chunks;
+        chunks = long_k ? 3 : 2;
+        if (chunks > nsb) chunks = nsb;
     }
     const int splits = (nsb + chunks - 1) / chunks;
+    d->l2_local = splits > 1 ? xcd_mapping_verified() : 0;
     d->waves = waves;
     d->chunks = chunks;
     d->splits = splits;
@@ -306,7 +248,8 @@ static int launch_t(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const
     float* partial = ws ? (float*)((char*)ws + partial_off) : nullptr;
     hipLaunchKernelGGL((decode_kernel<WAVES, NCH, BF16>), dim3(d.grid), dim3(WAVES * 64), 0, s,
                        (const uint4*)codes, (const uint4*)scales, act, out, partial, counters, ts,
-                       M, p->K, p->N, p->Kp / kSuperK, d.splits, d.n_groups, p->Np / kTileN);
+                       M, p->K, p->N, p->Kp / kSuperK, d.splits, d.n_groups, p->Np / kTileN,
+                       d.l2_local);
     NVFP4_HIP(hipGetLastError());
     return NVFP4_OK;
 }

@@ -1,0 +1,160 @@
+// Device building blocks of the decode GEMM, shared by the split-K kernel
+// (decode.hip) and the streaming kernels (stream.hip).  The operand mapping
+// is described at the top of decode.hip.
+#pragma once
+
+#include "common.h"
+
+namespace nvfp4 {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr int kLdsPad = 8;         // bf16 elements of padding per LDS row
+constexpr int kMaxChunks = 4;  // superblocks of 512 k per wave (all loaded up front)
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_out(void* out, size_t idx, float v) {
+    if (BF16)
+        ((uint16_t*)out)[idx] = f32_to_bf16_rne(v);
+    else
+        ((float*)out)[idx] = v;
+}
+
+// 8 E2M1 codes (4 bytes, low nibble first) -> 8 bf16 values in k order.
+__device__ __forceinline__ bf16x8 e2m1x8_to_bf16(uint32_t w) {
+    bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
+    bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
+    bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2);
+    bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
+    return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// The packed bytes one wave streams per 512-k superblock: 4 code chunks (16 B
+// per lane each, 4 MFMA steps apiece) and one 16-byte scale word per lane.
+struct Chunk {
+    uint4 c[4];
+    uint4 s;
+};
+
+__device__ __forceinline__ void load_chunk(Chunk& x, const uint4* cp, const uint4* sp) {
+    x.c[0] = cp[0];
+    x.c[1] = cp[64];
+    x.c[2] = cp[128];
+    x.c[3] = cp[192];
+    x.s = sp[0];
+}
+
+__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// 128 k: four independent MFMAs (one per 32-k step), then the block scales.
+// a: this lane's A-operand pointer for the first step of the 128.
+__device__ __forceinline__ void kb_steps(float (&acc)[4], const uint4& cw, uint32_t sw,
+                                         const __bf16* a) {
+    f32x4 r[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const bf16x8 av = *(const bf16x8*)(a + 32 * s);
+        const bf16x8 bv = e2m1x8_to_bf16(word(cw, s));
+        r[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    }
+    const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 0);
+    const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 1);
+    const float s2 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 2);
+    const float s3 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 3);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        acc[j] = __builtin_fmaf(s0, r[0][j], acc[j]);
+        acc[j] = __builtin_fmaf(s1, r[1][j], acc[j]);
+        acc[j] = __builtin_fmaf(s2, r[2][j], acc[j]);
+        acc[j] = __builtin_fmaf(s3, r[3][j], acc[j]);
+    }
+}
+
+__device__ __forceinline__ void chunk_steps(float (&acc)[4], const Chunk& x, const __bf16* a) {
+    kb_steps(acc, x.c[0], x.s.x, a);
+    kb_steps(acc, x.c[1], x.s.y, a + 128);
+    kb_steps(acc, x.c[2], x.s.z, a + 256);
+    kb_steps(acc, x.c[3], x.s.w, a + 384);
+}
+
+// Stage rows 0..7 of an activation K slice plus one zero row (row 8) into LDS
+// (row stride kStride bf16).  ACTIVATION loads are issued here and written
+// after `between()` runs, so the caller can issue its weight loads in between
+// and they stay in flight.  Loads are unconditional with clamped addresses;
+// rows >= M, k >= K and the zero row are stored as zeros.
+template <int kThreads, int NCH, int kStride>
+struct ActStage {
+    static constexpr int kVecs = 9 * NCH * (kSuperK / 8);
+    static constexpr int kPer = (kVecs + kThreads - 1) / kThreads;
+    uint4 v[kPer];
+
+    __device__ __forceinline__ void load(const uint16_t* act, int M, int K, int k0, int nch) {
+        const int row_vecs = nch * (kSuperK / 8);
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int idx = threadIdx.x + i * kThreads;
+            const int r = idx / row_vecs, oct = idx - r * row_vecs;
+            const int m = min(r, M - 1);
+            const int k = min(k0 + 8 * oct, K - 8);
+            v[i] = *(const uint4*)(act + (size_t)m * K + k);
+        }
+    }
+
+    __device__ __forceinline__ void store(__bf16* lds, int M, int K, int k0, int nch) const {
+        const int row_vecs = nch * (kSuperK / 8);
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int idx = threadIdx.x + i * kThreads;
+            const int r = idx / row_vecs, oct = idx - r * row_vecs;
+            if (r < 9) {
+                const int k = k0 + 8 * oct;
+                const bool keep = r < M && k < K;
+                uint4 x = v[i];
+                x.x = keep ? x.x : 0u;
+                x.y = keep ? x.y : 0u;
+                x.z = keep ? x.z : 0u;
+                x.w = keep ? x.w : 0u;
+                *(uint4*)(lds + r * kStride + 8 * oct) = x;
+            }
+        }
+    }
+};
+
+// Sum, in split order, the `splits` partial sums of output (mm, c) of one
+// column group (layout [split][8 rows][kCols]); l2_local: written with plain
+// stores into this XCD's L2, else with device-coherent stores.  The loads are issued in batches of 8 before any is
+// added, so the reduction costs ceil(splits / 8) memory round trips, not
+// `splits`.
+template <int kCols>
+__device__ __forceinline__ float sum_partials(const float* gbase, int splits, int mm, int c,
+                                              int l2_local = 0) {
+    float sum = 0.f;
+    for (int s0 = 0; s0 < splits; s0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const float* src = gbase + (size_t)((s0 + t) * 8 + mm) * kCols + c;
+            v[t] = (s0 + t < splits)
+                       ? (l2_local ? *src
+                                   : __hip_atomic_load(src, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT))
+                       : 0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            if (s0 + t < splits) sum += v[t];
+    }
+    return sum;
+}
+
+}  // namespace nvfp4

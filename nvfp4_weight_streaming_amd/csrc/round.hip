@@ -3,9 +3,13 @@
 // "Ignis" README, "The decode round": the round for all lanes is replayed
 // from one captured graph per batch width (widths 1..8) rather than issued
 // launch by launch.  Here a round is a list of weight matrices run in list
-// order on one stream, each with its own activation input and output; the
-// graph of width M runs every matrix for M lanes, and nvfp4_round_run
-// replays it.
+// order, each with its own activation input and output; the graph of width M
+// runs every matrix for M lanes, and nvfp4_round_run replays it.  Two forms:
+//   NVFP4_ROUND_PERSISTENT - the graph holds one persistent kernel that walks
+//     all matrices, each starting only when the previous one is final, with
+//     the weight stream running on across the boundary (stream.hip);
+//   NVFP4_ROUND_PER_MATRIX - the graph holds one decode kernel per matrix on
+//     one stream.
 #include <new>
 #include <vector>
 
@@ -14,6 +18,9 @@
 struct nvfp4_round_plan {
     uint32_t magic;
     int max_M;
+    int mode;
+    int grid;    // persistent form: resident workgroups
+    nvfp4::StreamRoundLayout lay;
     std::vector<nvfp4_layer> layers;
     std::vector<nvfp4_gemm_plan*> plans;
     void* ws;
@@ -25,6 +32,11 @@ struct nvfp4_round_plan {
 };
 
 namespace nvfp4 {
+
+// Polling rounds before a wait of the persistent round gives up (each round
+// is one coherent load plus a short sleep, about a microsecond: tens of
+// milliseconds in all, far above any one matrix's time).
+constexpr unsigned int kDefaultSpinLimit = 1u << 16;
 
 static void free_round(nvfp4_round_plan* r) {
     for (int i = 0; i < NVFP4_DECODE_MAX_M; ++i) {
@@ -62,8 +74,9 @@ using namespace nvfp4;
 
 extern "C" {
 
-// Workspace of a round: one counter region at the start, sized for the plan
-// with the most counters, then one partial-sum region sized for the largest.
+// Workspace of a per-matrix round: one counter region at the start, sized for
+// the plan with the most counters, then one partial-sum region sized for the
+// largest.
 static int round_layout(const nvfp4_layer* layers, int n_layers, int max_M, size_t* counters,
                         size_t* partials) {
     size_t mc = 0, mp = 0;
@@ -81,12 +94,25 @@ static int round_layout(const nvfp4_layer* layers, int n_layers, int max_M, size
     return NVFP4_OK;
 }
 
-int nvfp4_round_workspace_bytes(const nvfp4_layer* layers, int n_layers, int max_M,
-                                size_t* workspace_bytes) {
+static int check_mode(int mode) {
+    if (mode != NVFP4_ROUND_PERSISTENT && mode != NVFP4_ROUND_PER_MATRIX)
+        return set_error(NVFP4_EINVAL, "mode: %d is neither PERSISTENT (0) nor PER_MATRIX (1)", mode);
+    return NVFP4_OK;
+}
+
+int nvfp4_round_workspace_bytes_ex(const nvfp4_layer* layers, int n_layers, int max_M, int mode,
+                                   size_t* workspace_bytes) {
     clear_error();
     int st = validate_layers(layers, n_layers, max_M);
     if (st) return st;
+    st = check_mode(mode);
+    if (st) return st;
     if (!workspace_bytes) return set_error(NVFP4_EINVAL, "workspace_bytes: NULL");
+    if (mode == NVFP4_ROUND_PERSISTENT) {
+        StreamRoundLayout lay;
+        *workspace_bytes = stream_round_layout(n_layers, &lay);
+        return NVFP4_OK;
+    }
     size_t c = 0, p = 0;
     st = round_layout(layers, n_layers, max_M, &c, &p);
     if (st) return st;
@@ -94,17 +120,30 @@ int nvfp4_round_workspace_bytes(const nvfp4_layer* layers, int n_layers, int max
     return NVFP4_OK;
 }
 
-int nvfp4_round_create(nvfp4_round* plan, const nvfp4_layer* layers, int n_layers, int max_M,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+int nvfp4_round_workspace_bytes(const nvfp4_layer* layers, int n_layers, int max_M,
+                                size_t* workspace_bytes) {
+    return nvfp4_round_workspace_bytes_ex(layers, n_layers, max_M, NVFP4_ROUND_PER_MATRIX,
+                                          workspace_bytes);
+}
+
+int nvfp4_round_create_ex(nvfp4_round* plan, const nvfp4_layer* layers, int n_layers, int max_M,
+                          int mode, void* workspace, size_t workspace_bytes, void* stream) {
     clear_error();
     if (!plan) return set_error(NVFP4_EINVAL, "plan: NULL");
     *plan = nullptr;
     int st = validate_layers(layers, n_layers, max_M);
     if (st) return st;
-    size_t need_c = 0, need_p = 0;
-    st = round_layout(layers, n_layers, max_M, &need_c, &need_p);
+    st = check_mode(mode);
     if (st) return st;
-    const size_t need = need_c + need_p;
+    size_t need_c = 0, need_p = 0;
+    StreamRoundLayout lay{};
+    if (mode == NVFP4_ROUND_PERSISTENT) {
+        stream_round_layout(n_layers, &lay);
+    } else {
+        st = round_layout(layers, n_layers, max_M, &need_c, &need_p);
+        if (st) return st;
+    }
+    const size_t need = mode == NVFP4_ROUND_PERSISTENT ? lay.total : need_c + need_p;
     if (workspace_bytes < need)
         return set_error(NVFP4_EINVAL, "workspace_bytes: %zu < %zu needed", workspace_bytes, need);
     if (need && !workspace) return set_error(NVFP4_EINVAL, "workspace: NULL");
@@ -114,6 +153,8 @@ int nvfp4_round_create(nvfp4_round* plan, const nvfp4_layer* layers, int n_layer
     if (!r) return set_error(NVFP4_EINVAL, "plan: out of host memory");
     r->magic = kRoundMagic;
     r->max_M = max_M;
+    r->mode = mode;
+    r->lay = lay;
     r->layers.assign(layers, layers + n_layers);
     r->ws = workspace;
     r->ws_bytes = workspace_bytes;
@@ -144,6 +185,15 @@ int nvfp4_round_create(nvfp4_round* plan, const nvfp4_layer* layers, int n_layer
         e = hipStreamSynchronize(user);
         if (e != hipSuccess) st = hip_fail(e, "hipStreamSynchronize");
     }
+    if (!st && mode == NVFP4_ROUND_PERSISTENT) {
+        st = stream_round_grid(&r->grid);
+        if (!st) st = stream_round_write_descs(layers, n_layers, r->grid, workspace, lay, user);
+        if (!st) {
+            const unsigned int limit = kDefaultSpinLimit;
+            e = hipMemcpy((char*)workspace + lay.status_off + 4, &limit, 4, hipMemcpyHostToDevice);
+            if (e != hipSuccess) st = hip_fail(e, "hipMemcpy(spin limit)");
+        }
+    }
     for (int M = 1; M <= max_M && !st; ++M) {
         e = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal);
         if (e != hipSuccess) {
@@ -151,10 +201,14 @@ int nvfp4_round_create(nvfp4_round* plan, const nvfp4_layer* layers, int n_layer
             break;
         }
         int lst = NVFP4_OK;
-        for (int i = 0; i < n_layers && !lst; ++i) {
-            const nvfp4_layer& l = r->layers[i];
-            lst = run_gemm(r->plans[i], M, l.codes_dev, l.scales_dev, l.tensor_scale, l.act_dev,
-                           l.out_dev, workspace, r->partial_off, cap);
+        if (mode == NVFP4_ROUND_PERSISTENT) {
+            lst = stream_launch_round(n_layers, M, r->grid, workspace, lay, cap);
+        } else {
+            for (int i = 0; i < n_layers && !lst; ++i) {
+                const nvfp4_layer& l = r->layers[i];
+                lst = run_gemm(r->plans[i], M, l.codes_dev, l.scales_dev, l.tensor_scale,
+                               l.act_dev, l.out_dev, workspace, r->partial_off, cap);
+            }
         }
         hipGraph_t g = nullptr;
         e = hipStreamEndCapture(cap, &g);
@@ -192,6 +246,44 @@ int nvfp4_round_create(nvfp4_round* plan, const nvfp4_layer* layers, int n_layer
         return st;
     }
     *plan = r;
+    return NVFP4_OK;
+}
+
+int nvfp4_round_create(nvfp4_round* plan, const nvfp4_layer* layers, int n_layers, int max_M,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    return nvfp4_round_create_ex(plan, layers, n_layers, max_M, NVFP4_ROUND_PER_MATRIX, workspace,
+                                 workspace_bytes, stream);
+}
+
+int nvfp4_round_status(nvfp4_round plan, unsigned int* flags) {
+    clear_error();
+    if (!plan || plan->magic != kRoundMagic) return set_error(NVFP4_ESTATE, "plan: invalid handle");
+    if (!flags) return set_error(NVFP4_EINVAL, "flags: NULL");
+    *flags = 0;
+    if (plan->mode != NVFP4_ROUND_PERSISTENT) return NVFP4_OK;
+    void* p = (char*)plan->ws + plan->lay.status_off;
+    NVFP4_HIP(hipDeviceSynchronize());
+    NVFP4_HIP(hipMemcpy(flags, p, 4, hipMemcpyDeviceToHost));
+    const unsigned int zero = 0;
+    NVFP4_HIP(hipMemcpy(p, &zero, 4, hipMemcpyHostToDevice));
+    if (*flags) {
+        // A replay that timed out may have left completion counters behind:
+        // zero them (the descriptors after them stay) so the plan is usable.
+        NVFP4_HIP(hipMemset((char*)plan->ws + plan->lay.done_off, 0, plan->lay.status_off));
+        NVFP4_HIP(hipMemset((char*)plan->ws + plan->lay.flags_off, 0,
+                            plan->lay.total - plan->lay.flags_off));
+        NVFP4_HIP(hipDeviceSynchronize());
+    }
+    return NVFP4_OK;
+}
+
+int nvfp4_round_set_spin_limit(nvfp4_round plan, unsigned int limit) {
+    clear_error();
+    if (!plan || plan->magic != kRoundMagic) return set_error(NVFP4_ESTATE, "plan: invalid handle");
+    if (plan->mode != NVFP4_ROUND_PERSISTENT) return NVFP4_OK;
+    NVFP4_HIP(hipDeviceSynchronize());
+    NVFP4_HIP(hipMemcpy((char*)plan->ws + plan->lay.status_off + 4, &limit, 4,
+                        hipMemcpyHostToDevice));
     return NVFP4_OK;
 }
 

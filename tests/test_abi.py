@@ -85,23 +85,37 @@ def test_gemm_config_validation(nv):
     with pytest.raises(nv.Nvfp4Error) as e:
         nv.nvfp4_gemm_create(8, 5120, 5120, 1, split_k=0, waves=3)
     assert "waves" in e.value.message
-    plan, ws = nv.nvfp4_gemm_create(8, 5120, 5120, 1, split_k=5, waves=8)
+    SPLITK = nv.KERNEL_SPLITK
+    plan, ws = nv.nvfp4_gemm_create(8, 5120, 5120, 1, split_k=5, waves=8, kernel=SPLITK)
     assert ws > 0
     nv.nvfp4_gemm_destroy(plan)
-    plan, ws = nv.nvfp4_gemm_create(8, 2048, 5120, 1, split_k=1, waves=4)
+    plan, ws = nv.nvfp4_gemm_create(8, 2048, 5120, 1, split_k=1, waves=4, kernel=SPLITK)
     assert ws == 0  # no K split: no partials, no counters
     nv.nvfp4_gemm_destroy(plan)
     # a workgroup holds at most 4 x 512 values of K, so K = 5120 needs 3 slices
     with pytest.raises(nv.Nvfp4Error) as e:
-        nv.nvfp4_gemm_create(8, 5120, 5120, 1, split_k=1)
+        nv.nvfp4_gemm_create(8, 5120, 5120, 1, split_k=1, kernel=SPLITK)
     assert e.value.message.startswith("config.split_k")
     for bad in (0 - 1, 5):
         with pytest.raises(nv.Nvfp4Error) as e:
-            nv.nvfp4_gemm_create(8, 5120, 5120, 1, chunks=bad)
+            nv.nvfp4_gemm_create(8, 5120, 5120, 1, chunks=bad, kernel=SPLITK)
         assert e.value.message.startswith("config.chunks")
-    plan, ws = nv.nvfp4_gemm_create(8, 5120, 5120, 1, chunks=4)
+    plan, ws = nv.nvfp4_gemm_create(8, 5120, 5120, 1, chunks=4, kernel=SPLITK)
     assert ws > 0
     nv.nvfp4_gemm_destroy(plan)
+    # the streaming kernel needs no workspace
+    for tiles in (0, 2, 4, 8):
+        plan, ws = nv.nvfp4_gemm_create(8, 5120, 5120, 1, tiles=tiles, kernel=nv.KERNEL_STREAM)
+        assert ws == 0
+        nv.nvfp4_gemm_destroy(plan)
+    for bad_kernel in (-1, 3):
+        with pytest.raises(nv.Nvfp4Error) as e:
+            nv.nvfp4_gemm_create(8, 5120, 5120, 1, kernel=bad_kernel)
+        assert e.value.message.startswith("config.kernel")
+    for bad_tiles in (1, 3, 16):
+        with pytest.raises(nv.Nvfp4Error) as e:
+            nv.nvfp4_gemm_create(8, 5120, 5120, 1, tiles=bad_tiles)
+        assert e.value.message.startswith("config.tiles")
 
 
 def test_workspace_sizes_for_round_shapes(nv):
@@ -121,7 +135,8 @@ FAKE = 1 << 20  # a 16-byte-aligned non-null address; never dereferenced
     (dict(act=FAKE + 8), "act", 1), (dict(out=FAKE + 2), "out", 1),
     (dict(workspace=None), "workspace", 1), (dict(workspace=FAKE + 4), "workspace", 1)])
 def test_gemm_run_validates_before_any_gpu_call(nv, kw, word, status):
-    plan, ws = nv.nvfp4_gemm_create(8, 5120, 5120, 1)
+    # a split-K plan: it needs a workspace, so every argument is checked
+    plan, ws = nv.nvfp4_gemm_create(8, 5120, 5120, 1, kernel=nv.KERNEL_SPLITK)
     assert ws > 0
     args = dict(M=4, K=5120, N=5120, codes=FAKE, scales=FAKE, act=FAKE, out=FAKE,
                 workspace=FAKE)

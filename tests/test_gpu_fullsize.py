@@ -48,9 +48,12 @@ def full_round():
     import torch
     nv = require_gpu()
     specs, keep = bench.build_round(nv, layers=64)
-    ws_bytes = nv.nvfp4_round_workspace_bytes(specs, 8)
-    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
-    plan = nv.nvfp4_round_create(specs, 8, ws, ws_bytes)
+    plans = {}
+    for mode in (nv.ROUND_PERSISTENT, nv.ROUND_PER_MATRIX):
+        ws_bytes = nv.nvfp4_round_workspace_bytes(specs, 8, mode=mode)
+        ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+        plans[mode] = nv.nvfp4_round_create(specs, 8, ws, ws_bytes, mode=mode)
+        keep.append(ws)
     refs = {}
     for layer, name in SAMPLED:
         s = next(x for x in specs if x["layer"] == layer and x["name"] == name)
@@ -60,16 +63,19 @@ def full_round():
         act = bf16_bits(s["act"])
         y, S = oracle.gemm(act, c, sc, t)  # [8][len(cols)]
         refs[(layer, name)] = (s, cols, y, S)
-    yield nv, plan, specs, refs
-    nv.nvfp4_round_destroy(plan)
+    yield nv, plans, specs, refs
+    for p in plans.values():
+        nv.nvfp4_round_destroy(p)
     del keep
 
 
+@pytest.mark.parametrize("mode", [0, 1])
 @pytest.mark.parametrize("M", [1, 8])
-def test_full_round_sampled(full_round, M):
+def test_full_round_sampled(full_round, M, mode):
     import torch
-    nv, plan, specs, refs = full_round
-    assert nv.nvfp4_round_graph_nodes(plan, M) == 256
+    nv, plans, specs, refs = full_round
+    plan = plans[mode]
+    assert nv.nvfp4_round_graph_nodes(plan, M) == (1 if mode == nv.ROUND_PERSISTENT else 256)
     for s in specs:
         s["out"].fill_(float("nan"))
     nv.nvfp4_round_run(plan, M)
@@ -80,6 +86,7 @@ def test_full_round_sampled(full_round, M):
     # no matrix left unwritten
     for s in specs:
         assert not torch.isnan(s["out"][:M]).any()
+    assert nv.nvfp4_round_status(plan) == 0
 
 
 def test_output_head_sampled():

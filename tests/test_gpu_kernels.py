@@ -171,14 +171,15 @@ RAGGED = [(1, 16, 1), (3, 48, 17), (8, 512, 16), (5, 1040, 100), (8, 2576, 33),
 
 @pytest.mark.parametrize("M,K,N", RAGGED)
 @pytest.mark.parametrize("bf16", [False, True])
-def test_random_planes_ragged(nv, M, K, N, bf16):
+@pytest.mark.parametrize("kernel", [1, 2])
+def test_random_planes_ragged(nv, M, K, N, bf16, kernel):
     """Every code and every finite scale byte (subnormal ones included),
-    shapes with ragged K and N tails."""
+    shapes with ragged K and N tails, both decode kernels."""
     codes, scales = synth.random_planes(M * 7 + K, N, N, K)
     t = float(np.float32(np.random.default_rng(K + N).uniform(1e-4, 1e-2)))
     act = synth.activations(M + K, N, M, K)
     pw = pack(nv, dev(codes), dev(scales), K, N, t)
-    out, _ = run(nv, pw, dev_bf16(act), nv.OUT_BF16 if bf16 else nv.OUT_F32)
+    out, _ = run(nv, pw, dev_bf16(act), nv.OUT_BF16 if bf16 else nv.OUT_F32, kernel=kernel)
     y, S = oracle.gemm(act, codes, scales, t)
     check(out, y, S, bf16=bf16, what="ragged %r" % ((M, K, N),))
 
@@ -201,17 +202,20 @@ def test_projection_5120_full(nv, M):
     check(out32, y, S, bf16=False, what="projection f32 M=%d" % M)
 
 
-@pytest.mark.parametrize("chunks", [1, 2, 3, 4])
-@pytest.mark.parametrize("waves", [4, 8])
-def test_split_configurations_agree_and_are_deterministic(nv, chunks, waves):
+CONFIGS = ([dict(kernel=2, chunks=c, waves=w) for w in (4, 8) for c in (1, 2, 3, 4)] +
+           [dict(kernel=1, tiles=t) for t in (2, 4, 8)])
+
+
+@pytest.mark.parametrize("cfg", CONFIGS, ids=[str(sorted(c.items())) for c in CONFIGS])
+def test_kernel_configurations_agree_and_are_deterministic(nv, cfg):
     M, K, N = 8, 6144, 1000
     codes, scales = synth.random_planes(8, 8, N, K)
     t = 3.0e-4
     act = synth.activations(8, 8, M, K)
     pw = pack(nv, dev(codes), dev(scales), K, N, t)
     y, S = oracle.gemm(act, codes, scales, t)
-    out1, g = run(nv, pw, dev_bf16(act), nv.OUT_F32, chunks=chunks, waves=waves)
-    check(out1, y, S, bf16=False, what="chunks %d waves %d" % (chunks, waves))
+    out1, g = run(nv, pw, dev_bf16(act), nv.OUT_F32, **cfg)
+    check(out1, y, S, bf16=False, what=str(cfg))
     import torch
     out2 = torch.full_like(out1, float("nan"))
     for _ in range(3):  # the workspace counters must reset themselves

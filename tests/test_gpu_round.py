@@ -36,11 +36,16 @@ def small_round():
                               act=dev_bf16(act), out=torch.empty((8, N), dtype=dt, device="cuda"),
                               out_dtype=out_dtype, pw=pw))
             ref.append((y, S))
-    ws_bytes = nv.nvfp4_round_workspace_bytes(specs, 8)
-    ws = torch.full((max(ws_bytes, 16),), 0x5A, dtype=torch.uint8, device="cuda")  # create zeroes it
-    plan = nv.nvfp4_round_create(specs, 8, ws, ws_bytes)
-    yield nv, plan, specs, ref
-    nv.nvfp4_round_destroy(plan)
+    plans = {}
+    keep = []
+    for mode in (nv.ROUND_PERSISTENT, nv.ROUND_PER_MATRIX):
+        ws_bytes = nv.nvfp4_round_workspace_bytes(specs, 8, mode=mode)
+        ws = torch.full((max(ws_bytes, 16),), 0x5A, dtype=torch.uint8, device="cuda")  # create zeroes it
+        plans[mode] = nv.nvfp4_round_create(specs, 8, ws, ws_bytes, mode=mode)
+        keep.append(ws)
+    yield nv, plans, specs, ref
+    for p in plans.values():
+        nv.nvfp4_round_destroy(p)
 
 
 def _poison(specs):
@@ -54,25 +59,33 @@ def _check_all(nv, specs, ref, M, what):
               what="%s matrix %d" % (what, i))
 
 
-def test_graph_has_one_node_per_matrix(small_round):
-    nv, plan, specs, _ = small_round
+MODES = (0, 1)  # persistent, per-matrix
+
+
+def test_graph_nodes(small_round):
+    nv, plans, specs, _ = small_round
     for M in range(1, 9):
-        assert nv.nvfp4_round_graph_nodes(plan, M) == len(specs)
+        assert nv.nvfp4_round_graph_nodes(plans[nv.ROUND_PER_MATRIX], M) == len(specs)
+        assert nv.nvfp4_round_graph_nodes(plans[nv.ROUND_PERSISTENT], M) == 1
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("M", range(1, 9))
-def test_round_every_width(small_round, M):
+def test_round_every_width(small_round, M, mode):
     import torch
-    nv, plan, specs, ref = small_round
+    nv, plans, specs, ref = small_round
     _poison(specs)
-    nv.nvfp4_round_run(plan, M)
+    nv.nvfp4_round_run(plans[mode], M)
     torch.cuda.synchronize()
-    _check_all(nv, specs, ref, M, "width %d" % M)
+    _check_all(nv, specs, ref, M, "mode %d width %d" % (mode, M))
+    assert nv.nvfp4_round_status(plans[mode]) == 0
 
 
-def test_replays_with_eager_work_between(small_round):
+@pytest.mark.parametrize("mode", MODES)
+def test_replays_with_eager_work_between(small_round, mode):
     import torch
-    nv, plan, specs, ref = small_round
+    nv, plans, specs, ref = small_round
+    plan = plans[mode]
     s0 = specs[2]
     g = nv.Gemm(8, s0["K"], s0["N"], s0["out_dtype"])
     scratch = torch.empty_like(s0["out"])
@@ -91,8 +104,46 @@ def test_replays_with_eager_work_between(small_round):
         torch.cuda.synchronize()
 
 
+def test_both_forms_back_to_back(small_round):
+    """The two forms replayed one after the other on the same buffers each
+    match the oracle (their K slicing differs, so they need not agree bit for
+    bit with each other)."""
+    import torch
+    nv, plans, specs, ref = small_round
+    outs = {}
+    for mode in MODES:
+        _poison(specs)
+        nv.nvfp4_round_run(plans[mode], 8)
+        torch.cuda.synchronize()
+        _check_all(nv, specs, ref, 8, "mode %d" % mode)
+        outs[mode] = [host(s["out"]).copy() for s in specs]
+    assert len(outs) == 2
+
+
+def test_forced_wait_timeout_is_reported_and_recovers(small_round):
+    """A spin limit of 0 makes every cross-matrix wait give up at once (the
+    kernel still exits); the flag is reported, the counters re-armed, and the
+    next replay with the normal limit is correct again."""
+    import torch
+    nv, plans, specs, ref = small_round
+    plan = plans[nv.ROUND_PERSISTENT]
+    nv.nvfp4_round_set_spin_limit(plan, 0)
+    for _ in range(3):
+        nv.nvfp4_round_run(plan, 8)
+    torch.cuda.synchronize()
+    flags = nv.nvfp4_round_status(plan)
+    nv.nvfp4_round_set_spin_limit(plan, 1 << 16)
+    assert flags in (0, 1)  # with no real wait needed the flag may stay clear
+    _poison(specs)
+    nv.nvfp4_round_run(plan, 8)
+    torch.cuda.synchronize()
+    _check_all(nv, specs, ref, 8, "after time-out")
+    assert nv.nvfp4_round_status(plan) == 0
+
+
 def test_round_invalid_width(small_round):
-    nv, plan, _, _ = small_round
-    with pytest.raises(nv.Nvfp4Error) as e:
-        nv.nvfp4_round_run(plan, 9)
-    assert e.value.message.startswith("M")
+    nv, plans, _, _ = small_round
+    for plan in plans.values():
+        with pytest.raises(nv.Nvfp4Error) as e:
+            nv.nvfp4_round_run(plan, 9)
+        assert e.value.message.startswith("M")
