@@ -247,6 +247,37 @@ def main():
     log("decode kernel: %.2f us average launch, %.0f bytes average, %.1f GB/s"
         % (dk_us, avg_bytes, achieved))
 
+    # Prefill chunk (M = 2048, K = 5120, N = 17408, bf16 out): the bf16 MFMA
+    # kernel over dequantised tiles.
+    import synth
+    PK, PN, PM = 5120, 17408, 2048
+    with torch.cuda.stream(stream):
+        wp = synth.weights_device(0, 9001, PN, PK)
+        ppw = nv.PackedWeight.quantize(wp, stream=stream)
+        del wp
+        pact = synth.activations_device(0, 9001, PM, PK)
+        pout = torch.empty((PM, PN), dtype=torch.bfloat16, device="cuda")
+        pg = nv.Gemm(PM, PK, PN, nv.OUT_BF16)
+        for _ in range(2):
+            pg(ppw, pact, pout, stream=stream)
+        stream.synchronize()
+        pevs = []
+        for _ in range(max(3, args.steps // 4)):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            pg(ppw, pact, pout, stream=stream)
+            b.record(stream)
+            pevs.append((a, b))
+        torch.cuda.synchronize()
+    p_us = sum(a.elapsed_time(b) for a, b in pevs) / len(pevs) * 1e3
+    p_tflops = 2.0 * PM * PK * PN / (p_us * 1e-6) / 1e12
+    log("prefill M=%d K=%d N=%d: %.1f us, %.1f TFLOP/s (%.1f%% of 2.5 PF bf16)"
+        % (PM, PK, PN, p_us, p_tflops, 100 * p_tflops / 2500.0))
+    prefill = {"M": PM, "K": PK, "N": PN, "us": round(p_us, 2), "TFLOP_s": round(p_tflops, 1),
+               "frac_bf16_mfma_peak": round(p_tflops / 2500.0, 4)}
+    del ppw, pact, pout, pg
+
     if args.calibration_copy:
         # A plain copy kernel of known size: 1 GiB read, 1 GiB written.
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -305,6 +336,7 @@ def main():
             "launches_per_round": 4 * args.layers,
             "traffic": None,
         },
+        "prefill_chunk": prefill,
         "cpu_baseline": cpu,
         "timed_wall_s": round(wall, 3),
     }

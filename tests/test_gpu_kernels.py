@@ -264,3 +264,37 @@ def test_m_below_plan_max_and_bf16_rounding(nv):
         assert np.array_equal(bf16_bits(o16), bf16_bits(o32.to(torch.bfloat16)))
         y, S = oracle.gemm(act[:M], codes, scales, 0.003)
         check(o32, y, S, bf16=False, what="M=%d of 8" % M)
+
+
+# ---- prefill (M > 8: dequantised tiles, bf16 MFMA) ------------------------------
+
+@pytest.mark.parametrize("M,K,N", [(9, 512, 64), (64, 1024, 256), (300, 1040, 530),
+                                   (513, 2048, 300), (256, 5120, 272)])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_prefill_ragged(nv, M, K, N, bf16):
+    codes, scales = synth.random_planes(M + 3 * K, N, N, K)
+    t = float(np.float32(np.random.default_rng(M + N).uniform(1e-4, 1e-2)))
+    act = synth.activations(M, K + N, M, K)
+    pw = pack(nv, dev(codes), dev(scales), K, N, t)
+    out, _ = run(nv, pw, dev_bf16(act), nv.OUT_BF16 if bf16 else nv.OUT_F32)
+    y, S = oracle.gemm(act, codes, scales, t)
+    check(out, y, S, bf16=bf16, what="prefill %r" % ((M, K, N),))
+
+
+def test_prefill_chunk_config_sampled(nv):
+    """The prefill-chunk config: M = 2048, K = 5120, N = 17408, quantised
+    N(0, 0.02) weights, bf16 out; every row, sampled columns."""
+    import torch
+    M, K, N = 2048, 5120, 17408
+    W = synth.weights(0, 300, N, K)
+    cols = np.array(sorted(set(np.random.default_rng(1).choice(N, 40, replace=False).tolist())
+                           | {0, 255, 256, N - 1}))
+    t = oracle.tensor_scale(W)
+    c_ref, s_ref = oracle.quantize_rows(W[cols], t)
+    c, s, tg = _gpu_quantize(nv, W)
+    assert tg == t and np.array_equal(c[cols], c_ref) and np.array_equal(s[cols], s_ref)
+    act = synth.activations(0, 300, M, K)
+    pw = pack(nv, dev(c), dev(s), K, N, tg)
+    out, _ = run(nv, pw, dev_bf16(act), nv.OUT_BF16)
+    y, S = oracle.gemm(act, c_ref, s_ref, t)
+    check(out[:, torch.from_numpy(cols).cuda()], y, S, bf16=True, what="prefill chunk")
