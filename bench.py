@@ -9,8 +9,9 @@ Prints one JSON line (rank 0):
   value        = algorithmic bytes of the round (NVFP4 weights + bf16
                  activations in + bf16 outputs) / device time per round, GB/s
   roofline     = the decode kernel: average algorithmic bytes per launch over
-                 the round's matrices / average launch duration (HIP events
-                 around each launch) against the MI355X HBM peak of 8 TB/s
+                 the round's matrices / average launch duration (the timed
+                 region's HIP event time over the round's launches) against
+                 the MI355X HBM peak of 8 TB/s
   cpu_baseline = the CPU oracle timed on the host's cores on a bounded sample
                  of the same workload (see cpu_baseline() below)
 
@@ -34,6 +35,34 @@ LAYERS = 64
 ROUND_SHAPES = (("qkv", 5120, 7168), ("o", 6144, 5120), ("gate_up", 5120, 34816),
                 ("down", 17408, 5120))
 METRIC = "NVFP4 decode GEMM GB/s & % HBM peak at M=1..8; 27B-class round ms"
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_traffic.json")
+KERNEL_SOURCES = ("nvfp4_weight_streaming_amd/csrc/decode.hip",
+                  "nvfp4_weight_streaming_amd/csrc/decode_device.h")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter runs
+    (FETCH_SIZE and WRITE_SIZE, each scaled by its reading for a plain copy of
+    known size), or None if the kernel sources changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t
 
 
 def weight_bytes(K, N):
@@ -91,35 +120,45 @@ def build_round(nv, seed=0, layers=LAYERS, max_M=8, log=None):
     return specs, keep
 
 
-def cpu_baseline(rows=None, lanes=8, threads=None):
+def cpu_baseline(layers=None, lanes=8, threads=None):
     """The CPU oracle, as it stands, on a bounded sample of the round: the
-    first `rows` output columns of each of layer 0's four matrices, M = 8
-    lanes.  Quantisation of the sample (with the oracle's quantiser) is not
-    timed; the oracle GEMM is.  Returns (GB/s of NVFP4 weights processed,
-    threads, sample description, seconds)."""
+    first `layers` layers' four matrices in full (default four layers, 335.5 M
+    weights each), M = 8 lanes.  Drawing and quantising the sample (with the
+    oracle's quantiser, rows split over threads) is not timed; the oracle GEMM
+    is.  Returns (GB/s of NVFP4 weights processed, threads, sample
+    description, seconds)."""
+    from concurrent.futures import ThreadPoolExecutor
     import numpy as np
     import oracle
     import synth
     if threads is None:
         threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    if rows is None:
-        rows = int(os.environ.get("NVFP4_CPU_SAMPLE_ROWS", "1024"))
+    if layers is None:
+        layers = int(os.environ.get("NVFP4_CPU_SAMPLE_LAYERS", "4"))
     oracle.build()
-    work = []
-    for name, K, N in ROUND_SHAPES:
-        W = synth.weights(0, synth.stream_id(0, name), rows, K)
-        codes, scales, t = oracle.quantize(W)
-        act = synth.activations(0, synth.stream_id(0, name), lanes, K)
-        work.append((K, codes, scales, t, act))
-    t0 = time.perf_counter()
-    nbytes = 0
-    for K, codes, scales, t, act in work:
-        oracle.gemm(act, codes, scales, t, threads=threads)
-        nbytes += weight_bytes(K, rows)
-    dt = time.perf_counter() - t0
-    desc = ("oracle GEMM (fp64, exact dequantisation) on the first %d output columns of each "
-            "of layer 0's qkv/o/gate_up/down matrices, M=%d lanes; %d weight bytes in %.2f s"
-            % (rows, lanes, nbytes, dt))
+    dt, nbytes = 0.0, 0
+    with ThreadPoolExecutor(threads) as pool:
+        for layer in range(layers):
+            for name, K, N in ROUND_SHAPES:
+                sid = synth.stream_id(layer, name)
+                W = synth.weights(0, sid, N, K)
+                t = oracle.tensor_scale(W)
+                bounds = [N * i // threads for i in range(threads + 1)]
+                parts = list(pool.map(lambda ab: oracle.quantize_rows(W[ab[0]:ab[1]], t),
+                                      zip(bounds[:-1], bounds[1:])))
+                del W
+                codes = np.concatenate([c for c, _ in parts])
+                scales = np.concatenate([s for _, s in parts])
+                del parts
+                act = synth.activations(0, sid, lanes, K)
+                t0 = time.perf_counter()
+                oracle.gemm(act, codes, scales, t, threads=threads)
+                dt += time.perf_counter() - t0
+                nbytes += weight_bytes(K, N)
+    desc = ("oracle GEMM (fp64, exact dequantisation) over layer%s 0%s of the round in full "
+            "(qkv, o, gate_up, down), M=%d lanes: %d weight bytes in %.2f s"
+            % ("s" if layers > 1 else "", "..%d" % (layers - 1) if layers > 1 else "", lanes,
+               nbytes, dt))
     return nbytes / dt / 1e9, threads, desc, dt
 
 
@@ -130,6 +169,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=LAYERS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the M=1..8 sweep (profiling runs: keep only M=8 launches)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (for scaling memory counters)")
     ap.add_argument("--quiet", action="store_true")
@@ -205,7 +246,7 @@ def main():
     log("M=8 round: %.3f ms, %.1f GB/s (%.1f%% of 8 TB/s)" % (ms8, gbs8, 100 * gbs8 / HBM_PEAK_GBS))
 
     sweep, sweep_ps = {}, {}
-    for M in range(1, 9):
+    for M in ([] if args.no_sweep else range(1, 9)):
         for mode, tab in ((nv.ROUND_PER_MATRIX, sweep), (nv.ROUND_PERSISTENT, sweep_ps)):
             ms = time_round(plans[mode], M, max(5, args.steps // 2), 2)
             gbs = round_bytes(M, args.layers) / (ms * 1e-3) / 1e9
@@ -216,33 +257,13 @@ def main():
     flags = nv.nvfp4_round_status(persistent)
     assert flags == 0, "persistent round wait timed out (flags %d)" % flags
 
-    # Roofline of the dominant kernel, the decode kernel (one launch per
-    # matrix): the same matrices launched one at a time with HIP events around
-    # each launch, on the stream they run on.
-    gplans = {}
-    for _, K, N in ROUND_SHAPES:
-        gplans[(K, N)] = nv.Gemm(8, K, N, nv.OUT_BF16)
-    dur, nbytes = [], []
-    with torch.cuda.stream(stream):
-        for r in range(3):
-            evs = []
-            for sp in specs:
-                a = torch.cuda.Event(enable_timing=True)
-                b = torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                g = gplans[(sp["K"], sp["N"])]
-                nv.nvfp4_gemm_run(g.plan, 8, sp["K"], sp["N"], sp["codes"], sp["scales"],
-                                  sp["tensor_scale"], sp["act"], sp["out"], g.workspace, stream)
-                b.record(stream)
-                evs.append((a, b, sp))
-            torch.cuda.synchronize()
-            if r == 0:
-                continue  # warm-up pass
-            for a, b, sp in evs:
-                dur.append(a.elapsed_time(b) * 1e-3)
-                nbytes.append(weight_bytes(sp["K"], sp["N"]) + 8 * sp["K"] * 2 + 8 * sp["N"] * 2)
-    dk_us = sum(dur) / len(dur) * 1e6
-    avg_bytes = sum(nbytes) / len(nbytes)
+    # Roofline of the dominant kernel.  The M = 8 round graph runs nothing but
+    # decode kernels, one per matrix, in sequence on `stream`, so its average
+    # launch duration is the timed region's event time over the launches (it
+    # includes the short gaps between graph nodes, so it is an upper bound).
+    launches = nodes[nv.ROUND_PER_MATRIX]
+    dk_us = ms8 * 1e3 / launches
+    avg_bytes = bytes8 / launches
     achieved = avg_bytes / (dk_us * 1e-6) / 1e9
     log("decode kernel: %.2f us average launch, %.0f bytes average, %.1f GB/s"
         % (dk_us, avg_bytes, achieved))
@@ -295,6 +316,10 @@ def main():
 
     for p in plans.values():
         nv.nvfp4_round_destroy(p)
+    tr = measured_traffic()
+    traffic = None
+    if tr is not None:
+        traffic = round(tr["fetch_bytes_per_launch"] + tr["write_bytes_per_launch"])
     line = {
         "metric": METRIC,
         "value": round(gbs8, 2),
@@ -334,7 +359,7 @@ def main():
             "avg_launch_us": round(dk_us, 3),
             "avg_algorithmic_bytes_per_launch": round(avg_bytes),
             "launches_per_round": 4 * args.layers,
-            "traffic": None,
+            "traffic": traffic,
         },
         "prefill_chunk": prefill,
         "cpu_baseline": cpu,

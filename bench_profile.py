@@ -1,0 +1,235 @@
+"""rocprofv3 runs behind the benchmark's roofline figures, and their summaries.
+
+Runs bench.py (M = 8 round only, no CPU leg, plus one plain 1 GiB device copy)
+three times under rocprofv3 -- a kernel trace with statistics, then a
+FETCH_SIZE pass and a WRITE_SIZE pass, each in a run of its own -- and writes
+short text summaries to profiles/:
+
+  decode_round_m8_kernel_trace.md   per-kernel durations, per-shape decode
+                                    averages, agreement with bench.py's own
+                                    event-timed average launch
+  decode_round_m8_hbm_counters.md   HBM bytes per decode launch from the two
+                                    counter passes, each scaled by its reading
+                                    for the plain copy of known size
+  decode_kernel_traffic.json        the same bytes for bench.py, tagged with a
+                                    hash of the decode kernel sources (bench.py
+                                    reports them only while the hash matches)
+
+Usage (on a machine with the GPU):  python3 bench_profile.py --out DIR
+`--summarize-only` rebuilds the summaries from DIR without profiling.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402  (host-only helpers; importing it touches no GPU)
+
+BENCH_ARGS = ["--steps", "10", "--warmup", "2", "--no-cpu-baseline", "--no-sweep",
+              "--calibration-copy"]
+PASSES = (
+    ("trace", ["--kernel-trace", "--stats"], 600),
+    ("fetch", ["--pmc", "FETCH_SIZE"], 300),
+    ("write", ["--pmc", "WRITE_SIZE"], 300),
+)
+CALIB_BYTES = 1 << 30
+DECODE = "nvfp4::decode_kernel<"
+PREFILL = "nvfp4::prefill_kernel<"
+COPY = "__amd_rocclr_copyBuffer"
+
+
+def rocprof_cmd(flags, out_dir):
+    return (["rocprofv3"] + flags + ["--output-format", "csv", "-d", out_dir, "-o", "run", "--",
+                                     "python3", "-u", os.path.join(ROOT, "bench.py")] + BENCH_ARGS)
+
+
+def shown(cmd):
+    return " ".join(os.path.relpath(c, ROOT) if c.startswith(ROOT) else c for c in cmd)
+
+
+def run_passes(out):
+    env = dict(os.environ, TMPDIR="/tmp")
+    for name, flags, limit in PASSES:
+        d = os.path.join(out, name)
+        cmd = rocprof_cmd(flags, d)
+        print("== %s: %s" % (name, shown(cmd)), flush=True)
+        with open(os.path.join(out, name + ".log"), "w") as log:
+            r = subprocess.run(["timeout", "-s", "KILL", str(limit)] + cmd, cwd="/tmp", env=env,
+                               stdout=log, stderr=subprocess.STDOUT)
+        if r.returncode != 0:
+            print("pass %s failed with status %d" % (name, r.returncode), flush=True)
+            sys.exit(r.returncode)
+
+
+def find_csv(d, suffix):
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    raise FileNotFoundError("no *%s under %s" % (suffix, d))
+
+
+def bench_line(log_path):
+    with open(log_path) as f:
+        for line in f:
+            if line.startswith("{\"metric\""):
+                return json.loads(line)
+    raise ValueError("no bench JSON line in " + log_path)
+
+
+def short(name):
+    n = name.split("(")[0]
+    return n.replace("void ", "")
+
+
+def summarize(out, dest):
+    line = bench_line(os.path.join(out, "trace.log"))
+    trace = list(csv.DictReader(open(find_csv(os.path.join(out, "trace"), "kernel_trace.csv"))))
+    stats = list(csv.DictReader(open(find_csv(os.path.join(out, "trace"), "kernel_stats.csv"))))
+
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+    dec = [r for r in trace if DECODE in r["Kernel_Name"]]
+    pre = [r for r in trace if PREFILL in r["Kernel_Name"]]
+    dur = lambda r: int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    dec_avg_us = sum(map(dur, dec)) / len(dec) / 1e3
+    pre_avg_us = sum(map(dur, pre)) / len(pre) / 1e3 if pre else float("nan")
+
+    # the first replay's first four launches are layer 0's qkv, o, gate_up, down
+    layers = bench.LAYERS
+    per_round = 4 * layers
+    names = {}
+    for i, r in enumerate(dec[:4]):
+        names[(r["Kernel_Name"], r["Grid_Size_X"])] = bench.ROUND_SHAPES[i]
+    by_shape = collections.defaultdict(list)
+    for r in dec:
+        by_shape[(r["Kernel_Name"], r["Grid_Size_X"])].append(dur(r))
+
+    roof = line["roofline"]
+    algo = roof["avg_algorithmic_bytes_per_launch"]
+    cmd_trace = shown(rocprof_cmd(PASSES[0][1], "OUT/trace"))
+    md = []
+    md.append("# Decode round (M = 8) and prefill chunk: kernel trace\n")
+    md.append("Command (from the repository root, with `TMPDIR=/tmp`, run in /tmp):\n")
+    md.append("    python3 bench_profile.py --out OUT\n")
+    md.append("which runs, for this pass:\n")
+    md.append("    " + cmd_trace + "\n")
+    md.append("Workload: 27B-class round, 64 layers x {qkv 5120x7168, o 6144x5120, gate_up "
+              "5120x34816, down 17408x5120} (K x N), NVFP4 weights, bf16 activations and "
+              "outputs, M = 8 lanes, %d warm-up + %d timed graph replays (%d decode launches "
+              "each); prefill chunk M = 2048, K = 5120, N = 17408.\n"
+              % (line["warmup"], line["steps"], per_round))
+    md.append("## Agreement with bench.py's event timing (same run)\n")
+    md.append("| figure | bench.py (HIP events) | rocprofv3 kernel trace |")
+    md.append("|---|---|---|")
+    md.append("| decode kernel, average launch (us) | %.3f | %.3f |" % (roof["avg_launch_us"],
+                                                                        dec_avg_us))
+    md.append("| decode kernel, GB/s (algorithmic %d B per launch) | %.1f | %.1f |"
+              % (algo, roof["achieved"], algo / (dec_avg_us * 1e-6) / 1e9))
+    md.append("| M = 8 round (ms) | %.4f | %.4f (sum of kernel durations / replays) |"
+              % (line["ms_per_step"], sum(map(dur, dec)) / (len(dec) / per_round) / 1e6))
+    md.append("| prefill kernel (us) | %.2f | %.2f |\n" % (line["prefill_chunk"]["us"],
+                                                           pre_avg_us))
+    md.append("bench.py's average launch is the timed region's event time over the %d "
+              "launches of a replay, so it includes the gaps between graph nodes; the "
+              "trace's figure is kernel time only.\n" % per_round)
+    md.append("## Decode kernel per matrix shape\n")
+    md.append("| matrix (K x N) | kernel | grid (threads) | launches | average (us) | "
+              "algorithmic GB/s |")
+    md.append("|---|---|---|---|---|---|")
+    for key, ds in by_shape.items():
+        name, K, N = names.get(key, ("?", 0, 0))
+        nbytes = bench.weight_bytes(K, N) + 8 * K * 2 + 8 * N * 2
+        avg = sum(ds) / len(ds)
+        md.append("| %s %dx%d | %s | %s | %d | %.2f | %.1f |"
+                  % (name, K, N, short(key[0]), key[1], len(ds), avg / 1e3, nbytes / avg))
+    md.append("\n## All kernels in the run (rocprofv3 --stats)\n")
+    md.append("| kernel | calls | average (us) | min (us) | max (us) | % of GPU time |")
+    md.append("|---|---|---|---|---|---|")
+    for r in stats[:14]:
+        md.append("| %s | %s | %.2f | %.2f | %.2f | %s |"
+                  % (short(r["Name"])[:90], r["Calls"], float(r["AverageNs"]) / 1e3,
+                     float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, r["Percentage"]))
+    md.append("\nKernels other than decode, prefill and the copy belong to building the "
+              "inputs (weight draws, quantiser, packing) before the timed region.\n")
+    with open(os.path.join(dest, "decode_round_m8_kernel_trace.md"), "w") as f:
+        f.write("\n".join(md))
+
+    # ---- counters
+    def counter(pass_name):
+        rows = list(csv.DictReader(open(find_csv(os.path.join(out, pass_name),
+                                                 "counter_collection.csv"))))
+        per = collections.defaultdict(float)
+        meta = {}
+        for r in rows:
+            k = int(r["Dispatch_Id"])
+            per[k] += float(r["Counter_Value"])
+            meta[k] = (r["Kernel_Name"], r["Grid_Size"])
+        dec_v = [v for k, v in per.items() if DECODE in meta[k][0]]
+        cal = max(v for k, v in per.items() if COPY in meta[k][0])
+        return dec_v, cal, len(dec_v)
+
+    f_dec, f_cal, nf = counter("fetch")
+    w_dec, w_cal, nw = counter("write")
+    f_factor = CALIB_BYTES / (f_cal * 1024)
+    w_factor = CALIB_BYTES / (w_cal * 1024)
+    fetch_b = sum(f_dec) / nf * 1024 * f_factor
+    write_b = sum(w_dec) / nw * 1024 * w_factor
+    md = []
+    md.append("# Decode kernel (M = 8 round): HBM traffic per launch\n")
+    md.append("Commands (from the repository root, with `TMPDIR=/tmp`, run in /tmp), each a "
+              "run of its own via `python3 bench_profile.py --out OUT`:\n")
+    md.append("    " + shown(rocprof_cmd(PASSES[1][1], "OUT/fetch")))
+    md.append("    " + shown(rocprof_cmd(PASSES[2][1], "OUT/write")) + "\n")
+    md.append("Calibration: the same runs include one plain device copy of 1 GiB "
+              "(`%s`, 1 GiB read and 1 GiB written).\n" % COPY)
+    md.append("| counter | copy reading (KiB) | expected (KiB) | scale factor |")
+    md.append("|---|---|---|---|")
+    md.append("| FETCH_SIZE | %.0f | %d | %.4f |" % (f_cal, CALIB_BYTES // 1024, f_factor))
+    md.append("| WRITE_SIZE | %.0f | %d | %.4f |\n" % (w_cal, CALIB_BYTES // 1024, w_factor))
+    md.append("| per decode launch (average over %d launches) | bytes |" % nf)
+    md.append("|---|---|")
+    md.append("| FETCH_SIZE x factor | %.0f |" % fetch_b)
+    md.append("| WRITE_SIZE x factor | %.0f |" % write_b)
+    md.append("| HBM traffic | %.0f |" % (fetch_b + write_b))
+    md.append("| algorithmic (weights + activations in + bf16 out) | %d |" % algo)
+    md.append("| traffic / algorithmic | %.3f |\n" % ((fetch_b + write_b) / algo))
+    with open(os.path.join(dest, "decode_round_m8_hbm_counters.md"), "w") as f:
+        f.write("\n".join(md))
+    with open(os.path.join(dest, "decode_kernel_traffic.json"), "w") as f:
+        json.dump({"kernel_source_hash": bench.kernel_source_hash(),
+                   "fetch_bytes_per_launch": round(fetch_b),
+                   "write_bytes_per_launch": round(write_b),
+                   "algorithmic_bytes_per_launch": algo,
+                   "launches": nf,
+                   "fetch_scale": round(f_factor, 4), "write_scale": round(w_factor, 4),
+                   "workload": "M = 8 27B-class round, all 256 decode launches per replay"},
+                  f, indent=1)
+        f.write("\n")
+    print("decode: trace %.3f us vs bench %.3f us; traffic %.0f B vs algorithmic %d B"
+          % (dec_avg_us, roof["avg_launch_us"], fetch_b + write_b, algo))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--out", required=True, help="directory for rocprofv3 output and logs")
+    ap.add_argument("--summarize-only", action="store_true")
+    ap.add_argument("--dest", default=os.path.join(ROOT, "profiles"))
+    args = ap.parse_args()
+    out = os.path.abspath(args.out)
+    os.makedirs(out, exist_ok=True)
+    if not args.summarize_only:
+        run_passes(out)
+    os.makedirs(args.dest, exist_ok=True)
+    summarize(out, args.dest)
+
+
+if __name__ == "__main__":
+    main()
