@@ -21,8 +21,21 @@ FLAGS = [
 ]
 
 
+# The prefill kernel keeps its 256 accumulators per lane in the accumulation
+# registers, so it is built without the VGPR form.
+AGPR_SOURCES = ("prefill.hip",)
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def flags_for(src):
+    fl = [f for f in FLAGS if f != "-shared"]
+    if os.path.basename(src) in AGPR_SOURCES:
+        i = fl.index("-amdgpu-mfma-vgpr-form")
+        del fl[i - 1:i + 1]
+    return fl
 
 
 def build(verbose: bool = False) -> str:
@@ -32,7 +45,7 @@ def build(verbose: bool = False) -> str:
     procs = []
     for src in sources():
         obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
-        cmd = [HIPCC] + [f for f in FLAGS if f != "-shared"] + ["-c", src, "-o", obj]
+        cmd = [HIPCC] + flags_for(src) + ["-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

@@ -99,7 +99,6 @@ int run_gemm(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_
         return NVFP4_OK;
     }
     return launch_decode(p, M, codes, scales, ts, act, out, ws, partial_off, s);
-    return launch_prefill(p, M, codes, scales, ts, act, out, ws, s);
 }
 
 }  // namespace nvfp4

@@ -132,17 +132,18 @@ struct ActStage {
 
 // Sum, in split order, the `splits` partial sums of output (mm, c) of one
 // column group (layout [split][8 rows][kCols]); l2_local: written with plain
-// stores into this XCD's L2, else with device-coherent stores.  The loads are issued in batches of 8 before any is
-// added, so the reduction costs ceil(splits / 8) memory round trips, not
-// `splits`.
+// stores into this XCD's L2, else with device-coherent stores.  The loads are
+// issued in batches of 16 before any is added, so the reduction costs
+// ceil(splits / 16) memory round trips, not `splits`.
 template <int kCols>
 __device__ __forceinline__ float sum_partials(const float* gbase, int splits, int mm, int c,
                                               int l2_local = 0) {
+    constexpr int kBatch = 16;
     float sum = 0.f;
-    for (int s0 = 0; s0 < splits; s0 += 8) {
-        float v[8];
+    for (int s0 = 0; s0 < splits; s0 += kBatch) {
+        float v[kBatch];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
+        for (int t = 0; t < kBatch; ++t) {
             const float* src = gbase + (size_t)((s0 + t) * 8 + mm) * kCols + c;
             v[t] = (s0 + t < splits)
                        ? (l2_local ? *src
@@ -151,7 +152,7 @@ __device__ __forceinline__ float sum_partials(const float* gbase, int splits, in
                        : 0.f;
         }
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
+        for (int t = 0; t < kBatch; ++t)
             if (s0 + t < splits) sum += v[t];
     }
     return sum;

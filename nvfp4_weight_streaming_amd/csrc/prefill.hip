@@ -12,12 +12,21 @@
 // is exact.  The per-tensor fp32 scale is applied to the fp32 accumulators in
 // the epilogue.
 //
-// Tiling: block tile 256 (rows of activations) x 256 (outputs) x 128 (K, one
-// 128-value slice of the packed layout, so the weights are read as stored);
-// 8 waves as 2 x 4, each owning 128 x 64 outputs as 4 x 2 MFMA tiles of 32 x 32
-// (128 fp32 accumulators per lane).  The next K tile is loaded into registers
-// while the current one is multiplied; LDS holds one activation tile and one
-// dequantised weight tile.
+// Tiling: block tile 256 (rows of activations) x 256 (outputs), K in stages of
+// 64, double-buffered in LDS (two stages of 256 x 64 activations and 256 x 64
+// dequantised weights, 128 KiB).  8 waves as 2 x 4, each owning 128 x 64
+// outputs as 4 x 2 MFMA tiles of 32 x 32 (128 fp32 accumulators per lane, in
+// the accumulation registers); two waves per SIMD, so one multiplies while
+// the other waits on memory.  Two stages are held in registers ahead of
+// the one being multiplied; after the multiply the next is written (weights
+// dequantised on the way) into the other LDS buffer and the one after that is
+// loaded, and one barrier per stage separates the two buffers.  LDS rows are 128 bytes (8 segments of 16): segment j of row r is
+// stored in slot j ^ (r % 8), so the 32 rows an MFMA operand read touches are
+// spread over the banks.
+//
+// Column blocks beyond a multiple of the compute units' worth are run as
+// 128 x 128 tiles (a quarter of the work each), so the last round of
+// workgroups is short instead of mostly idle.
 #include "decode_device.h"
 
 namespace nvfp4 {
@@ -25,43 +34,24 @@ namespace nvfp4 {
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 
-constexpr int kPBM = 256, kPBN = 256, kPBK = 128;
-constexpr int kPThreads = 512;
-constexpr int kPStride = kPBK + 8;  // LDS row: 128 bf16 + 16 B pad
+constexpr int kPBK = 64;          // K per stage
+constexpr int kPThreads = 512;    // 8 waves
+// s_waitcnt vmcnt(n) encodings (vmcnt in bits 3:0 and 15:14; expcnt and
+// lgkmcnt fields at their maxima do not wait).
+constexpr int vmcnt_enc(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+// Loads per thread per stage: weights BN / 64 (BN / 128 lane slots, a code
+// load and a scale load each), activations BM / 64 copies.
 
-// Register-held next tile: activations (8 x 16 B per thread) and packed
-// weights (2 x 16 B of codes and 2 scale words per thread).
-struct PTile {
-    uint4 a[8];
-    uint4 c[2];
-    uint32_t s[2];
+struct PrefillLds {
+    __bf16 a[3][256 * kPBK];  // activations [row][k], swizzled segments: 3 stages
+    __bf16 b[2][256 * kPBK];  // dequantised weights [output][k], swizzled segments
 };
 
-__device__ __forceinline__ void p_load(PTile& t, const uint16_t* __restrict__ act,
-                                       const uint4* __restrict__ codes,
-                                       const uint8_t* __restrict__ scales, int M, int K, int nsb,
-                                       int n_tiles, int m0, int nt0, int kt) {
-    const int k0 = kt * kPBK;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int idx = threadIdx.x + i * kPThreads;  // 256 rows x 16 vectors
-        const int r = idx >> 4, c = idx & 15;
-        const int m = min(m0 + r, M - 1);
-        const int k = min(k0 + 8 * c, K - 8);
-        t.a[i] = *(const uint4*)(act + (size_t)m * K + k);
-    }
-    const int sb = k0 / kSuperK, kb = (k0 % kSuperK) / 128;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int idx = threadIdx.x + i * kPThreads;  // 16 column tiles x 64 lanes
-        const int tl = idx >> 6, lane = idx & 63;
-        const int nt = min(nt0 + tl, n_tiles - 1);
-        t.c[i] = codes[((size_t)nt * nsb + sb) * 256 + kb * 64 + lane];
-        const int col = lane & 15, p = (lane >> 4) >> 1;
-        t.s[i] = *(const uint32_t*)(scales + ((size_t)nt * nsb + sb) * kScaleBytesPerSuper +
-                                    (col * 2 + p) * 16 + kb * 4);
-    }
-}
+// Slot of segment `seg` in LDS row `row`: seg ^ ((row / 2) % 8).  A 16-byte
+// operand read serves 16 lanes (16 consecutive rows, one segment) per pass;
+// with this key those 16 reads cover all 64 banks once.
+__device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz(int row, int seg) { return row * kPBK + 8 * (seg ^ swz_key(row)); }
 
 // 2 codes (byte B of w) times scale sc -> 2 bf16 packed in one word.
 template <int B>
@@ -81,108 +71,249 @@ __device__ __forceinline__ uint4 dequant8(uint32_t w, float sc) {
                       dequant2<3>(w, sc));
 }
 
-// Step S of a packed 16-byte lane chunk: k = 32 S + 8 g .. + 7, block
-// 2 S + g / 2, whose scale is byte S of the lane's scale word.
-template <int S>
-__device__ __forceinline__ void dequant_step(__bf16* row, int g, const uint4& cw, uint32_t sw) {
-    const uint32_t w = S == 0 ? cw.x : S == 1 ? cw.y : S == 2 ? cw.z : cw.w;
-    const float sc = __builtin_amdgcn_cvt_f32_fp8((int)sw, S);
-    *(uint4*)(row + 32 * S + 8 * g) = dequant8(w, sc);
+// Global memory is read through buffer resources (base and size in scalar
+// registers, a 32-bit offset per lane, a scalar offset per stage): compact
+// addressing, and reads past the resource's size return zero.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kRawBuffer = 0x00020000;  // buffer resource word 3: raw 32-bit data
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t prefill_rsrc(const void* base, size_t bytes) {
+    const int n = bytes > 0x7FFFFFFFu ? 0x7FFFFFFF : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kRawBuffer);
 }
 
-__device__ __forceinline__ void p_store(const PTile& t, __bf16* la, __bf16* lb, int M, int K,
-                                        int m0, int kt) {
-    const int k0 = kt * kPBK;
+// Activations of one stage (BM rows x 64 k) go straight from global memory to
+// LDS: one direct-to-LDS load moves 8 rows of 128 bytes; lane i fills slot
+// i % 8 of row i / 8 with the segment that belongs there, (i % 8) ^ key(row).
+// The resource covers rows m0 .. M-1 (rows past M read zero); k past K reads
+// the next row (finite values; the weights past K are zero).  The 8 waves take
+// BM / 64 loads each; voff[i] is this lane's offset for load i.
+template <int BM>
+struct PrefillA {
+    __amdgpu_buffer_rsrc_t rsrc;
+    int voff[BM / 64];
+
+    __device__ __forceinline__ void init(const uint16_t* act, int M, int K, int m0, int wave,
+                                         int lane) {
+        rsrc = prefill_rsrc(act + (size_t)m0 * K, (size_t)(M - m0) * K * 2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int idx = threadIdx.x + i * kPThreads;
-        const int r = idx >> 4, c = idx & 15;
-        const bool keep = m0 + r < M && k0 + 8 * c < K;
-        uint4 v = t.a[i];
-        v.x = keep ? v.x : 0u;
-        v.y = keep ? v.y : 0u;
-        v.z = keep ? v.z : 0u;
-        v.w = keep ? v.w : 0u;
-        *(uint4*)(la + r * kPStride + 8 * c) = v;
+        for (int i = 0; i < BM / 64; ++i) {
+            const int r = (wave * (BM / 64) + i) * 8 + (lane >> 3);
+            voff[i] = r * K * 2 + 16 * ((lane & 7) ^ swz_key(r));
+        }
     }
+
+    __device__ __forceinline__ void copy(__bf16* la, int kt, int wave) const {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int idx = threadIdx.x + i * kPThreads;
-        const int tl = idx >> 6, lane = idx & 63;
-        const int col = lane & 15, g = lane >> 4;
-        __bf16* row = lb + (tl * kTileN + col) * kPStride;  // weight row n of the tile
-        dequant_step<0>(row, g, t.c[i], t.s[i]);
-        dequant_step<1>(row, g, t.c[i], t.s[i]);
-        dequant_step<2>(row, g, t.c[i], t.s[i]);
-        dequant_step<3>(row, g, t.c[i], t.s[i]);
+        for (int i = 0; i < BM / 64; ++i) {
+            const int r0 = (wave * (BM / 64) + i) * 8;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (__attribute__((address_space(3))) void*)(la + r0 * kPBK), 16, voff[i],
+                kt * kPBK * 2, 0, 0);
+        }
+    }
+};
+
+// Weights of one stage held in registers between their global loads and
+// their (dequantising) LDS stores: BN / 16 column tiles x 64 lane slots of
+// the packed layout; a stage of 64 k is half of a slot's 16 bytes (steps 2h,
+// 2h+1 of 128-k chunk kb) plus the two matching scale bytes.  The resources
+// start at the block's first column tile and end at the last real one, so
+// tiles past N read zero.
+template <int BN>
+struct PrefillB {
+    static constexpr int kB = BN / 16 * 64 / kPThreads;
+    __amdgpu_buffer_rsrc_t rc, rs;
+    int coff[kB], soff[kB];
+
+    __device__ __forceinline__ void init(const uint8_t* codes, const uint8_t* scales, int nsb,
+                                         int n_tiles, int nt0) {
+        const size_t tiles = (size_t)(n_tiles - nt0);
+        rc = prefill_rsrc(codes + (size_t)nt0 * nsb * kCodeBytesPerSuper,
+                          tiles * nsb * kCodeBytesPerSuper);
+        rs = prefill_rsrc(scales + (size_t)nt0 * nsb * kScaleBytesPerSuper,
+                          tiles * nsb * kScaleBytesPerSuper);
+#pragma unroll
+        for (int i = 0; i < kB; ++i) {
+            const int u = threadIdx.x + kPThreads * i;
+            const int t = u >> 6, ls = u & 63;
+            const int col = ls & 15, p = (ls >> 4) >> 1;
+            coff[i] = t * nsb * kCodeBytesPerSuper + ls * 16;
+            soff[i] = t * nsb * kScaleBytesPerSuper + (col * 2 + p) * 16;
+        }
+    }
+};
+
+template <int BN>
+struct PStage {
+    static constexpr int kB = BN / 16 * 64 / kPThreads;
+    u32x2 c[kB];
+    uint32_t s[kB];
+
+    __device__ __forceinline__ void load(const PrefillB<BN>& B, int kt) {
+        const int k0 = kt * kPBK;
+        const int sb = k0 / kSuperK, kb = (k0 % kSuperK) / 128, h = (k0 % 128) / 64;
+        const int cso = sb * kCodeBytesPerSuper + kb * 1024 + h * 8;
+        const int sso = sb * kScaleBytesPerSuper + kb * 4 + h * 2;
+#pragma unroll
+        for (int i = 0; i < kB; ++i) {
+            c[i] = __builtin_amdgcn_raw_buffer_load_b64(B.rc, B.coff[i], cso, 0);
+            s[i] = __builtin_amdgcn_raw_buffer_load_b16(B.rs, B.soff[i], sso, 0);
+        }
+    }
+
+    __device__ __forceinline__ void store(__bf16* lb) const {
+#pragma unroll
+        for (int i = 0; i < kB; ++i) {
+            const int u = threadIdx.x + kPThreads * i;
+            const int ls = u & 63;
+            const int col = (u >> 6) * 16 + (ls & 15), g = ls >> 4;
+            const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)s[i], 0);
+            const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)s[i], 1);
+            // step 2h: k = 8 g .. 8 g + 7 of the stage; step 2h + 1: 32 further
+            *(uint4*)(lb + swz(col, g)) = dequant8(c[i].x, s0);
+            *(uint4*)(lb + swz(col, 4 + g)) = dequant8(c[i].y, s1);
+        }
+    }
+};
+
+// The MFMAs of one stage (64 k = 4 steps of 16) for this wave's (BM/64) x
+// (BN/128) tiles.  The operands of step ks + 1 are read from LDS before the
+// multiplies of step ks are issued, so the reads overlap the matrix cores.
+template <int BM, int BN>
+__device__ __forceinline__ void prefill_mma(f32x16 (&acc)[BM / 64][BN / 128], const __bf16* la,
+                                            const __bf16* lb, int wm, int wn, int r32, int half) {
+    constexpr int TI = BM / 64, TJ = BN / 128;
+    bf16x8 av[2][TI], bv[2][TJ];
+    auto read = [&](int ks, int buf) {
+        const int seg = 2 * ks + half;
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+            av[buf][i] = *(const bf16x8*)(la + swz(wm * (BM / 2) + 32 * i + r32, seg));
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+            bv[buf][j] = *(const bf16x8*)(lb + swz(wn * (BN / 4) + 32 * j + r32, seg));
+    };
+    read(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < kPBK / 16; ++ks) {
+        const int buf = ks & 1;
+        if (ks + 1 < kPBK / 16) read(ks + 1, buf ^ 1);
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int j = 0; j < TJ; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[buf][i], bv[buf][j],
+                                                                    acc[i][j], 0, 0, 0);
     }
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(kPThreads) void prefill_kernel(
-    const uint4* __restrict__ codes, const uint8_t* __restrict__ scales,
-    const uint16_t* __restrict__ act, void* __restrict__ out, float ts, int M, int K, int N,
-    int nsb, int n_tiles, int mblocks) {
-    __shared__ __attribute__((aligned(16))) __bf16 la[kPBM * kPStride];
-    __shared__ __attribute__((aligned(16))) __bf16 lb[kPBN * kPStride];
-
-    // Column-block major order with the row blocks of one column block
-    // adjacent in blockIdx, so consecutive workgroups share weight tiles.
-    const int mb = blockIdx.x % mblocks, nb = blockIdx.x / mblocks;
-    const int m0 = mb * kPBM, nt0 = nb * (kPBN / kTileN);
+// One BM x BN block tile; wave w owns rows (w / 4) * BM/2 and columns
+// (w % 4) * BN/4, as (BM/64) x (BN/128) MFMA tiles of 32 x 32.
+template <int BM, int BN, bool BF16>
+__device__ __forceinline__ void prefill_tile(PrefillLds& L, const uint8_t* __restrict__ codes,
+                                             const uint8_t* __restrict__ scales,
+                                             const uint16_t* __restrict__ act,
+                                             void* __restrict__ out, float ts, int M, int K,
+                                             int N, int nsb, int n_tiles, int m0, int n0) {
+    constexpr int TI = BM / 64, TJ = BN / 128;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves, 128 x 64 each
-    const int ktiles = (K + kPBK - 1) / kPBK;
+    const int wm = wave >> 2, wn = wave & 3;
+    const int nt0 = n0 / kTileN;
+    const int nk = (K + kPBK - 1) / kPBK;
 
-    f32x16 acc[4][2];
+    f32x16 acc[TI][TJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    PTile t;
-    p_load(t, act, codes, scales, M, K, nsb, n_tiles, m0, nt0, 0);
-    for (int kt = 0; kt < ktiles; ++kt) {
-        __syncthreads();  // previous tile fully read
-        p_store(t, la, lb, M, K, m0, kt);
-        __syncthreads();
-        if (kt + 1 < ktiles) p_load(t, act, codes, scales, M, K, nsb, n_tiles, m0, nt0, kt + 1);
-        // 8 MFMA k-steps of 16 over the tile.
-        const int r32 = lane & 31, kq = lane >> 5;
-#pragma unroll
-        for (int ks = 0; ks < kPBK / 16; ++ks) {
-            const int kk = 16 * ks + 8 * kq;
-            bf16x8 av[4], bv[2];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                av[i] = *(const bf16x8*)(la + (wm * 128 + 32 * i + r32) * kPStride + kk);
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                bv[j] = *(const bf16x8*)(lb + (wn * 64 + 32 * j + r32) * kPStride + kk);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0,
-                                                                        0, 0);
-        }
-    }
+    // Activations run two stages ahead in three LDS buffers (stage kt in
+    // buffer kt % 3); weights run two stages ahead in registers (st0 / st1
+    // alternately hold stages kt + 1 and kt + 2) and are dequantised into two
+    // LDS buffers (stage kt in buffer kt % 2).  Stages past the end re-read
+    // the last one into buffers nobody reads again.
+    PrefillA<BM> A;
+    A.init(act, M, K, m0, wave, lane);
+    PrefillB<BN> B;
+    B.init(codes, scales, nsb, n_tiles, nt0);
+    PStage<BN> st0, st1;
+    A.copy(L.a[0], 0, wave);
+    A.copy(L.a[1], min(1, nk - 1), wave);
+    st0.load(B, 0);
+    st0.store(L.b[0]);
+    st0.load(B, min(1, nk - 1));
+    st1.load(B, min(2, nk - 1));
+    // Outstanding, oldest first: the loads of stage 1 into st0 and of stage 2
+    // into st1 (BN / 64 each); the activation copies before them are complete.
+    __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * (BN / 64)));
+    __syncthreads();
 
-    // Epilogue: C element (row, col) of a 32 x 32 tile in lane l, register r:
-    // col = l % 32, row = 8 (r / 4) + 4 (l / 32) + r % 4.
+    const int r32 = lane & 31, half = lane >> 5;
+    // Per stage, issued in this order: activation copy of stage kt + 2
+    // (BM / 64 loads), the multiplies, the dequantised store of stage kt + 1,
+    // the weight loads of stage kt + 3 (BN / 64 loads).  Before the barrier the
+    // copy of stage kt + 1 (issued one stage earlier) must have landed: the
+    // loads after it may still be in flight.
+    auto stage = [&](int kt, PStage<BN>& next, int kt_next) {
+        A.copy(L.a[(kt + 2) % 3], min(kt + 2, nk - 1), wave);
+        __builtin_amdgcn_sched_barrier(0);
+        prefill_mma<BM, BN>(acc, L.a[kt % 3], L.b[kt & 1], wm, wn, r32, half);
+        __builtin_amdgcn_sched_barrier(0);
+        next.store(L.b[(kt + 1) & 1]);
+        next.load(B, kt_next);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * (BN / 64) + BM / 64));
+        __syncthreads();
+    };
+    // Unrolled by two so st0 and st1 keep fixed registers (copying a register
+    // set whose loads are in flight would wait for them); an odd last stage
+    // runs after the loop.
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        stage(kt, st0, min(kt + 3, nk - 1));
+        stage(kt + 1, st1, min(kt + 4, nk - 1));
+    }
+    if (kt < nk) stage(kt, st0, min(kt + 3, nk - 1));
+
+    // Epilogue: element r of a 32 x 32 tile in lane l is
+    // (row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32).
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int n = nt0 * kTileN + wn * 64 + 32 * j + (lane & 31);
+        for (int j = 0; j < TJ; ++j) {
+            const int n = n0 + wn * (BN / 4) + 32 * j + r32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const int m = m0 + wm * (BM / 2) + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
                 if (m < M && n < N) store_out<BF16>(out, (size_t)m * N + n, acc[i][j][r] * ts);
             }
         }
+}
+
+// Workgroups 0 .. n_big-1 take 256 x 256 tiles over the first nb_big column
+// blocks (row block = id % mblocks256); the rest take 128 x 128 tiles over
+// the remaining columns.
+template <bool BF16>
+__global__ __launch_bounds__(kPThreads) void prefill_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+    const uint16_t* __restrict__ act, void* __restrict__ out, float ts, int M, int K, int N,
+    int nsb, int n_tiles, int mblocks256, int n_big, int n_col0, int mblocks128) {
+    __shared__ __attribute__((aligned(16))) PrefillLds L;
+    const int b = blockIdx.x;
+    if (b < n_big) {
+        const int mb = b % mblocks256, nb = b / mblocks256;
+        prefill_tile<256, 256, BF16>(L, codes, scales, act, out, ts, M, K, N, nsb, n_tiles,
+                                     mb * 256, nb * 256);
+    } else {
+        const int q = b - n_big;
+        const int mb = q % mblocks128, nb = q / mblocks128;
+        prefill_tile<128, 128, BF16>(L, codes, scales, act, out, ts, M, K, N, nsb, n_tiles,
+                                     mb * 128, n_col0 + nb * 128);
+    }
 }
 
 int make_prefill_config(int max_M, int K, int N, PrefillConfig* out) {
@@ -193,19 +324,48 @@ int make_prefill_config(int max_M, int K, int N, PrefillConfig* out) {
     return NVFP4_OK;
 }
 
+static int prefill_cus() {
+    static int cached = 0;
+    if (cached) return cached;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    cached = cus;
+    return cus;
+}
+
 int launch_prefill(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
                    float ts, const uint16_t* act, void* out, void* ws, hipStream_t s) {
     (void)ws;
-    const int mblocks = (M + kPBM - 1) / kPBM;
-    const int nblocks = (p->Np + kPBN - 1) / kPBN;
     const int n_tiles = p->Np / kTileN, nsb = p->Kp / kSuperK;
-    const dim3 grid((unsigned)(mblocks * nblocks));
+    const int mb256 = (M + 255) / 256, mb128 = (M + 127) / 128;
+    const int nb256 = (p->N + 255) / 256;
+    // Full rounds of 256 x 256 tiles (one workgroup per compute unit at a
+    // time); the column blocks of a last, partial round become 128 x 128
+    // tiles, four per block, when that shortens it.
+    const int cus = prefill_cus();
+    const int tiles = mb256 * nb256;
+    int nb_big = nb256;
+    if (tiles > cus && tiles % cus != 0) {
+        const int full = tiles / cus * cus;  // tiles in full rounds
+        nb_big = full / mb256;               // whole column blocks in them
+    }
+    const int n_big = mb256 * nb_big, n_col0 = nb_big * 256;
+    const int cols_left = p->N > n_col0 ? p->N - n_col0 : 0;
+    const int n_small = mb128 * ((cols_left + 127) / 128);
+    const dim3 grid((unsigned)(n_big + n_small));
     if (p->out_dtype == NVFP4_OUT_BF16)
-        hipLaunchKernelGGL(prefill_kernel<true>, grid, dim3(kPThreads), 0, s, (const uint4*)codes,
-                           scales, act, out, ts, M, p->K, p->N, nsb, n_tiles, mblocks);
+        hipLaunchKernelGGL(prefill_kernel<true>, grid, dim3(kPThreads), 0, s, codes,
+                           scales, act, out, ts, M, p->K, p->N, nsb, n_tiles, mb256, n_big,
+                           n_col0, mb128);
     else
-        hipLaunchKernelGGL(prefill_kernel<false>, grid, dim3(kPThreads), 0, s, (const uint4*)codes,
-                           scales, act, out, ts, M, p->K, p->N, nsb, n_tiles, mblocks);
+        hipLaunchKernelGGL(prefill_kernel<false>, grid, dim3(kPThreads), 0, s, codes,
+                           scales, act, out, ts, M, p->K, p->N, nsb, n_tiles, mb256, n_big,
+                           n_col0, mb128);
     NVFP4_HIP(hipGetLastError());
     return NVFP4_OK;
 }
