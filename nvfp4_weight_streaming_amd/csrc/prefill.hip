@@ -39,6 +39,7 @@ constexpr int kPThreads = 512;    // 8 waves
 // s_waitcnt vmcnt(n) encodings (vmcnt in bits 3:0 and 15:14; expcnt and
 // lgkmcnt fields at their maxima do not wait).
 constexpr int vmcnt_enc(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+constexpr int kPWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
 // Loads per thread per stage: weights BN / 64 (BN / 128 lane slots, a code
 // load and a scale load each), activations BM / 64 copies.
 
@@ -118,7 +119,7 @@ struct PrefillA {
 // Weights of one stage held in registers between their global loads and
 // their (dequantising) LDS stores: BN / 16 column tiles x 64 lane slots of
 // the packed layout; a stage of 64 k is half of a slot's 16 bytes (steps 2h,
-// 2h+1 of 128-k chunk kb) plus the two matching scale bytes.  The resources
+// 2h+1 of 128-k chunk kb) plus bytes 2h, 2h+1 of its scale word.  The resources
 // start at the block's first column tile and end at the last real one, so
 // tiles past N read zero.
 template <int BN>
@@ -155,22 +156,26 @@ struct PStage {
         const int k0 = kt * kPBK;
         const int sb = k0 / kSuperK, kb = (k0 % kSuperK) / 128, h = (k0 % 128) / 64;
         const int cso = sb * kCodeBytesPerSuper + kb * 1024 + h * 8;
-        const int sso = sb * kScaleBytesPerSuper + kb * 4 + h * 2;
+        const int sso = sb * kScaleBytesPerSuper + kb * 4;
 #pragma unroll
         for (int i = 0; i < kB; ++i) {
             c[i] = __builtin_amdgcn_raw_buffer_load_b64(B.rc, B.coff[i], cso, 0);
-            s[i] = __builtin_amdgcn_raw_buffer_load_b16(B.rs, B.soff[i], sso, 0);
+            // the scale word of the whole 128-k chunk (steps 0..3); this
+            // stage's two bytes are picked at the store
+            s[i] = __builtin_amdgcn_raw_buffer_load_b32(B.rs, B.soff[i], sso, 0);
         }
     }
 
-    __device__ __forceinline__ void store(__bf16* lb) const {
+    __device__ __forceinline__ void store(__bf16* lb, int kt) const {
+        const int h = (kt * kPBK % 128) / 64;
 #pragma unroll
         for (int i = 0; i < kB; ++i) {
             const int u = threadIdx.x + kPThreads * i;
             const int ls = u & 63;
             const int col = (u >> 6) * 16 + (ls & 15), g = ls >> 4;
-            const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)s[i], 0);
-            const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)s[i], 1);
+            const int sw = (int)(s[i] >> (16 * h));
+            const float s0 = __builtin_amdgcn_cvt_f32_fp8(sw, 0);
+            const float s1 = __builtin_amdgcn_cvt_f32_fp8(sw, 1);
             // step 2h: k = 8 g .. 8 g + 7 of the stage; step 2h + 1: 32 further
             *(uint4*)(lb + swz(col, g)) = dequant8(c[i].x, s0);
             *(uint4*)(lb + swz(col, 4 + g)) = dequant8(c[i].y, s1);
@@ -244,7 +249,7 @@ __device__ __forceinline__ void prefill_tile(PrefillLds& L, const uint8_t* __res
     A.copy(L.a[0], 0, wave);
     A.copy(L.a[1], min(1, nk - 1), wave);
     st0.load(B, 0);
-    st0.store(L.b[0]);
+    st0.store(L.b[0], 0);
     st0.load(B, min(1, nk - 1));
     st1.load(B, min(2, nk - 1));
     // Outstanding, oldest first: the loads of stage 1 into st0 and of stage 2
@@ -263,11 +268,17 @@ __device__ __forceinline__ void prefill_tile(PrefillLds& L, const uint8_t* __res
         __builtin_amdgcn_sched_barrier(0);
         prefill_mma<BM, BN>(acc, L.a[kt % 3], L.b[kt & 1], wm, wn, r32, half);
         __builtin_amdgcn_sched_barrier(0);
-        next.store(L.b[(kt + 1) & 1]);
+        next.store(L.b[(kt + 1) & 1], min(kt + 1, nk - 1));
         next.load(B, kt_next);
         __builtin_amdgcn_sched_barrier(0);
+        // Then the barrier, without a memory fence (a fence would also wait
+        // for the copy of stage kt + 2 just issued): this wave's LDS stores
+        // are complete, and the compiler may not move memory accesses across.
         __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * (BN / 64) + BM / 64));
-        __syncthreads();
+        __builtin_amdgcn_s_waitcnt(kPWaitLgkm0);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
     };
     // Unrolled by two so st0 and st1 keep fixed registers (copying a register
     // set whose loads are in flight would wait for them); an odd last stage
