@@ -166,6 +166,20 @@ struct PStage {
         }
     }
 
+    // Piece q (0 .. 2 kB - 1) of the dequantised store: lane slot q / 2, word
+    // q % 2 (8 values).
+    template <int Q>
+    __device__ __forceinline__ void store_piece(__bf16* lb, int kt) const {
+        constexpr int i = Q / 2, w = Q % 2;
+        const int h = (kt * kPBK % 128) / 64;
+        const int u = threadIdx.x + kPThreads * i;
+        const int ls = u & 63;
+        const int col = (u >> 6) * 16 + (ls & 15), g = ls >> 4;
+        const int sw = (int)(s[i] >> (16 * h));
+        const float sc = __builtin_amdgcn_cvt_f32_fp8(sw, w);
+        *(uint4*)(lb + swz(col, 4 * w + g)) = dequant8(w ? c[i].y : c[i].x, sc);
+    }
+
     __device__ __forceinline__ void store(__bf16* lb, int kt) const {
         const int h = (kt * kPBK % 128) / 64;
 #pragma unroll
@@ -184,11 +198,23 @@ struct PStage {
 };
 
 // The MFMAs of one stage (64 k = 4 steps of 16) for this wave's (BM/64) x
-// (BN/128) tiles.  The operands of step ks + 1 are read from LDS before the
-// multiplies of step ks are issued, so the reads overlap the matrix cores.
+// (BN/128) tiles, with the dequantised store of the next weight stage (`nx`,
+// into the other LDS buffer) spread over the steps: after each step's
+// multiplies are issued the wave converts and stores a share of it while the
+// matrix cores work.  The operands of step ks + 1 are read before the
+// multiplies of step ks.
+template <int BM, int BN, int Q>
+__device__ __forceinline__ void prefill_store_share(const PStage<BN>& nx, __bf16* lbn, int ktn,
+                                                    int ks) {
+    constexpr int kPieces = 2 * PStage<BN>::kB;
+    // pieces ks * kPieces / 4 .. (ks + 1) * kPieces / 4 - 1
+    if (Q < kPieces && Q * 4 / kPieces == ks) nx.template store_piece<Q>(lbn, ktn);
+}
+
 template <int BM, int BN>
 __device__ __forceinline__ void prefill_mma(f32x16 (&acc)[BM / 64][BN / 128], const __bf16* la,
-                                            const __bf16* lb, int wm, int wn, int r32, int half) {
+                                            const __bf16* lb, const PStage<BN>& nx, __bf16* lbn,
+                                            int ktn, int wm, int wn, int r32, int half) {
     constexpr int TI = BM / 64, TJ = BN / 128;
     bf16x8 av[2][TI], bv[2][TJ];
     auto read = [&](int ks, int buf) {
@@ -211,6 +237,10 @@ __device__ __forceinline__ void prefill_mma(f32x16 (&acc)[BM / 64][BN / 128], co
             for (int j = 0; j < TJ; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[buf][i], bv[buf][j],
                                                                     acc[i][j], 0, 0, 0);
+        prefill_store_share<BM, BN, 0>(nx, lbn, ktn, ks);
+        prefill_store_share<BM, BN, 1>(nx, lbn, ktn, ks);
+        prefill_store_share<BM, BN, 2>(nx, lbn, ktn, ks);
+        prefill_store_share<BM, BN, 3>(nx, lbn, ktn, ks);
     }
 }
 
@@ -259,16 +289,16 @@ __device__ __forceinline__ void prefill_tile(PrefillLds& L, const uint8_t* __res
 
     const int r32 = lane & 31, half = lane >> 5;
     // Per stage, issued in this order: activation copy of stage kt + 2
-    // (BM / 64 loads), the multiplies, the dequantised store of stage kt + 1,
-    // the weight loads of stage kt + 3 (BN / 64 loads).  Before the barrier the
+    // (BM / 64 loads), the multiplies with the dequantised store of stage
+    // kt + 1 interleaved, the weight loads of stage kt + 3 (BN / 64 loads).  Before the barrier the
     // copy of stage kt + 1 (issued one stage earlier) must have landed: the
     // loads after it may still be in flight.
     auto stage = [&](int kt, PStage<BN>& next, int kt_next) {
         A.copy(L.a[(kt + 2) % 3], min(kt + 2, nk - 1), wave);
         __builtin_amdgcn_sched_barrier(0);
-        prefill_mma<BM, BN>(acc, L.a[kt % 3], L.b[kt & 1], wm, wn, r32, half);
+        prefill_mma<BM, BN>(acc, L.a[kt % 3], L.b[kt & 1], next, L.b[(kt + 1) & 1],
+                            min(kt + 1, nk - 1), wm, wn, r32, half);
         __builtin_amdgcn_sched_barrier(0);
-        next.store(L.b[(kt + 1) & 1], min(kt + 1, nk - 1));
         next.load(B, kt_next);
         __builtin_amdgcn_sched_barrier(0);
         // Then the barrier, without a memory fence (a fence would also wait
