@@ -54,16 +54,19 @@ struct PrefillLds {
 __device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int swz(int row, int seg) { return row * kPBK + 8 * (seg ^ swz_key(row)); }
 
-// 2 codes (byte B of w) times scale sc -> 2 bf16 packed in one word.
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// 2 codes (byte B of w) times scale sc -> 2 bf16 packed in one word (one
+// paired conversion; exact, as the products have at most 6 significant bits).
 template <int B>
 __device__ __forceinline__ uint32_t dequant2(uint32_t w, float sc) {
     const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, B);
-    const __bf16 lo = (__bf16)(v[0] * sc);
-    const __bf16 hi = (__bf16)(v[1] * sc);
-    uint16_t ul, uh;
-    __builtin_memcpy(&ul, &lo, 2);
-    __builtin_memcpy(&uh, &hi, 2);
-    return (uint32_t)ul | ((uint32_t)uh << 16);
+    const f32x2v x = {v[0] * sc, v[1] * sc};
+    const bf16x2v b = __builtin_convertvector(x, bf16x2v);
+    uint32_t r;
+    __builtin_memcpy(&r, &b, 4);
+    return r;
 }
 
 // 8 codes (one 4-byte word, low nibble first) times scale sc -> 8 bf16.
