@@ -230,6 +230,7 @@ __device__ __forceinline__ void prefill_mma(f32x16 (&acc)[BM / 64][BN / 128], co
             bv[buf][j] = *(const bf16x8*)(lb + swz(wn * (BN / 4) + 32 * j + r32, seg));
     };
     read(0, 0);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < kPBK / 16; ++ks) {
         const int buf = ks & 1;
@@ -245,6 +246,7 @@ __device__ __forceinline__ void prefill_mma(f32x16 (&acc)[BM / 64][BN / 128], co
         prefill_store_share<BM, BN, 2>(nx, lbn, ktn, ks);
         prefill_store_share<BM, BN, 3>(nx, lbn, ktn, ks);
     }
+    __builtin_amdgcn_s_setprio(0);
 }
 
 // One BM x BN block tile; wave w owns rows (w / 4) * BM/2 and columns
