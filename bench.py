@@ -196,15 +196,15 @@ def main():
     plans, wss = {}, []
     with torch.cuda.stream(stream):
         specs, keep = build_round(nv, layers=args.layers, log=log)
-        for mode in (nv.ROUND_PERSISTENT, nv.ROUND_PER_MATRIX):
+        for mode in (nv.ROUND_PERSISTENT, nv.ROUND_PER_MATRIX, nv.ROUND_CHAIN):
             ws_bytes = nv.nvfp4_round_workspace_bytes(specs, 8, mode=mode)
             ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
             wss.append(ws)
             plans[mode] = nv.nvfp4_round_create(specs, 8, ws, ws_bytes, stream, mode=mode)
     torch.cuda.synchronize()
     nodes = {m: nv.nvfp4_round_graph_nodes(p, 8) for m, p in plans.items()}
-    log("round graphs: persistent %d node(s), per-matrix %d nodes per width"
-        % (nodes[nv.ROUND_PERSISTENT], nodes[nv.ROUND_PER_MATRIX]))
+    log("round graphs: persistent %d node(s), per-matrix %d nodes, chained %d node(s) per width"
+        % (nodes[nv.ROUND_PERSISTENT], nodes[nv.ROUND_PER_MATRIX], nodes[nv.ROUND_CHAIN]))
 
     def time_round(plan, M, steps, warmup):
         """Mean device time per replay (ms): one HIP event pair around each
@@ -245,17 +245,21 @@ def main():
     gbs8 = bytes8 / (ms8 * 1e-3) / 1e9
     log("M=8 round: %.3f ms, %.1f GB/s (%.1f%% of 8 TB/s)" % (ms8, gbs8, 100 * gbs8 / HBM_PEAK_GBS))
 
-    sweep, sweep_ps = {}, {}
+    sweep, sweep_ps, sweep_ch = {}, {}, {}
     for M in ([] if args.no_sweep else range(1, 9)):
-        for mode, tab in ((nv.ROUND_PER_MATRIX, sweep), (nv.ROUND_PERSISTENT, sweep_ps)):
+        for mode, tab in ((nv.ROUND_PER_MATRIX, sweep), (nv.ROUND_PERSISTENT, sweep_ps),
+                          (nv.ROUND_CHAIN, sweep_ch)):
             ms = time_round(plans[mode], M, max(5, args.steps // 2), 2)
             gbs = round_bytes(M, args.layers) / (ms * 1e-3) / 1e9
             tab[str(M)] = {"round_ms": round(ms, 4), "GB_s": round(gbs, 1),
                            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
-        log("M=%d: per-matrix graph %.3f ms (%.1f GB/s), persistent %.3f ms"
-            % (M, sweep[str(M)]["round_ms"], sweep[str(M)]["GB_s"], sweep_ps[str(M)]["round_ms"]))
-    flags = nv.nvfp4_round_status(persistent)
-    assert flags == 0, "persistent round wait timed out (flags %d)" % flags
+        log("M=%d: per-matrix graph %.3f ms (%.1f GB/s), persistent %.3f ms, chained %.3f ms "
+            "(%.1f GB/s)" % (M, sweep[str(M)]["round_ms"], sweep[str(M)]["GB_s"],
+                             sweep_ps[str(M)]["round_ms"], sweep_ch[str(M)]["round_ms"],
+                             sweep_ch[str(M)]["GB_s"]))
+    for mode in (nv.ROUND_PERSISTENT, nv.ROUND_CHAIN):
+        flags = nv.nvfp4_round_status(plans[mode])
+        assert flags == 0, "round form %d: a wait timed out (flags %d)" % (mode, flags)
 
     # Roofline of the dominant kernel.  The M = 8 round graph runs nothing but
     # decode kernels, one per matrix, in sequence on `stream`, so its average
@@ -349,6 +353,7 @@ def main():
         "round_ms_m1_to_m8": {k: v["round_ms"] for k, v in sweep.items()},
         "round_sweep": sweep,
         "round_sweep_persistent_kernel": sweep_ps,
+        "round_sweep_chained": sweep_ch,
         "roofline": {
             "bound": "hbm",
             "kernel": "nvfp4::decode_kernel<WAVES, CHUNKS, true> (split-K decode, bf16 out), M=8",

@@ -182,7 +182,8 @@ typedef struct nvfp4_round_plan* nvfp4_round;
 /* Forms of a round (see nvfp4_round_create_ex). */
 enum nvfp4_round_mode {
     NVFP4_ROUND_PERSISTENT = 0, /* one persistent kernel walks every matrix */
-    NVFP4_ROUND_PER_MATRIX = 1  /* one decode kernel per matrix */
+    NVFP4_ROUND_PER_MATRIX = 1, /* one decode kernel per matrix */
+    NVFP4_ROUND_CHAIN = 2       /* one launch whose workgroups run the matrices in order */
 };
 
 /* Workspace a round over these layers needs in the given form (the default
@@ -205,6 +206,19 @@ int nvfp4_round_workspace_bytes_ex(const nvfp4_layer* layers, int n_layers, int 
  *                are bounded: a wait that times out raises a flag read by
  *                nvfp4_round_status (the results are then not valid).  The
  *                grid assumes it has the device to itself while it runs.
+ *   CHAIN      : the graph holds one launch whose workgroups are the
+ *                decode workgroups of every matrix, in list order ("Ignis"
+ *                README, "Lineage": "Credits" -- the round's decode kernels
+ *                are chained so that each GEMM's start overlaps the previous
+ *                one's drain).  A workgroup issues its weight loads, then
+ *                waits until the previous matrix is complete, then reads its
+ *                activations.  Outputs are written with device-coherent
+ *                stores; activations that overlap an earlier matrix's output
+ *                are read with device-coherent loads.  Waits are bounded as in
+ *                PERSISTENT.  Needs workgroups spread evenly over the 8 XCDs
+ *                (checked here: NVFP4_EUNSUPPORTED otherwise).  The workspace
+ *                holds a split-K region per matrix (about 10.5 MB per layer of
+ *                the 27B-class round).
  * The layer array is copied; the device buffers it names must stay valid
  * while the plan lives.  The workspace (nvfp4_round_workspace_bytes_ex
  * bytes, 16-byte aligned) is zeroed and written here, then owned by the plan
@@ -219,7 +233,7 @@ int nvfp4_round_create_ex(nvfp4_round* plan, const nvfp4_layer* layers, int n_la
  * so later replays are valid again.  Synchronises the device.  Always 0 for
  * PER_MATRIX. */
 int nvfp4_round_status(nvfp4_round plan, unsigned int* flags);
-/* Bound on the polling rounds of each wait of a PERSISTENT round (default
+/* Bound on the polling rounds of each wait of a PERSISTENT or CHAIN round (default
  * 2^16, tens of milliseconds).  Synchronises the device. */
 int nvfp4_round_set_spin_limit(nvfp4_round plan, unsigned int limit);
 /* Replay the graph of width M (1..max_M) on `stream`. */

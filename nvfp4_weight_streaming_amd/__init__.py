@@ -33,7 +33,7 @@ EXPORTS = (
     "nvfp4_round_create_ex", "nvfp4_round_status", "nvfp4_round_set_spin_limit",
     "nvfp4_round_run", "nvfp4_round_graph_nodes", "nvfp4_round_destroy",
 )
-ROUND_PERSISTENT, ROUND_PER_MATRIX = 0, 1
+ROUND_PERSISTENT, ROUND_PER_MATRIX, ROUND_CHAIN = 0, 1, 2
 
 
 class Nvfp4Error(RuntimeError):

@@ -113,6 +113,20 @@ int stream_round_write_descs(const nvfp4_layer* L, int n, int grid, void* ws,
 int stream_launch_round(int n, int M, int grid, void* ws, const StreamRoundLayout& lay,
                         hipStream_t s);
 
+// Chained round (chain.hip): every matrix of a round in one launch.  Layout of
+// its workspace, in bytes: status, per-XCD ticket counters, per-matrix done
+// counters, completion flags, then (written once by the plan) one record per
+// ticket, then one counter + partial-sum region per matrix.
+struct ChainLayout {
+    int n;
+    size_t per_xcd;  // workgroups (tickets) per XCD
+    size_t status_off, tickets_off, done_off, flags_off, desc_off, regions_off, total;
+};
+size_t chain_round_layout(const nvfp4_layer* L, int n, ChainLayout* out);
+int chain_round_write(const nvfp4_layer* L, int n, int max_M, void* ws, const ChainLayout& y);
+int chain_check_dispatch(void* ws, const ChainLayout& y);
+int chain_launch_round(int M, void* ws, const ChainLayout& y, hipStream_t s);
+
 // Shared validation of a GEMM run against its plan.
 int validate_run(const nvfp4_gemm_plan* p, int M, int K, int N, const void* codes,
                  const void* scales, const void* act, const void* out, const void* ws);

@@ -138,11 +138,18 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
     __syncthreads();
     if (!s_last) return;
     const float* gbase = partial + (size_t)ng * splits * 8 * kCols;
-    for (int idx = threadIdx.x; idx < M * kCols; idx += kThreads) {
+    constexpr int kR = (8 * kCols + kThreads - 1) / kThreads;
+    float sum[kR];
+    if (l2_local)
+        sum_partials<kCols, kThreads, kR, true>(gbase, splits, M * kCols, sum);
+    else
+        sum_partials<kCols, kThreads, kR, false>(gbase, splits, M * kCols, sum);
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+        const int idx = threadIdx.x + r * kThreads;
         const int mm = idx / kCols, c = idx - mm * kCols;
         const int n = ng * kCols + c;
-        const float sum = sum_partials<kCols>(gbase, splits, mm, c, l2_local);
-        if (n < N) store_out<BF16>(out, (size_t)mm * N + n, sum * ts);
+        if (idx < M * kCols && n < N) store_out<BF16>(out, (size_t)mm * N + n, sum[r] * ts);
     }
     if (threadIdx.x == 0)  // leave the counter zeroed for the next run
         __hip_atomic_store(&counters[ng], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -130,32 +130,46 @@ struct ActStage {
     }
 };
 
-// Sum, in split order, the `splits` partial sums of output (mm, c) of one
-// column group (layout [split][8 rows][kCols]); l2_local: written with plain
-// stores into this XCD's L2, else with device-coherent stores.  The loads are
-// issued in batches of 16 before any is added, so the reduction costs
-// ceil(splits / 16) memory round trips, not `splits`.
-template <int kCols>
-__device__ __forceinline__ float sum_partials(const float* gbase, int splits, int mm, int c,
-                                              int l2_local = 0) {
-    constexpr int kBatch = 16;
-    float sum = 0.f;
-    for (int s0 = 0; s0 < splits; s0 += kBatch) {
-        float v[kBatch];
+// Sums, in split order, the `splits` partial sums of one column group (layout
+// [split][8 rows][kCols]) for the outputs idx = threadIdx.x + r * kThreads,
+// r < kR (row idx / kCols, column idx % kCols); only idx < n_out are valid.
+// L2_LOCAL: the partials were written with plain stores into this XCD's L2;
+// else with device-coherent stores, and they are read device-coherently.
+// Every load of a batch of kSB splits, for all kR outputs, is issued before
+// any is added, so a batch costs one memory round trip.  Within a wave that
+// has valid outputs the output index is clamped to n_out - 1 (repeated
+// addresses within a wave cost one request).
+template <int kCols, int kThreads, int kR, bool L2_LOCAL>
+__device__ __forceinline__ void sum_partials(const float* gbase, int splits, int n_out,
+                                             float (&sum)[kR]) {
+    constexpr int kSB = 16 / kR;
 #pragma unroll
-        for (int t = 0; t < kBatch; ++t) {
-            const float* src = gbase + (size_t)((s0 + t) * 8 + mm) * kCols + c;
-            v[t] = (s0 + t < splits)
-                       ? (l2_local ? *src
-                                   : __hip_atomic_load(src, __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT))
-                       : 0.f;
+    for (int r = 0; r < kR; ++r) sum[r] = 0.f;
+    for (int s0 = 0; s0 < splits; s0 += kSB) {
+        float v[kR][kSB];
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+            // Waves with no valid output in this block issue nothing.
+            const int wave0 = __builtin_amdgcn_readfirstlane((int)(threadIdx.x & ~63u)) + r * kThreads;
+            const int idx = min((int)threadIdx.x + r * kThreads, n_out - 1);
+            const int mm = idx / kCols, c = idx - mm * kCols;
+#pragma unroll
+            for (int t = 0; t < kSB; ++t) {
+                v[r][t] = 0.f;
+                if (wave0 < n_out && s0 + t < splits) {
+                    const int off = ((s0 + t) * 8 + mm) * kCols + c;
+                    v[r][t] = L2_LOCAL ? gbase[off]
+                                       : __hip_atomic_load(gbase + off, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
         }
 #pragma unroll
-        for (int t = 0; t < kBatch; ++t)
-            if (s0 + t < splits) sum += v[t];
+        for (int r = 0; r < kR; ++r)
+#pragma unroll
+            for (int t = 0; t < kSB; ++t)
+                if (s0 + t < splits) sum[r] += v[r][t];
     }
-    return sum;
 }
 
 }  // namespace nvfp4

@@ -211,7 +211,9 @@ __device__ __forceinline__ void prefill_store_share(const PStage<BN>& nx, __bf16
                                                     int ks) {
     constexpr int kPieces = 2 * PStage<BN>::kB;
     // pieces ks * kPieces / 4 .. (ks + 1) * kPieces / 4 - 1
-    if (Q < kPieces && Q * 4 / kPieces == ks) nx.template store_piece<Q>(lbn, ktn);
+    if constexpr (Q < kPieces) {
+        if (Q * 4 / kPieces == ks) nx.template store_piece<Q>(lbn, ktn);
+    }
 }
 
 template <int BM, int BN>

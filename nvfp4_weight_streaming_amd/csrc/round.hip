@@ -9,7 +9,10 @@
 //     all matrices, each starting only when the previous one is final, with
 //     the weight stream running on across the boundary (stream.hip);
 //   NVFP4_ROUND_PER_MATRIX - the graph holds one decode kernel per matrix on
-//     one stream.
+//     one stream;
+//   NVFP4_ROUND_CHAIN - the graph holds one launch of the chained kernel
+//     (chain.hip), whose workgroups run the matrices in order, each one's
+//     weight loads issued before the previous matrix is complete.
 #include <new>
 #include <vector>
 
@@ -21,6 +24,7 @@ struct nvfp4_round_plan {
     int mode;
     int grid;    // persistent form: resident workgroups
     nvfp4::StreamRoundLayout lay;
+    nvfp4::ChainLayout chain;
     std::vector<nvfp4_layer> layers;
     std::vector<nvfp4_gemm_plan*> plans;
     void* ws;
@@ -95,9 +99,25 @@ static int round_layout(const nvfp4_layer* layers, int n_layers, int max_M, size
 }
 
 static int check_mode(int mode) {
-    if (mode != NVFP4_ROUND_PERSISTENT && mode != NVFP4_ROUND_PER_MATRIX)
-        return set_error(NVFP4_EINVAL, "mode: %d is neither PERSISTENT (0) nor PER_MATRIX (1)", mode);
+    if (mode != NVFP4_ROUND_PERSISTENT && mode != NVFP4_ROUND_PER_MATRIX &&
+        mode != NVFP4_ROUND_CHAIN)
+        return set_error(NVFP4_EINVAL,
+                         "mode: %d is not PERSISTENT (0), PER_MATRIX (1) or CHAIN (2)", mode);
     return NVFP4_OK;
+}
+
+// Workspace offsets of a plan's status words and of its synchronisation state
+// (re-zeroed after a time-out), for the forms that have them.
+static bool sync_state(const nvfp4_round_plan* r, size_t* status_off) {
+    if (r->mode == NVFP4_ROUND_PERSISTENT) {
+        *status_off = r->lay.status_off;
+        return true;
+    }
+    if (r->mode == NVFP4_ROUND_CHAIN) {
+        *status_off = r->chain.status_off;
+        return true;
+    }
+    return false;
 }
 
 int nvfp4_round_workspace_bytes_ex(const nvfp4_layer* layers, int n_layers, int max_M, int mode,
@@ -111,6 +131,11 @@ int nvfp4_round_workspace_bytes_ex(const nvfp4_layer* layers, int n_layers, int 
     if (mode == NVFP4_ROUND_PERSISTENT) {
         StreamRoundLayout lay;
         *workspace_bytes = stream_round_layout(n_layers, &lay);
+        return NVFP4_OK;
+    }
+    if (mode == NVFP4_ROUND_CHAIN) {
+        ChainLayout y;
+        *workspace_bytes = chain_round_layout(layers, n_layers, &y);
         return NVFP4_OK;
     }
     size_t c = 0, p = 0;
@@ -137,13 +162,18 @@ int nvfp4_round_create_ex(nvfp4_round* plan, const nvfp4_layer* layers, int n_la
     if (st) return st;
     size_t need_c = 0, need_p = 0;
     StreamRoundLayout lay{};
+    ChainLayout chain{};
     if (mode == NVFP4_ROUND_PERSISTENT) {
         stream_round_layout(n_layers, &lay);
+    } else if (mode == NVFP4_ROUND_CHAIN) {
+        chain_round_layout(layers, n_layers, &chain);
     } else {
         st = round_layout(layers, n_layers, max_M, &need_c, &need_p);
         if (st) return st;
     }
-    const size_t need = mode == NVFP4_ROUND_PERSISTENT ? lay.total : need_c + need_p;
+    const size_t need = mode == NVFP4_ROUND_PERSISTENT ? lay.total
+                        : mode == NVFP4_ROUND_CHAIN    ? chain.total
+                                                       : need_c + need_p;
     if (workspace_bytes < need)
         return set_error(NVFP4_EINVAL, "workspace_bytes: %zu < %zu needed", workspace_bytes, need);
     if (need && !workspace) return set_error(NVFP4_EINVAL, "workspace: NULL");
@@ -155,6 +185,7 @@ int nvfp4_round_create_ex(nvfp4_round* plan, const nvfp4_layer* layers, int n_la
     r->max_M = max_M;
     r->mode = mode;
     r->lay = lay;
+    r->chain = chain;
     r->layers.assign(layers, layers + n_layers);
     r->ws = workspace;
     r->ws_bytes = workspace_bytes;
@@ -194,6 +225,16 @@ int nvfp4_round_create_ex(nvfp4_round* plan, const nvfp4_layer* layers, int n_la
             if (e != hipSuccess) st = hip_fail(e, "hipMemcpy(spin limit)");
         }
     }
+    if (!st && mode == NVFP4_ROUND_CHAIN) {
+        st = chain_round_write(layers, n_layers, max_M, workspace, chain);
+        if (!st) {
+            const unsigned int limit = kDefaultSpinLimit;
+            e = hipMemcpy((char*)workspace + chain.status_off + 4, &limit, 4,
+                          hipMemcpyHostToDevice);
+            if (e != hipSuccess) st = hip_fail(e, "hipMemcpy(spin limit)");
+        }
+        if (!st) st = chain_check_dispatch(workspace, chain);
+    }
     for (int M = 1; M <= max_M && !st; ++M) {
         e = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal);
         if (e != hipSuccess) {
@@ -203,6 +244,8 @@ int nvfp4_round_create_ex(nvfp4_round* plan, const nvfp4_layer* layers, int n_la
         int lst = NVFP4_OK;
         if (mode == NVFP4_ROUND_PERSISTENT) {
             lst = stream_launch_round(n_layers, M, r->grid, workspace, lay, cap);
+        } else if (mode == NVFP4_ROUND_CHAIN) {
+            lst = chain_launch_round(M, workspace, chain, cap);
         } else {
             for (int i = 0; i < n_layers && !lst; ++i) {
                 const nvfp4_layer& l = r->layers[i];
@@ -260,13 +303,21 @@ int nvfp4_round_status(nvfp4_round plan, unsigned int* flags) {
     if (!plan || plan->magic != kRoundMagic) return set_error(NVFP4_ESTATE, "plan: invalid handle");
     if (!flags) return set_error(NVFP4_EINVAL, "flags: NULL");
     *flags = 0;
-    if (plan->mode != NVFP4_ROUND_PERSISTENT) return NVFP4_OK;
-    void* p = (char*)plan->ws + plan->lay.status_off;
+    size_t status_off = 0;
+    if (!sync_state(plan, &status_off)) return NVFP4_OK;
+    void* p = (char*)plan->ws + status_off;
     NVFP4_HIP(hipDeviceSynchronize());
     NVFP4_HIP(hipMemcpy(flags, p, 4, hipMemcpyDeviceToHost));
     const unsigned int zero = 0;
     NVFP4_HIP(hipMemcpy(p, &zero, 4, hipMemcpyHostToDevice));
-    if (*flags) {
+    if (*flags && plan->mode == NVFP4_ROUND_CHAIN) {
+        // Tickets, done counters, flags and every matrix's split-K counters
+        // (the ticket records between them stay).
+        const ChainLayout& y = plan->chain;
+        NVFP4_HIP(hipMemset((char*)plan->ws + y.tickets_off, 0, y.desc_off - y.tickets_off));
+        NVFP4_HIP(hipMemset((char*)plan->ws + y.regions_off, 0, y.total - y.regions_off));
+        NVFP4_HIP(hipDeviceSynchronize());
+    } else if (*flags) {
         // A replay that timed out may have left completion counters behind:
         // zero them (the descriptors after them stay) so the plan is usable.
         NVFP4_HIP(hipMemset((char*)plan->ws + plan->lay.done_off, 0, plan->lay.status_off));
@@ -280,10 +331,10 @@ int nvfp4_round_status(nvfp4_round plan, unsigned int* flags) {
 int nvfp4_round_set_spin_limit(nvfp4_round plan, unsigned int limit) {
     clear_error();
     if (!plan || plan->magic != kRoundMagic) return set_error(NVFP4_ESTATE, "plan: invalid handle");
-    if (plan->mode != NVFP4_ROUND_PERSISTENT) return NVFP4_OK;
+    size_t status_off = 0;
+    if (!sync_state(plan, &status_off)) return NVFP4_OK;
     NVFP4_HIP(hipDeviceSynchronize());
-    NVFP4_HIP(hipMemcpy((char*)plan->ws + plan->lay.status_off + 4, &limit, 4,
-                        hipMemcpyHostToDevice));
+    NVFP4_HIP(hipMemcpy((char*)plan->ws + status_off + 4, &limit, 4, hipMemcpyHostToDevice));
     return NVFP4_OK;
 }
 

@@ -49,7 +49,7 @@ def full_round():
     nv = require_gpu()
     specs, keep = bench.build_round(nv, layers=64)
     plans = {}
-    for mode in (nv.ROUND_PERSISTENT, nv.ROUND_PER_MATRIX):
+    for mode in (nv.ROUND_PERSISTENT, nv.ROUND_PER_MATRIX, nv.ROUND_CHAIN):
         ws_bytes = nv.nvfp4_round_workspace_bytes(specs, 8, mode=mode)
         ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
         plans[mode] = nv.nvfp4_round_create(specs, 8, ws, ws_bytes, mode=mode)
@@ -69,13 +69,13 @@ def full_round():
     del keep
 
 
-@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("mode", [0, 1, 2])
 @pytest.mark.parametrize("M", [1, 8])
 def test_full_round_sampled(full_round, M, mode):
     import torch
     nv, plans, specs, refs = full_round
     plan = plans[mode]
-    assert nv.nvfp4_round_graph_nodes(plan, M) == (1 if mode == nv.ROUND_PERSISTENT else 256)
+    assert nv.nvfp4_round_graph_nodes(plan, M) == (256 if mode == nv.ROUND_PER_MATRIX else 1)
     for s in specs:
         s["out"].fill_(float("nan"))
     nv.nvfp4_round_run(plan, M)

@@ -2,15 +2,19 @@
 
 A round of 12 matrices (3 layers x the four projections of the 27B-class
 structure, at the real K and 1/16 of the real N) is replayed at every width
-M = 1..8 and every matrix's output is compared with the oracle.  Replays are
-repeated with eager GEMM work between them, each checked, and the outputs are
-poisoned before every replay so a skipped node shows."""
+M = 1..8 in each of the three forms (persistent, per-matrix, chained) and
+every matrix's output is compared with the oracle.  Replays are repeated with
+eager GEMM work between them, each checked, and the outputs are poisoned
+before every replay so a skipped node shows.  A second round feeds outputs
+into later matrices' activations (overwriting buffers that earlier matrices
+read) to check the ordering and visibility guarantees of the one-launch
+forms."""
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from tests.gpu_util import check, dev, dev_bf16, host, pack, require_gpu
+from tests.gpu_util import bf16_bits, check, dev, dev_bf16, host, pack, require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -38,7 +42,7 @@ def small_round():
             ref.append((y, S))
     plans = {}
     keep = []
-    for mode in (nv.ROUND_PERSISTENT, nv.ROUND_PER_MATRIX):
+    for mode in (nv.ROUND_PERSISTENT, nv.ROUND_PER_MATRIX, nv.ROUND_CHAIN):
         ws_bytes = nv.nvfp4_round_workspace_bytes(specs, 8, mode=mode)
         ws = torch.full((max(ws_bytes, 16),), 0x5A, dtype=torch.uint8, device="cuda")  # create zeroes it
         plans[mode] = nv.nvfp4_round_create(specs, 8, ws, ws_bytes, mode=mode)
@@ -59,7 +63,7 @@ def _check_all(nv, specs, ref, M, what):
               what="%s matrix %d" % (what, i))
 
 
-MODES = (0, 1)  # persistent, per-matrix
+MODES = (0, 1, 2)  # persistent, per-matrix, chained
 
 
 def test_graph_nodes(small_round):
@@ -67,6 +71,7 @@ def test_graph_nodes(small_round):
     for M in range(1, 9):
         assert nv.nvfp4_round_graph_nodes(plans[nv.ROUND_PER_MATRIX], M) == len(specs)
         assert nv.nvfp4_round_graph_nodes(plans[nv.ROUND_PERSISTENT], M) == 1
+        assert nv.nvfp4_round_graph_nodes(plans[nv.ROUND_CHAIN], M) == 1
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -104,10 +109,10 @@ def test_replays_with_eager_work_between(small_round, mode):
         torch.cuda.synchronize()
 
 
-def test_both_forms_back_to_back(small_round):
-    """The two forms replayed one after the other on the same buffers each
-    match the oracle (their K slicing differs, so they need not agree bit for
-    bit with each other)."""
+def test_all_forms_back_to_back(small_round):
+    """The forms replayed one after the other on the same buffers each match
+    the oracle.  The chained and per-matrix forms slice K alike for K < 16384,
+    so there they agree bit for bit."""
     import torch
     nv, plans, specs, ref = small_round
     outs = {}
@@ -117,16 +122,20 @@ def test_both_forms_back_to_back(small_round):
         torch.cuda.synchronize()
         _check_all(nv, specs, ref, 8, "mode %d" % mode)
         outs[mode] = [host(s["out"]).copy() for s in specs]
-    assert len(outs) == 2
+    assert len(outs) == 3
+    for i, s in enumerate(specs):
+        if s["K"] < 16384:
+            assert np.array_equal(outs[1][i].view(np.uint8), outs[2][i].view(np.uint8)), i
 
 
-def test_forced_wait_timeout_is_reported_and_recovers(small_round):
+@pytest.mark.parametrize("mode", (0, 2))
+def test_forced_wait_timeout_is_reported_and_recovers(small_round, mode):
     """A spin limit of 0 makes every cross-matrix wait give up at once (the
     kernel still exits); the flag is reported, the counters re-armed, and the
     next replay with the normal limit is correct again."""
     import torch
     nv, plans, specs, ref = small_round
-    plan = plans[nv.ROUND_PERSISTENT]
+    plan = plans[mode]
     nv.nvfp4_round_set_spin_limit(plan, 0)
     for _ in range(3):
         nv.nvfp4_round_run(plan, 8)
@@ -147,3 +156,70 @@ def test_round_invalid_width(small_round):
         with pytest.raises(nv.Nvfp4Error) as e:
             nv.nvfp4_round_run(plan, 9)
         assert e.value.message.startswith("M")
+
+
+def test_chain_outputs_feed_later_matrices():
+    """Outputs of a round feed later matrices' activations, and buffers that
+    earlier matrices read are overwritten and read again within the launch:
+        m0: A -> B   m1: B -> A   m2: A -> C (fp32)   m3: A -> D
+        m4: D -> B   m5: B -> E (fp32)
+    Every replay starts from A = X0 and poisoned B..E.  The chained form must
+    equal the per-matrix form (kernel boundaries between matrices) bit for bit
+    on every output, and the matrices whose inputs are still in place at the
+    end (m2..m5) must match the oracle on those inputs."""
+    import torch
+    nv = require_gpu()
+    dims = [(1024, 1536, "A", "B", nv.OUT_BF16), (1536, 1024, "B", "A", nv.OUT_BF16),
+            (1024, 2048, "A", "C", nv.OUT_F32), (1024, 512, "A", "D", nv.OUT_BF16),
+            (512, 1024, "D", "B", nv.OUT_BF16), (1024, 768, "B", "E", nv.OUT_F32)]
+    bufs = {"A": torch.empty((8, 1024), dtype=torch.bfloat16, device="cuda"),
+            "B": torch.empty((8, 1536), dtype=torch.bfloat16, device="cuda"),
+            "C": torch.empty((8, 2048), dtype=torch.float32, device="cuda"),
+            "D": torch.empty((8, 512), dtype=torch.bfloat16, device="cuda"),
+            "E": torch.empty((8, 768), dtype=torch.float32, device="cuda")}
+    x0 = dev_bf16(synth.activations(3, 7, 8, 1024))
+    specs, planes = [], []
+    for i, (K, N, a, o, dt) in enumerate(dims):
+        W = synth.weights(3, 100 + i, N, K)
+        codes, scales, t = oracle.quantize(W)
+        pw = pack(nv, dev(codes), dev(scales), K, N, t)
+        # B is [8][1536]; as m4's output it holds N = 1024 values per row and
+        # as m5's input K = 1024: the row stride must be the layer's own width.
+        out = bufs[o] if bufs[o].shape[1] == N else bufs[o].view(-1)[:8 * N].view(8, N)
+        act = bufs[a] if bufs[a].shape[1] == K else bufs[a].view(-1)[:8 * K].view(8, K)
+        specs.append(dict(K=K, N=N, codes=pw.codes, scales=pw.scales, tensor_scale=t, act=act,
+                          out=out, out_dtype=dt, pw=pw))
+        planes.append((codes, scales, t))
+
+    def reset():
+        bufs["A"].copy_(x0)
+        for k in "BCDE":
+            bufs[k].fill_(float("nan"))
+
+    results, keep = {}, []
+    for mode in (nv.ROUND_PER_MATRIX, nv.ROUND_CHAIN):
+        wsb = nv.nvfp4_round_workspace_bytes(specs, 8, mode=mode)
+        ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda")
+        keep.append(ws)
+        plan = nv.nvfp4_round_create(specs, 8, ws, wsb, mode=mode)
+        try:
+            for M in (8, 3, 8):
+                reset()
+                nv.nvfp4_round_run(plan, M)
+                torch.cuda.synchronize()
+                snap = {k: host(v).copy() for k, v in bufs.items()}
+                results.setdefault(M, {})[mode] = snap
+                assert nv.nvfp4_round_status(plan) == 0
+        finally:
+            nv.nvfp4_round_destroy(plan)
+    for M, by_mode in results.items():
+        a, b = by_mode[nv.ROUND_PER_MATRIX], by_mode[nv.ROUND_CHAIN]
+        for k in bufs:
+            assert np.array_equal(a[k][:M].view(np.uint8), b[k][:M].view(np.uint8)), (M, k)
+    # Oracle on the inputs left in place (width 8).
+    for i in (2, 3, 4, 5):
+        s = specs[i]
+        codes, scales, t = planes[i]
+        act = bf16_bits(s["act"])
+        y, S = oracle.gemm(act, codes, scales, t)
+        check(s["out"], y, S, bf16=s["out_dtype"] == nv.OUT_BF16, what="chained m%d" % i)
