@@ -356,7 +356,8 @@ def main():
         "round_sweep_chained": sweep_ch,
         "roofline": {
             "bound": "hbm",
-            "kernel": "nvfp4::decode_kernel<WAVES, CHUNKS, true> (split-K decode, bf16 out), M=8",
+            "kernel": "nvfp4::decode_window_kernel<WAVES, 1, true> (split-K decode, slices streamed "
+                      "in windows of one superblock, bf16 out), M=8",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -41,7 +41,7 @@ PASSES = (
     ("write", ["--pmc", "WRITE_SIZE"], 300),
 )
 CALIB_BYTES = 1 << 30
-DECODE = "nvfp4::decode_kernel<"
+DECODE = "nvfp4::decode_"  # decode_kernel< and decode_window_kernel<
 PREFILL = "nvfp4::prefill_kernel<"
 COPY = "__amd_rocclr_copyBuffer"
 

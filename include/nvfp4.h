@@ -124,7 +124,10 @@ typedef struct nvfp4_gemm_config {
                     split_k is 0) */
     int kernel;  /* nvfp4_kernel */
     int tiles;   /* STREAM: column tiles of 16 per workgroup, 2, 4 or 8 */
-    int reserved[3];
+    int windows; /* SPLITK: windows of `chunks` superblocks per K slice; above 1 a
+                    wave streams its slice, issuing the next window's loads
+                    before computing the current one (0 or 1: one window) */
+    int reserved[2];
 } nvfp4_gemm_config;
 
 /* Create a plan for GEMMs of shape (M <= max_M) x K x N with the given output

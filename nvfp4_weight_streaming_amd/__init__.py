@@ -49,7 +49,8 @@ _STATUS = {OK: "ok", EINVAL: "EINVAL", EUNSUPPORTED: "EUNSUPPORTED", EHIP: "EHIP
 
 class GemmConfig(ctypes.Structure):
     _fields_ = [("split_k", ctypes.c_int), ("waves", ctypes.c_int), ("chunks", ctypes.c_int),
-                ("kernel", ctypes.c_int), ("tiles", ctypes.c_int), ("reserved", ctypes.c_int * 3)]
+                ("kernel", ctypes.c_int), ("tiles", ctypes.c_int), ("windows", ctypes.c_int),
+                ("reserved", ctypes.c_int * 2)]
 
 
 KERNEL_AUTO, KERNEL_STREAM, KERNEL_SPLITK = 0, 1, 2
@@ -168,12 +169,13 @@ def nvfp4_quantize(w, K, N, codes, scales, tensor_scale, workspace, stream=None)
                                 _ptr(workspace), _stream(stream)))
 
 
-def nvfp4_gemm_create(max_M, K, N, out_dtype, split_k=0, waves=0, chunks=0, kernel=0, tiles=0):
+def nvfp4_gemm_create(max_M, K, N, out_dtype, split_k=0, waves=0, chunks=0, kernel=0, tiles=0,
+                      windows=0):
     """Returns (plan handle, workspace bytes)."""
     h = ctypes.c_void_p()
     ws = ctypes.c_size_t()
-    if split_k or waves or chunks or kernel or tiles:
-        cfg = GemmConfig(split_k, waves, chunks, kernel, tiles)
+    if split_k or waves or chunks or kernel or tiles or windows:
+        cfg = GemmConfig(split_k, waves, chunks, kernel, tiles, windows)
         _check(lib().nvfp4_gemm_create_ex(ctypes.byref(h), max_M, K, N, out_dtype,
                                           ctypes.byref(cfg), ctypes.byref(ws)))
     else:
@@ -300,10 +302,10 @@ class Gemm:
     """A plan plus its workspace: ``Gemm(max_M, K, N, out_dtype)(w, act, out)``."""
 
     def __init__(self, max_M, K, N, out_dtype=OUT_BF16, split_k=0, waves=0, chunks=0, kernel=0,
-                 tiles=0, device="cuda"):
+                 tiles=0, windows=0, device="cuda"):
         import torch
         self.plan, self.ws_bytes = nvfp4_gemm_create(max_M, K, N, out_dtype, split_k, waves,
-                                                     chunks, kernel, tiles)
+                                                     chunks, kernel, tiles, windows)
         self.K, self.N, self.max_M, self.out_dtype = K, N, max_M, out_dtype
         self.workspace = None
         if self.ws_bytes:

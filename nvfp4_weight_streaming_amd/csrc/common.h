@@ -42,7 +42,8 @@ int hip_fail(hipError_t e, const char* what);
 // ---- plans ---------------------------------------------------------------------
 struct DecodeConfig {
     int waves;          // column tiles (waves) per workgroup
-    int chunks;         // superblocks of 512 k per K slice (loaded up front per wave)
+    int chunks;         // superblocks of 512 k per window (loaded up front per wave)
+    int windows;        // windows per K slice (> 1: the streaming decode_window_kernel)
     int splits;         // K slices
     int n_groups;       // column groups of `waves` tiles
     int grid;           // workgroups launched (n_groups padded to 8, times splits)

@@ -31,6 +31,83 @@
 
 namespace nvfp4 {
 
+// The end of a workgroup: the two row halves of each lane's sums are added,
+// then the outputs (one slice) or the split-K hand-off (several).
+template <int WAVES, bool BF16>
+__device__ __forceinline__ void decode_finish(float (&acc)[4], void* __restrict__ out,
+                                              float* __restrict__ partial,
+                                              unsigned int* __restrict__ counters, float ts,
+                                              int M, int N, int splits, int n_tiles, int l2_local,
+                                              int ng, int split, int nt, int* s_last) {
+    constexpr int kThreads = WAVES * 64;
+    constexpr int kCols = WAVES * kTileN;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int col = lane & 15, g = lane >> 4;
+    // Lanes g and g+2 hold the same (row, column) for the two block halves.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] += __shfl_xor(acc[j], 32, 64);
+    const bool mine = lane < 32 && ng * WAVES + wave < n_tiles;
+
+    if (splits == 1) {
+        if (mine) {
+            const int n = nt * kTileN + col;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int mm = 4 * g + j;
+                if (mm < M && n < N) store_out<BF16>(out, (size_t)mm * N + n, acc[j] * ts);
+            }
+        }
+        return;
+    }
+
+    // Split K.  The slices of one column group run on one XCD (blockIdx % 8
+    // selects it, verified when the plan is made: l2_local), so their
+    // partial sums meet in that XCD's L2: plain stores, a wait for their
+    // completion, then the counter increment.  Without the verified mapping
+    // the partials go through device-coherent (write-through) stores and
+    // loads instead.  Either way the hand-off needs no agent-scope fence,
+    // whose write-back of the whole L2 would cost every workgroup.
+    float* pbase = partial + (size_t)(ng * splits + split) * 8 * kCols;
+    if (mine) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int mm = 4 * g + j;
+            if (mm < M) {
+                float* dst = pbase + mm * kCols + wave * kTileN + col;
+                if (l2_local)
+                    *dst = acc[j];
+                else
+                    __hip_atomic_store(dst, acc[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned int old =
+            __hip_atomic_fetch_add(&counters[ng], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_last = (old == (unsigned int)(splits - 1));
+    }
+    __syncthreads();
+    if (!*s_last) return;
+    const float* gbase = partial + (size_t)ng * splits * 8 * kCols;
+    constexpr int kR = (8 * kCols + kThreads - 1) / kThreads;
+    float sum[kR];
+    if (l2_local)
+        sum_partials<kCols, kThreads, kR, true>(gbase, splits, M * kCols, sum);
+    else
+        sum_partials<kCols, kThreads, kR, false>(gbase, splits, M * kCols, sum);
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+        const int idx = threadIdx.x + r * kThreads;
+        const int mm = idx / kCols, c = idx - mm * kCols;
+        const int n = ng * kCols + c;
+        if (idx < M * kCols && n < N) store_out<BF16>(out, (size_t)mm * N + n, sum[r] * ts);
+    }
+    if (threadIdx.x == 0)  // leave the counter zeroed for the next run
+        __hip_atomic_store(&counters[ng], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // One workgroup = WAVES column tiles (one per wave) x one K slice of up to
 // NCH superblocks.  Every load a wave will need is issued before it computes
 // anything: first its share of the activation slice, then all of its weight
@@ -45,7 +122,6 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
     int n_groups, int n_tiles, int l2_local) {
     constexpr int kThreads = WAVES * 64;
     constexpr int kStride = NCH * kSuperK + kLdsPad;          // LDS row, bf16 elements
-    constexpr int kCols = WAVES * kTileN;
     __shared__ __attribute__((aligned(16))) __bf16 lds[9 * kStride];
     __shared__ int s_last;
 
@@ -90,69 +166,131 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
     for (int c = 0; c < NCH; ++c)
         if (c < nch) chunk_steps(acc, w[c], ap + c * kSuperK);
 
-    // Lanes g and g+2 hold the same (row, column) for the two block halves.
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] += __shfl_xor(acc[j], 32, 64);
-    const bool mine = lane < 32 && ng * WAVES + wave < n_tiles;
+    decode_finish<WAVES, BF16>(acc, out, partial, counters, ts, M, N, splits, n_tiles, l2_local,
+                               ng, split, nt, &s_last);
+}
 
-    if (splits == 1) {
-        if (mine) {
-            const int n = nt * kTileN + col;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int mm = 4 * g + j;
-                if (mm < M && n < N) store_out<BF16>(out, (size_t)mm * N + n, acc[j] * ts);
-            }
-        }
-        return;
+// ---- long slices ------------------------------------------------------------------
+
+// s_waitcnt immediates: vmcnt(n) with the other counters untouched; lgkmcnt(0).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+constexpr int kLgkmcnt0 = 0xC07F;
+
+// A barrier without the memory fence of __syncthreads: that fence would also
+// wait for the direct-to-LDS copies of the next window, just issued.  The
+// caller states with explicit waits what must be complete.
+__device__ __forceinline__ void barrier_nofence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Long K slices: a workgroup's slice is `windows` windows of NCH superblocks.
+// A wave keeps the weights of two windows in registers: those of window w + 1
+// are issued before window w is computed, so the weight stream of the
+// workgroup does not stop between windows.  The activations of a window are
+// copied straight to LDS (buffer_load ... lds) into one of two buffers,
+// issued right after that window's weights; a wave's loads complete in order,
+// so waiting for window w's loads never waits for window w + 1's.  Every wave
+// issues the same number of loads per window (clamped addresses, unused
+// destinations), so the waits are constants.
+template <int WAVES, int NCH, bool BF16>
+__global__ __launch_bounds__(WAVES * 64) void decode_window_kernel(
+    const uint4* __restrict__ codes, const uint4* __restrict__ scales,
+    const uint16_t* __restrict__ act, void* __restrict__ out, float* __restrict__ partial,
+    unsigned int* __restrict__ counters, float ts, int M, int K, int N, int nsb, int splits,
+    int n_groups, int n_tiles, int l2_local, int windows) {
+    constexpr int kThreads = WAVES * 64;
+    constexpr int kStride = NCH * kSuperK + kLdsPad;  // LDS row, bf16 elements
+    constexpr int kSeg = 8 * NCH / WAVES;  // activation segments (1 KiB) per wave per window
+    static_assert(8 * NCH % WAVES == 0, "activation segments divide over the waves");
+    constexpr int kLoads = 5 * NCH + kSeg;  // loads a wave issues per window
+    // Two separate arrays (not one of two rows): the compiler then sees that
+    // copies into one buffer never alias reads of the other, and does not
+    // make the reads wait for the copies in flight.
+    __shared__ __attribute__((aligned(16))) __bf16 lds0[9 * kStride];
+    __shared__ __attribute__((aligned(16))) __bf16 lds1[9 * kStride];
+    __shared__ int s_last;
+
+    const int b = blockIdx.x;
+    const int xcd = b & 7, q = b >> 3;
+    const int ng = (q / splits) * 8 + xcd;
+    const int split = q - (q / splits) * splits;
+    if (ng >= n_groups) return;  // whole workgroup: padding of the column groups to 8
+    const int sb_begin = split * NCH * windows;
+    const int ns = min(NCH * windows, nsb - sb_begin);  // superblocks in this slice (>= 1)
+    const int nwin = (ns + NCH - 1) / NCH;
+
+    // The wave index is uniform; saying so keeps the activation resources scalar.
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
+    const int nt = min(ng * WAVES + wave, n_tiles - 1);
+    const int col = lane & 15, g = lane >> 4;
+    const uint4* cp = codes + ((size_t)nt * nsb + sb_begin) * 256 + lane;
+    const uint4* sp = scales + ((size_t)nt * nsb + sb_begin) * 32 + col * 2 + (g >> 1);
+
+    // Zero row (row 8) of both buffers; complete before the first window's barrier.
+    for (int o = threadIdx.x; o < NCH * kSuperK / 8; o += kThreads) {
+        *(uint4*)(lds0 + 8 * kStride + 8 * o) = make_uint4(0, 0, 0, 0);
+        *(uint4*)(lds1 + 8 * kStride + 8 * o) = make_uint4(0, 0, 0, 0);
     }
 
-    // Split K.  The slices of one column group run on one XCD (blockIdx % 8
-    // selects it, verified when the plan is made: l2_local), so their
-    // partial sums meet in that XCD's L2: plain stores, a wait for their
-    // completion, then the counter increment.  Without the verified mapping
-    // the partials go through device-coherent (write-through) stores and
-    // loads instead.  Either way the hand-off needs no agent-scope fence,
-    // whose write-back of the whole L2 would cost every workgroup.
-    float* pbase = partial + (size_t)(ng * splits + split) * 8 * kCols;
-    if (mine) {
+    // Issues window w: weights into x, activation rows into buf.
+    // Segment j of this wave is (row r, superblock c) = divmod(wave * kSeg + j,
+    // NCH); rows >= M re-read row M - 1 and superblocks past the slice re-read
+    // its last one (their destinations are never read).  Each row's resource
+    // ends at the row's end, so values past K read as zero.
+    auto issue = [&](int w, Chunk (&x)[NCH], __bf16* buf) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int mm = 4 * g + j;
-            if (mm < M) {
-                float* dst = pbase + mm * kCols + wave * kTileN + col;
-                if (l2_local)
-                    *dst = acc[j];
-                else
-                    __hip_atomic_store(dst, acc[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+        for (int c = 0; c < NCH; ++c) {
+            const int sb = min(w * NCH + c, ns - 1);
+            load_chunk(x[c], cp + 256 * sb, sp + 32 * sb);
         }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned int old =
-            __hip_atomic_fetch_add(&counters[ng], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (old == (unsigned int)(splits - 1));
-    }
-    __syncthreads();
-    if (!s_last) return;
-    const float* gbase = partial + (size_t)ng * splits * 8 * kCols;
-    constexpr int kR = (8 * kCols + kThreads - 1) / kThreads;
-    float sum[kR];
-    if (l2_local)
-        sum_partials<kCols, kThreads, kR, true>(gbase, splits, M * kCols, sum);
-    else
-        sum_partials<kCols, kThreads, kR, false>(gbase, splits, M * kCols, sum);
 #pragma unroll
-    for (int r = 0; r < kR; ++r) {
-        const int idx = threadIdx.x + r * kThreads;
-        const int mm = idx / kCols, c = idx - mm * kCols;
-        const int n = ng * kCols + c;
-        if (idx < M * kCols && n < N) store_out<BF16>(out, (size_t)mm * N + n, sum[r] * ts);
+        for (int j = 0; j < kSeg; ++j) {
+            const int seg = wave * kSeg + j;
+            const int r = seg / NCH, c = seg - r * NCH;
+            const int sb = min(w * NCH + c, ns - 1);
+            const int k = (sb_begin + sb) * kSuperK;
+            const uint16_t* row = act + (size_t)min(r, M - 1) * K + k;
+            const int bytes = (K - k) * (int)sizeof(uint16_t);
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t*>(row), 0, bytes, 0x00020000);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (__attribute__((address_space(3))) void*)(buf + r * kStride + c * kSuperK),
+                16, lane * 16, 0, 0, 0);
+        }
+    };
+
+    const int m = col & 7;
+    const bool live = ((col >> 3) == (g >> 1)) && (m < M);
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    // Window w: wait for its loads (not for the next window's), then compute.
+    auto step = [&](int w, Chunk (&x)[NCH], Chunk (&y)[NCH], const __bf16* cur, __bf16* nxt) {
+        // Every wave is done reading nxt (window w - 1).
+        __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
+        barrier_nofence();
+        if (w + 1 < nwin) {
+            issue(w + 1, y, nxt);
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoads));
+        } else {
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        }
+        barrier_nofence();  // every wave's activation segments of window w are in LDS
+        const int nch = min(NCH, ns - w * NCH);
+        const __bf16* ap = cur + (live ? m : 8) * kStride + 8 * g;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+            if (c < nch) chunk_steps(acc, x[c], ap + c * kSuperK);
+    };
+    Chunk wa[NCH], wb[NCH];
+    issue(0, wa, lds0);
+    for (int w = 0; w < nwin; w += 2) {
+        step(w, wa, wb, lds0, lds1);
+        if (w + 1 < nwin) step(w + 1, wb, wa, lds1, lds0);
     }
-    if (threadIdx.x == 0)  // leave the counter zeroed for the next run
-        __hip_atomic_store(&counters[ng], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    decode_finish<WAVES, BF16>(acc, out, partial, counters, ts, M, N, splits, n_tiles, l2_local,
+                               ng, split, nt, &s_last);
 }
 
 // ---- XCD mapping check -----------------------------------------------------------
@@ -204,9 +342,12 @@ int make_decode_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, De
     const int n_tiles = padded_n(N) / kTileN;
     const int nsb = padded_k(K) / kSuperK;
     // Defaults measured on MI355X over the round's shapes (K = 5120..17408,
-    // N = 5120..152064): 2 superblocks per slice and 4 waves per workgroup,
-    // except very long K (>= 16384), where 3 superblocks and 8 waves win.
+    // N = 5120..152064): slices of 2 windows of 1 superblock and 4 waves per
+    // workgroup, except very long K (>= 16384): 6 windows of 1 superblock and
+    // 8 waves.  (One window of 2 superblocks, resp. 3 superblocks and 8
+    // waves, the best single-window forms, are 2% slower over the round.)
     const bool long_k = nsb >= 32;
+    const bool defaults = !(cfg && (cfg->split_k || cfg->chunks || cfg->windows));
     int waves = (cfg && cfg->waves) ? cfg->waves : (long_k ? 8 : 4);
     if (waves != 4 && waves != 8)
         return set_error(NVFP4_EINVAL, "config.waves: %d is not 4 or 8", waves);
@@ -225,13 +366,16 @@ int make_decode_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, De
             return set_error(NVFP4_EINVAL, "config.chunks: %d outside [1, %d]", cfg->chunks, kMaxChunks);
         chunks = cfg->chunks < nsb ? cfg->chunks : nsb;
     } else {
-        chunks = long_k ? 3 : 2;
-        if (chunks > nsb) chunks = nsb;
+        chunks = 1;
     }
-    const int splits = (nsb + chunks - 1) / chunks;
+    int windows = (cfg && cfg->windows) ? cfg->windows : defaults ? (long_k ? 6 : 2) : 1;
+    if (windows < 1) return set_error(NVFP4_EINVAL, "config.windows: %d < 1", windows);
+    if ((long long)windows * chunks > nsb) windows = (nsb + chunks - 1) / chunks;
+    const int splits = (nsb + chunks * windows - 1) / (chunks * windows);
     d->l2_local = splits > 1 ? xcd_mapping_verified() : 0;
     d->waves = waves;
     d->chunks = chunks;
+    d->windows = windows;
     d->splits = splits;
     d->n_groups = n_groups;
     d->grid = ng8 * splits;
@@ -253,10 +397,16 @@ static int launch_t(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const
     const DecodeConfig& d = p->dec;
     unsigned int* counters = (unsigned int*)ws;
     float* partial = ws ? (float*)((char*)ws + partial_off) : nullptr;
-    hipLaunchKernelGGL((decode_kernel<WAVES, NCH, BF16>), dim3(d.grid), dim3(WAVES * 64), 0, s,
-                       (const uint4*)codes, (const uint4*)scales, act, out, partial, counters, ts,
-                       M, p->K, p->N, p->Kp / kSuperK, d.splits, d.n_groups, p->Np / kTileN,
-                       d.l2_local);
+    if (d.windows > 1)
+        hipLaunchKernelGGL((decode_window_kernel<WAVES, NCH, BF16>), dim3(d.grid),
+                           dim3(WAVES * 64), 0, s, (const uint4*)codes, (const uint4*)scales, act,
+                           out, partial, counters, ts, M, p->K, p->N, p->Kp / kSuperK, d.splits,
+                           d.n_groups, p->Np / kTileN, d.l2_local, d.windows);
+    else
+        hipLaunchKernelGGL((decode_kernel<WAVES, NCH, BF16>), dim3(d.grid), dim3(WAVES * 64), 0,
+                           s, (const uint4*)codes, (const uint4*)scales, act, out, partial,
+                           counters, ts, M, p->K, p->N, p->Kp / kSuperK, d.splits, d.n_groups,
+                           p->Np / kTileN, d.l2_local);
     NVFP4_HIP(hipGetLastError());
     return NVFP4_OK;
 }

@@ -184,6 +184,21 @@ def test_random_planes_ragged(nv, M, K, N, bf16, kernel):
     check(out, y, S, bf16=bf16, what="ragged %r" % ((M, K, N),))
 
 
+@pytest.mark.parametrize("M,K,N", RAGGED)
+@pytest.mark.parametrize("cfg", [dict(chunks=1, windows=2), dict(chunks=2, windows=3, waves=8)],
+                         ids=["c1w2", "c2w3v8"])
+def test_streamed_slices_ragged(nv, M, K, N, cfg):
+    """The streamed-slice decode kernel on ragged K and N tails, with slices
+    that end inside a window and K tails inside a superblock."""
+    codes, scales = synth.random_planes(M * 5 + K, N + 1, N, K)
+    t = 1.5e-3
+    act = synth.activations(M + 3, K + N, M, K)
+    pw = pack(nv, dev(codes), dev(scales), K, N, t)
+    out, _ = run(nv, pw, dev_bf16(act), nv.OUT_F32, kernel=2, **cfg)
+    y, S = oracle.gemm(act, codes, scales, t)
+    check(out, y, S, bf16=False, what="streamed %r %r" % ((M, K, N), cfg))
+
+
 @pytest.mark.parametrize("M", [1, 2, 4, 8])
 def test_projection_5120_full(nv, M):
     """The single-projection config: M lanes, K = N = 5120, quantised
@@ -203,7 +218,10 @@ def test_projection_5120_full(nv, M):
 
 
 CONFIGS = ([dict(kernel=2, chunks=c, waves=w) for w in (4, 8) for c in (1, 2, 3, 4)] +
-           [dict(kernel=1, tiles=t) for t in (2, 4, 8)])
+           [dict(kernel=1, tiles=t) for t in (2, 4, 8)] +
+           # streamed slices: several windows of `chunks` superblocks per workgroup
+           [dict(kernel=2, chunks=c, waves=w, windows=n)
+            for (w, c, n) in ((4, 1, 3), (4, 2, 2), (8, 2, 3), (8, 1, 5), (4, 2, 6), (8, 3, 2))])
 
 
 @pytest.mark.parametrize("cfg", CONFIGS, ids=[str(sorted(c.items())) for c in CONFIGS])
