@@ -78,13 +78,15 @@ __host__ __device__ inline size_t chain_counter_bytes(int n_groups) {
 typedef unsigned int cu32x4 __attribute__((ext_vector_type(4)));
 constexpr int kChainRaw = 0x00020000;  // buffer resource word 3: raw 32-bit data
 constexpr int kSc1 = 16;               // cache policy bits: device scope (sc1)
+constexpr int kNt = 2;                 // cache policy bits: non-temporal (weights, read once)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t chain_rsrc(const void* base, size_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kChainRaw);
 }
 
+template <int AUX>
 __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    const cu32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+    const cu32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, AUX);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -165,8 +167,8 @@ __global__ __launch_bounds__((WAVES + 1) * 64) void chain_kernel(
             const uint32_t cc = (uint32_t)min(c, nch - 1);  // a short slice re-reads its last chunk
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                w[c].c[i] = bload16(rc, coff + i * 1024, cc * kCodeBytesPerSuper);
-            w[c].s = bload16(rs, soff, cc * kScaleBytesPerSuper);
+                w[c].c[i] = bload16<kNt>(rc, coff + i * 1024, cc * kCodeBytesPerSuper);
+            w[c].s = bload16<kNt>(rs, soff, cc * kScaleBytesPerSuper);
         }
     } else {
         // 2. Wait until the previous matrix is complete (its flag reads >= index).
