@@ -43,6 +43,7 @@ PASSES = (
 CALIB_BYTES = 1 << 30
 DECODE = "nvfp4::decode_"  # decode_kernel< and decode_window_kernel<
 PREFILL = "nvfp4::prefill_kernel<"
+PREFILL_SUM = "nvfp4::prefill_reduce_kernel<"
 COPY = "__amd_rocclr_copyBuffer"
 
 
@@ -101,6 +102,8 @@ def summarize(out, dest):
     dur = lambda r: int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
     dec_avg_us = sum(map(dur, dec)) / len(dec) / 1e3
     pre_avg_us = sum(map(dur, pre)) / len(pre) / 1e3 if pre else float("nan")
+    psum = [r for r in trace if PREFILL_SUM in r["Kernel_Name"]]
+    psum_avg_us = sum(map(dur, psum)) / len(psum) / 1e3 if psum else 0.0
 
     # the first replay's first four launches are layer 0's qkv, o, gate_up, down
     layers = bench.LAYERS
@@ -135,8 +138,9 @@ def summarize(out, dest):
               % (algo, roof["achieved"], algo / (dec_avg_us * 1e-6) / 1e9))
     md.append("| M = 8 round (ms) | %.4f | %.4f (sum of kernel durations / replays) |"
               % (line["ms_per_step"], sum(map(dur, dec)) / (len(dec) / per_round) / 1e6))
-    md.append("| prefill kernel (us) | %.2f | %.2f |\n" % (line["prefill_chunk"]["us"],
-                                                           pre_avg_us))
+    md.append("| prefill chunk (us): tile kernel + K-piece sum kernel | %.2f | %.2f + %.2f "
+              "= %.2f |\n" % (line["prefill_chunk"]["us"], pre_avg_us, psum_avg_us,
+                             pre_avg_us + psum_avg_us))
     md.append("bench.py's average launch is the timed region's event time over the %d "
               "launches of a replay, so it includes the gaps between graph nodes; the "
               "trace's figure is kernel time only.\n" % per_round)

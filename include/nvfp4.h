@@ -158,7 +158,10 @@ void nvfp4_gemm_destroy(nvfp4_gemm plan);
  *                           if the plan needs none
  * (K, N) must equal the plan's, 1 <= M <= max_M.  M <= 8 uses the decode
  * kernel (one pass over the weights for all M rows); larger M uses the bf16
- * MFMA prefill kernel.  Asynchronous; no synchronisation. */
+ * MFMA prefill kernel, and, when the 256 x 256 output tiles leave a last
+ * partial round on the device's compute units, a second kernel that adds the
+ * fp32 partial sums of those tiles' K pieces (kept in the workspace, after
+ * the decode counters).  Asynchronous; no synchronisation. */
 int nvfp4_gemm_run(nvfp4_gemm plan, int M, int K, int N, const uint8_t* codes_dev,
                    const uint8_t* scales_dev, float tensor_scale, const uint16_t* act_dev,
                    void* out_dev, void* workspace_dev, void* stream);

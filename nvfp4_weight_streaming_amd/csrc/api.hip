@@ -161,8 +161,11 @@ static int create_plan(nvfp4_gemm* plan, int max_M, int K, int N, int out_dtype,
         delete p;
         return st;
     }
+    // [decode counters and partial sums][prefill partial sums]: decode counters
+    // must stay zero between runs, so the prefill area never overlaps them.
     const size_t dec_ws = p->str.enabled ? 0 : p->dec.ws_bytes;
-    p->ws_bytes = dec_ws > p->pre.ws_bytes ? dec_ws : p->pre.ws_bytes;
+    p->pre.ws_off = (dec_ws + 255) & ~(size_t)255;
+    p->ws_bytes = p->pre.ws_bytes ? p->pre.ws_off + p->pre.ws_bytes : dec_ws;
     *workspace_bytes = p->ws_bytes;
     *plan = p;
     return NVFP4_OK;

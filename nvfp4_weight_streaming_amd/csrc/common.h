@@ -64,7 +64,8 @@ struct StreamConfig {
 
 struct PrefillConfig {
     int enabled;
-    size_t ws_bytes;
+    size_t ws_off;    // partial sums of K-split tiles: offset in the workspace
+    size_t ws_bytes;  // and their size (0: no M the plan serves splits)
 };
 
 }  // namespace nvfp4

@@ -13,20 +13,23 @@
 // the epilogue.
 //
 // Tiling: block tile 256 (rows of activations) x 256 (outputs), K in stages of
-// 64, double-buffered in LDS (two stages of 256 x 64 activations and 256 x 64
-// dequantised weights, 128 KiB).  8 waves as 2 x 4, each owning 128 x 64
-// outputs as 4 x 2 MFMA tiles of 32 x 32 (128 fp32 accumulators per lane, in
-// the accumulation registers); two waves per SIMD, so one multiplies while
-// the other waits on memory.  Two stages are held in registers ahead of
-// the one being multiplied; after the multiply the next is written (weights
-// dequantised on the way) into the other LDS buffer and the one after that is
-// loaded, and one barrier per stage separates the two buffers.  LDS rows are 128 bytes (8 segments of 16): segment j of row r is
-// stored in slot j ^ (r % 8), so the 32 rows an MFMA operand read touches are
-// spread over the banks.
+// 64.  LDS holds three stages of 256 x 64 activations and two of 256 x 64
+// dequantised weights (160 KiB, one workgroup per compute unit).  8 waves as
+// 2 x 4, each owning 128 x 64 outputs as 4 x 2 MFMA tiles of 32 x 32 (128 fp32
+// accumulators per lane, in the accumulation registers).  Activations run two
+// stages ahead (direct-to-LDS copies); weights run two stages ahead in
+// registers and are dequantised into LDS one stage ahead, the conversion
+// interleaved with the multiplies; one barrier per stage.  LDS rows are 128
+// bytes (8 segments of 16): segment j of row r sits in slot j ^ ((r / 2) % 8),
+// so the 16 rows one operand read pass touches cover all banks once.
 //
-// Column blocks beyond a multiple of the compute units' worth are run as
-// 128 x 128 tiles (a quarter of the work each), so the last round of
-// workgroups is short instead of mostly idle.
+// Last round: the tiles beyond a multiple of the compute units' count would
+// leave most of the chip idle in a last, partial round.  They are split along
+// K instead, S pieces each (S = compute units / leftover tiles, at most one
+// piece per 4 stages); every piece writes its fp32 accumulators to the
+// workspace, and a second kernel adds the S partial sums of each output in
+// piece order, applies the tensor scale and stores.  The pieces come first in
+// the grid; the stream order makes every partial complete before the sum.
 #include "decode_device.h"
 
 namespace nvfp4 {
@@ -251,19 +254,26 @@ __device__ __forceinline__ void prefill_mma(f32x16 (&acc)[BM / 64][BN / 128], co
     __builtin_amdgcn_s_setprio(0);
 }
 
-// One BM x BN block tile; wave w owns rows (w / 4) * BM/2 and columns
-// (w % 4) * BN/4, as (BM/64) x (BN/128) MFMA tiles of 32 x 32.
+// One BM x BN block tile over K stages kt0 .. kt1 - 1; wave w owns rows
+// (w / 4) * BM/2 and columns (w % 4) * BN/4, as (BM/64) x (BN/128) MFMA tiles
+// of 32 x 32.  With part == nullptr the tile covers all of K and stores
+// acc * ts to out; otherwise it stores its raw accumulators to part (BM * BN
+// floats, in register order: float4 ((((w TI + i) TJ + j) 4 + r / 4) 64 +
+// lane) holds elements r .. r + 3 of lane's MFMA tile (i, j)).
 template <int BM, int BN, bool BF16>
 __device__ __forceinline__ void prefill_tile(PrefillLds& L, const uint8_t* __restrict__ codes,
                                              const uint8_t* __restrict__ scales,
                                              const uint16_t* __restrict__ act,
-                                             void* __restrict__ out, float ts, int M, int K,
-                                             int N, int nsb, int n_tiles, int m0, int n0) {
+                                             void* __restrict__ out, float* __restrict__ part,
+                                             float ts, int M, int K, int N, int nsb, int n_tiles,
+                                             int m0, int n0, int kt0, int kt1) {
     constexpr int TI = BM / 64, TJ = BN / 128;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wm = wave >> 2, wn = wave & 3;
     const int nt0 = n0 / kTileN;
-    const int nk = (K + kPBK - 1) / kPBK;
+    const int nks = kt1 - kt0;
+    // absolute stage of relative stage u, clamped to the last one
+    auto at = [&](int u) { return kt0 + min(u, nks - 1); };
 
     f32x16 acc[TI][TJ];
 #pragma unroll
@@ -273,43 +283,43 @@ __device__ __forceinline__ void prefill_tile(PrefillLds& L, const uint8_t* __res
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // Activations run two stages ahead in three LDS buffers (stage kt in
-    // buffer kt % 3); weights run two stages ahead in registers (st0 / st1
-    // alternately hold stages kt + 1 and kt + 2) and are dequantised into two
-    // LDS buffers (stage kt in buffer kt % 2).  Stages past the end re-read
+    // Activations run two stages ahead in three LDS buffers (relative stage
+    // u in buffer u % 3); weights run two stages ahead in registers (st0 /
+    // st1 alternately hold stages u + 1 and u + 2) and are dequantised into
+    // two LDS buffers (stage u in buffer u % 2).  Stages past the end re-read
     // the last one into buffers nobody reads again.
     PrefillA<BM> A;
     A.init(act, M, K, m0, wave, lane);
     PrefillB<BN> B;
     B.init(codes, scales, nsb, n_tiles, nt0);
     PStage<BN> st0, st1;
-    A.copy(L.a[0], 0, wave);
-    A.copy(L.a[1], min(1, nk - 1), wave);
-    st0.load(B, 0);
-    st0.store(L.b[0], 0);
-    st0.load(B, min(1, nk - 1));
-    st1.load(B, min(2, nk - 1));
+    A.copy(L.a[0], at(0), wave);
+    A.copy(L.a[1], at(1), wave);
+    st0.load(B, at(0));
+    st0.store(L.b[0], at(0));
+    st0.load(B, at(1));
+    st1.load(B, at(2));
     // Outstanding, oldest first: the loads of stage 1 into st0 and of stage 2
     // into st1 (BN / 64 each); the activation copies before them are complete.
     __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * (BN / 64)));
     __syncthreads();
 
     const int r32 = lane & 31, half = lane >> 5;
-    // Per stage, issued in this order: activation copy of stage kt + 2
+    // Per stage, issued in this order: activation copy of stage u + 2
     // (BM / 64 loads), the multiplies with the dequantised store of stage
-    // kt + 1 interleaved, the weight loads of stage kt + 3 (BN / 64 loads).  Before the barrier the
-    // copy of stage kt + 1 (issued one stage earlier) must have landed: the
-    // loads after it may still be in flight.
-    auto stage = [&](int kt, PStage<BN>& next, int kt_next) {
-        A.copy(L.a[(kt + 2) % 3], min(kt + 2, nk - 1), wave);
+    // u + 1 interleaved, the weight loads of stage u + 3 (BN / 64 loads).
+    // Before the barrier the copy of stage u + 1 (issued one stage earlier)
+    // must have landed: the loads after it may still be in flight.
+    auto stage = [&](int u, PStage<BN>& next, int u_next) {
+        A.copy(L.a[(u + 2) % 3], at(u + 2), wave);
         __builtin_amdgcn_sched_barrier(0);
-        prefill_mma<BM, BN>(acc, L.a[kt % 3], L.b[kt & 1], next, L.b[(kt + 1) & 1],
-                            min(kt + 1, nk - 1), wm, wn, r32, half);
+        prefill_mma<BM, BN>(acc, L.a[u % 3], L.b[u & 1], next, L.b[(u + 1) & 1], at(u + 1), wm,
+                            wn, r32, half);
         __builtin_amdgcn_sched_barrier(0);
-        next.load(B, kt_next);
+        next.load(B, at(u_next));
         __builtin_amdgcn_sched_barrier(0);
         // Then the barrier, without a memory fence (a fence would also wait
-        // for the copy of stage kt + 2 just issued): this wave's LDS stores
+        // for the copy of stage u + 2 just issued): this wave's LDS stores
         // are complete, and the compiler may not move memory accesses across.
         __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * (BN / 64) + BM / 64));
         __builtin_amdgcn_s_waitcnt(kPWaitLgkm0);
@@ -320,13 +330,27 @@ __device__ __forceinline__ void prefill_tile(PrefillLds& L, const uint8_t* __res
     // Unrolled by two so st0 and st1 keep fixed registers (copying a register
     // set whose loads are in flight would wait for them); an odd last stage
     // runs after the loop.
-    int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-        stage(kt, st0, min(kt + 3, nk - 1));
-        stage(kt + 1, st1, min(kt + 4, nk - 1));
+    int u = 0;
+    for (; u + 1 < nks; u += 2) {
+        stage(u, st0, u + 3);
+        stage(u + 1, st1, u + 4);
     }
-    if (kt < nk) stage(kt, st0, min(kt + 3, nk - 1));
+    if (u < nks) stage(u, st0, u + 3);
 
+    if (part) {
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    const int v = (((wave * TI + i) * TJ + j) * 4 + rq) * 64 + lane;
+                    *(float4*)(part + 4 * v) =
+                        make_float4(acc[i][j][4 * rq], acc[i][j][4 * rq + 1],
+                                    acc[i][j][4 * rq + 2], acc[i][j][4 * rq + 3]);
+                }
+        return;
+    }
     // Epilogue: element r of a 32 x 32 tile in lane l is
     // (row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32).
 #pragma unroll
@@ -342,34 +366,69 @@ __device__ __forceinline__ void prefill_tile(PrefillLds& L, const uint8_t* __res
         }
 }
 
-// Workgroups 0 .. n_big-1 take 256 x 256 tiles over the first nb_big column
-// blocks (row block = id % mblocks256); the rest take 128 x 128 tiles over
-// the remaining columns.
+constexpr int kPTile = 256;                      // block tile edge (rows and outputs)
+constexpr int kPTileFloats = kPTile * kPTile;    // one piece's partial sums
+constexpr int kPMinPieceStages = 4;              // K stages per piece, at least
+
+// Tile t covers rows (t % mblocks) * 256 and outputs (t / mblocks) * 256.
+// Workgroups 0 .. pieces - 1 are the K pieces of the last n_tail tiles
+// (piece b: tile tiles - n_tail + b % n_tail, split b / n_tail, stages
+// split * nk / S .. (split + 1) * nk / S - 1; its partial sums at part +
+// b * 65536); the rest are whole tiles 0, 1, ...
 template <bool BF16>
 __global__ __launch_bounds__(kPThreads) void prefill_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-    const uint16_t* __restrict__ act, void* __restrict__ out, float ts, int M, int K, int N,
-    int nsb, int n_tiles, int mblocks256, int n_big, int n_col0, int mblocks128) {
+    const uint16_t* __restrict__ act, void* __restrict__ out, float* __restrict__ part, float ts,
+    int M, int K, int N, int nsb, int n_tiles, int mblocks, int tiles, int n_tail, int splits) {
     __shared__ __attribute__((aligned(16))) PrefillLds L;
+    const int nk = (K + kPBK - 1) / kPBK;
+    const int pieces = n_tail * splits;
     const int b = blockIdx.x;
-    if (b < n_big) {
-        const int mb = b % mblocks256, nb = b / mblocks256;
-        prefill_tile<256, 256, BF16>(L, codes, scales, act, out, ts, M, K, N, nsb, n_tiles,
-                                     mb * 256, nb * 256);
+    if (b < pieces) {
+        const int t = tiles - n_tail + b % n_tail, split = b / n_tail;
+        prefill_tile<kPTile, kPTile, BF16>(
+            L, codes, scales, act, out, part + (size_t)b * kPTileFloats, ts, M, K, N, nsb,
+            n_tiles, (t % mblocks) * kPTile, (t / mblocks) * kPTile, split * nk / splits,
+            (split + 1) * nk / splits);
     } else {
-        const int q = b - n_big;
-        const int mb = q % mblocks128, nb = q / mblocks128;
-        prefill_tile<128, 128, BF16>(L, codes, scales, act, out, ts, M, K, N, nsb, n_tiles,
-                                     mb * 128, n_col0 + nb * 128);
+        const int t = b - pieces;
+        prefill_tile<kPTile, kPTile, BF16>(L, codes, scales, act, out, nullptr, ts, M, K, N,
+                                           nsb, n_tiles, (t % mblocks) * kPTile,
+                                           (t / mblocks) * kPTile, 0, nk);
     }
 }
 
-int make_prefill_config(int max_M, int K, int N, PrefillConfig* out) {
-    (void)K;
-    (void)N;
-    out->enabled = max_M > NVFP4_DECODE_MAX_M;
-    out->ws_bytes = 0;
-    return NVFP4_OK;
+// Sum of the split tiles' partials: thread p of tile q adds float4 p of its
+// S pieces in piece order, scales by ts and stores the 4 outputs it maps to
+// (the register order prefill_tile stores them in).
+constexpr int kPReduceThreads = 256;
+template <bool BF16>
+__global__ __launch_bounds__(kPReduceThreads) void prefill_reduce_kernel(
+    const float* __restrict__ part, void* __restrict__ out, float ts, int M, int N, int mblocks,
+    int tiles, int n_tail, int splits) {
+    constexpr int kBlocksPerTile = kPTileFloats / 4 / kPReduceThreads;
+    constexpr int TI = kPTile / 64, TJ = kPTile / 128;
+    const int q = blockIdx.x / kBlocksPerTile;
+    const int p = (blockIdx.x % kBlocksPerTile) * kPReduceThreads + threadIdx.x;
+    const int t = tiles - n_tail + q;
+    const int lane = p & 63, rq = (p >> 6) & 3, j = (p >> 8) % TJ, i = (p >> 8) / TJ % TI;
+    const int wave = (p >> 8) / (TI * TJ);
+    const int wm = wave >> 2, wn = wave & 3;
+    const int n = (t / mblocks) * kPTile + wn * (kPTile / 4) + 32 * j + (lane & 31);
+    const int m = (t % mblocks) * kPTile + wm * (kPTile / 2) + 32 * i + 8 * rq + 4 * (lane >> 5);
+    if (n >= N || m >= M) return;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < splits; ++s) {
+        const float4 x = *(const float4*)(part + (size_t)(s * n_tail + q) * kPTileFloats + 4 * p);
+        v.x += x.x;
+        v.y += x.y;
+        v.z += x.z;
+        v.w += x.w;
+    }
+    const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        if (m + r < M) store_out<BF16>(out, (size_t)(m + r) * N + n, e[r] * ts);
 }
 
 static int prefill_cus() {
@@ -380,40 +439,73 @@ static int prefill_cus() {
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus < 1) {
         (void)hipGetLastError();
-        return 256;
+        cus = 256;  // MI355X; kept, so plans and launches agree on the split
     }
     cached = cus;
     return cus;
 }
 
+// Tiles beyond whole rounds (one tile per compute unit at a time) are split
+// along K when at least two pieces each fit: n_tail tiles, S pieces each.
+struct PrefillSplit {
+    int tiles, n_tail, splits;
+};
+
+static PrefillSplit prefill_split(int M, int K, int N, int cus) {
+    const int mblocks = (M + kPTile - 1) / kPTile, nblocks = (N + kPTile - 1) / kPTile;
+    const int nk = (K + kPBK - 1) / kPBK;
+    PrefillSplit s{mblocks * nblocks, 0, 1};
+    const int left = s.tiles % cus;
+    const int S = left ? min(cus / left, nk / kPMinPieceStages) : 1;
+    if (S >= 2) {
+        s.n_tail = left;
+        s.splits = S;
+    }
+    return s;
+}
+
+int make_prefill_config(int max_M, int K, int N, PrefillConfig* out) {
+    out->enabled = max_M > NVFP4_DECODE_MAX_M;
+    out->ws_off = 0;
+    out->ws_bytes = 0;
+    if (!out->enabled) return NVFP4_OK;
+    // The largest partial-sum area over every M the plan serves (the split
+    // depends on M only through the row blocks).
+    const int cus = prefill_cus();
+    for (int mb = 1; mb <= (max_M + kPTile - 1) / kPTile; ++mb) {
+        const PrefillSplit s = prefill_split(mb * kPTile, K, N, cus);
+        const size_t bytes = (size_t)s.n_tail * s.splits * kPTileFloats * sizeof(float);
+        if (bytes > out->ws_bytes) out->ws_bytes = bytes;
+    }
+    return NVFP4_OK;
+}
+
 int launch_prefill(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
                    float ts, const uint16_t* act, void* out, void* ws, hipStream_t s) {
-    (void)ws;
     const int n_tiles = p->Np / kTileN, nsb = p->Kp / kSuperK;
-    const int mb256 = (M + 255) / 256, mb128 = (M + 127) / 128;
-    const int nb256 = (p->N + 255) / 256;
-    // Full rounds of 256 x 256 tiles (one workgroup per compute unit at a
-    // time); the column blocks of a last, partial round become 128 x 128
-    // tiles, four per block, when that shortens it.
-    const int cus = prefill_cus();
-    const int tiles = mb256 * nb256;
-    int nb_big = nb256;
-    if (tiles > cus && tiles % cus != 0) {
-        const int full = tiles / cus * cus;  // tiles in full rounds
-        nb_big = full / mb256;               // whole column blocks in them
-    }
-    const int n_big = mb256 * nb_big, n_col0 = nb_big * 256;
-    const int cols_left = p->N > n_col0 ? p->N - n_col0 : 0;
-    const int n_small = mb128 * ((cols_left + 127) / 128);
-    const dim3 grid((unsigned)(n_big + n_small));
-    if (p->out_dtype == NVFP4_OUT_BF16)
-        hipLaunchKernelGGL(prefill_kernel<true>, grid, dim3(kPThreads), 0, s, codes,
-                           scales, act, out, ts, M, p->K, p->N, nsb, n_tiles, mb256, n_big,
-                           n_col0, mb128);
+    const int mblocks = (M + kPTile - 1) / kPTile;
+    const PrefillSplit sp = prefill_split(M, p->K, p->N, prefill_cus());
+    const int pieces = sp.n_tail * sp.splits;
+    float* part = pieces ? (float*)((char*)ws + p->pre.ws_off) : nullptr;
+    const dim3 grid((unsigned)(sp.tiles - sp.n_tail + pieces));
+    const bool bf16 = p->out_dtype == NVFP4_OUT_BF16;
+    if (bf16)
+        hipLaunchKernelGGL(prefill_kernel<true>, grid, dim3(kPThreads), 0, s, codes, scales, act,
+                           out, part, ts, M, p->K, p->N, nsb, n_tiles, mblocks, sp.tiles,
+                           sp.n_tail, sp.splits);
     else
-        hipLaunchKernelGGL(prefill_kernel<false>, grid, dim3(kPThreads), 0, s, codes,
-                           scales, act, out, ts, M, p->K, p->N, nsb, n_tiles, mb256, n_big,
-                           n_col0, mb128);
+        hipLaunchKernelGGL(prefill_kernel<false>, grid, dim3(kPThreads), 0, s, codes, scales,
+                           act, out, part, ts, M, p->K, p->N, nsb, n_tiles, mblocks, sp.tiles,
+                           sp.n_tail, sp.splits);
+    NVFP4_HIP(hipGetLastError());
+    if (!pieces) return NVFP4_OK;
+    const dim3 rgrid((unsigned)(sp.n_tail * (kPTileFloats / 4 / kPReduceThreads)));
+    if (bf16)
+        hipLaunchKernelGGL(prefill_reduce_kernel<true>, rgrid, dim3(kPReduceThreads), 0, s, part,
+                           out, ts, M, p->N, mblocks, sp.tiles, sp.n_tail, sp.splits);
+    else
+        hipLaunchKernelGGL(prefill_reduce_kernel<false>, rgrid, dim3(kPReduceThreads), 0, s,
+                           part, out, ts, M, p->N, mblocks, sp.tiles, sp.n_tail, sp.splits);
     NVFP4_HIP(hipGetLastError());
     return NVFP4_OK;
 }

@@ -286,8 +286,10 @@ def test_m_below_plan_max_and_bf16_rounding(nv):
 
 # ---- prefill (M > 8: dequantised tiles, bf16 MFMA) ------------------------------
 
+# All but the last split their tiles along K (fp32 partial sums and a second
+# kernel); K = 256 is too short to split (4 stages of 64).
 @pytest.mark.parametrize("M,K,N", [(9, 512, 64), (64, 1024, 256), (300, 1040, 530),
-                                   (513, 2048, 300), (256, 5120, 272)])
+                                   (513, 2048, 300), (256, 5120, 272), (40, 256, 1000)])
 @pytest.mark.parametrize("bf16", [False, True])
 def test_prefill_ragged(nv, M, K, N, bf16):
     codes, scales = synth.random_planes(M + 3 * K, N, N, K)
@@ -299,14 +301,36 @@ def test_prefill_ragged(nv, M, K, N, bf16):
     check(out, y, S, bf16=bf16, what="prefill %r" % ((M, K, N),))
 
 
+def test_prefill_and_decode_share_a_workspace(nv):
+    """One plan alternates prefill runs (K-split tiles: partial sums in the
+    workspace) and decode runs (split-K counters in the same workspace): the
+    prefill area must leave the decode counters zero."""
+    import torch
+    M, K, N = 513, 2048, 300
+    codes, scales = synth.random_planes(77, N, N, K)
+    t = 0.004
+    act = synth.activations(77, K + N, M, K)
+    pw = pack(nv, dev(codes), dev(scales), K, N, t)
+    g = nv.Gemm(M, K, N, nv.OUT_F32)
+    a = dev_bf16(act)
+    for m in (M, 8, M, 3, 8):
+        out = torch.full((m, N), float("nan"), dtype=torch.float32, device="cuda")
+        g(pw, a[:m], out, M=m)
+        torch.cuda.synchronize()
+        y, S = oracle.gemm(act[:m], codes, scales, t)
+        check(out, y, S, bf16=False, what="M=%d after the other path" % m)
+
+
 def test_prefill_chunk_config_sampled(nv):
     """The prefill-chunk config: M = 2048, K = 5120, N = 17408, quantised
-    N(0, 0.02) weights, bf16 out; every row, sampled columns."""
+    N(0, 0.02) weights, bf16 out; every row, sampled columns (some of them in
+    the last four column blocks, whose tiles are split along K on a
+    256-CU device)."""
     import torch
     M, K, N = 2048, 5120, 17408
     W = synth.weights(0, 300, N, K)
     cols = np.array(sorted(set(np.random.default_rng(1).choice(N, 40, replace=False).tolist())
-                           | {0, 255, 256, N - 1}))
+                           | {0, 255, 256, 16383, 16384, 16895, 17000, N - 1}))
     t = oracle.tensor_scale(W)
     c_ref, s_ref = oracle.quantize_rows(W[cols], t)
     c, s, tg = _gpu_quantize(nv, W)
