@@ -286,22 +286,54 @@ def main():
         for _ in range(2):
             pg(ppw, pact, pout, stream=stream)
         stream.synchronize()
-        pevs = []
-        for _ in range(max(3, args.steps // 4)):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
+        # back-to-back calls between one pair of events (throughput, as a
+        # chunk loop issues them)
+        n_pre = max(3, args.steps // 4)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n_pre):
             pg(ppw, pact, pout, stream=stream)
-            b.record(stream)
-            pevs.append((a, b))
+        b.record(stream)
         torch.cuda.synchronize()
-    p_us = sum(a.elapsed_time(b) for a, b in pevs) / len(pevs) * 1e3
+    p_us = a.elapsed_time(b) / n_pre * 1e3
     p_tflops = 2.0 * PM * PK * PN / (p_us * 1e-6) / 1e12
     log("prefill M=%d K=%d N=%d: %.1f us, %.1f TFLOP/s (%.1f%% of 2.5 PF bf16)"
         % (PM, PK, PN, p_us, p_tflops, 100 * p_tflops / 2500.0))
     prefill = {"M": PM, "K": PK, "N": PN, "us": round(p_us, 2), "TFLOP_s": round(p_tflops, 1),
                "frac_bf16_mfma_peak": round(p_tflops / 2500.0, 4)}
     del ppw, pact, pout, pg
+
+    # Output head (M = 8, K = 5120, N = 152064, fp32 logits): one decode launch
+    # per call, default plan; back-to-back calls between one pair of events.
+    HK, HN = 5120, 152064
+    with torch.cuda.stream(stream):
+        wh = synth.weights_device(0, 9002, HN, HK)
+        hpw = nv.PackedWeight.quantize(wh, stream=stream)
+        del wh
+        hact = synth.activations_device(0, 9002, 8, HK)
+        hout = torch.empty((8, HN), dtype=torch.float32, device="cuda")
+        hg = nv.Gemm(8, HK, HN, nv.OUT_F32)
+        for _ in range(3):
+            hg(hpw, hact, hout, stream=stream)
+        stream.synchronize()
+        n_head = max(5, args.steps)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n_head):
+            hg(hpw, hact, hout, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+    h_us = a.elapsed_time(b) / n_head * 1e3
+    h_bytes = weight_bytes(HK, HN) + 8 * HK * 2 + 8 * HN * 4
+    h_gbs = h_bytes / (h_us * 1e-6) / 1e9
+    log("output head M=8 K=%d N=%d (fp32 out): %.1f us, %.1f GB/s (%.1f%% of 8 TB/s)"
+        % (HK, HN, h_us, h_gbs, 100 * h_gbs / HBM_PEAK_GBS))
+    head = {"M": 8, "K": HK, "N": HN, "out": "fp32", "us": round(h_us, 2),
+            "algorithmic_bytes": h_bytes, "GB_s": round(h_gbs, 1),
+            "frac_hbm_peak": round(h_gbs / HBM_PEAK_GBS, 4)}
+    del hpw, hact, hout, hg
 
     if args.calibration_copy:
         # A plain copy kernel of known size: 1 GiB read, 1 GiB written.
@@ -368,6 +400,7 @@ def main():
             "traffic": traffic,
         },
         "prefill_chunk": prefill,
+        "output_head": head,
         "cpu_baseline": cpu,
         "timed_wall_s": round(wall, 3),
     }

@@ -98,12 +98,18 @@ def summarize(out, dest):
 
     trace.sort(key=lambda r: int(r["Start_Timestamp"]))
     dec = [r for r in trace if DECODE in r["Kernel_Name"]]
+    # the round's launches are those of the first replay's four shapes; the
+    # other decode launches are the output head's
+    round_keys = {(r["Kernel_Name"], r["Grid_Size_X"]) for r in dec[:4]}
+    head = [r for r in dec if (r["Kernel_Name"], r["Grid_Size_X"]) not in round_keys]
+    dec = [r for r in dec if (r["Kernel_Name"], r["Grid_Size_X"]) in round_keys]
     pre = [r for r in trace if PREFILL in r["Kernel_Name"]]
     dur = lambda r: int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
     dec_avg_us = sum(map(dur, dec)) / len(dec) / 1e3
     pre_avg_us = sum(map(dur, pre)) / len(pre) / 1e3 if pre else float("nan")
     psum = [r for r in trace if PREFILL_SUM in r["Kernel_Name"]]
     psum_avg_us = sum(map(dur, psum)) / len(psum) / 1e3 if psum else 0.0
+    head_avg_us = sum(map(dur, head)) / len(head) / 1e3 if head else float("nan")
 
     # the first replay's first four launches are layer 0's qkv, o, gate_up, down
     layers = bench.LAYERS
@@ -139,8 +145,12 @@ def summarize(out, dest):
     md.append("| M = 8 round (ms) | %.4f | %.4f (sum of kernel durations / replays) |"
               % (line["ms_per_step"], sum(map(dur, dec)) / (len(dec) / per_round) / 1e6))
     md.append("| prefill chunk (us): tile kernel + K-piece sum kernel | %.2f | %.2f + %.2f "
-              "= %.2f |\n" % (line["prefill_chunk"]["us"], pre_avg_us, psum_avg_us,
-                             pre_avg_us + psum_avg_us))
+              "= %.2f |" % (line["prefill_chunk"]["us"], pre_avg_us, psum_avg_us,
+                            pre_avg_us + psum_avg_us))
+    if "output_head" in line:
+        md.append("| output head, M = 8, K = 5120, N = 152064, fp32 out (us) | %.2f | %.2f |"
+                  % (line["output_head"]["us"], head_avg_us))
+    md.append("")
     md.append("bench.py's average launch is the timed region's event time over the %d "
               "launches of a replay, so it includes the gaps between graph nodes; the "
               "trace's figure is kernel time only.\n" % per_round)
@@ -176,7 +186,9 @@ def summarize(out, dest):
             k = int(r["Dispatch_Id"])
             per[k] += float(r["Counter_Value"])
             meta[k] = (r["Kernel_Name"], r["Grid_Size"])
-        dec_v = [v for k, v in per.items() if DECODE in meta[k][0]]
+        dec_ids = sorted(k for k in per if DECODE in meta[k][0])
+        keys = {meta[k] for k in dec_ids[:4]}  # the round's four shapes (not the head)
+        dec_v = [per[k] for k in dec_ids if meta[k] in keys]
         cal = max(v for k, v in per.items() if COPY in meta[k][0])
         return dec_v, cal, len(dec_v)
 

@@ -84,6 +84,8 @@ namespace nvfp4 {
 constexpr uint32_t kGemmMagic = 0x4E564634u;  // "NVF4"
 constexpr uint32_t kRoundMagic = 0x524F4E44u;
 
+// Compute units of the current device (cached per device; 256 if the query fails).
+int device_cus();
 int make_decode_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, DecodeConfig* out);
 int make_prefill_config(int max_M, int K, int N, PrefillConfig* out);
 

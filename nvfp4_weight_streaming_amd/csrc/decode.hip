@@ -293,6 +293,25 @@ __global__ __launch_bounds__(WAVES * 64) void decode_window_kernel(
                                ng, split, nt, &s_last);
 }
 
+// ---- device facts ----------------------------------------------------------------
+
+int device_cus() {
+    static int cached[64];
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    if (cached[dev]) return cached[dev];
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1) {
+        (void)hipGetLastError();
+        cus = 256;  // MI355X; kept, so plans and launches agree
+    }
+    cached[dev] = cus;
+    return cus;
+}
+
 // ---- XCD mapping check -----------------------------------------------------------
 
 // Workgroups are dispatched to the 8 XCDs round-robin (workgroup b on XCD
@@ -342,16 +361,22 @@ int make_decode_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, De
     const int n_tiles = padded_n(N) / kTileN;
     const int nsb = padded_k(K) / kSuperK;
     // Defaults measured on MI355X over the round's shapes (K = 5120..17408,
-    // N = 5120..152064): slices of 2 windows of 1 superblock and 4 waves per
+    // N = 5120..34816): slices of 2 windows of 1 superblock and 4 waves per
     // workgroup, except very long K (>= 16384): 6 windows of 1 superblock and
     // 8 waves.  (One window of 2 superblocks, resp. 3 superblocks and 8
     // waves, the best single-window forms, are 2% slower over the round.)
+    // Column groups that alone give every compute unit 4 or more workgroups
+    // (the output head: 2376) take no K split at all: one slice of the whole
+    // K per workgroup, streamed window by window, and no hand-off (the head
+    // at M = 8: 72 us against 94 with 5 splits).  The round's matrices have
+    // 112..544 groups and keep their splits.
     const bool long_k = nsb >= 32;
     const bool defaults = !(cfg && (cfg->split_k || cfg->chunks || cfg->windows));
     int waves = (cfg && cfg->waves) ? cfg->waves : (long_k ? 8 : 4);
     if (waves != 4 && waves != 8)
         return set_error(NVFP4_EINVAL, "config.waves: %d is not 4 or 8", waves);
     const int n_groups = (n_tiles + waves - 1) / waves;
+    const bool wide = n_groups >= 4 * device_cus();
     const int ng8 = round_up(n_groups, 8);
     int chunks;
     if (cfg && cfg->split_k) {
@@ -368,7 +393,9 @@ int make_decode_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, De
     } else {
         chunks = 1;
     }
-    int windows = (cfg && cfg->windows) ? cfg->windows : defaults ? (long_k ? 6 : 2) : 1;
+    int windows = (cfg && cfg->windows) ? cfg->windows
+                  : defaults                 ? (wide ? nsb : long_k ? 6 : 2)
+                                             : 1;
     if (windows < 1) return set_error(NVFP4_EINVAL, "config.windows: %d < 1", windows);
     if ((long long)windows * chunks > nsb) windows = (nsb + chunks - 1) / chunks;
     const int splits = (nsb + chunks * windows - 1) / (chunks * windows);

@@ -431,20 +431,6 @@ __global__ __launch_bounds__(kPReduceThreads) void prefill_reduce_kernel(
         if (m + r < M) store_out<BF16>(out, (size_t)(m + r) * N + n, e[r] * ts);
 }
 
-static int prefill_cus() {
-    static int cached = 0;
-    if (cached) return cached;
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus < 1) {
-        (void)hipGetLastError();
-        cus = 256;  // MI355X; kept, so plans and launches agree on the split
-    }
-    cached = cus;
-    return cus;
-}
-
 // Tiles beyond whole rounds (one tile per compute unit at a time) are split
 // along K when at least two pieces each fit: n_tail tiles, S pieces each.
 struct PrefillSplit {
@@ -471,7 +457,7 @@ int make_prefill_config(int max_M, int K, int N, PrefillConfig* out) {
     if (!out->enabled) return NVFP4_OK;
     // The largest partial-sum area over every M the plan serves (the split
     // depends on M only through the row blocks).
-    const int cus = prefill_cus();
+    const int cus = device_cus();
     for (int mb = 1; mb <= (max_M + kPTile - 1) / kPTile; ++mb) {
         const PrefillSplit s = prefill_split(mb * kPTile, K, N, cus);
         const size_t bytes = (size_t)s.n_tail * s.splits * kPTileFloats * sizeof(float);
@@ -484,7 +470,7 @@ int launch_prefill(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const 
                    float ts, const uint16_t* act, void* out, void* ws, hipStream_t s) {
     const int n_tiles = p->Np / kTileN, nsb = p->Kp / kSuperK;
     const int mblocks = (M + kPTile - 1) / kPTile;
-    const PrefillSplit sp = prefill_split(M, p->K, p->N, prefill_cus());
+    const PrefillSplit sp = prefill_split(M, p->K, p->N, device_cus());
     const int pieces = sp.n_tail * sp.splits;
     float* part = pieces ? (float*)((char*)ws + p->pre.ws_off) : nullptr;
     const dim3 grid((unsigned)(sp.tiles - sp.n_tail + pieces));

@@ -185,8 +185,9 @@ def test_random_planes_ragged(nv, M, K, N, bf16, kernel):
 
 
 @pytest.mark.parametrize("M,K,N", RAGGED)
-@pytest.mark.parametrize("cfg", [dict(chunks=1, windows=2), dict(chunks=2, windows=3, waves=8)],
-                         ids=["c1w2", "c2w3v8"])
+@pytest.mark.parametrize("cfg", [dict(chunks=1, windows=2), dict(chunks=2, windows=3, waves=8),
+                                 dict(chunks=1, windows=64)],
+                         ids=["c1w2", "c2w3v8", "c1-all-of-K"])
 def test_streamed_slices_ragged(nv, M, K, N, cfg):
     """The streamed-slice decode kernel on ragged K and N tails, with slices
     that end inside a window and K tails inside a superblock."""
@@ -197,6 +198,24 @@ def test_streamed_slices_ragged(nv, M, K, N, cfg):
     out, _ = run(nv, pw, dev_bf16(act), nv.OUT_F32, kernel=2, **cfg)
     y, S = oracle.gemm(act, codes, scales, t)
     check(out, y, S, bf16=False, what="streamed %r %r" % ((M, K, N), cfg))
+
+
+@pytest.mark.parametrize("M,bf16", [(8, False), (3, True)])
+def test_wide_matrix_default_has_no_k_split(nv, M, bf16):
+    """Column groups enough for 4 workgroups per compute unit (4098 tiles of
+    16 on a 256-CU device): by default one slice covers all of K (windows of
+    one superblock, the last one ragged) and no workspace is needed."""
+    K, N = 528, 65563
+    codes, scales = synth.random_planes(M + 40, N, N, K)
+    t = 2.5e-3
+    act = synth.activations(M + 41, K, M, K)
+    pw = pack(nv, dev(codes), dev(scales), K, N, t)
+    out, g = run(nv, pw, dev_bf16(act), nv.OUT_BF16 if bf16 else nv.OUT_F32)
+    import torch
+    if torch.cuda.get_device_properties(0).multi_processor_count <= 256:
+        assert g.ws_bytes == 0
+    y, S = oracle.gemm(act, codes, scales, t)
+    check(out, y, S, bf16=bf16, what="wide %r" % ((M, K, N),))
 
 
 @pytest.mark.parametrize("M", [1, 2, 4, 8])
