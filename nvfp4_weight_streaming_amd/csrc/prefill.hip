@@ -417,13 +417,25 @@ __global__ __launch_bounds__(kPReduceThreads) void prefill_reduce_kernel(
     const int n = (t / mblocks) * kPTile + wn * (kPTile / 4) + 32 * j + (lane & 31);
     const int m = (t % mblocks) * kPTile + wm * (kPTile / 2) + 32 * i + 8 * rq + 4 * (lane >> 5);
     if (n >= N || m >= M) return;
+    // Batches of 8 pieces: every load of a batch is issued before any is
+    // added (one memory round trip per batch).
+    constexpr int kBatch = 8;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < splits; ++s) {
-        const float4 x = *(const float4*)(part + (size_t)(s * n_tail + q) * kPTileFloats + 4 * p);
-        v.x += x.x;
-        v.y += x.y;
-        v.z += x.z;
-        v.w += x.w;
+    for (int s0 = 0; s0 < splits; s0 += kBatch) {
+        float4 x[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int s = min(s0 + u, splits - 1);
+            x[u] = *(const float4*)(part + (size_t)(s * n_tail + q) * kPTileFloats + 4 * p);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            if (s0 + u < splits) {
+                v.x += x[u].x;
+                v.y += x[u].y;
+                v.z += x[u].z;
+                v.w += x[u].w;
+            }
     }
     const float e[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
