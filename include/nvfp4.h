@@ -58,8 +58,13 @@ enum nvfp4_status {
 enum nvfp4_out_dtype { NVFP4_OUT_F32 = 0, NVFP4_OUT_BF16 = 1 };
 
 /* Largest number of lanes (activation rows) the decode kernel serves in one
- * weight pass; larger M goes to the prefill kernel. */
+ * weight pass. */
 #define NVFP4_DECODE_MAX_M 8
+/* Largest M of the verify-width decode kernel ("Ignis" README, "Speculative
+ * decoding (DFlash2)": up to seven drafts per lane are checked in the same
+ * pass, so 8 lanes x (1 + 7) rows); still one pass over the weights.  Larger
+ * M goes to the prefill kernel. */
+#define NVFP4_VERIFY_MAX_M 64
 
 /* ---- status ----------------------------------------------------------------- */
 
@@ -127,7 +132,9 @@ typedef struct nvfp4_gemm_config {
     int windows; /* SPLITK: windows of `chunks` superblocks per K slice; above 1 a
                     wave streams its slice, issuing the next window's loads
                     before computing the current one (0 or 1: one window) */
-    int reserved[2];
+    int verify_waves;   /* verify widths (8 < M <= 64): waves per workgroup, 8 or
+                           16 (0: by shape) */
+    int verify_windows; /* verify widths: superblocks per K slice (0: by shape) */
 } nvfp4_gemm_config;
 
 /* Create a plan for GEMMs of shape (M <= max_M) x K x N with the given output
@@ -157,11 +164,13 @@ void nvfp4_gemm_destroy(nvfp4_gemm plan);
  *   workspace_dev         : the plan's workspace (16-byte aligned), or NULL
  *                           if the plan needs none
  * (K, N) must equal the plan's, 1 <= M <= max_M.  M <= 8 uses the decode
- * kernel (one pass over the weights for all M rows); larger M uses the bf16
- * MFMA prefill kernel, and, when the 256 x 256 output tiles leave a last
- * partial round on the device's compute units, a second kernel that adds the
- * fp32 partial sums of those tiles' K pieces (kept in the workspace, after
- * the decode counters).  Asynchronous; no synchronisation. */
+ * kernel and 8 < M <= 64 the verify-width decode kernel (each one pass over
+ * the weights for all M rows); larger M uses the bf16 MFMA prefill kernel,
+ * and, when the 256 x 256 output tiles leave a last partial round on the
+ * device's compute units, a second kernel that adds the fp32 partial sums of
+ * those tiles' K pieces.  The workspace holds, in this order, the decode,
+ * verify and prefill areas the plan's max_M needs.  Asynchronous; no
+ * synchronisation. */
 int nvfp4_gemm_run(nvfp4_gemm plan, int M, int K, int N, const uint8_t* codes_dev,
                    const uint8_t* scales_dev, float tensor_scale, const uint16_t* act_dev,
                    void* out_dev, void* workspace_dev, void* stream);
@@ -199,12 +208,15 @@ int nvfp4_round_workspace_bytes(const nvfp4_layer* layers, int n_layers, int max
 int nvfp4_round_workspace_bytes_ex(const nvfp4_layer* layers, int n_layers, int max_M, int mode,
                                    size_t* workspace_bytes);
 
-/* Capture one HIP graph per width M = 1..max_M (max_M <= 8), each running the
- * n_layers GEMMs in list order, as the reference engine replays one graph per
- * batch width.  Matrix i+1 starts computing only once every output of matrix
+/* Capture one HIP graph per width M = 1..max_M, each running the n_layers
+ * GEMMs in list order, as the reference engine replays one graph per batch
+ * width.  max_M <= 64 for PER_MATRIX (widths above 8, the verify widths of
+ * speculative decoding, launch the verify-width kernel), <= 8 for the other
+ * forms.  Matrix i+1 starts computing only once every output of matrix
  * i is written (the order of a forward pass in which each matrix consumes the
  * previous one's result).
- *   PER_MATRIX : the graph holds one decode kernel launch per matrix.
+ *   PER_MATRIX : the graph holds one decode (or verify-width) kernel launch
+ *                per matrix.
  *   PERSISTENT : the graph holds one kernel whose resident workgroups walk
  *                every matrix; the next matrix's weights are fetched while the
  *                previous matrix finishes (no launch boundary between them).

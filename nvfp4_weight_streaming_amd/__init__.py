@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
 OK, EINVAL, EUNSUPPORTED, EHIP, ESTATE = 0, 1, 2, 3, 4
 OUT_F32, OUT_BF16 = 0, 1
 DECODE_MAX_M = 8
+VERIFY_MAX_M = 64
 
 # Every symbol include/nvfp4.h declares.
 EXPORTS = (
@@ -50,7 +51,7 @@ _STATUS = {OK: "ok", EINVAL: "EINVAL", EUNSUPPORTED: "EUNSUPPORTED", EHIP: "EHIP
 class GemmConfig(ctypes.Structure):
     _fields_ = [("split_k", ctypes.c_int), ("waves", ctypes.c_int), ("chunks", ctypes.c_int),
                 ("kernel", ctypes.c_int), ("tiles", ctypes.c_int), ("windows", ctypes.c_int),
-                ("reserved", ctypes.c_int * 2)]
+                ("verify_waves", ctypes.c_int), ("verify_windows", ctypes.c_int)]
 
 
 KERNEL_AUTO, KERNEL_STREAM, KERNEL_SPLITK = 0, 1, 2
@@ -170,12 +171,13 @@ def nvfp4_quantize(w, K, N, codes, scales, tensor_scale, workspace, stream=None)
 
 
 def nvfp4_gemm_create(max_M, K, N, out_dtype, split_k=0, waves=0, chunks=0, kernel=0, tiles=0,
-                      windows=0):
+                      windows=0, verify_waves=0, verify_windows=0):
     """Returns (plan handle, workspace bytes)."""
     h = ctypes.c_void_p()
     ws = ctypes.c_size_t()
-    if split_k or waves or chunks or kernel or tiles or windows:
-        cfg = GemmConfig(split_k, waves, chunks, kernel, tiles, windows)
+    if split_k or waves or chunks or kernel or tiles or windows or verify_waves or verify_windows:
+        cfg = GemmConfig(split_k, waves, chunks, kernel, tiles, windows, verify_waves,
+                         verify_windows)
         _check(lib().nvfp4_gemm_create_ex(ctypes.byref(h), max_M, K, N, out_dtype,
                                           ctypes.byref(cfg), ctypes.byref(ws)))
     else:
@@ -302,10 +304,11 @@ class Gemm:
     """A plan plus its workspace: ``Gemm(max_M, K, N, out_dtype)(w, act, out)``."""
 
     def __init__(self, max_M, K, N, out_dtype=OUT_BF16, split_k=0, waves=0, chunks=0, kernel=0,
-                 tiles=0, windows=0, device="cuda"):
+                 tiles=0, windows=0, device="cuda", verify_waves=0, verify_windows=0):
         import torch
         self.plan, self.ws_bytes = nvfp4_gemm_create(max_M, K, N, out_dtype, split_k, waves,
-                                                     chunks, kernel, tiles, windows)
+                                                     chunks, kernel, tiles, windows,
+                                                     verify_waves, verify_windows)
         self.K, self.N, self.max_M, self.out_dtype = K, N, max_M, out_dtype
         self.workspace = None
         if self.ws_bytes:

@@ -82,11 +82,19 @@ int validate_run(const nvfp4_gemm_plan* p, int M, int K, int N, const void* code
     return NVFP4_OK;
 }
 
+RunOffsets gemm_offsets(const nvfp4_gemm_plan* p) {
+    return RunOffsets{p->dec.counter_bytes, p->ver.ws_off, p->ver.ws_off + p->ver.d.counter_bytes};
+}
+
 int run_gemm(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
-             float ts, const uint16_t* act, void* out, void* ws, size_t partial_off,
+             float ts, const uint16_t* act, void* out, void* ws, const RunOffsets& off,
              hipStream_t s) {
-    if (M > NVFP4_DECODE_MAX_M && p->pre.enabled)
+    const size_t partial_off = off.dec_partial;
+    if (M > NVFP4_VERIFY_MAX_M && p->pre.enabled)
         return launch_prefill(p, M, codes, scales, ts, act, out, ws, s);
+    if (M > NVFP4_DECODE_MAX_M && p->ver.enabled)
+        return launch_verify(p, M, codes, scales, ts, act, out, ws, off.ver_counters,
+                             off.ver_partial, s);
     if (p->str.enabled) {
         // Rows beyond 8 (when no prefill kernel applies) run as further passes.
         const size_t esz = p->out_dtype == NVFP4_OUT_BF16 ? 2 : 4;
@@ -155,17 +163,22 @@ static int create_plan(nvfp4_gemm* plan, int max_M, int K, int N, int out_dtype,
     p->str.enabled = kernel == NVFP4_KERNEL_STREAM;
     p->str.tiles = tiles;
     if (!st) st = make_decode_config(K, N, max_M, cfg, &p->dec);
+    if (!st) st = make_verify_config(K, N, max_M, cfg, &p->ver);
     if (!st) st = make_prefill_config(max_M, K, N, &p->pre);
     if (st != NVFP4_OK) {
         p->magic = 0;
         delete p;
         return st;
     }
-    // [decode counters and partial sums][prefill partial sums]: decode counters
-    // must stay zero between runs, so the prefill area never overlaps them.
+    // [decode counters, partials][verify counters, partials][prefill partials]:
+    // the counters must stay zero between runs, so no area overlaps another.
+    auto align = [](size_t v) { return (v + 255) & ~(size_t)255; };
     const size_t dec_ws = p->str.enabled ? 0 : p->dec.ws_bytes;
-    p->pre.ws_off = (dec_ws + 255) & ~(size_t)255;
-    p->ws_bytes = p->pre.ws_bytes ? p->pre.ws_off + p->pre.ws_bytes : dec_ws;
+    p->ver.ws_off = align(dec_ws);
+    size_t end = p->ver.d.ws_bytes ? p->ver.ws_off + p->ver.d.ws_bytes : dec_ws;
+    p->pre.ws_off = align(end);
+    if (p->pre.ws_bytes) end = p->pre.ws_off + p->pre.ws_bytes;
+    p->ws_bytes = end;
     *workspace_bytes = p->ws_bytes;
     *plan = p;
     return NVFP4_OK;
@@ -195,7 +208,7 @@ int nvfp4_gemm_run(nvfp4_gemm plan, int M, int K, int N, const uint8_t* codes_de
     int st = validate_run(plan, M, K, N, codes_dev, scales_dev, act_dev, out_dev, workspace_dev);
     if (st != NVFP4_OK) return st;
     return run_gemm(plan, M, codes_dev, scales_dev, tensor_scale, act_dev, out_dev,
-                    workspace_dev, plan->dec.counter_bytes, (hipStream_t)stream);
+                    workspace_dev, gemm_offsets(plan), (hipStream_t)stream);
 }
 
 int nvfp4_workspace_clear(void* workspace_dev, size_t bytes, void* stream) {

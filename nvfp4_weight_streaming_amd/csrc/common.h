@@ -62,6 +62,14 @@ struct StreamConfig {
     int tiles;    // forced column tiles per workgroup (0: by shape)
 };
 
+// Verify widths (8 < M <= 64): the decode layout for 16 G rows, G = ceil(M / 16).
+struct VerifyConfig {
+    int enabled;   // max_M > 8
+    int rows;      // rows the workspace holds: ceil(min(max_M, 64) / 16) * 16
+    DecodeConfig d;
+    size_t ws_off; // offset of its counters and partials in the plan's workspace
+};
+
 struct PrefillConfig {
     int enabled;
     size_t ws_off;    // partial sums of K-split tiles: offset in the workspace
@@ -76,6 +84,7 @@ struct nvfp4_gemm_plan {
     int Kp, Np;
     nvfp4::DecodeConfig dec;
     nvfp4::StreamConfig str;
+    nvfp4::VerifyConfig ver;
     nvfp4::PrefillConfig pre;
     size_t ws_bytes;
 };
@@ -86,6 +95,9 @@ constexpr uint32_t kRoundMagic = 0x524F4E44u;
 
 // Compute units of the current device (cached per device; 256 if the query fails).
 int device_cus();
+// Workgroup b runs on XCD b % 8 on the current device (checked once per device).
+int xcd_mapping_verified();
+int make_verify_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, VerifyConfig* out);
 int make_decode_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, DecodeConfig* out);
 int make_prefill_config(int max_M, int K, int N, PrefillConfig* out);
 
@@ -95,6 +107,9 @@ int make_prefill_config(int max_M, int K, int N, PrefillConfig* out);
 int launch_decode(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
                   float ts, const uint16_t* act, void* out, void* ws, size_t partial_off,
                   hipStream_t s);
+int launch_verify(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
+                  float ts, const uint16_t* act, void* out, void* ws, size_t counters_off,
+                  size_t partial_off, hipStream_t s);
 int launch_prefill(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
                    float ts, const uint16_t* act, void* out, void* ws, hipStream_t s);
 int launch_fill_zero(void* p, size_t bytes, hipStream_t s);
@@ -134,7 +149,15 @@ int chain_launch_round(int M, void* ws, const ChainLayout& y, hipStream_t s);
 // Shared validation of a GEMM run against its plan.
 int validate_run(const nvfp4_gemm_plan* p, int M, int K, int N, const void* codes,
                  const void* scales, const void* act, const void* out, const void* ws);
+// Where a run's split-K state sits in the workspace: a plan's own layout
+// (gemm_offsets), or the shared counter and partial regions of a round.
+struct RunOffsets {
+    size_t dec_partial;   // decode partials (its counters start at 0)
+    size_t ver_counters;  // verify-width counters
+    size_t ver_partial;   // verify-width partials
+};
+RunOffsets gemm_offsets(const nvfp4_gemm_plan* p);
 int run_gemm(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
-             float ts, const uint16_t* act, void* out, void* ws, size_t partial_off,
+             float ts, const uint16_t* act, void* out, void* ws, const RunOffsets& off,
              hipStream_t s);
 }  // namespace nvfp4

@@ -172,19 +172,6 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
 
 // ---- long slices ------------------------------------------------------------------
 
-// s_waitcnt immediates: vmcnt(n) with the other counters untouched; lgkmcnt(0).
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
-constexpr int kLgkmcnt0 = 0xC07F;
-
-// A barrier without the memory fence of __syncthreads: that fence would also
-// wait for the direct-to-LDS copies of the next window, just issued.  The
-// caller states with explicit waits what must be complete.
-__device__ __forceinline__ void barrier_nofence() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
 // Long K slices: a workgroup's slice is `windows` windows of NCH superblocks.
 // A wave keeps the weights of two windows in registers: those of window w + 1
 // are issued before window w is computed, so the weight stream of the
@@ -326,7 +313,7 @@ __global__ void xcc_probe_kernel() {
     if (threadIdx.x == 0) g_xcc_probe[blockIdx.x] = v & 0xFu;
 }
 
-static int xcd_mapping_verified() {
+int xcd_mapping_verified() {
     static int cached[64];
     static bool init = false;
     if (!init) {

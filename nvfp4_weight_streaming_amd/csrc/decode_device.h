@@ -28,6 +28,19 @@ __device__ __forceinline__ void store_out(void* out, size_t idx, float v) {
         ((float*)out)[idx] = v;
 }
 
+// s_waitcnt immediates: vmcnt(n) with the other counters untouched; lgkmcnt(0).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+constexpr int kLgkmcnt0 = 0xC07F;
+
+// A barrier without the memory fence of __syncthreads: that fence would also
+// wait for direct-to-LDS copies just issued.  The caller states with explicit
+// waits what must be complete.
+__device__ __forceinline__ void barrier_nofence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // 8 E2M1 codes (4 bytes, low nibble first) -> 8 bf16 values in k order.
 __device__ __forceinline__ bf16x8 e2m1x8_to_bf16(uint32_t w) {
     bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
@@ -35,6 +48,29 @@ __device__ __forceinline__ bf16x8 e2m1x8_to_bf16(uint32_t w) {
     bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2);
     bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
     return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// 8 E2M1 codes times the block scale sc -> 8 bf16 values in k order.  Exact:
+// an E2M1 value has at most 2 significant bits and an E4M3 scale 4, so the
+// fp32 product has at most 6 and converts to bf16 without rounding (and the
+// exponent range of E2M1 x E4M3, 2^-10 .. 2688, is inside bf16's).
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+template <int B>
+__device__ __forceinline__ uint32_t e2m1x2_scaled(uint32_t w, float sc) {
+    const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, B);
+    const f32x2v x = {v[0] * sc, v[1] * sc};
+    const bf16x2v b = __builtin_convertvector(x, bf16x2v);
+    uint32_t r;
+    __builtin_memcpy(&r, &b, 4);
+    return r;
+}
+__device__ __forceinline__ bf16x8 e2m1x8_scaled_bf16(uint32_t w, float sc) {
+    const uint32_t r[4] = {e2m1x2_scaled<0>(w, sc), e2m1x2_scaled<1>(w, sc),
+                           e2m1x2_scaled<2>(w, sc), e2m1x2_scaled<3>(w, sc)};
+    bf16x8 v;
+    __builtin_memcpy(&v, r, 16);
+    return v;
 }
 
 // The packed bytes one wave streams per 512-k superblock: 4 code chunks (16 B
@@ -140,7 +176,7 @@ struct ActStage {
 };
 
 // Sums, in split order, the `splits` partial sums of one column group (layout
-// [split][8 rows][kCols]) for the outputs idx = threadIdx.x + r * kThreads,
+// [split][kSplitRows rows][kCols]) for the outputs idx = threadIdx.x + r * kThreads,
 // r < kR (row idx / kCols, column idx % kCols); only idx < n_out are valid.
 // L2_LOCAL: the partials were written with plain stores into this XCD's L2;
 // else with device-coherent stores, and they are read device-coherently.
@@ -148,9 +184,10 @@ struct ActStage {
 // any is added, so a batch costs one memory round trip.  Within a wave that
 // has valid outputs the output index is clamped to n_out - 1 (repeated
 // addresses within a wave cost one request).
-template <int kCols, int kThreads, int kR, bool L2_LOCAL>
+template <int kCols, int kThreads, int kR, bool L2_LOCAL, int kSplitRows = 8>
 __device__ __forceinline__ void sum_partials(const float* gbase, int splits, int n_out,
                                              float (&sum)[kR]) {
+    static_assert(kR >= 1 && kR <= 16, "1 .. 16 outputs per thread");
     constexpr int kSB = 16 / kR;
 #pragma unroll
     for (int r = 0; r < kR; ++r) sum[r] = 0.f;
@@ -166,7 +203,7 @@ __device__ __forceinline__ void sum_partials(const float* gbase, int splits, int
             for (int t = 0; t < kSB; ++t) {
                 v[r][t] = 0.f;
                 if (wave0 < n_out && s0 + t < splits) {
-                    const int off = ((s0 + t) * 8 + mm) * kCols + c;
+                    const int off = ((s0 + t) * kSplitRows + mm) * kCols + c;
                     v[r][t] = L2_LOCAL ? gbase[off]
                                        : __hip_atomic_load(gbase + off, __ATOMIC_RELAXED,
                                                            __HIP_MEMORY_SCOPE_AGENT);

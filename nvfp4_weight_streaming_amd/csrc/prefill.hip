@@ -57,25 +57,11 @@ struct PrefillLds {
 __device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int swz(int row, int seg) { return row * kPBK + 8 * (seg ^ swz_key(row)); }
 
-typedef float f32x2v __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-
-// 2 codes (byte B of w) times scale sc -> 2 bf16 packed in one word (one
-// paired conversion; exact, as the products have at most 6 significant bits).
-template <int B>
-__device__ __forceinline__ uint32_t dequant2(uint32_t w, float sc) {
-    const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, B);
-    const f32x2v x = {v[0] * sc, v[1] * sc};
-    const bf16x2v b = __builtin_convertvector(x, bf16x2v);
-    uint32_t r;
-    __builtin_memcpy(&r, &b, 4);
-    return r;
-}
-
 // 8 codes (one 4-byte word, low nibble first) times scale sc -> 8 bf16.
+// (exact: e2m1x2_scaled)
 __device__ __forceinline__ uint4 dequant8(uint32_t w, float sc) {
-    return make_uint4(dequant2<0>(w, sc), dequant2<1>(w, sc), dequant2<2>(w, sc),
-                      dequant2<3>(w, sc));
+    return make_uint4(e2m1x2_scaled<0>(w, sc), e2m1x2_scaled<1>(w, sc), e2m1x2_scaled<2>(w, sc),
+                      e2m1x2_scaled<3>(w, sc));
 }
 
 // Global memory is read through buffer resources (base and size in scalar
@@ -463,7 +449,7 @@ static PrefillSplit prefill_split(int M, int K, int N, int cus) {
 }
 
 int make_prefill_config(int max_M, int K, int N, PrefillConfig* out) {
-    out->enabled = max_M > NVFP4_DECODE_MAX_M;
+    out->enabled = max_M > NVFP4_VERIFY_MAX_M;
     out->ws_off = 0;
     out->ws_bytes = 0;
     if (!out->enabled) return NVFP4_OK;

@@ -30,9 +30,9 @@ struct nvfp4_round_plan {
     void* ws;
     size_t ws_bytes;
     size_t partial_off;  // shared offset of the partial sums (after every plan's counters)
-    hipGraph_t graph[NVFP4_DECODE_MAX_M];
-    hipGraphExec_t exec[NVFP4_DECODE_MAX_M];
-    int nodes[NVFP4_DECODE_MAX_M];
+    hipGraph_t graph[NVFP4_VERIFY_MAX_M];
+    hipGraphExec_t exec[NVFP4_VERIFY_MAX_M];
+    int nodes[NVFP4_VERIFY_MAX_M];
 };
 
 namespace nvfp4 {
@@ -43,7 +43,7 @@ namespace nvfp4 {
 constexpr unsigned int kDefaultSpinLimit = 1u << 16;
 
 static void free_round(nvfp4_round_plan* r) {
-    for (int i = 0; i < NVFP4_DECODE_MAX_M; ++i) {
+    for (int i = 0; i < NVFP4_VERIFY_MAX_M; ++i) {
         if (r->exec[i]) (void)hipGraphExecDestroy(r->exec[i]);
         if (r->graph[i]) (void)hipGraphDestroy(r->graph[i]);
     }
@@ -55,8 +55,8 @@ static void free_round(nvfp4_round_plan* r) {
 static int validate_layers(const nvfp4_layer* L, int n, int max_M) {
     if (!L) return set_error(NVFP4_EINVAL, "layers: NULL");
     if (n < 1) return set_error(NVFP4_EINVAL, "n_layers: %d < 1", n);
-    if (max_M < 1 || max_M > NVFP4_DECODE_MAX_M)
-        return set_error(NVFP4_EINVAL, "max_M: %d outside [1, %d]", max_M, NVFP4_DECODE_MAX_M);
+    if (max_M < 1 || max_M > NVFP4_VERIFY_MAX_M)
+        return set_error(NVFP4_EINVAL, "max_M: %d outside [1, %d]", max_M, NVFP4_VERIFY_MAX_M);
     for (int i = 0; i < n; ++i) {
         const nvfp4_layer& l = L[i];
         if (l.K < 16 || l.K % 16) return set_error(NVFP4_EINVAL, "layers[%d].K: %d is not a positive multiple of 16", i, l.K);
@@ -80,7 +80,8 @@ extern "C" {
 
 // Workspace of a per-matrix round: one counter region at the start, sized for
 // the plan with the most counters, then one partial-sum region sized for the
-// largest.
+// largest (decode or verify width).  The graph's nodes run one after another
+// and each leaves its counters zeroed, so all of them share both regions.
 static int round_layout(const nvfp4_layer* layers, int n_layers, int max_M, size_t* counters,
                         size_t* partials) {
     size_t mc = 0, mp = 0;
@@ -91,6 +92,8 @@ static int round_layout(const nvfp4_layer* layers, int n_layers, int max_M, size
         if (st) return st;
         if (p->dec.counter_bytes > mc) mc = p->dec.counter_bytes;
         if (p->dec.partial_bytes > mp) mp = p->dec.partial_bytes;
+        if (p->ver.d.counter_bytes > mc) mc = p->ver.d.counter_bytes;
+        if (p->ver.d.partial_bytes > mp) mp = p->ver.d.partial_bytes;
         nvfp4_gemm_destroy(p);
     }
     *counters = mc;
@@ -98,11 +101,17 @@ static int round_layout(const nvfp4_layer* layers, int n_layers, int max_M, size
     return NVFP4_OK;
 }
 
-static int check_mode(int mode) {
+// The single-launch forms serve decode widths only; the per-matrix form
+// also the verify widths (its graphs launch the verify-width kernel).
+static int check_mode(int mode, int max_M) {
     if (mode != NVFP4_ROUND_PERSISTENT && mode != NVFP4_ROUND_PER_MATRIX &&
         mode != NVFP4_ROUND_CHAIN)
         return set_error(NVFP4_EINVAL,
                          "mode: %d is not PERSISTENT (0), PER_MATRIX (1) or CHAIN (2)", mode);
+    if (mode != NVFP4_ROUND_PER_MATRIX && max_M > NVFP4_DECODE_MAX_M)
+        return set_error(NVFP4_EINVAL, "max_M: %d above %d, the largest of the %s form", max_M,
+                         NVFP4_DECODE_MAX_M,
+                         mode == NVFP4_ROUND_PERSISTENT ? "PERSISTENT" : "CHAIN");
     return NVFP4_OK;
 }
 
@@ -125,7 +134,7 @@ int nvfp4_round_workspace_bytes_ex(const nvfp4_layer* layers, int n_layers, int 
     clear_error();
     int st = validate_layers(layers, n_layers, max_M);
     if (st) return st;
-    st = check_mode(mode);
+    st = check_mode(mode, max_M);
     if (st) return st;
     if (!workspace_bytes) return set_error(NVFP4_EINVAL, "workspace_bytes: NULL");
     if (mode == NVFP4_ROUND_PERSISTENT) {
@@ -158,7 +167,7 @@ int nvfp4_round_create_ex(nvfp4_round* plan, const nvfp4_layer* layers, int n_la
     *plan = nullptr;
     int st = validate_layers(layers, n_layers, max_M);
     if (st) return st;
-    st = check_mode(mode);
+    st = check_mode(mode, max_M);
     if (st) return st;
     size_t need_c = 0, need_p = 0;
     StreamRoundLayout lay{};
@@ -250,7 +259,8 @@ int nvfp4_round_create_ex(nvfp4_round* plan, const nvfp4_layer* layers, int n_la
             for (int i = 0; i < n_layers && !lst; ++i) {
                 const nvfp4_layer& l = r->layers[i];
                 lst = run_gemm(r->plans[i], M, l.codes_dev, l.scales_dev, l.tensor_scale,
-                               l.act_dev, l.out_dev, workspace, r->partial_off, cap);
+                               l.act_dev, l.out_dev, workspace,
+                               RunOffsets{r->partial_off, 0, r->partial_off}, cap);
             }
         }
         hipGraph_t g = nullptr;

@@ -1,0 +1,299 @@
+// Verify-width decode GEMM: 8 < M <= 64 rows served by one pass over NVFP4
+// weights.
+//
+// "Ignis" README, "Speculative decoding (DFlash2)": a drafter proposes up to
+// seven tokens per lane and the model checks them in the same pass, so one
+// round multiplies lanes x (1 + drafts) <= 64 activation rows by each weight
+// matrix.  That is still one read of every weight byte ("The decode round":
+// the round streams the weights at the card's bandwidth); only the work per
+// byte grows, up to 128 flops at M = 64.
+//
+// gfx950 mapping.  As in the M <= 8 kernel, one wave owns a tile of 16
+// output columns and streams a K slice window by window (one 512-k
+// superblock per window, the next window's loads in flight while the current
+// one is computed), and a workgroup of WAVES tiles stages the activation rows
+// of a window in LDS with direct-to-LDS copies.  The multiply differs:
+//   B operand (32 k x 16 columns): each lane turns its 8 codes of the step
+//     into 8 exact bf16 values of code x E4M3 block scale (at most 6
+//     significant bits).  The 8 values of a lane lie in one 16-k block, so a
+//     lane needs one scale per step.
+//   A operand (16 rows x 32 k): 16 activation rows, one MFMA
+//     (v_mfma_f32_16x16x32_bf16) per 16-row group accumulates into that
+//     group's fp32 sums directly.
+// The dequantisation (16 VALU operations per lane and step) is shared by the
+// G = ceil(M / 16) MFMAs of the step.  Split-K and the deterministic
+// last-workgroup hand-off are those of the M <= 8 kernel, for 16 G rows.
+#include "decode_device.h"
+
+namespace nvfp4 {
+
+constexpr int kVerifyWaves = 8;
+constexpr int kVerifyStride = kSuperK + kLdsPad;  // LDS row, bf16 elements (1040 B)
+
+// End of a workgroup: outputs (one slice) or the split-K hand-off (several).
+// acc[gi][j] holds row 16 gi + 4 (lane / 16) + j, column lane % 16 of the
+// wave's tile.
+template <int WAVES, int G, bool BF16>
+__device__ __forceinline__ void verify_finish(const f32x4 (&acc)[G], void* __restrict__ out,
+                                              float* __restrict__ partial,
+                                              unsigned int* __restrict__ counters, float ts,
+                                              int M, int N, int splits, int n_tiles, int l2_local,
+                                              int ng, int split, int nt, int* s_last) {
+    constexpr int kThreads = WAVES * 64;
+    constexpr int kCols = WAVES * kTileN;
+    constexpr int kRows = 16 * G;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int col = lane & 15, g = lane >> 4;
+    const bool mine = ng * WAVES + wave < n_tiles;
+
+    if (splits == 1) {
+        if (mine) {
+            const int n = nt * kTileN + col;
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int mm = 16 * gi + 4 * g + j;
+                    if (mm < M && n < N) store_out<BF16>(out, (size_t)mm * N + n, acc[gi][j] * ts);
+                }
+        }
+        return;
+    }
+
+    // Split K: the same hand-off as the M <= 8 kernel (partials in this XCD's
+    // L2 when the workgroup-to-XCD mapping is verified, else device-coherent).
+    float* pbase = partial + (size_t)(ng * splits + split) * kRows * kCols;
+    if (mine) {
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int mm = 16 * gi + 4 * g + j;
+                if (mm < M) {
+                    float* dst = pbase + mm * kCols + wave * kTileN + col;
+                    if (l2_local)
+                        *dst = acc[gi][j];
+                    else
+                        __hip_atomic_store(dst, acc[gi][j], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned int old =
+            __hip_atomic_fetch_add(&counters[ng], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_last = (old == (unsigned int)(splits - 1));
+    }
+    __syncthreads();
+    if (!*s_last) return;
+    const float* gbase = partial + (size_t)ng * splits * kRows * kCols;
+    constexpr int kR = kRows * kCols / kThreads;
+    static_assert(kRows * kCols % kThreads == 0 && kR <= 16, "outputs divide over the threads");
+    float sum[kR];
+    if (l2_local)
+        sum_partials<kCols, kThreads, kR, true, kRows>(gbase, splits, M * kCols, sum);
+    else
+        sum_partials<kCols, kThreads, kR, false, kRows>(gbase, splits, M * kCols, sum);
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+        const int idx = threadIdx.x + r * kThreads;
+        const int mm = idx / kCols, c = idx - mm * kCols;
+        const int n = ng * kCols + c;
+        if (idx < M * kCols && n < N) store_out<BF16>(out, (size_t)mm * N + n, sum[r] * ts);
+    }
+    if (threadIdx.x == 0)  // leave the counter zeroed for the next run
+        __hip_atomic_store(&counters[ng], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One workgroup = WAVES column tiles x one K slice of `windows` superblocks.
+// Window w's weights (5 loads per lane) and activation rows (16 G rows of
+// 1 KiB, 2 G copies per wave) are issued before window w - 1 is computed;
+// loads complete in order per wave, so the wait before window w is the
+// constant vmcnt of one window's loads.
+template <int WAVES, int G, bool BF16>
+__global__ __launch_bounds__(WAVES * 64) void verify_kernel(
+    const uint4* __restrict__ codes, const uint4* __restrict__ scales,
+    const uint16_t* __restrict__ act, void* __restrict__ out, float* __restrict__ partial,
+    unsigned int* __restrict__ counters, float ts, int M, int K, int N, int nsb, int splits,
+    int n_groups, int n_tiles, int l2_local, int windows) {
+    constexpr int kRows = 16 * G;
+    constexpr int kSeg = kRows / WAVES;  // activation rows a wave copies per window
+    static_assert(kRows % WAVES == 0, "activation rows divide over the waves");
+    constexpr int kLoads = 5 + kSeg;     // loads a wave issues per window
+    // Two separate arrays: the compiler then sees that copies into one never
+    // alias reads of the other.
+    __shared__ __attribute__((aligned(16))) __bf16 lds0[kRows * kVerifyStride];
+    __shared__ __attribute__((aligned(16))) __bf16 lds1[kRows * kVerifyStride];
+    __shared__ int s_last;
+
+    const int b = blockIdx.x;
+    const int xcd = b & 7, q = b >> 3;
+    const int ng = (q / splits) * 8 + xcd;
+    const int split = q - (q / splits) * splits;
+    if (ng >= n_groups) return;  // whole workgroup: padding of the column groups to 8
+    const int sb_begin = split * windows;
+    const int nwin = min(windows, nsb - sb_begin);  // superblocks in this slice (>= 1)
+
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
+    const int nt = min(ng * WAVES + wave, n_tiles - 1);
+    const int col = lane & 15, g = lane >> 4;
+    const uint4* cp = codes + ((size_t)nt * nsb + sb_begin) * 256 + lane;
+    const uint4* sp = scales + ((size_t)nt * nsb + sb_begin) * 32 + col * 2 + (g >> 1);
+
+    // Window w: weights into x, activation rows into buf.  Row r of the
+    // window is activation row min(r, M - 1) (rows >= M are never stored);
+    // each row's resource ends at the row's end, so values past K read zero
+    // (the weights there are zero too).
+    auto issue = [&](int w, Chunk& x, __bf16* buf) {
+        const int sb = min(w, nwin - 1);
+        load_chunk(x, cp + 256 * sb, sp + 32 * sb);
+        const int k = (sb_begin + sb) * kSuperK;
+        const int bytes = (K - k) * (int)sizeof(uint16_t);
+#pragma unroll
+        for (int j = 0; j < kSeg; ++j) {
+            const int r = wave * kSeg + j;
+            const uint16_t* row = act + (size_t)min(r, M - 1) * K + k;
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t*>(row), 0, bytes, 0x00020000);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (__attribute__((address_space(3))) void*)(buf + r * kVerifyStride), 16,
+                lane * 16, 0, 0, 0);
+        }
+    };
+
+    f32x4 acc[G];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) acc[gi] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // A operand of this lane: row lane % 16 of each 16-row group, k octet g.
+    const int a_off = col * kVerifyStride + 8 * g;
+    auto step = [&](int w, Chunk& x, Chunk& y, const __bf16* cur, __bf16* nxt) {
+        // Every wave is done reading nxt (window w - 1).
+        __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
+        barrier_nofence();
+        if (w + 1 < nwin) {
+            issue(w + 1, y, nxt);
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoads));
+        } else {
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        }
+        barrier_nofence();  // every wave's activation rows of window w are in LDS
+        const __bf16* ap = cur + a_off;
+        // 16 steps of 32 k.  The A fragments of step t + 1 are read before the
+        // multiplies of step t, so no MFMA waits on a read issued just before.
+        bf16x8 av[2][G];
+        auto read_a = [&](int t, bf16x8 (&dst)[G]) {
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi)
+                dst[gi] = *(const bf16x8*)(ap + 16 * gi * kVerifyStride + 32 * t);
+        };
+        read_a(0, av[0]);
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const int kb = t >> 2, s = t & 3;
+            if (t + 1 < 16) read_a(t + 1, av[(t + 1) & 1]);
+            // keep those reads ahead of this step's work (the scheduler would
+            // otherwise move each read next to its use)
+            __builtin_amdgcn_sched_barrier(0);
+            const int sw = (int)word(x.s, kb);
+            const float sc = s == 0   ? __builtin_amdgcn_cvt_f32_fp8(sw, 0)
+                             : s == 1 ? __builtin_amdgcn_cvt_f32_fp8(sw, 1)
+                             : s == 2 ? __builtin_amdgcn_cvt_f32_fp8(sw, 2)
+                                      : __builtin_amdgcn_cvt_f32_fp8(sw, 3);
+            const bf16x8 bv = e2m1x8_scaled_bf16(word(x.c[kb], s), sc);
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi)
+                acc[gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[t & 1][gi], bv, acc[gi], 0,
+                                                                  0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    Chunk wa, wb;
+    issue(0, wa, lds0);
+    for (int w = 0; w < nwin; w += 2) {
+        step(w, wa, wb, lds0, lds1);
+        if (w + 1 < nwin) step(w + 1, wb, wa, lds1, lds0);
+    }
+    verify_finish<WAVES, G, BF16>(acc, out, partial, counters, ts, M, N, splits, n_tiles,
+                                  l2_local, ng, split, nt, &s_last);
+}
+
+// Plan: the M <= 8 defaults (a window of one superblock per step, 2 windows
+// per slice, 6 for K >= 16384; no split for column groups that alone give
+// every compute unit 4 workgroups), with 8 waves per workgroup, and a
+// workspace for 16 G rows (G = ceil(min(max_M, 64) / 16)).
+int make_verify_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, VerifyConfig* v) {
+    v->enabled = max_M > NVFP4_DECODE_MAX_M;
+    v->ws_off = 0;
+    v->rows = 0;
+    DecodeConfig& d = v->d;
+    d = DecodeConfig{};
+    if (!v->enabled) return NVFP4_OK;
+    const int m = max_M < NVFP4_VERIFY_MAX_M ? max_M : NVFP4_VERIFY_MAX_M;
+    v->rows = (m + 15) / 16 * 16;
+    const int n_tiles = padded_n(N) / kTileN;
+    const int nsb = padded_k(K) / kSuperK;
+    const int waves = (cfg && cfg->verify_waves) ? cfg->verify_waves : kVerifyWaves;
+    if (waves != 8 && waves != 16)
+        return set_error(NVFP4_EINVAL, "config.verify_waves: %d is not 8 or 16", waves);
+    if (cfg && cfg->verify_windows < 0)
+        return set_error(NVFP4_EINVAL, "config.verify_windows: %d < 0", cfg->verify_windows);
+    const int n_groups = (n_tiles + waves - 1) / waves;
+    const int ng8 = round_up(n_groups, 8);
+    const bool wide = n_groups >= 4 * device_cus();
+    int windows = (cfg && cfg->verify_windows) ? cfg->verify_windows
+                  : wide                        ? nsb
+                  : nsb >= 32                   ? 6
+                                                : 2;
+    if (windows > nsb) windows = nsb;
+    const int splits = (nsb + windows - 1) / windows;
+    d.l2_local = splits > 1 ? xcd_mapping_verified() : 0;
+    d.waves = waves;
+    d.chunks = 1;
+    d.windows = windows;
+    d.splits = splits;
+    d.n_groups = n_groups;
+    d.grid = ng8 * splits;
+    if (splits > 1) {
+        d.counter_bytes = ((size_t)ng8 * sizeof(unsigned int) + 255) / 256 * 256;
+        d.partial_bytes = (size_t)ng8 * splits * v->rows * waves * kTileN * sizeof(float);
+    }
+    d.ws_bytes = d.counter_bytes + d.partial_bytes;
+    return NVFP4_OK;
+}
+
+int launch_verify(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
+                  float ts, const uint16_t* act, void* out, void* ws, size_t counters_off,
+                  size_t partial_off, hipStream_t s) {
+    const DecodeConfig& d = p->ver.d;
+    unsigned int* counters = d.splits > 1 ? (unsigned int*)((char*)ws + counters_off) : nullptr;
+    float* partial = d.splits > 1 ? (float*)((char*)ws + partial_off) : nullptr;
+    const int G = (M + 15) / 16;
+    const bool bf16 = p->out_dtype == NVFP4_OUT_BF16;
+    const dim3 grid(d.grid), block(d.waves * 64);
+    const int nsb = p->Kp / kSuperK, n_tiles = p->Np / kTileN;
+#define NVFP4_VERIFY_LAUNCH(WW, GG, BB)                                                       \
+    hipLaunchKernelGGL((verify_kernel<WW, GG, BB>), grid, block, 0, s, (const uint4*)codes,    \
+                       (const uint4*)scales, act, out, partial, counters, ts, M, p->K, p->N,   \
+                       nsb, d.splits, d.n_groups, n_tiles, d.l2_local, d.windows)
+#define NVFP4_VERIFY_G(WW, BB)                              \
+    switch (G) {                                            \
+        case 1: NVFP4_VERIFY_LAUNCH(WW, 1, BB); break;      \
+        case 2: NVFP4_VERIFY_LAUNCH(WW, 2, BB); break;      \
+        case 3: NVFP4_VERIFY_LAUNCH(WW, 3, BB); break;      \
+        default: NVFP4_VERIFY_LAUNCH(WW, 4, BB); break;     \
+    }
+    if (d.waves == 16) {
+        if (bf16) NVFP4_VERIFY_G(16, true) else NVFP4_VERIFY_G(16, false)
+    } else {
+        if (bf16) NVFP4_VERIFY_G(8, true) else NVFP4_VERIFY_G(8, false)
+    }
+#undef NVFP4_VERIFY_G
+#undef NVFP4_VERIFY_LAUNCH
+    NVFP4_HIP(hipGetLastError());
+    return NVFP4_OK;
+}
+
+}  // namespace nvfp4

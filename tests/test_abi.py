@@ -33,6 +33,14 @@ def test_header_and_binding_agree(nv):
     assert sorted(nv.EXPORTS) == declared
 
 
+def test_width_constants_match_the_header(nv):
+    text = open(HEADER).read()
+    for name, value in (("NVFP4_DECODE_MAX_M", nv.DECODE_MAX_M),
+                        ("NVFP4_VERIFY_MAX_M", nv.VERIFY_MAX_M)):
+        m = re.search(r"#define\s+%s\s+(\d+)" % name, text)
+        assert m and int(m.group(1)) == value, name
+
+
 def test_library_exports_every_declared_symbol(nv):
     L = ctypes.CDLL(nv.LIB_PATH)
     for name in _declared_functions():
@@ -118,6 +126,20 @@ def test_gemm_config_validation(nv):
         assert e.value.message.startswith("config.tiles")
 
 
+def test_verify_width_config(nv):
+    for bad, word in ((dict(verify_waves=4), "config.verify_waves"),
+                      (dict(verify_windows=-1), "config.verify_windows")):
+        with pytest.raises(nv.Nvfp4Error) as e:
+            nv.nvfp4_gemm_create(64, 5120, 5120, 1, **bad)
+        assert e.value.message.startswith(word), e.value.message
+    # a verify-width plan appends its own split-K area to the decode one
+    p8, ws8 = nv.nvfp4_gemm_create(8, 5120, 5120, 1)
+    p64, ws64 = nv.nvfp4_gemm_create(64, 5120, 5120, 1)
+    assert ws64 > ws8 > 0
+    nv.nvfp4_gemm_destroy(p8)
+    nv.nvfp4_gemm_destroy(p64)
+
+
 def test_workspace_sizes_for_round_shapes(nv):
     for K, N in [(5120, 7168), (6144, 5120), (5120, 34816), (17408, 5120), (5120, 152064)]:
         plan, ws = nv.nvfp4_gemm_create(8, K, N, 1)
@@ -186,9 +208,16 @@ def test_round_validation(nv):
         with pytest.raises(nv.Nvfp4Error) as e:
             nv.nvfp4_round_workspace_bytes(layers, 8)
         assert e.value.message.startswith(word), e.value.message
+    # per-matrix rounds take the verify widths too; the single-launch forms
+    # only decode widths
+    assert nv.nvfp4_round_workspace_bytes([good] * 2, 64) >= 0
     with pytest.raises(nv.Nvfp4Error) as e:
-        nv.nvfp4_round_workspace_bytes([good], 9)
+        nv.nvfp4_round_workspace_bytes([good], 65)
     assert e.value.message.startswith("max_M")
+    for mode in (nv.ROUND_PERSISTENT, nv.ROUND_CHAIN):
+        with pytest.raises(nv.Nvfp4Error) as e:
+            nv.nvfp4_round_workspace_bytes([good], 9, mode=mode)
+        assert e.value.message.startswith("max_M"), e.value.message
     L = nv.lib()
     assert L.nvfp4_round_run(None, 1, None) == nv.ESTATE
     assert nv.nvfp4_round_graph_nodes(None, 1) == 0

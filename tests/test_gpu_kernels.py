@@ -303,6 +303,60 @@ def test_m_below_plan_max_and_bf16_rounding(nv):
         check(o32, y, S, bf16=False, what="M=%d of 8" % M)
 
 
+# ---- verify widths (8 < M <= 64: one weight pass, 16-row MFMA groups) ----------
+
+# (M, K, N): every row-group count (M 9..16, ..64), ragged K inside a
+# superblock and N inside a tile, one superblock (no split) and long K.
+VERIFY = [(9, 512, 16), (16, 1040, 100), (17, 2576, 33), (31, 5136, 515), (33, 1536, 200),
+          (48, 3072, 7), (49, 12288, 40), (64, 5120, 130), (64, 17408, 48), (24, 256, 1000)]
+
+
+@pytest.mark.parametrize("M,K,N", VERIFY)
+@pytest.mark.parametrize("bf16", [False, True])
+def test_verify_width_ragged(nv, M, K, N, bf16):
+    codes, scales = synth.random_planes(M * 7 + K, N + 5, N, K)
+    t = float(np.float32(np.random.default_rng(K + N).uniform(1e-4, 1e-2)))
+    act = synth.activations(M * 7 + 1, K + N, M, K)
+    pw = pack(nv, dev(codes), dev(scales), K, N, t)
+    out, _ = run(nv, pw, dev_bf16(act), nv.OUT_BF16 if bf16 else nv.OUT_F32)
+    y, S = oracle.gemm(act, codes, scales, t)
+    check(out, y, S, bf16=bf16, what="verify %r" % ((M, K, N),))
+
+
+def test_verify_width_rows_share_one_plan_and_repeat_bitwise(nv):
+    """A plan with max_M = 64 serves every M (decode, verify), its split-K
+    counters reset themselves, and repeated runs are bit-identical."""
+    import torch
+    K, N = 6144, 1000
+    codes, scales = synth.random_planes(5, 6, N, K)
+    t = 3.0e-4
+    act = synth.activations(5, 7, 64, K)
+    pw = pack(nv, dev(codes), dev(scales), K, N, t)
+    g = nv.Gemm(64, K, N, nv.OUT_F32)
+    a = dev_bf16(act)
+    for m in (64, 8, 17, 1, 40, 9, 64):
+        out = torch.full((m, N), float("nan"), dtype=torch.float32, device="cuda")
+        g(pw, a[:m], out, M=m)
+        again = torch.full_like(out, float("nan"))
+        g(pw, a[:m], again, M=m)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out).view(np.uint32), host(again).view(np.uint32)), m
+        y, S = oracle.gemm(act[:m], codes, scales, t)
+        check(out, y, S, bf16=False, what="M=%d of a max_M=64 plan" % m)
+
+
+def test_verify_width_boundary_to_prefill(nv):
+    """M = 64 is the last verify width and M = 65 the first prefill one."""
+    K, N = 1024, 300
+    codes, scales = synth.random_planes(11, 12, N, K)
+    act = synth.activations(11, 13, 65, K)
+    pw = pack(nv, dev(codes), dev(scales), K, N, 0.002)
+    for m in (64, 65):
+        out, _ = run(nv, pw, dev_bf16(act[:m]), nv.OUT_F32, max_M=65)
+        y, S = oracle.gemm(act[:m], codes, scales, 0.002)
+        check(out, y, S, bf16=False, what="M=%d" % m)
+
+
 # ---- prefill (M > 8: dequantised tiles, bf16 MFMA) ------------------------------
 
 # All but the last split their tiles along K (fp32 partial sums and a second

@@ -223,3 +223,45 @@ def test_chain_outputs_feed_later_matrices():
         act = bf16_bits(s["act"])
         y, S = oracle.gemm(act, codes, scales, t)
         check(s["out"], y, S, bf16=s["out_dtype"] == nv.OUT_BF16, what="chained m%d" % i)
+
+
+# ---- verify widths (per-matrix round with max_M = 64) ----------------------------
+
+@pytest.fixture(scope="module")
+def verify_round():
+    """One layer of the four projections at 1/16 of the real N, 64 rows of
+    activations, a per-matrix round over widths 1..64."""
+    import torch
+    nv = require_gpu()
+    specs, ref = [], []
+    for j, (name, K, N) in enumerate(SHAPES):
+        sid = synth.stream_id(7, name)
+        W = synth.weights(2, sid, N, K)
+        codes, scales, t = oracle.quantize(W)
+        act = synth.activations(2, sid, 64, K)
+        y, S = oracle.gemm(act, codes, scales, t)
+        out_dtype = nv.OUT_F32 if j % 2 == 0 else nv.OUT_BF16
+        dt = torch.float32 if out_dtype == nv.OUT_F32 else torch.bfloat16
+        pw = pack(nv, dev(codes), dev(scales), K, N, t)
+        specs.append(dict(K=K, N=N, codes=pw.codes, scales=pw.scales, tensor_scale=t,
+                          act=dev_bf16(act), out=torch.empty((64, N), dtype=dt, device="cuda"),
+                          out_dtype=out_dtype, pw=pw))
+        ref.append((y, S))
+    ws_bytes = nv.nvfp4_round_workspace_bytes(specs, 64)
+    ws = torch.full((max(ws_bytes, 16),), 0x5A, dtype=torch.uint8, device="cuda")
+    plan = nv.nvfp4_round_create(specs, 64, ws, ws_bytes)
+    yield nv, plan, specs, ref
+    nv.nvfp4_round_destroy(plan)
+    del ws
+
+
+@pytest.mark.parametrize("M", [1, 8, 9, 16, 17, 33, 48, 64])
+def test_verify_width_round(verify_round, M):
+    import torch
+    nv, plan, specs, ref = verify_round
+    assert nv.nvfp4_round_graph_nodes(plan, M) == len(specs)
+    for rep in range(2):  # counters must reset between replays
+        _poison(specs)
+        nv.nvfp4_round_run(plan, M)
+        torch.cuda.synchronize()
+        _check_all(nv, specs, ref, M, "verify round M=%d replay %d" % (M, rep))
