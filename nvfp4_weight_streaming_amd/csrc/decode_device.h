@@ -180,15 +180,15 @@ struct ActStage {
 // r < kR (row idx / kCols, column idx % kCols); only idx < n_out are valid.
 // L2_LOCAL: the partials were written with plain stores into this XCD's L2;
 // else with device-coherent stores, and they are read device-coherently.
-// Every load of a batch of kSB splits, for all kR outputs, is issued before
-// any is added, so a batch costs one memory round trip.  Within a wave that
+// Every load of a batch of kSB = kBatch / kR splits, for all kR outputs, is
+// issued before any is added, so a batch costs one memory round trip.  Within a wave that
 // has valid outputs the output index is clamped to n_out - 1 (repeated
 // addresses within a wave cost one request).
-template <int kCols, int kThreads, int kR, bool L2_LOCAL, int kSplitRows = 8>
+template <int kCols, int kThreads, int kR, bool L2_LOCAL, int kSplitRows = 8, int kBatch = 16>
 __device__ __forceinline__ void sum_partials(const float* gbase, int splits, int n_out,
                                              float (&sum)[kR]) {
-    static_assert(kR >= 1 && kR <= 16, "1 .. 16 outputs per thread");
-    constexpr int kSB = 16 / kR;
+    static_assert(kR >= 1 && kR <= kBatch, "1 .. kBatch outputs per thread");
+    constexpr int kSB = kBatch / kR;  // splits per batch: kBatch values in flight
 #pragma unroll
     for (int r = 0; r < kR; ++r) sum[r] = 0.f;
     for (int s0 = 0; s0 < splits; s0 += kSB) {

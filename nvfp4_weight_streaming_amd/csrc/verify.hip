@@ -28,7 +28,6 @@
 namespace nvfp4 {
 
 constexpr int kVerifyWaves = 8;
-constexpr int kVerifyStride = kSuperK + kLdsPad;  // LDS row, bf16 elements (1040 B)
 
 // End of a workgroup: outputs (one slice) or the split-K hand-off (several).
 // acc[gi][j] holds row 16 gi + 4 (lane / 16) + j, column lane % 16 of the
@@ -107,25 +106,55 @@ __device__ __forceinline__ void verify_finish(const f32x4 (&acc)[G], void* __res
         __hip_atomic_store(&counters[ng], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One workgroup = WAVES column tiles x one K slice of `windows` superblocks.
-// Window w's weights (5 loads per lane) and activation rows (16 G rows of
-// 1 KiB, 2 G copies per wave) are issued before window w - 1 is computed;
-// loads complete in order per wave, so the wait before window w is the
-// constant vmcnt of one window's loads.
+// Window length (in 128-k chunks) for G row groups: with 48 or 64 rows a
+// superblock's activations take 50-66 KiB of LDS per buffer, so the window is
+// half a superblock and two workgroups fit on a compute unit.
+constexpr int verify_kbw(int G) { return G >= 3 ? 2 : 4; }
+
+// Weights of one window: KBW code chunks (16 B per lane each, 4 MFMA steps
+// apiece) and their KBW scale words (one E4M3 byte per step).
+template <int KBW>
+struct VWin {
+    uint4 c[KBW];
+    uint32_t s[KBW];
+};
+
+typedef unsigned int u32v2 __attribute__((ext_vector_type(2)));
+
+// One workgroup = WAVES column tiles x one K slice of `slice_sb` superblocks,
+// streamed in windows of 128 KBW k.  Window w's weights (KBW + 1 loads per
+// lane) and activation rows (16 G rows) are issued before window w - 1 is
+// computed; loads complete in order per wave, so the wait before window w is
+// the constant vmcnt of one window's loads.
+//
+// LDS rows hold one window of one activation row, unpadded (1 KiB or 512 B),
+// in 16-byte segments: segment j of row r sits in slot j ^ (r % 16).  An
+// operand read serves 16 lanes (rows r0 .. r0 + 15, one segment) per pass and
+// a row's bank group is its slot % 16, so those reads cover all banks once.
+// A direct-to-LDS copy writes 1 KiB to consecutive slots (one row, or two
+// rows of a half-superblock window); each lane fetches the segment its slot
+// needs.  The copies address the whole activation buffer: k past K reads the
+// next row (finite values; the weights there are zero) and the last row's
+// tail reads zero.
 template <int WAVES, int G, bool BF16>
 __global__ __launch_bounds__(WAVES * 64) void verify_kernel(
     const uint4* __restrict__ codes, const uint4* __restrict__ scales,
     const uint16_t* __restrict__ act, void* __restrict__ out, float* __restrict__ partial,
     unsigned int* __restrict__ counters, float ts, int M, int K, int N, int nsb, int splits,
-    int n_groups, int n_tiles, int l2_local, int windows) {
+    int n_groups, int n_tiles, int l2_local, int slice_sb) {
+    constexpr int KBW = verify_kbw(G);
+    constexpr int kWinK = 128 * KBW;            // k per window = bf16 per LDS row
+    constexpr int kWinPerSb = 4 / KBW;
+    constexpr int kSlots = kWinK / 8;           // 16-byte segments per row: 64 or 32
     constexpr int kRows = 16 * G;
-    constexpr int kSeg = kRows / WAVES;  // activation rows a wave copies per window
-    static_assert(kRows % WAVES == 0, "activation rows divide over the waves");
-    constexpr int kLoads = 5 + kSeg;     // loads a wave issues per window
+    constexpr int kRowsPerCopy = 64 / kSlots;   // rows one 1 KiB copy fills: 1 or 2
+    constexpr int kCopies = kRows / kRowsPerCopy;
+    constexpr int kSeg = (kCopies + WAVES - 1) / WAVES;  // copies per wave per window
+    constexpr int kLoads = KBW + 1 + kSeg;      // loads a wave issues per window
     // Two separate arrays: the compiler then sees that copies into one never
     // alias reads of the other.
-    __shared__ __attribute__((aligned(16))) __bf16 lds0[kRows * kVerifyStride];
-    __shared__ __attribute__((aligned(16))) __bf16 lds1[kRows * kVerifyStride];
+    __shared__ __attribute__((aligned(16))) __bf16 lds0[kRows * kWinK];
+    __shared__ __attribute__((aligned(16))) __bf16 lds1[kRows * kWinK];
     __shared__ int s_last;
 
     const int b = blockIdx.x;
@@ -133,43 +162,63 @@ __global__ __launch_bounds__(WAVES * 64) void verify_kernel(
     const int ng = (q / splits) * 8 + xcd;
     const int split = q - (q / splits) * splits;
     if (ng >= n_groups) return;  // whole workgroup: padding of the column groups to 8
-    const int sb_begin = split * windows;
-    const int nwin = min(windows, nsb - sb_begin);  // superblocks in this slice (>= 1)
+    const int w_begin = split * slice_sb * kWinPerSb;                       // first window
+    const int nwin = min(slice_sb * kWinPerSb, nsb * kWinPerSb - w_begin);  // >= 1
 
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
     const int nt = min(ng * WAVES + wave, n_tiles - 1);
     const int col = lane & 15, g = lane >> 4;
-    const uint4* cp = codes + ((size_t)nt * nsb + sb_begin) * 256 + lane;
-    const uint4* sp = scales + ((size_t)nt * nsb + sb_begin) * 32 + col * 2 + (g >> 1);
+    const uint4* cp = codes + (size_t)nt * nsb * 256 + lane;
+    const uint4* sp = scales + (size_t)nt * nsb * 32 + col * 2 + (g >> 1);
+    const __amdgpu_buffer_rsrc_t act_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(act), 0, M * K * (int)sizeof(uint16_t), 0x00020000);
+    // This lane's slot in a copy: row r0 + lane / kSlots, slot lane % kSlots.
+    const int c_row = lane / kSlots, c_slot = lane % kSlots;
 
     // Window w: weights into x, activation rows into buf.  Row r of the
-    // window is activation row min(r, M - 1) (rows >= M are never stored);
-    // each row's resource ends at the row's end, so values past K read zero
-    // (the weights there are zero too).
-    auto issue = [&](int w, Chunk& x, __bf16* buf) {
-        const int sb = min(w, nwin - 1);
-        load_chunk(x, cp + 256 * sb, sp + 32 * sb);
-        const int k = (sb_begin + sb) * kSuperK;
-        const int bytes = (K - k) * (int)sizeof(uint16_t);
+    // window is activation row min(r, M - 1) (rows >= M are never stored).
+    auto issue = [&](int w, VWin<KBW>& x, __bf16* buf) {
+        const int gw = w_begin + min(w, nwin - 1);
+        const int sb = gw / kWinPerSb, kb0 = (gw % kWinPerSb) * KBW;
+#pragma unroll
+        for (int i = 0; i < KBW; ++i) x.c[i] = load_stream(cp + 256 * sb + 64 * (kb0 + i));
+        if constexpr (KBW == 4) {
+            const uint4 v = load_stream(sp + 32 * sb);
+            x.s[0] = v.x;
+            x.s[1] = v.y;
+            x.s[2] = v.z;
+            x.s[3] = v.w;
+        } else {
+            const u32v2 v =
+                __builtin_nontemporal_load((const u32v2*)(sp + 32 * sb) + (kb0 >> 1));
+            x.s[0] = v.x;
+            x.s[1] = v.y;
+        }
+        const int k = gw * kWinK;
 #pragma unroll
         for (int j = 0; j < kSeg; ++j) {
-            const int r = wave * kSeg + j;
-            const uint16_t* row = act + (size_t)min(r, M - 1) * K + k;
-            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<uint16_t*>(row), 0, bytes, 0x00020000);
+            // copies past the last repeat it (same bytes to the same place)
+            const int ci = min(wave * kSeg + j, kCopies - 1);
+            const int r0 = ci * kRowsPerCopy, r = r0 + c_row;
+            const int seg = c_slot ^ (r & 15);
+            const int voff = ((min(r, M - 1) * K + k) + 8 * seg) * (int)sizeof(uint16_t);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rs, (__attribute__((address_space(3))) void*)(buf + r * kVerifyStride), 16,
-                lane * 16, 0, 0, 0);
+                act_rs, (__attribute__((address_space(3))) void*)(buf + r0 * kWinK), 16, voff,
+                0, 0, 0);
         }
     };
 
     f32x4 acc[G];
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) acc[gi] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // A operand of this lane: row lane % 16 of each 16-row group, k octet g.
-    const int a_off = col * kVerifyStride + 8 * g;
-    auto step = [&](int w, Chunk& x, Chunk& y, const __bf16* cur, __bf16* nxt) {
+    // A operand of this lane at step t: row col of each 16-row group, segment
+    // 4 t + g, in slot (4 t + g) ^ col = 4 (t ^ (col / 4)) + (g ^ (col % 4)):
+    // the four offsets for t % 4 = 0..3, plus 32 (t - t % 4) bf16.
+    int a_off[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) a_off[u] = col * kWinK + 8 * (4 * (u ^ (col >> 2)) + (g ^ (col & 3)));
+    auto step = [&](int w, VWin<KBW>& x, VWin<KBW>& y, const __bf16* cur, __bf16* nxt) {
         // Every wave is done reading nxt (window w - 1).
         __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
         barrier_nofence();
@@ -180,24 +229,24 @@ __global__ __launch_bounds__(WAVES * 64) void verify_kernel(
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         }
         barrier_nofence();  // every wave's activation rows of window w are in LDS
-        const __bf16* ap = cur + a_off;
-        // 16 steps of 32 k.  The A fragments of step t + 1 are read before the
+        // Steps of 32 k.  The A fragments of step t + 1 are read before the
         // multiplies of step t, so no MFMA waits on a read issued just before.
+        constexpr int kSteps = 4 * KBW;
         bf16x8 av[2][G];
         auto read_a = [&](int t, bf16x8 (&dst)[G]) {
 #pragma unroll
             for (int gi = 0; gi < G; ++gi)
-                dst[gi] = *(const bf16x8*)(ap + 16 * gi * kVerifyStride + 32 * t);
+                dst[gi] = *(const bf16x8*)(cur + a_off[t & 3] + 16 * gi * kWinK + 32 * (t & ~3));
         };
         read_a(0, av[0]);
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
+        for (int t = 0; t < kSteps; ++t) {
             const int kb = t >> 2, s = t & 3;
-            if (t + 1 < 16) read_a(t + 1, av[(t + 1) & 1]);
+            if (t + 1 < kSteps) read_a(t + 1, av[(t + 1) & 1]);
             // keep those reads ahead of this step's work (the scheduler would
             // otherwise move each read next to its use)
             __builtin_amdgcn_sched_barrier(0);
-            const int sw = (int)word(x.s, kb);
+            const int sw = (int)x.s[kb];
             const float sc = s == 0   ? __builtin_amdgcn_cvt_f32_fp8(sw, 0)
                              : s == 1 ? __builtin_amdgcn_cvt_f32_fp8(sw, 1)
                              : s == 2 ? __builtin_amdgcn_cvt_f32_fp8(sw, 2)
@@ -210,7 +259,7 @@ __global__ __launch_bounds__(WAVES * 64) void verify_kernel(
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    Chunk wa, wb;
+    VWin<KBW> wa, wb;
     issue(0, wa, lds0);
     for (int w = 0; w < nwin; w += 2) {
         step(w, wa, wb, lds0, lds1);

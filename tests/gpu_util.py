@@ -52,11 +52,12 @@ def pack(nv, codes_dev, scales_dev, K, N, t):
 
 
 def run(nv, pw, act_dev, out_dtype, M=None, split_k=0, waves=0, chunks=0, kernel=0, tiles=0,
-        max_M=None, windows=0):
+        max_M=None, windows=0, verify_waves=0, verify_windows=0):
     import torch
     M = act_dev.shape[0] if M is None else M
     g = nv.Gemm(max_M or M, pw.K, pw.N, out_dtype, split_k=split_k, waves=waves, chunks=chunks,
-                kernel=kernel, tiles=tiles, windows=windows)
+                kernel=kernel, tiles=tiles, windows=windows, verify_waves=verify_waves,
+                verify_windows=verify_windows)
     dt = torch.float32 if out_dtype == nv.OUT_F32 else torch.bfloat16
     out = torch.full((M, pw.N), float("nan"), dtype=dt, device="cuda")  # poison
     g(pw, act_dev, out, M=M)

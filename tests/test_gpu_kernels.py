@@ -323,6 +323,22 @@ def test_verify_width_ragged(nv, M, K, N, bf16):
     check(out, y, S, bf16=bf16, what="verify %r" % ((M, K, N),))
 
 
+@pytest.mark.parametrize("M,K,N", [(40, 5136, 515), (64, 3072, 300), (20, 12288, 70)])
+@pytest.mark.parametrize("cfg", [dict(verify_waves=16), dict(verify_windows=3),
+                                 dict(verify_waves=16, verify_windows=1)],
+                         ids=["w16", "s3", "w16s1"])
+def test_verify_width_configs(nv, M, K, N, cfg):
+    """Non-default verify-width plans: 16 waves per workgroup, other slice
+    lengths (ragged last slice, one superblock per slice)."""
+    codes, scales = synth.random_planes(M + 71, K, N, K)
+    t = 1.25e-3
+    act = synth.activations(M + 72, N, M, K)
+    pw = pack(nv, dev(codes), dev(scales), K, N, t)
+    out, _ = run(nv, pw, dev_bf16(act), nv.OUT_F32, **cfg)
+    y, S = oracle.gemm(act, codes, scales, t)
+    check(out, y, S, bf16=False, what="verify %r %r" % ((M, K, N), cfg))
+
+
 def test_verify_width_rows_share_one_plan_and_repeat_bitwise(nv):
     """A plan with max_M = 64 serves every M (decode, verify), its split-K
     counters reset themselves, and repeated runs are bit-identical."""
