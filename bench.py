@@ -120,6 +120,13 @@ def build_round(nv, seed=0, layers=LAYERS, max_M=8, log=None):
     return specs, keep
 
 
+def synth_act(spec, rows, seed=0):
+    """bf16 activations [rows][K] for one matrix of the round (its own stream)."""
+    import synth
+    return synth.activations_device(seed, synth.stream_id(spec["layer"], spec["name"]), rows,
+                                    spec["K"])
+
+
 def cpu_baseline(layers=None, lanes=8, threads=None):
     """The CPU oracle, as it stands, on a bounded sample of the round: the
     first `layers` layers' four matrices in full (default four layers, 335.5 M
@@ -261,6 +268,33 @@ def main():
         flags = nv.nvfp4_round_status(plans[mode])
         assert flags == 0, "round form %d: a wait timed out (flags %d)" % (mode, flags)
 
+    # Verify widths (speculative decoding checks up to 7 drafts per lane in the
+    # same pass: up to 8 x 8 = 64 rows): the same weights, 64-row activation
+    # and output buffers, a per-matrix round with one graph per width 1..64.
+    verify = {}
+    if not args.no_sweep:
+        t_v = time.time()
+        with torch.cuda.stream(stream):
+            vspecs = []
+            for sp in specs:
+                vspecs.append(dict(sp, act=synth_act(sp, 64),
+                                   out=torch.empty((64, sp["N"]), dtype=torch.bfloat16,
+                                                   device="cuda")))
+            vws_bytes = nv.nvfp4_round_workspace_bytes(vspecs, 64)
+            vws = torch.zeros(max(vws_bytes, 16), dtype=torch.uint8, device="cuda")
+            vplan = nv.nvfp4_round_create(vspecs, 64, vws, vws_bytes, stream)
+        torch.cuda.synchronize()
+        log("verify-width round (widths 1..64) built in %.1f s" % (time.time() - t_v))
+        for M in (16, 32, 64):
+            ms = time_round(vplan, M, max(5, args.steps // 2), 2)
+            gbs = round_bytes(M, args.layers) / (ms * 1e-3) / 1e9
+            verify[str(M)] = {"round_ms": round(ms, 4), "GB_s": round(gbs, 1),
+                              "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+            log("verify width M=%d: %.3f ms, %.1f GB/s (%.1f%% of 8 TB/s)"
+                % (M, ms, gbs, 100 * gbs / HBM_PEAK_GBS))
+        nv.nvfp4_round_destroy(vplan)
+        del vspecs, vws
+
     # Roofline of the dominant kernel.  The M = 8 round graph runs nothing but
     # decode kernels, one per matrix, in sequence on `stream`, so its average
     # launch duration is the timed region's event time over the launches (it
@@ -386,6 +420,7 @@ def main():
         "round_sweep": sweep,
         "round_sweep_persistent_kernel": sweep_ps,
         "round_sweep_chained": sweep_ch,
+        "verify_width_rounds": verify,
         "roofline": {
             "bound": "hbm",
             "kernel": "nvfp4::decode_window_kernel<WAVES, 1, true> (split-K decode, slices streamed "
