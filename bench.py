@@ -367,7 +367,38 @@ def main():
     head = {"M": 8, "K": HK, "N": HN, "out": "fp32", "us": round(h_us, 2),
             "algorithmic_bytes": h_bytes, "GB_s": round(h_gbs, 1),
             "frac_hbm_peak": round(h_gbs / HBM_PEAK_GBS, 4)}
-    del hpw, hact, hout, hg
+
+    # Top-k over the vocabulary, the step after the head: on the head's own
+    # logits (k = 1, the greedy argmax, and k = 8), and on 7 rows of a
+    # 248320-entry vocabulary (the size class of the pages' drafter top-k).
+    def time_topk(logits, k, reps=20):
+        M, V = logits.shape
+        idx = torch.empty((M, k), dtype=torch.int32, device="cuda")
+        val = torch.empty((M, k), dtype=torch.float32, device="cuda")
+        wsb = nv.nvfp4_topk_workspace_bytes(M, V, k)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                nv.nvfp4_topk(logits, M, V, V, k, idx, val, ws, wsb, stream)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                nv.nvfp4_topk(logits, M, V, V, k, idx, val, ws, wsb, stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e3
+    import synth
+    topk = {}
+    for k in (1, 8):
+        us = time_topk(hout, k)
+        topk["head_M8_V%d_k%d" % (HN, k)] = {"us": round(us, 2)}
+        log("top-k of the head's logits (M=8, V=%d, k=%d): %.2f us" % (HN, k, us))
+    lg = torch.from_numpy(synth.logits(0, 9003, 7, 248320)).cuda()
+    us = time_topk(lg, 7)
+    topk["M7_V248320_k7"] = {"us": round(us, 2)}
+    log("top-k M=7 V=248320 k=7: %.2f us" % us)
+    del hpw, hact, hout, hg, lg
 
     if args.calibration_copy:
         # A plain copy kernel of known size: 1 GiB read, 1 GiB written.
@@ -436,6 +467,7 @@ def main():
         },
         "prefill_chunk": prefill,
         "output_head": head,
+        "topk": topk,
         "cpu_baseline": cpu,
         "timed_wall_s": round(wall, 3),
     }

@@ -66,6 +66,9 @@ enum nvfp4_out_dtype { NVFP4_OUT_F32 = 0, NVFP4_OUT_BF16 = 1 };
  * M goes to the prefill kernel. */
 #define NVFP4_VERIFY_MAX_M 64
 
+/* Largest k of nvfp4_topk. */
+#define NVFP4_TOPK_MAX_K 64
+
 /* ---- status ----------------------------------------------------------------- */
 
 /* Static text of a status code. */
@@ -259,6 +262,25 @@ int nvfp4_round_run(nvfp4_round plan, int M, void* stream);
 /* Number of kernel nodes in the graph of width M (0 on error). */
 int nvfp4_round_graph_nodes(nvfp4_round plan, int M);
 void nvfp4_round_destroy(nvfp4_round plan);
+
+/* ---- top-k over the vocabulary ---------------------------------------------- */
+
+/* The step after the output head ("Ignis" README, "Speculative decoding
+ * (DFlash2)": the drafter's top-k over the vocabulary, replaced by a
+ * row-split kernel with the same answer).  For each row m < M of the fp32
+ * logits [M][ld] (first V entries), writes the k largest values in
+ * descending order to val_dev[m][0..k-1] and their indices to
+ * idx_dev[m][0..k-1] (int32); equal values are listed by ascending index,
+ * and -0.0 equals +0.0.  The answer is unique, so it is bit-identical to any
+ * correct top-k; values are copied from the logits bit for bit.  NaN logits
+ * are out of contract.  1 <= k <= min(V, NVFP4_TOPK_MAX_K), ld >= V,
+ * M * ld < 2^31, pointers 4-byte aligned.
+ *   workspace_dev: nvfp4_topk_workspace_bytes(M, V, k) bytes (16-byte
+ *   aligned; 0 for V <= 1024), any content; owned by the call while it runs.
+ * Asynchronous on `stream`; no synchronisation. */
+size_t nvfp4_topk_workspace_bytes(int M, int V, int k);
+int nvfp4_topk(const float* logits_dev, int M, int V, int ld, int k, int* idx_dev,
+               float* val_dev, void* workspace_dev, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -33,7 +33,9 @@ EXPORTS = (
     "nvfp4_round_workspace_bytes", "nvfp4_round_workspace_bytes_ex", "nvfp4_round_create",
     "nvfp4_round_create_ex", "nvfp4_round_status", "nvfp4_round_set_spin_limit",
     "nvfp4_round_run", "nvfp4_round_graph_nodes", "nvfp4_round_destroy",
+    "nvfp4_topk_workspace_bytes", "nvfp4_topk",
 )
+TOPK_MAX_K = 64
 ROUND_PERSISTENT, ROUND_PER_MATRIX, ROUND_CHAIN = 0, 1, 2
 
 
@@ -106,6 +108,9 @@ def lib():
         L.nvfp4_round_graph_nodes.argtypes = [vp, i]
         L.nvfp4_round_destroy.argtypes = [vp]
         L.nvfp4_round_destroy.restype = None
+        L.nvfp4_topk_workspace_bytes.argtypes = [i, i, i]
+        L.nvfp4_topk_workspace_bytes.restype = sz
+        L.nvfp4_topk.argtypes = [vp, i, i, i, i, vp, vp, vp, sz, vp]
         for name in EXPORTS:
             getattr(L, name)
         _lib = L
@@ -168,6 +173,27 @@ def nvfp4_quantize_workspace_bytes() -> int:
 def nvfp4_quantize(w, K, N, codes, scales, tensor_scale, workspace, stream=None):
     _check(lib().nvfp4_quantize(_ptr(w), K, N, _ptr(codes), _ptr(scales), _ptr(tensor_scale),
                                 _ptr(workspace), _stream(stream)))
+
+
+def nvfp4_topk_workspace_bytes(M, V, k) -> int:
+    return lib().nvfp4_topk_workspace_bytes(M, V, k)
+
+
+def nvfp4_topk(logits, M, V, ld, k, idx, val, workspace=None, workspace_bytes=0, stream=None):
+    _check(lib().nvfp4_topk(_ptr(logits), M, V, ld, k, _ptr(idx), _ptr(val), _ptr(workspace),
+                            workspace_bytes, _stream(stream)))
+
+
+def topk(logits, k, stream=None):
+    """(indices int32 [M][k], values [M][k]) of a device fp32 [M][V] tensor."""
+    import torch
+    M, V = logits.shape
+    idx = torch.empty((M, k), dtype=torch.int32, device=logits.device)
+    val = torch.empty((M, k), dtype=torch.float32, device=logits.device)
+    wsb = nvfp4_topk_workspace_bytes(M, V, k)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=logits.device) if wsb else None
+    nvfp4_topk(logits, M, V, logits.stride(0), k, idx, val, ws, wsb, stream)
+    return idx, val
 
 
 def nvfp4_gemm_create(max_M, K, N, out_dtype, split_k=0, waves=0, chunks=0, kernel=0, tiles=0,

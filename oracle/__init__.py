@@ -17,6 +17,12 @@ It implements, on the CPU and in fp64 where the format allows exactness:
   over the weights serves all lanes): ``y[m][n] = sum_k a[m][k] * w[n][k]``
   with exact fp64 products, ascending-k fp64 sums, and ``S = sum |a*w|``.
 
+* the top-k of the output head's logits ("Ignis" README, "Speculative
+  decoding (DFlash2)": the drafter's top-k over the vocabulary, replaced by a
+  row-split kernel with an identical answer): per row, the k largest values in
+  descending order, equal values in ascending index order (IEEE comparison,
+  so -0.0 and +0.0 are equal).
+
 Every function here is pinned by ``tests/test_oracle_pins.py`` against tables,
 library routines, closed forms and exact rational brute force.
 """
@@ -187,3 +193,19 @@ def tolerance_bf16(y: np.ndarray, S: np.ndarray) -> np.ndarray:
     rounding plus half a bf16 ulp of the (bounded) value."""
     tol = np.ldexp(S, -16)
     return tol + np.ldexp(np.abs(y) + tol, -8)
+
+
+def topk(logits: np.ndarray, k: int):
+    """Top-k of each row of a float32 [M][V] array: (indices int32 [M][k],
+    values float32 [M][k]), values descending, ties by ascending index.  The
+    values are the input elements themselves (bit for bit)."""
+    x = np.ascontiguousarray(logits, dtype=np.float32)
+    M, V = x.shape
+    assert 1 <= k <= V
+    idx = np.empty((M, k), np.int32)
+    for m in range(M):
+        # lexsort's last key is the primary one: descending value, then index
+        order = np.lexsort((np.arange(V), -x[m].astype(np.float64)))
+        idx[m] = order[:k]
+    vals = np.take_along_axis(x, idx.astype(np.int64), axis=1)
+    return idx, vals

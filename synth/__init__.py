@@ -11,7 +11,10 @@ pages describe in "Models and artifacts" but which is not available here):
 * weights: fp32 draws from N(0, 0.02), shape [N][K] (N output rows of K
   values, K contiguous), one independent stream per matrix;
 * activations: fp32 draws from N(0, 1) rounded to bf16 (round to nearest
-  even), shape [M][K], returned as the 16-bit patterns.
+  even), shape [M][K], returned as the 16-bit patterns;
+* logits for the top-k step: fp32 draws from N(0, 4), shape [M][V], or, for
+  tie-heavy cases, draws from a small pool of values that includes -0.0,
+  +0.0 and the infinities.
 
 Host draws use numpy's Philox-4x32 counter-based generator keyed by
 (seed, stream).  Draws for full-size workloads are made on the GPU with
@@ -93,3 +96,15 @@ def random_planes(seed: int, stream: int, N: int, K: int):
     codes = g.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
     scales = g.integers(0, 0x7F, size=(N, K // 16), dtype=np.uint8)
     return codes, scales
+
+
+LOGIT_POOL = np.array([-np.inf, -3.0, -1.0, -0.0, 0.0, 0.5, 1.0, 2.0, 2.0, 7.5, np.inf],
+                      np.float32)
+
+
+def logits(seed: int, stream: int, M: int, V: int, ties: bool = False) -> np.ndarray:
+    """fp32 [M][V]: N(0, 4) draws, or (ties=True) draws from LOGIT_POOL."""
+    rng = _rng(seed, stream)
+    if ties:
+        return LOGIT_POOL[rng.integers(0, len(LOGIT_POOL), (M, V))]
+    return (rng.standard_normal((M, V)) * 4.0).astype(np.float32)

@@ -140,6 +140,27 @@ def test_verify_width_config(nv):
     nv.nvfp4_gemm_destroy(p64)
 
 
+def test_topk_validation_and_workspace(nv):
+    L = nv.lib()
+    assert nv.nvfp4_topk_workspace_bytes(8, 1024, 8) == 0       # one unit per row
+    assert nv.nvfp4_topk_workspace_bytes(8, 152064, 8) > 0
+    assert nv.nvfp4_topk_workspace_bytes(8, 100, 101) == 0      # k > V: invalid
+    assert nv.nvfp4_topk_workspace_bytes(8, 100, 65) == 0       # k > 64: invalid
+    for args, word in (((FAKE, 0, 10, 10, 1), "M"), ((FAKE, 2, 0, 10, 1), "V"),
+                       ((FAKE, 2, 10, 9, 1), "ld"), ((FAKE, 2, 10, 10, 0), "k"),
+                       ((FAKE, 2, 10, 10, 11), "k"), ((FAKE, 2, 100, 100, 65), "k"),
+                       ((None, 2, 10, 10, 1), "logits")):
+        assert L.nvfp4_topk(*args, FAKE, FAKE, None, 0, None) == nv.EINVAL
+        assert nv.last_error().startswith(word), nv.last_error()
+    assert L.nvfp4_topk(FAKE, 2, 10, 10, 1, None, FAKE, None, 0, None) == nv.EINVAL
+    assert nv.last_error().startswith("idx")
+    assert L.nvfp4_topk(FAKE + 2, 2, 10, 10, 1, FAKE, FAKE, None, 0, None) == nv.EINVAL
+    assert "aligned" in nv.last_error()
+    need = nv.nvfp4_topk_workspace_bytes(8, 152064, 8)
+    assert L.nvfp4_topk(FAKE, 8, 152064, 152064, 8, FAKE, FAKE, FAKE, need - 1, None) == nv.EINVAL
+    assert nv.last_error().startswith("workspace_bytes")
+
+
 def test_workspace_sizes_for_round_shapes(nv):
     for K, N in [(5120, 7168), (6144, 5120), (5120, 34816), (17408, 5120), (5120, 152064)]:
         plan, ws = nv.nvfp4_gemm_create(8, K, N, 1)

@@ -9,6 +9,9 @@
   the nearest-value invariants on random N(0, 0.02) matrices.
 * GEMM: exact rational brute force (Python fractions over the golden/torch
   tables), a closed form, one-hot reconstruction, zero scales.
+* Top-k: hand-worked cases (tests/golden/topk_worked_cases.txt), numpy's
+  first-occurrence argmax (k = 1) and stable argsort (k = V), and order and
+  selection invariants on random rows with many ties.
 * A set of deliberately broken oracles (mistakes planted on the CPU) must
   fail these pins, which shows they can catch a dropped term, a swapped
   nibble order, a transposed operand or a wrong block index.
@@ -304,3 +307,74 @@ MUTANTS = {
 def test_planted_mistakes_fail_brute_force(oracle_mod, golden_dir, name):
     mutant = MUTANTS[name]
     assert not _check_brute_force(lambda a, c, s, t: mutant(oracle_mod, a, c, s, t), golden_dir)
+
+
+# ---- top-k --------------------------------------------------------------------
+
+def _golden_topk(golden_dir):
+    cases = []
+    with open(os.path.join(golden_dir, "topk_worked_cases.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            row, k, idx = line.split("|")
+            vals = np.array([float(v) for v in row.split(":")[1].split()], np.float32)
+            cases.append((vals, int(k.split(":")[1]), [int(i) for i in idx.split(":")[1].split()]))
+    assert len(cases) >= 7
+    return cases
+
+
+def _topk_pins(topk, golden_dir):
+    """Every top-k pin, for the oracle and for planted mistakes."""
+    for vals, k, want in _golden_topk(golden_dir):
+        idx, got = topk(vals[None, :], k)
+        assert idx[0].tolist() == want, (vals, k, idx[0].tolist(), want)
+        assert np.array_equal(got[0].view(np.uint32), vals[want].view(np.uint32))
+    rng = np.random.default_rng(5)
+    for M, V, k in ((3, 50, 1), (2, 37, 37), (4, 200, 9), (1, 1000, 64)):
+        # few distinct values (many ties), both zeros, some infinities
+        pool = np.array([-np.inf, -2.5, -1, -0.0, 0.0, 0.5, 1, 1, 3, np.inf], np.float32)
+        x = pool[rng.integers(0, len(pool), (M, V))]
+        idx, got = topk(x, k)
+        for m in range(M):
+            if k == 1:
+                assert idx[m, 0] == np.argmax(x[m])  # first occurrence of the maximum
+            if k == V:
+                assert idx[m].tolist() == np.argsort(-x[m], kind="stable").tolist()
+            sel = idx[m].tolist()
+            assert len(set(sel)) == k
+            v = x[m, sel]
+            for a in range(k - 1):  # descending; ties by ascending index
+                assert v[a] > v[a + 1] or (v[a] == v[a + 1] and sel[a] < sel[a + 1])
+            rest = np.setdiff1d(np.arange(V), sel)
+            kth, kth_i = v[-1], sel[-1]
+            assert np.all((x[m, rest] < kth) | ((x[m, rest] == kth) & (rest > kth_i)))
+
+
+def test_topk_pins(oracle_mod, golden_dir):
+    _topk_pins(oracle_mod.topk, golden_dir)
+
+
+def _topk_mutant(kind):
+    def f(x, k):
+        x = np.asarray(x, np.float32)
+        M, V = x.shape
+        idx = np.empty((M, k), np.int32)
+        for m in range(M):
+            if kind == "ties_descending_index":
+                order = np.lexsort((-np.arange(V), -x[m].astype(np.float64)))
+            elif kind == "negative_zero_below":  # total order on the bits: -0 < +0
+                key = x[m].view(np.int32).astype(np.int64)
+                key = np.where(key < 0, -(key & 0x7FFFFFFF) - 1, key)
+                order = np.lexsort((np.arange(V), -key))
+            else:  # "ascending"
+                order = np.lexsort((np.arange(V), x[m].astype(np.float64)))
+            idx[m] = order[:k]
+        return idx, np.take_along_axis(x, idx.astype(np.int64), axis=1)
+    return f
+
+
+@pytest.mark.parametrize("kind", ["ties_descending_index", "negative_zero_below", "ascending"])
+def test_topk_planted_mistakes_fail_the_pins(golden_dir, kind):
+    with pytest.raises(AssertionError):
+        _topk_pins(_topk_mutant(kind), golden_dir)
