@@ -35,11 +35,17 @@ import bench  # noqa: E402  (host-only helpers; importing it touches no GPU)
 
 BENCH_ARGS = ["--steps", "10", "--warmup", "2", "--no-cpu-baseline", "--no-sweep",
               "--calibration-copy"]
+# The widths sweep, the verify-width rounds and the top-k timings (kernel
+# trace only): the whole bench with few steps.
+WIDE_ARGS = ["--steps", "4", "--warmup", "1", "--no-cpu-baseline"]
 PASSES = (
-    ("trace", ["--kernel-trace", "--stats"], 600),
-    ("fetch", ["--pmc", "FETCH_SIZE"], 300),
-    ("write", ["--pmc", "WRITE_SIZE"], 300),
+    ("trace", ["--kernel-trace", "--stats"], 600, BENCH_ARGS),
+    ("fetch", ["--pmc", "FETCH_SIZE"], 300, BENCH_ARGS),
+    ("write", ["--pmc", "WRITE_SIZE"], 300, BENCH_ARGS),
+    ("trace_wide", ["--kernel-trace", "--stats"], 600, WIDE_ARGS),
 )
+VERIFY = "nvfp4::verify_kernel<"
+TOPK = "nvfp4::topk_level_kernel<"
 CALIB_BYTES = 1 << 30
 DECODE = "nvfp4::decode_"  # decode_kernel< and decode_window_kernel<
 PREFILL = "nvfp4::prefill_kernel<"
@@ -47,9 +53,9 @@ PREFILL_SUM = "nvfp4::prefill_reduce_kernel<"
 COPY = "__amd_rocclr_copyBuffer"
 
 
-def rocprof_cmd(flags, out_dir):
+def rocprof_cmd(flags, out_dir, args=BENCH_ARGS):
     return (["rocprofv3"] + flags + ["--output-format", "csv", "-d", out_dir, "-o", "run", "--",
-                                     "python3", "-u", os.path.join(ROOT, "bench.py")] + BENCH_ARGS)
+                                     "python3", "-u", os.path.join(ROOT, "bench.py")] + args)
 
 
 def shown(cmd):
@@ -58,9 +64,9 @@ def shown(cmd):
 
 def run_passes(out):
     env = dict(os.environ, TMPDIR="/tmp")
-    for name, flags, limit in PASSES:
+    for name, flags, limit, args in PASSES:
         d = os.path.join(out, name)
-        cmd = rocprof_cmd(flags, d)
+        cmd = rocprof_cmd(flags, d, args)
         print("== %s: %s" % (name, shown(cmd)), flush=True)
         with open(os.path.join(out, name + ".log"), "w") as log:
             r = subprocess.run(["timeout", "-s", "KILL", str(limit)] + cmd, cwd="/tmp", env=env,
@@ -231,6 +237,56 @@ def summarize(out, dest):
         f.write("\n")
     print("decode: trace %.3f us vs bench %.3f us; traffic %.0f B vs algorithmic %d B"
           % (dec_avg_us, roof["avg_launch_us"], fetch_b + write_b, algo))
+    if os.path.isdir(os.path.join(out, "trace_wide")):
+        summarize_wide(out, dest)
+
+
+def summarize_wide(out, dest):
+    """Verify-width rounds and top-k: per-kernel averages from the wide trace."""
+    line = bench_line(os.path.join(out, "trace_wide.log"))
+    trace = list(csv.DictReader(open(find_csv(os.path.join(out, "trace_wide"),
+                                              "kernel_trace.csv"))))
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+    dur = lambda r: int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    md = ["# Verify-width rounds and top-k over the vocabulary: kernel trace\n"]
+    md.append("Command (from the repository root, with `TMPDIR=/tmp`, run in /tmp):\n")
+    md.append("    python3 bench_profile.py --out OUT\n")
+    md.append("which runs, for this pass:\n")
+    md.append("    " + shown(rocprof_cmd(PASSES[3][1], "OUT/trace_wide", WIDE_ARGS)) + "\n")
+    md.append("## Verify-width rounds (64 layers, per-matrix graph; bench.py's round time beside)\n")
+    ver = [r for r in trace if VERIFY in r["Kernel_Name"]]
+    per_round = 4 * bench.LAYERS
+    md.append("| M | bench.py round (ms) | trace: sum of kernel time per replay (ms) | "
+              "qkv (us) | o (us) | gate_up (us) | down (us) |")
+    md.append("|---|---|---|---|---|---|---|")
+    # replays run M = 16, 32, 64 in order: 2 warm-up + max(5, steps // 2) timed each
+    vr = line.get("verify_width_rounds", {})
+    reps = 2 + max(5, 4 // 2)
+    for i, M in enumerate((16, 32, 64)):
+        seg = ver[i * reps * per_round:(i + 1) * reps * per_round]
+        if len(seg) < per_round:
+            continue
+        shapes = collections.defaultdict(list)
+        for j, r in enumerate(seg):
+            shapes[j % 4].append(dur(r))
+        avg = [sum(v) / len(v) / 1e3 for _, v in sorted(shapes.items())]
+        md.append("| %d | %s | %.4f | %.2f | %.2f | %.2f | %.2f |"
+                  % (M, vr.get(str(M), {}).get("round_ms", "-"),
+                     sum(map(dur, seg)) / (len(seg) / per_round) / 1e6, *avg))
+    md.append("\n## Top-k levels (per launch)\n")
+    md.append("| kernel | grid X x Y (threads x rows) | launches | average (us) |")
+    md.append("|---|---|---|---|")
+    groups = collections.OrderedDict()
+    for r in trace:
+        if TOPK in r["Kernel_Name"]:
+            key = (short(r["Kernel_Name"]), r["Grid_Size_X"], r.get("Grid_Size_Y", "1"))
+            groups.setdefault(key, []).append(dur(r))
+    for (name, gx, gy), ds in groups.items():
+        md.append("| %s | %s x %s | %d | %.2f |" % (name, gx, gy, len(ds), sum(ds) / len(ds) / 1e3))
+    md.append("\nbench.py's top-k figures (back-to-back calls, levels included): %s\n"
+              % json.dumps(line.get("topk", {})))
+    with open(os.path.join(dest, "verify_topk_kernel_trace.md"), "w") as f:
+        f.write("\n".join(md))
 
 
 def main():
