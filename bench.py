@@ -268,6 +268,33 @@ def main():
         flags = nv.nvfp4_round_status(plans[mode])
         assert flags == 0, "round form %d: a wait timed out (flags %d)" % (mode, flags)
 
+    # Chained MLP: the same round with each down matrix reading the SwiGLU of
+    # its layer's gate_up output (one more graph node per layer), so the
+    # gate_up -> down pair is a dependent chain as in a forward pass.
+    chained = {}
+    if not args.no_sweep:
+        with torch.cuda.stream(stream):
+            cspecs = []
+            for sp in specs:
+                if sp["name"] == "down":
+                    sp = dict(sp, act=torch.empty((8, sp["K"]), dtype=torch.bfloat16,
+                                                  device="cuda"), act_op=nv.ACT_SWIGLU_PREV)
+                cspecs.append(sp)
+            cws_bytes = nv.nvfp4_round_workspace_bytes(cspecs, 8)
+            cws = torch.zeros(max(cws_bytes, 16), dtype=torch.uint8, device="cuda")
+            cplan = nv.nvfp4_round_create(cspecs, 8, cws, cws_bytes, stream)
+        torch.cuda.synchronize()
+        for M in (1, 8):
+            ms = time_round(cplan, M, max(5, args.steps // 2), 2)
+            gbs = round_bytes(M, args.layers) / (ms * 1e-3) / 1e9
+            chained[str(M)] = {"round_ms": round(ms, 4), "GB_s": round(gbs, 1),
+                               "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                               "graph_nodes": nv.nvfp4_round_graph_nodes(cplan, M)}
+            log("chained-MLP round M=%d (SwiGLU between gate_up and down): %.3f ms, %.1f GB/s"
+                % (M, ms, gbs))
+        nv.nvfp4_round_destroy(cplan)
+        del cspecs, cws
+
     # Verify widths (speculative decoding checks up to 7 drafts per lane in the
     # same pass: up to 8 x 8 = 64 rows): the same weights, 64-row activation
     # and output buffers, a per-matrix round with one graph per width 1..64.
@@ -452,6 +479,7 @@ def main():
         "round_sweep_persistent_kernel": sweep_ps,
         "round_sweep_chained": sweep_ch,
         "verify_width_rounds": verify,
+        "chained_mlp_rounds": chained,
         "roofline": {
             "bound": "hbm",
             "kernel": "nvfp4::decode_window_kernel<WAVES, 1, true> (split-K decode, slices streamed "

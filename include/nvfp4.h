@@ -183,8 +183,17 @@ int nvfp4_workspace_clear(void* workspace_dev, size_t bytes, void* stream);
 
 /* ---- decode round ---------------------------------------------------------------------- */
 
+/* Where a round matrix's activations come from (nvfp4_layer.act_op). */
+enum nvfp4_act_op {
+    NVFP4_ACT_INPUT = 0,       /* act_dev as the caller filled it */
+    NVFP4_ACT_SWIGLU_PREV = 1  /* written by the round before this matrix:
+                                  nvfp4_swiglu of the previous matrix's bf16
+                                  output (its N must be 2 K): the gated MLP
+                                  step between gate_up and down */
+};
+
 /* One matrix of a round.  act_dev holds max_M rows of K bf16 values, out_dev
- * max_M rows of N outputs. */
+ * max_M rows of N outputs.  act_op: nvfp4_act_op (PER_MATRIX rounds only). */
 typedef struct nvfp4_layer {
     int K, N;
     const uint8_t* codes_dev;  /* packed */
@@ -193,6 +202,7 @@ typedef struct nvfp4_layer {
     const uint16_t* act_dev;
     void* out_dev;
     int out_dtype;
+    int act_op;
 } nvfp4_layer;
 
 typedef struct nvfp4_round_plan* nvfp4_round;
@@ -262,6 +272,15 @@ int nvfp4_round_run(nvfp4_round plan, int M, void* stream);
 /* Number of kernel nodes in the graph of width M (0 on error). */
 int nvfp4_round_graph_nodes(nvfp4_round plan, int M);
 void nvfp4_round_destroy(nvfp4_round plan);
+
+/* ---- SwiGLU between gate_up and down ------------------------------------------ */
+
+/* out[m][j] = silu(g) * u for g = gate_up[m][j], u = gate_up[m][F + j]
+ * (bf16 [M][2F] in, bf16 [M][F] out, row-major), silu(g) = g / (1 + e^-g).
+ * The pages leave the layer's non-GEMM steps unstated; this is the reading
+ * the round's shapes support (gate_up N = 2 x down K).  Computed in fp64 and
+ * rounded once to bf16 (nearest, ties to even).  Asynchronous on `stream`. */
+int nvfp4_swiglu(const uint16_t* gate_up_dev, int M, int F, uint16_t* out_dev, void* stream);
 
 /* ---- top-k over the vocabulary ---------------------------------------------- */
 

@@ -33,7 +33,7 @@ EXPORTS = (
     "nvfp4_round_workspace_bytes", "nvfp4_round_workspace_bytes_ex", "nvfp4_round_create",
     "nvfp4_round_create_ex", "nvfp4_round_status", "nvfp4_round_set_spin_limit",
     "nvfp4_round_run", "nvfp4_round_graph_nodes", "nvfp4_round_destroy",
-    "nvfp4_topk_workspace_bytes", "nvfp4_topk",
+    "nvfp4_topk_workspace_bytes", "nvfp4_topk", "nvfp4_swiglu",
 )
 TOPK_MAX_K = 64
 ROUND_PERSISTENT, ROUND_PER_MATRIX, ROUND_CHAIN = 0, 1, 2
@@ -63,7 +63,11 @@ class Layer(ctypes.Structure):
     _fields_ = [("K", ctypes.c_int), ("N", ctypes.c_int),
                 ("codes_dev", ctypes.c_void_p), ("scales_dev", ctypes.c_void_p),
                 ("tensor_scale", ctypes.c_float), ("act_dev", ctypes.c_void_p),
-                ("out_dev", ctypes.c_void_p), ("out_dtype", ctypes.c_int)]
+                ("out_dev", ctypes.c_void_p), ("out_dtype", ctypes.c_int),
+                ("act_op", ctypes.c_int)]
+
+
+ACT_INPUT, ACT_SWIGLU_PREV = 0, 1
 
 
 _lib = None
@@ -111,6 +115,7 @@ def lib():
         L.nvfp4_topk_workspace_bytes.argtypes = [i, i, i]
         L.nvfp4_topk_workspace_bytes.restype = sz
         L.nvfp4_topk.argtypes = [vp, i, i, i, i, vp, vp, vp, sz, vp]
+        L.nvfp4_swiglu.argtypes = [vp, i, i, vp, vp]
         for name in EXPORTS:
             getattr(L, name)
         _lib = L
@@ -175,6 +180,10 @@ def nvfp4_quantize(w, K, N, codes, scales, tensor_scale, workspace, stream=None)
                                 _ptr(workspace), _stream(stream)))
 
 
+def nvfp4_swiglu(gate_up, M, F, out, stream=None):
+    _check(lib().nvfp4_swiglu(_ptr(gate_up), M, F, _ptr(out), _stream(stream)))
+
+
 def nvfp4_topk_workspace_bytes(M, V, k) -> int:
     return lib().nvfp4_topk_workspace_bytes(M, V, k)
 
@@ -232,7 +241,7 @@ def _layers(layers):
     for i, l in enumerate(layers):
         arr[i] = Layer(l["K"], l["N"], _ptr(l["codes"]), _ptr(l["scales"]),
                        float(l["tensor_scale"]), _ptr(l["act"]), _ptr(l["out"]),
-                       int(l.get("out_dtype", OUT_BF16)))
+                       int(l.get("out_dtype", OUT_BF16)), int(l.get("act_op", ACT_INPUT)))
     return arr
 
 

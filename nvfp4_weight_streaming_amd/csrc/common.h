@@ -113,6 +113,7 @@ int launch_verify(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const u
 int launch_prefill(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
                    float ts, const uint16_t* act, void* out, void* ws, hipStream_t s);
 int launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+int launch_swiglu(const uint16_t* gate_up, uint16_t* out, int M, int F, hipStream_t s);
 
 // Streaming kernel (stream.hip).
 void stream_fill_desc(StreamDesc* d, int K, int N, const void* codes, const void* scales,

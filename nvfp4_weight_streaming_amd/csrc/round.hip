@@ -68,8 +68,24 @@ static int validate_layers(const nvfp4_layer* L, int n, int max_M) {
         if ((uintptr_t)l.out_dev & 3) return set_error(NVFP4_EINVAL, "layers[%d].out: not 4-byte aligned", i);
         if (l.out_dtype != NVFP4_OUT_F32 && l.out_dtype != NVFP4_OUT_BF16)
             return set_error(NVFP4_EINVAL, "layers[%d].out_dtype: %d", i, l.out_dtype);
+        if (l.act_op != NVFP4_ACT_INPUT && l.act_op != NVFP4_ACT_SWIGLU_PREV)
+            return set_error(NVFP4_EINVAL, "layers[%d].act_op: %d", i, l.act_op);
+        if (l.act_op == NVFP4_ACT_SWIGLU_PREV) {
+            if (i == 0) return set_error(NVFP4_EINVAL, "layers[0].act_op: SWIGLU_PREV needs a previous matrix");
+            if (L[i - 1].N != 2 * l.K)
+                return set_error(NVFP4_EINVAL, "layers[%d].act_op: previous N = %d is not 2 K = %d", i,
+                                 L[i - 1].N, 2 * l.K);
+            if (L[i - 1].out_dtype != NVFP4_OUT_BF16)
+                return set_error(NVFP4_EINVAL, "layers[%d].act_op: previous output is not bf16", i);
+        }
     }
     return NVFP4_OK;
+}
+
+static bool any_act_op(const nvfp4_layer* L, int n) {
+    for (int i = 0; i < n; ++i)
+        if (L[i].act_op != NVFP4_ACT_INPUT) return true;
+    return false;
 }
 
 }  // namespace nvfp4
@@ -136,6 +152,8 @@ int nvfp4_round_workspace_bytes_ex(const nvfp4_layer* layers, int n_layers, int 
     if (st) return st;
     st = check_mode(mode, max_M);
     if (st) return st;
+    if (mode != NVFP4_ROUND_PER_MATRIX && any_act_op(layers, n_layers))
+        return set_error(NVFP4_EUNSUPPORTED, "layers[].act_op: only the PER_MATRIX form chains");
     if (!workspace_bytes) return set_error(NVFP4_EINVAL, "workspace_bytes: NULL");
     if (mode == NVFP4_ROUND_PERSISTENT) {
         StreamRoundLayout lay;
@@ -169,6 +187,8 @@ int nvfp4_round_create_ex(nvfp4_round* plan, const nvfp4_layer* layers, int n_la
     if (st) return st;
     st = check_mode(mode, max_M);
     if (st) return st;
+    if (mode != NVFP4_ROUND_PER_MATRIX && any_act_op(layers, n_layers))
+        return set_error(NVFP4_EUNSUPPORTED, "layers[].act_op: only the PER_MATRIX form chains");
     size_t need_c = 0, need_p = 0;
     StreamRoundLayout lay{};
     ChainLayout chain{};
@@ -258,6 +278,10 @@ int nvfp4_round_create_ex(nvfp4_round* plan, const nvfp4_layer* layers, int n_la
         } else {
             for (int i = 0; i < n_layers && !lst; ++i) {
                 const nvfp4_layer& l = r->layers[i];
+                if (l.act_op == NVFP4_ACT_SWIGLU_PREV)
+                    lst = launch_swiglu((const uint16_t*)r->layers[i - 1].out_dev,
+                                        const_cast<uint16_t*>(l.act_dev), M, l.K, cap);
+                if (lst) break;
                 lst = run_gemm(r->plans[i], M, l.codes_dev, l.scales_dev, l.tensor_scale,
                                l.act_dev, l.out_dev, workspace,
                                RunOffsets{r->partial_off, 0, r->partial_off}, cap);

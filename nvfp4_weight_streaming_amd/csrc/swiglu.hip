@@ -1,0 +1,89 @@
+// SwiGLU between the gate_up and down matrices of a layer.
+//
+// The pages do not spell out the layer's non-GEMM steps; the round's shapes
+// do: the fused gate_up matrix has N = 2 F outputs and the down matrix takes
+// K = F (34816 = 2 x 17408).  The plainest reading is the gated MLP of the
+// model family: h = silu(gate) * up with silu(g) = g / (1 + exp(-g)), gate
+// the first F outputs and up the second.  With it, down consumes what gate_up
+// produced, so the two GEMMs of a round are a dependent chain as in a real
+// forward pass ("Ignis" README, "The decode round").
+//
+// Precision: each h is computed in fp64 from the bf16 inputs and rounded once
+// to bf16 (nearest, ties to even, no intermediate fp32), so the result is the
+// correctly rounded value except when fp64 rounding error moves it across a
+// bf16 rounding boundary (relative distance 2^-52 against 2^-9).
+#include "common.h"
+
+namespace nvfp4 {
+
+// fp64 -> bf16 bits, rounded once to nearest, ties to even.  Overflow goes to
+// infinity; NaN becomes the quiet NaN 0x7FC0 with the input's sign.
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
+    const unsigned long long b = (unsigned long long)__double_as_longlong(x);
+    const uint16_t sign = (uint16_t)((b >> 63) << 15);
+    const unsigned long long ax = b & 0x7FFFFFFFFFFFFFFFull;
+    if (ax > 0x7FF0000000000000ull) return sign | 0x7FC0;  // NaN
+    if (ax == 0x7FF0000000000000ull) return sign | 0x7F80;  // infinity
+    if (ax == 0) return sign;
+    int e = (int)(ax >> 52) - 1023;  // unbiased exponent (normal inputs)
+    unsigned long long m = (ax & 0xFFFFFFFFFFFFFull) | (1ull << 52);
+    if ((ax >> 52) == 0) return sign;  // fp64 subnormal: far below bf16's range
+    // bf16 keeps 8 significant bits for e >= -126 (shift 45); below, the
+    // subnormal grid of 2^-133 (shift 45 + (-126 - e)).
+    const int shift = e >= -126 ? 45 : 45 + (-126 - e);
+    if (shift >= 64) return sign;  // below half the smallest subnormal
+    unsigned long long q = m >> shift;
+    const unsigned long long rem = m & ((1ull << shift) - 1ull);
+    const unsigned long long half = 1ull << (shift - 1);
+    if (rem > half || (rem == half && (q & 1ull))) ++q;
+    if (e >= -126) {
+        if (q == 256) {  // carried into the next binade
+            q = 128;
+            ++e;
+        }
+        if (e > 127) return sign | 0x7F80;
+        return sign | (uint16_t)(((e + 127) << 7) | (int)(q & 127ull));
+    }
+    return sign | (uint16_t)q;  // subnormal, or 0x0080 after a carry: 2^-126
+}
+
+__device__ __forceinline__ double bf16_to_f64(uint16_t h) {
+    return (double)__uint_as_float((unsigned int)h << 16);
+}
+
+// h[m][j] = silu(gu[m][j]) * gu[m][F + j]; one thread per output.
+__global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t* __restrict__ gu,
+                                                     uint16_t* __restrict__ h, int M, int F) {
+    const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (t >= (long long)M * F) return;
+    const int m = (int)(t / F), j = (int)(t - (long long)m * F);
+    const double g = bf16_to_f64(gu[(size_t)m * 2 * F + j]);
+    const double u = bf16_to_f64(gu[(size_t)m * 2 * F + F + j]);
+    h[(size_t)m * F + j] = f64_to_bf16_rne(g * u / (1.0 + exp(-g)));
+}
+
+int launch_swiglu(const uint16_t* gu, uint16_t* h, int M, int F, hipStream_t s) {
+    const long long n = (long long)M * F;
+    hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, gu, h,
+                       M, F);
+    NVFP4_HIP(hipGetLastError());
+    return NVFP4_OK;
+}
+
+}  // namespace nvfp4
+
+using namespace nvfp4;
+
+extern "C" int nvfp4_swiglu(const uint16_t* gate_up_dev, int M, int F, uint16_t* out_dev,
+                            void* stream) {
+    clear_error();
+    if (M < 1) return set_error(NVFP4_EINVAL, "M: %d < 1", M);
+    if (F < 1) return set_error(NVFP4_EINVAL, "F: %d < 1", F);
+    if ((long long)M * 2 * F > 0x7FFFFFFF)
+        return set_error(NVFP4_EINVAL, "M * 2F: more than 2^31 - 1 elements");
+    if (!gate_up_dev) return set_error(NVFP4_EINVAL, "gate_up: NULL");
+    if (!out_dev) return set_error(NVFP4_EINVAL, "out: NULL");
+    if (((uintptr_t)gate_up_dev | (uintptr_t)out_dev) & 1)
+        return set_error(NVFP4_EINVAL, "gate_up/out: not 2-byte aligned");
+    return launch_swiglu(gate_up_dev, out_dev, M, F, (hipStream_t)stream);
+}

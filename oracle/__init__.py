@@ -17,6 +17,10 @@ It implements, on the CPU and in fp64 where the format allows exactness:
   over the weights serves all lanes): ``y[m][n] = sum_k a[m][k] * w[n][k]``
   with exact fp64 products, ascending-k fp64 sums, and ``S = sum |a*w|``.
 
+* the SwiGLU step between gate_up and down (a reading of the shapes: the
+  fused gate_up matrix has N = 2 x the down matrix's K): for bf16 [gate | up]
+  halves, silu(g) * u = g * u / (1 + exp(-g)) in fp64, rounded once to bf16
+  (nearest, ties to even);
 * the top-k of the output head's logits ("Ignis" README, "Speculative
   decoding (DFlash2)": the drafter's top-k over the vocabulary, replaced by a
   row-split kernel with an identical answer): per row, the k largest values in
@@ -209,3 +213,49 @@ def topk(logits: np.ndarray, k: int):
         idx[m] = order[:k]
     vals = np.take_along_axis(x, idx.astype(np.int64), axis=1)
     return idx, vals
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """float64 -> bf16 bits (uint16), rounded once to nearest, ties to even
+    (no intermediate float32).  Overflow goes to infinity; NaN stays NaN."""
+    x = np.asarray(x, np.float64)
+    bits = x.view(np.uint64)
+    sign = (bits >> np.uint64(63)).astype(np.uint16) << np.uint16(15)
+    a = np.abs(x)
+    out = np.zeros(x.shape, np.uint16)
+    for i, (v, sg) in enumerate(zip(a.ravel(), sign.ravel())):
+        if np.isnan(v):
+            out.flat[i] = 0x7FC0
+            continue
+        if v == 0:
+            out.flat[i] = sg
+            continue
+        # the two bf16 magnitudes around v, by exhaustive comparison of the
+        # neighbouring exponents' grids: bf16 has 8 significant bits
+        e = int(np.frexp(v)[1]) - 1  # v = m 2^e, 1 <= m < 2, exactly
+        lo_e = max(e, -126)
+        step = 2.0 ** (lo_e - 7)           # spacing of the 8-bit significand grid
+        q = np.floor(v / step)
+        lo, hi = q * step, (q + 1) * step
+        if v - lo < hi - v:
+            r = lo
+        elif v - lo > hi - v:
+            r = hi
+        else:  # tie: the even significand
+            r = lo if int(q) % 2 == 0 else hi
+        r32 = np.float32(r) if r < 2.0 ** 128 else np.float32(np.inf)  # 2^128: overflow
+        out.flat[i] = sg | (int(r32.view(np.uint32)) >> 16)
+    return out
+
+
+def swiglu(gate_up_bits: np.ndarray) -> np.ndarray:
+    """bf16 bits [M][2F] -> bf16 bits [M][F]: silu(g) * u in fp64, g = first
+    half, u = second half, rounded once to bf16."""
+    gu = np.ascontiguousarray(gate_up_bits, dtype=np.uint16)
+    M, F2 = gu.shape
+    F = F2 // 2
+    x = (gu.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    g, u = x[:, :F], x[:, F:]
+    with np.errstate(over="ignore"):
+        y = g * u / (1.0 + np.exp(-g))
+    return bf16_round(y)

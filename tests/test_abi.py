@@ -239,6 +239,25 @@ def test_round_validation(nv):
         with pytest.raises(nv.Nvfp4Error) as e:
             nv.nvfp4_round_workspace_bytes([good], 9, mode=mode)
         assert e.value.message.startswith("max_M"), e.value.message
+    # chaining: SwiGLU of the previous output needs a previous bf16 matrix of N = 2 K,
+    # and only the per-matrix form takes it
+    gu = dict(good, K=256, N=64)
+    dn = dict(good, K=32, N=256, act_op=nv.ACT_SWIGLU_PREV)
+    assert nv.nvfp4_round_workspace_bytes([gu, dn], 8) >= 0
+    for layers, word in (([dn], "layers[0].act_op"), ([good, dn], "layers[1].act_op"),
+                         ([dict(gu, out_dtype=0), dn], "layers[1].act_op"),
+                         ([gu, dict(dn, act_op=7)], "layers[1].act_op")):
+        with pytest.raises(nv.Nvfp4Error) as e:
+            nv.nvfp4_round_workspace_bytes(layers, 8)
+        assert e.value.message.startswith(word), e.value.message
+    with pytest.raises(nv.Nvfp4Error) as e:
+        nv.nvfp4_round_workspace_bytes([gu, dn], 8, mode=nv.ROUND_CHAIN)
+    assert e.value.status == nv.EUNSUPPORTED
     L = nv.lib()
+    for args, word in (((FAKE, 0, 4, FAKE, None), "M"), ((FAKE, 2, 0, FAKE, None), "F"),
+                       ((None, 2, 4, FAKE, None), "gate_up"), ((FAKE, 2, 4, None, None), "out"),
+                       ((FAKE + 1, 2, 4, FAKE, None), "gate_up/out")):
+        assert L.nvfp4_swiglu(*args) == nv.EINVAL
+        assert nv.last_error().startswith(word), nv.last_error()
     assert L.nvfp4_round_run(None, 1, None) == nv.ESTATE
     assert nv.nvfp4_round_graph_nodes(None, 1) == 0

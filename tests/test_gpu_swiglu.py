@@ -1,0 +1,88 @@
+"""GPU parity of the SwiGLU step (bit for bit against the oracle) and of a
+round that chains gate_up -> SwiGLU -> down (against the same steps run as
+separate calls)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import dev, dev_bf16, host, pack, require_gpu, bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nv():
+    return require_gpu()
+
+
+def _gate_up_bits(M, F, seed):
+    """bf16 [M][2F]: N(0, 1) draws with special values planted."""
+    x = synth.activations(seed, 77, M, 2 * F)
+    rng = np.random.default_rng(seed)
+    special = np.array([0x0000, 0x8000, 0x4300, 0xC300, 0x0001, 0x8001, 0x42C8, 0xC2C8,
+                        0x3F80, 0xBF80, 0x7F7F, 0x0080], np.uint16)  # 0, -0, +-128, +-2^-133,
+    #                                                  +-100, +-1, the largest, the smallest normal
+    idx = rng.choice(x.size, min(x.size, 4 * len(special)), replace=False)
+    x.flat[idx] = np.resize(special, len(idx))
+    return x
+
+
+@pytest.mark.parametrize("M,F", [(1, 1), (3, 7), (8, 17408), (64, 1000), (5, 4096)])
+def test_swiglu_matches_oracle(nv, M, F):
+    import torch
+    gu = _gate_up_bits(M, F, M + F)
+    out = torch.full((M, F), -1, dtype=torch.int16, device="cuda")
+    nv.nvfp4_swiglu(dev_bf16(gu), M, F, out)
+    torch.cuda.synchronize()
+    got = host(out).view(np.uint16)
+    want = oracle.swiglu(gu)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, (bad[:3], got[tuple(bad[0])], want[tuple(bad[0])])
+
+
+def test_chained_mlp_round(nv):
+    """Two layers of x -> gate_up -> SwiGLU -> down, the down matrices reading
+    the round-made SwiGLU of the gate_up outputs; every replay (widths 1, 5, 8)
+    must equal the same steps run as separate calls, bit for bit."""
+    import torch
+    K, F = 512, 1024
+    specs, mats = [], []
+    for layer in range(2):
+        for j, (k, n) in enumerate(((K, 2 * F), (F, K))):
+            codes, scales = synth.random_planes(40 + layer, j, n, k)
+            t = 2e-3 if j == 0 else 5e-4
+            pw = pack(nv, dev(codes), dev(scales), k, n, t)
+            if j == 0:
+                act = dev_bf16(synth.activations(41 + layer, 0, 8, k))
+            else:
+                act = torch.zeros((8, k), dtype=torch.bfloat16, device="cuda")  # round-made
+            out = torch.empty((8, n), dtype=torch.bfloat16, device="cuda")
+            specs.append(dict(K=k, N=n, codes=pw.codes, scales=pw.scales, tensor_scale=t,
+                              act=act, out=out, out_dtype=nv.OUT_BF16,
+                              act_op=nv.ACT_SWIGLU_PREV if j == 1 else nv.ACT_INPUT))
+            mats.append(pw)
+    ws_bytes = nv.nvfp4_round_workspace_bytes(specs, 8)
+    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    plan = nv.nvfp4_round_create(specs, 8, ws, ws_bytes)
+    try:
+        for M in (1, 5, 8):
+            assert nv.nvfp4_round_graph_nodes(plan, M) == len(specs) + 2  # + two SwiGLU nodes
+            for s in specs:
+                s["out"].fill_(float("nan"))
+            nv.nvfp4_round_run(plan, M)
+            torch.cuda.synchronize()
+            for layer in range(2):
+                gu_s, dn_s = specs[2 * layer], specs[2 * layer + 1]
+                g_ref = torch.empty((M, 2 * F), dtype=torch.bfloat16, device="cuda")
+                nv.Gemm(M, K, 2 * F, nv.OUT_BF16)(mats[2 * layer], gu_s["act"][:M], g_ref)
+                h_ref = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+                nv.nvfp4_swiglu(g_ref, M, F, h_ref)
+                d_ref = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+                nv.Gemm(M, F, K, nv.OUT_BF16)(mats[2 * layer + 1], h_ref, d_ref)
+                torch.cuda.synchronize()
+                assert np.array_equal(bf16_bits(gu_s["out"][:M]), bf16_bits(g_ref)), (M, layer)
+                assert np.array_equal(bf16_bits(dn_s["act"][:M]), bf16_bits(h_ref)), (M, layer)
+                assert np.array_equal(bf16_bits(dn_s["out"][:M]), bf16_bits(d_ref)), (M, layer)
+    finally:
+        nv.nvfp4_round_destroy(plan)

@@ -9,6 +9,9 @@
   the nearest-value invariants on random N(0, 0.02) matrices.
 * GEMM: exact rational brute force (Python fractions over the golden/torch
   tables), a closed form, one-hot reconstruction, zero scales.
+* SwiGLU: the fp64 -> bf16 rounding against hand-worked cases
+  (tests/golden/bf16_rounding_cases.txt) and torch's float32 -> bfloat16
+  cast; silu against closed forms and the tanh form of the logistic function.
 * Top-k: hand-worked cases (tests/golden/topk_worked_cases.txt), numpy's
   first-occurrence argmax (k = 1) and stable argsort (k = V), and order and
   selection invariants on random rows with many ties.
@@ -378,3 +381,101 @@ def _topk_mutant(kind):
 def test_topk_planted_mistakes_fail_the_pins(golden_dir, kind):
     with pytest.raises(AssertionError):
         _topk_pins(_topk_mutant(kind), golden_dir)
+
+
+# ---- SwiGLU -------------------------------------------------------------------
+
+def _golden_bf16_rounding(golden_dir):
+    cases = []
+    with open(os.path.join(golden_dir, "bf16_rounding_cases.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            v, b = line.split()
+            cases.append((float.fromhex(v), int(b, 16)))
+    assert len(cases) >= 14
+    return cases
+
+
+def _bits_bf16(x):
+    """float32 array -> bf16 bits by truncation (exact for bf16 values)."""
+    return (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _swiglu_pins(bf16_round, swiglu, golden_dir):
+    for v, want in _golden_bf16_rounding(golden_dir):
+        got = int(bf16_round(np.array([v]))[0])
+        assert got == want, (v.hex(), hex(got), hex(want))
+    # torch rounds float32 -> bfloat16 to nearest-even; for float32 values the
+    # single rounding from fp64 must agree
+    rng = np.random.default_rng(11)
+    x32 = (rng.standard_normal(4000) * np.exp2(rng.integers(-30, 30, 4000))).astype(np.float32)
+    want = torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(bf16_round(x32.astype(np.float64)), want)
+    # silu: closed forms (g = 0 and u = 0 give zero; g = 100 makes the logistic
+    # factor 1 in fp64, so the result is bf16(g * u)) and the tanh form
+    # 1 / (1 + e^-g) = (1 + tanh(g / 2)) / 2, another library routine
+    F = 256
+    g = (rng.standard_normal(F) * 3).astype(np.float32)
+    u = (rng.standard_normal(F) * 2).astype(np.float32)
+    g[:4] = [0.0, -0.0, 100.0, -100.0]
+    u[4:6] = [0.0, -0.0]
+    gb, ub = _bits_bf16(g), _bits_bf16(u)
+    gu = np.concatenate([gb, ub])[None, :]
+    got = swiglu(gu)[0]
+    gd = (gb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ud = (ub.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert got[0] in (0x0000, 0x8000) and got[1] in (0x0000, 0x8000)
+    assert got[4] in (0x0000, 0x8000) and got[5] in (0x0000, 0x8000)
+    assert got[2] == bf16_round(np.array([gd[2] * ud[2]]))[0]
+    want = bf16_round(gd * ud * (1.0 + np.tanh(gd / 2.0)) / 2.0)
+    assert np.array_equal(got[6:], want[6:]), np.argwhere(got[6:] != want[6:])[:3]
+    # g = -100: the logistic factor is e^g to fp64 precision (another closed form)
+    assert got[3] == bf16_round(np.array([gd[3] * ud[3] * np.exp(gd[3])]))[0]
+
+
+def test_swiglu_pins(oracle_mod, golden_dir):
+    _swiglu_pins(oracle_mod.bf16_round, oracle_mod.swiglu, golden_dir)
+
+
+def _swiglu_mutant(oracle_mod, kind):
+    def rnd(x):
+        x = np.asarray(x, np.float64)
+        if kind == "round_via_fp32":
+            x32 = x.astype(np.float32)
+            return _bits_bf16(x32) + ((x32.view(np.uint32) & 0xFFFF) > 0x8000).astype(np.uint16) \
+                + (((x32.view(np.uint32) & 0xFFFF) == 0x8000) & (_bits_bf16(x32) & 1 == 1)).astype(np.uint16)
+        if kind == "ties_away":
+            out = oracle_mod.bf16_round(x)
+            a = np.abs(x)
+            for i, v in enumerate(a.ravel()):
+                if v == 0 or not np.isfinite(v):
+                    continue
+                e = int(np.frexp(v)[1]) - 1
+                step = 2.0 ** (max(e, -126) - 7)
+                q = np.floor(v / step)
+                if v - q * step == step / 2:
+                    r = np.float32((q + 1) * step)
+                    out.flat[i] = (out.flat[i] & 0x8000) | (int(r.view(np.uint32)) >> 16)
+            return out
+        return oracle_mod.bf16_round(x)
+
+    def swi(gu_bits):
+        gu = np.ascontiguousarray(gu_bits, dtype=np.uint16)
+        M, F2 = gu.shape
+        F = F2 // 2
+        x = (gu.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        g, u = x[:, :F], x[:, F:]
+        if kind == "halves_swapped":
+            g, u = u, g
+        with np.errstate(over="ignore"):
+            y = g * u / (1.0 + np.exp(g if kind == "exp_sign" else -g))
+        return rnd(y)
+    return rnd, swi
+
+
+@pytest.mark.parametrize("kind", ["round_via_fp32", "ties_away", "halves_swapped", "exp_sign"])
+def test_swiglu_planted_mistakes_fail_the_pins(oracle_mod, golden_dir, kind):
+    rnd, swi = _swiglu_mutant(oracle_mod, kind)
+    with pytest.raises(AssertionError):
+        _swiglu_pins(rnd, swi, golden_dir)
