@@ -38,13 +38,12 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 
 constexpr int kPBK = 64;          // K per stage
-constexpr int kPThreads = 512;    // 8 waves
+constexpr int kPWaves = 8;        // waves per workgroup: 2 x 4 of 128 x 64 outputs
+constexpr int kPThreads = kPWaves * 64;
 // s_waitcnt vmcnt(n) encodings (vmcnt in bits 3:0 and 15:14; expcnt and
 // lgkmcnt fields at their maxima do not wait).
 constexpr int vmcnt_enc(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 constexpr int kPWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
-// Loads per thread per stage: weights BN / 64 (BN / 128 lane slots, a code
-// load and a scale load each), activations BM / 64 copies.
 
 struct PrefillLds {
     __bf16 a[3][256 * kPBK];  // activations [row][k], swizzled segments: 3 stages
@@ -80,27 +79,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t prefill_rsrc(const void* base,
 // LDS: one direct-to-LDS load moves 8 rows of 128 bytes; lane i fills slot
 // i % 8 of row i / 8 with the segment that belongs there, (i % 8) ^ key(row).
 // The resource covers rows m0 .. M-1 (rows past M read zero); k past K reads
-// the next row (finite values; the weights past K are zero).  The 8 waves take
-// BM / 64 loads each; voff[i] is this lane's offset for load i.
-template <int BM>
+// the next row (finite values; the weights past K are zero).  The NW waves
+// take kL = BM / (8 NW) loads each; voff[i] is this lane's offset for load i.
+template <int BM, int NW>
 struct PrefillA {
+    static constexpr int kL = BM / (8 * NW);
     __amdgpu_buffer_rsrc_t rsrc;
-    int voff[BM / 64];
+    int voff[kL];
 
     __device__ __forceinline__ void init(const uint16_t* act, int M, int K, int m0, int wave,
                                          int lane) {
         rsrc = prefill_rsrc(act + (size_t)m0 * K, (size_t)(M - m0) * K * 2);
 #pragma unroll
-        for (int i = 0; i < BM / 64; ++i) {
-            const int r = (wave * (BM / 64) + i) * 8 + (lane >> 3);
+        for (int i = 0; i < kL; ++i) {
+            const int r = (wave * kL + i) * 8 + (lane >> 3);
             voff[i] = r * K * 2 + 16 * ((lane & 7) ^ swz_key(r));
         }
     }
 
     __device__ __forceinline__ void copy(__bf16* la, int kt, int wave) const {
 #pragma unroll
-        for (int i = 0; i < BM / 64; ++i) {
-            const int r0 = (wave * (BM / 64) + i) * 8;
+        for (int i = 0; i < kL; ++i) {
+            const int r0 = (wave * kL + i) * 8;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rsrc, (__attribute__((address_space(3))) void*)(la + r0 * kPBK), 16, voff[i],
                 kt * kPBK * 2, 0, 0);
@@ -114,9 +114,9 @@ struct PrefillA {
 // 2h+1 of 128-k chunk kb) plus bytes 2h, 2h+1 of its scale word.  The resources
 // start at the block's first column tile and end at the last real one, so
 // tiles past N read zero.
-template <int BN>
+template <int BN, int NW>
 struct PrefillB {
-    static constexpr int kB = BN / 16 * 64 / kPThreads;
+    static constexpr int kB = BN / 16 * 64 / (NW * 64);
     __amdgpu_buffer_rsrc_t rc, rs;
     int coff[kB], soff[kB];
 
@@ -129,7 +129,7 @@ struct PrefillB {
                           tiles * nsb * kScaleBytesPerSuper);
 #pragma unroll
         for (int i = 0; i < kB; ++i) {
-            const int u = threadIdx.x + kPThreads * i;
+            const int u = threadIdx.x + NW * 64 * i;
             const int t = u >> 6, ls = u & 63;
             const int col = ls & 15, p = (ls >> 4) >> 1;
             coff[i] = t * nsb * kCodeBytesPerSuper + ls * 16;
@@ -138,13 +138,13 @@ struct PrefillB {
     }
 };
 
-template <int BN>
+template <int BN, int NW>
 struct PStage {
-    static constexpr int kB = BN / 16 * 64 / kPThreads;
+    static constexpr int kB = BN / 16 * 64 / (NW * 64);
     u32x2 c[kB];
     uint32_t s[kB];
 
-    __device__ __forceinline__ void load(const PrefillB<BN>& B, int kt) {
+    __device__ __forceinline__ void load(const PrefillB<BN, NW>& B, int kt) {
         const int k0 = kt * kPBK;
         const int sb = k0 / kSuperK, kb = (k0 % kSuperK) / 128, h = (k0 % 128) / 64;
         const int cso = sb * kCodeBytesPerSuper + kb * 1024 + h * 8;
@@ -164,7 +164,7 @@ struct PStage {
     __device__ __forceinline__ void store_piece(__bf16* lb, int kt) const {
         constexpr int i = Q / 2, w = Q % 2;
         const int h = (kt * kPBK % 128) / 64;
-        const int u = threadIdx.x + kPThreads * i;
+        const int u = threadIdx.x + NW * 64 * i;
         const int ls = u & 63;
         const int col = (u >> 6) * 16 + (ls & 15), g = ls >> 4;
         const int sw = (int)(s[i] >> (16 * h));
@@ -176,7 +176,7 @@ struct PStage {
         const int h = (kt * kPBK % 128) / 64;
 #pragma unroll
         for (int i = 0; i < kB; ++i) {
-            const int u = threadIdx.x + kPThreads * i;
+            const int u = threadIdx.x + NW * 64 * i;
             const int ls = u & 63;
             const int col = (u >> 6) * 16 + (ls & 15), g = ls >> 4;
             const int sw = (int)(s[i] >> (16 * h));
@@ -195,27 +195,39 @@ struct PStage {
 // multiplies are issued the wave converts and stores a share of it while the
 // matrix cores work.  The operands of step ks + 1 are read before the
 // multiplies of step ks.
-template <int BM, int BN, int Q>
-__device__ __forceinline__ void prefill_store_share(const PStage<BN>& nx, __bf16* lbn, int ktn,
-                                                    int ks) {
-    constexpr int kPieces = 2 * PStage<BN>::kB;
+template <int BM, int BN, int NW, int Q>
+__device__ __forceinline__ void prefill_store_share(const PStage<BN, NW>& nx, __bf16* lbn,
+                                                    int ktn, int ks) {
+    constexpr int kPieces = 2 * PStage<BN, NW>::kB;
     // pieces ks * kPieces / 4 .. (ks + 1) * kPieces / 4 - 1
     if constexpr (Q < kPieces) {
         if (Q * 4 / kPieces == ks) nx.template store_piece<Q>(lbn, ktn);
     }
 }
 
-template <int BM, int BN>
-__device__ __forceinline__ void prefill_mma(f32x16 (&acc)[BM / 64][BN / 128], const __bf16* la,
-                                            const __bf16* lb, const PStage<BN>& nx, __bf16* lbn,
-                                            int ktn, int wm, int wn, int r32, int half) {
-    constexpr int TI = BM / 64, TJ = BN / 128;
+// NW waves as (NW / 4) x 4: wave (wm, wn) owns rows wm * BM / (NW / 4) and
+// columns wn * BN / 4, as TI x TJ MFMA tiles of 32 x 32.
+constexpr int ptiles_i(int BM, int NW) { return BM / (NW / 4) / 32; }
+constexpr int ptiles_j(int BN) { return BN / 4 / 32; }
+template <int BM, int BN, int NW>
+struct PTiles {
+    static constexpr int WM = NW / 4;
+    static constexpr int TI = ptiles_i(BM, NW), TJ = ptiles_j(BN);
+};
+
+template <int BM, int BN, int NW>
+__device__ __forceinline__ void prefill_mma(
+    f32x16 (&acc)[ptiles_i(BM, NW)][ptiles_j(BN)], const __bf16* la,
+    const __bf16* lb, const PStage<BN, NW>& nx, __bf16* lbn, int ktn, int wm, int wn, int r32,
+    int half) {
+    constexpr int TI = PTiles<BM, BN, NW>::TI, TJ = PTiles<BM, BN, NW>::TJ;
+    constexpr int WM = PTiles<BM, BN, NW>::WM;
     bf16x8 av[2][TI], bv[2][TJ];
     auto read = [&](int ks, int buf) {
         const int seg = 2 * ks + half;
 #pragma unroll
         for (int i = 0; i < TI; ++i)
-            av[buf][i] = *(const bf16x8*)(la + swz(wm * (BM / 2) + 32 * i + r32, seg));
+            av[buf][i] = *(const bf16x8*)(la + swz(wm * (BM / WM) + 32 * i + r32, seg));
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
             bv[buf][j] = *(const bf16x8*)(lb + swz(wn * (BN / 4) + 32 * j + r32, seg));
@@ -232,28 +244,32 @@ __device__ __forceinline__ void prefill_mma(f32x16 (&acc)[BM / 64][BN / 128], co
             for (int j = 0; j < TJ; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[buf][i], bv[buf][j],
                                                                     acc[i][j], 0, 0, 0);
-        prefill_store_share<BM, BN, 0>(nx, lbn, ktn, ks);
-        prefill_store_share<BM, BN, 1>(nx, lbn, ktn, ks);
-        prefill_store_share<BM, BN, 2>(nx, lbn, ktn, ks);
-        prefill_store_share<BM, BN, 3>(nx, lbn, ktn, ks);
+        prefill_store_share<BM, BN, NW, 0>(nx, lbn, ktn, ks);
+        prefill_store_share<BM, BN, NW, 1>(nx, lbn, ktn, ks);
+        prefill_store_share<BM, BN, NW, 2>(nx, lbn, ktn, ks);
+        prefill_store_share<BM, BN, NW, 3>(nx, lbn, ktn, ks);
     }
     __builtin_amdgcn_s_setprio(0);
 }
 
 // One BM x BN block tile over K stages kt0 .. kt1 - 1; wave w owns rows
-// (w / 4) * BM/2 and columns (w % 4) * BN/4, as (BM/64) x (BN/128) MFMA tiles
-// of 32 x 32.  With part == nullptr the tile covers all of K and stores
+// (w / 4) * BM / (NW / 4) and columns (w % 4) * BN/4, as TI x TJ MFMA tiles
+// of 32 x 32 (PTiles).  With part == nullptr the tile covers all of K and stores
 // acc * ts to out; otherwise it stores its raw accumulators to part (BM * BN
 // floats, in register order: float4 ((((w TI + i) TJ + j) 4 + r / 4) 64 +
 // lane) holds elements r .. r + 3 of lane's MFMA tile (i, j)).
-template <int BM, int BN, bool BF16>
+template <int BM, int BN, int NW, bool BF16>
 __device__ __forceinline__ void prefill_tile(PrefillLds& L, const uint8_t* __restrict__ codes,
                                              const uint8_t* __restrict__ scales,
                                              const uint16_t* __restrict__ act,
                                              void* __restrict__ out, float* __restrict__ part,
                                              float ts, int M, int K, int N, int nsb, int n_tiles,
                                              int m0, int n0, int kt0, int kt1) {
-    constexpr int TI = BM / 64, TJ = BN / 128;
+    constexpr int TI = PTiles<BM, BN, NW>::TI, TJ = PTiles<BM, BN, NW>::TJ;
+    constexpr int WM = PTiles<BM, BN, NW>::WM;
+    // loads per thread per stage: weights (a code and a scale load per lane
+    // slot) and activation copies
+    constexpr int kWL = 2 * PStage<BN, NW>::kB, kAL = PrefillA<BM, NW>::kL;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wm = wave >> 2, wn = wave & 3;
     const int nt0 = n0 / kTileN;
@@ -274,11 +290,11 @@ __device__ __forceinline__ void prefill_tile(PrefillLds& L, const uint8_t* __res
     // st1 alternately hold stages u + 1 and u + 2) and are dequantised into
     // two LDS buffers (stage u in buffer u % 2).  Stages past the end re-read
     // the last one into buffers nobody reads again.
-    PrefillA<BM> A;
+    PrefillA<BM, NW> A;
     A.init(act, M, K, m0, wave, lane);
-    PrefillB<BN> B;
+    PrefillB<BN, NW> B;
     B.init(codes, scales, nsb, n_tiles, nt0);
-    PStage<BN> st0, st1;
+    PStage<BN, NW> st0, st1;
     A.copy(L.a[0], at(0), wave);
     A.copy(L.a[1], at(1), wave);
     st0.load(B, at(0));
@@ -286,8 +302,8 @@ __device__ __forceinline__ void prefill_tile(PrefillLds& L, const uint8_t* __res
     st0.load(B, at(1));
     st1.load(B, at(2));
     // Outstanding, oldest first: the loads of stage 1 into st0 and of stage 2
-    // into st1 (BN / 64 each); the activation copies before them are complete.
-    __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * (BN / 64)));
+    // into st1 (kWL each); the activation copies before them are complete.
+    __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * kWL));
     __syncthreads();
 
     const int r32 = lane & 31, half = lane >> 5;
@@ -296,18 +312,18 @@ __device__ __forceinline__ void prefill_tile(PrefillLds& L, const uint8_t* __res
     // u + 1 interleaved, the weight loads of stage u + 3 (BN / 64 loads).
     // Before the barrier the copy of stage u + 1 (issued one stage earlier)
     // must have landed: the loads after it may still be in flight.
-    auto stage = [&](int u, PStage<BN>& next, int u_next) {
+    auto stage = [&](int u, PStage<BN, NW>& next, int u_next) {
         A.copy(L.a[(u + 2) % 3], at(u + 2), wave);
         __builtin_amdgcn_sched_barrier(0);
-        prefill_mma<BM, BN>(acc, L.a[u % 3], L.b[u & 1], next, L.b[(u + 1) & 1], at(u + 1), wm,
-                            wn, r32, half);
+        prefill_mma<BM, BN, NW>(acc, L.a[u % 3], L.b[u & 1], next, L.b[(u + 1) & 1], at(u + 1),
+                                wm, wn, r32, half);
         __builtin_amdgcn_sched_barrier(0);
         next.load(B, at(u_next));
         __builtin_amdgcn_sched_barrier(0);
         // Then the barrier, without a memory fence (a fence would also wait
         // for the copy of stage u + 2 just issued): this wave's LDS stores
         // are complete, and the compiler may not move memory accesses across.
-        __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * (BN / 64) + BM / 64));
+        __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * kWL + kAL));
         __builtin_amdgcn_s_waitcnt(kPWaitLgkm0);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
@@ -346,7 +362,7 @@ __device__ __forceinline__ void prefill_tile(PrefillLds& L, const uint8_t* __res
             const int n = n0 + wn * (BN / 4) + 32 * j + r32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * (BM / 2) + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+                const int m = m0 + wm * (BM / WM) + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
                 if (m < M && n < N) store_out<BF16>(out, (size_t)m * N + n, acc[i][j][r] * ts);
             }
         }
@@ -372,15 +388,15 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(
     const int b = blockIdx.x;
     if (b < pieces) {
         const int t = tiles - n_tail + b % n_tail, split = b / n_tail;
-        prefill_tile<kPTile, kPTile, BF16>(
+        prefill_tile<kPTile, kPTile, kPWaves, BF16>(
             L, codes, scales, act, out, part + (size_t)b * kPTileFloats, ts, M, K, N, nsb,
             n_tiles, (t % mblocks) * kPTile, (t / mblocks) * kPTile, split * nk / splits,
             (split + 1) * nk / splits);
     } else {
         const int t = b - pieces;
-        prefill_tile<kPTile, kPTile, BF16>(L, codes, scales, act, out, nullptr, ts, M, K, N,
-                                           nsb, n_tiles, (t % mblocks) * kPTile,
-                                           (t / mblocks) * kPTile, 0, nk);
+        prefill_tile<kPTile, kPTile, kPWaves, BF16>(L, codes, scales, act, out, nullptr, ts, M,
+                                                    K, N, nsb, n_tiles, (t % mblocks) * kPTile,
+                                                    (t / mblocks) * kPTile, 0, nk);
     }
 }
 
@@ -393,7 +409,9 @@ __global__ __launch_bounds__(kPReduceThreads) void prefill_reduce_kernel(
     const float* __restrict__ part, void* __restrict__ out, float ts, int M, int N, int mblocks,
     int tiles, int n_tail, int splits) {
     constexpr int kBlocksPerTile = kPTileFloats / 4 / kPReduceThreads;
-    constexpr int TI = kPTile / 64, TJ = kPTile / 128;
+    constexpr int TI = PTiles<kPTile, kPTile, kPWaves>::TI;
+    constexpr int TJ = PTiles<kPTile, kPTile, kPWaves>::TJ;
+    constexpr int WM = PTiles<kPTile, kPTile, kPWaves>::WM;
     const int q = blockIdx.x / kBlocksPerTile;
     const int p = (blockIdx.x % kBlocksPerTile) * kPReduceThreads + threadIdx.x;
     const int t = tiles - n_tail + q;
@@ -401,7 +419,7 @@ __global__ __launch_bounds__(kPReduceThreads) void prefill_reduce_kernel(
     const int wave = (p >> 8) / (TI * TJ);
     const int wm = wave >> 2, wn = wave & 3;
     const int n = (t / mblocks) * kPTile + wn * (kPTile / 4) + 32 * j + (lane & 31);
-    const int m = (t % mblocks) * kPTile + wm * (kPTile / 2) + 32 * i + 8 * rq + 4 * (lane >> 5);
+    const int m = (t % mblocks) * kPTile + wm * (kPTile / WM) + 32 * i + 8 * rq + 4 * (lane >> 5);
     if (n >= N || m >= M) return;
     // Batches of 8 pieces: every load of a batch is issued before any is
     // added (one memory round trip per batch).
