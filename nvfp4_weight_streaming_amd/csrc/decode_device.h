@@ -41,6 +41,16 @@ __device__ __forceinline__ void barrier_nofence() {
     asm volatile("" ::: "memory");
 }
 
+// Marks registers as redefined at this point (no instruction is emitted), so
+// that work on them cannot be hoisted above the wait that precedes it.  Used
+// after a window's final wait, where every load is complete: left free to move,
+// the conversions of a window that both sides of a branch compute were hoisted
+// above the branch, holding every converted value at once (190 registers).
+__device__ __forceinline__ void opaque(uint32_t& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void opaque(uint4& v) {
+    asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+
 // 8 E2M1 codes (4 bytes, low nibble first) -> 8 bf16 values in k order.
 __device__ __forceinline__ bf16x8 e2m1x8_to_bf16(uint32_t w) {
     bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
