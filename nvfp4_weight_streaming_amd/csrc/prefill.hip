@@ -296,15 +296,22 @@ __device__ __forceinline__ void prefill_tile(PrefillLds& L, const uint8_t* __res
     B.init(codes, scales, nsb, n_tiles, nt0);
     PStage<BN, NW> st0, st1;
     A.copy(L.a[0], at(0), wave);
-    A.copy(L.a[1], at(1), wave);
     st0.load(B, at(0));
+    __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));
     st0.store(L.b[0], at(0));
+    // The loads in flight when the loop starts are issued in the order the
+    // loop itself leaves them at the end of each stage (weights of stage 1,
+    // activation copy of stage 1, weights of stage 2), so the compiler's own
+    // waits inside the loop are exact: a different order here merged with
+    // the loop's at its head and made each stage wait for the next stage's
+    // weights before dequantising.
     st0.load(B, at(1));
+    A.copy(L.a[1], at(1), wave);
     st1.load(B, at(2));
-    // Outstanding, oldest first: the loads of stage 1 into st0 and of stage 2
-    // into st1 (kWL each); the activation copies before them are complete.
-    __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * kWL));
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(kPWaitLgkm0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 
     const int r32 = lane & 31, half = lane >> 5;
     // Per stage, issued in this order: activation copy of stage u + 2
