@@ -299,10 +299,9 @@ __global__ __launch_bounds__(WAVES * 64) void verify_kernel(
                                   l2_local, ng, split, nt, &s_last);
 }
 
-// Plan: the M <= 8 defaults (a window of one superblock per step, 2 windows
-// per slice, 6 for K >= 16384; no split for column groups that alone give
-// every compute unit 4 workgroups), with 8 waves per workgroup, and a
-// workspace for 16 G rows (G = ceil(min(max_M, 64) / 16)).
+// Plan: 8 waves per workgroup, slices as below (no split for column groups
+// that alone give every compute unit 4 workgroups), and a workspace for 16 G
+// rows (G = ceil(min(max_M, 64) / 16)).
 int make_verify_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, VerifyConfig* v) {
     v->enabled = max_M > NVFP4_DECODE_MAX_M;
     v->ws_off = 0;
@@ -321,11 +320,23 @@ int make_verify_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, Ve
         return set_error(NVFP4_EINVAL, "config.verify_windows: %d < 0", cfg->verify_windows);
     const int n_groups = (n_tiles + waves - 1) / waves;
     const int ng8 = round_up(n_groups, 8);
-    const bool wide = n_groups >= 4 * device_cus();
-    int windows = (cfg && cfg->verify_windows) ? cfg->verify_windows
-                  : wide                        ? nsb
-                  : nsb >= 32                   ? 6
-                                                : 2;
+    const int cus = device_cus();
+    const bool wide = n_groups >= 4 * cus;
+    // Fewer column groups than compute units: as many K slices as still give
+    // every workgroup its own compute unit.  A workgroup of 48-64 rows holds a
+    // compute unit's LDS alone, so a grid a little larger than the unit count
+    // runs a second, nearly empty round (qkv: 5 slices of 2 superblocks made
+    // 280 workgroups; 4 slices of 3 make 224, and measured 17% faster).
+    int windows;
+    if (cfg && cfg->verify_windows)
+        windows = cfg->verify_windows;
+    else if (wide)
+        windows = nsb;
+    else if (ng8 < cus) {
+        const int s = cus / ng8;
+        windows = (nsb + s - 1) / s;
+    } else
+        windows = nsb >= 32 ? 6 : 2;
     if (windows > nsb) windows = nsb;
     const int splits = (nsb + windows - 1) / windows;
     d.l2_local = splits > 1 ? xcd_mapping_verified() : 0;
