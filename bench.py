@@ -35,6 +35,8 @@ LAYERS = 64
 ROUND_SHAPES = (("qkv", 5120, 7168), ("o", 6144, 5120), ("gate_up", 5120, 34816),
                 ("down", 17408, 5120))
 METRIC = "NVFP4 decode GEMM GB/s & % HBM peak at M=1..8; 27B-class round ms"
+# The prefill chunk timed beside the round: M, K, N (bf16 out).
+PREFILL_SHAPE = (2048, 5120, 17408)
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_traffic.json")
@@ -336,7 +338,7 @@ def main():
     # Prefill chunk (M = 2048, K = 5120, N = 17408, bf16 out): the bf16 MFMA
     # kernel over dequantised tiles.
     import synth
-    PK, PN, PM = 5120, 17408, 2048
+    PM, PK, PN = PREFILL_SHAPE
     with torch.cuda.stream(stream):
         wp = synth.weights_device(0, 9001, PN, PK)
         ppw = nv.PackedWeight.quantize(wp, stream=stream)

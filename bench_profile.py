@@ -14,6 +14,11 @@ short text summaries to profiles/:
   decode_kernel_traffic.json        the same bytes for bench.py, tagged with a
                                     hash of the decode kernel sources (bench.py
                                     reports them only while the hash matches)
+  verify_topk_kernel_trace.md       the verify-width and top-k kernels (a whole
+                                    bench run with few steps)
+  prefill_m2048_mfma_counters.md    the prefill tile kernel's counted MFMA flops,
+                                    rate against the bf16 peak, clock and MFMA
+                                    busy fraction (one more counter pass)
 
 Usage (on a machine with the GPU):  python3 bench_profile.py --out DIR
 `--summarize-only` rebuilds the summaries from DIR without profiling.
@@ -43,7 +48,11 @@ PASSES = (
     ("fetch", ["--pmc", "FETCH_SIZE"], 300, BENCH_ARGS),
     ("write", ["--pmc", "WRITE_SIZE"], 300, BENCH_ARGS),
     ("trace_wide", ["--kernel-trace", "--stats"], 600, WIDE_ARGS),
+    # MFMA work and busy cycles of the prefill chunk (the same runs time it)
+    ("mfma", ["--pmc", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES",
+              "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"], 300, BENCH_ARGS),
 )
+MFMA_COUNTERS = PASSES[4][1][1:]
 VERIFY = "nvfp4::verify_kernel<"
 TOPK = "nvfp4::topk_level_kernel<"
 CALIB_BYTES = 1 << 30
@@ -239,6 +248,74 @@ def summarize(out, dest):
           % (dec_avg_us, roof["avg_launch_us"], fetch_b + write_b, algo))
     if os.path.isdir(os.path.join(out, "trace_wide")):
         summarize_wide(out, dest)
+    if os.path.isdir(os.path.join(out, "mfma")):
+        summarize_mfma(out, dest)
+
+
+def summarize_mfma(out, dest):
+    """prefill_m2048_mfma_counters.md: the prefill tile kernel's MFMA work from
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 (units of 512 flops), checked against the
+    algorithmic 2 M K N, and its rate over the kernel-trace duration against
+    the 2.5 PFLOP/s bf16 peak; MFMA busy cycles as read."""
+    rows = list(csv.DictReader(open(find_csv(os.path.join(out, "mfma"),
+                                             "counter_collection.csv"))))
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    name = {}
+    for r in rows:
+        k = int(r["Dispatch_Id"])
+        per[k][r["Counter_Name"]] += float(r["Counter_Value"])
+        name[k] = r["Kernel_Name"]
+    ids = sorted(k for k in per if PREFILL in name[k])
+    avg = {c: sum(per[k][c] for k in ids) / len(ids) for c in MFMA_COUNTERS}
+    trace = list(csv.DictReader(open(find_csv(os.path.join(out, "trace"), "kernel_trace.csv"))))
+    durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace
+            if PREFILL in r["Kernel_Name"]]
+    us = sum(durs) / len(durs) / 1e3
+    M, K, N = bench.PREFILL_SHAPE
+    algo = 2.0 * M * K * N
+    flops = avg["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+    md = ["# Prefill chunk (M = %d, K = %d, N = %d): MFMA counters\n" % (M, K, N)]
+    md.append("Commands (from the repository root, with `TMPDIR=/tmp`, run in /tmp), each a run "
+              "of its own via `python3 bench_profile.py --out OUT`:\n")
+    md.append("    " + shown(rocprof_cmd(PASSES[4][1], "OUT/mfma")))
+    md.append("    " + shown(rocprof_cmd(PASSES[0][1], "OUT/trace")) + "\n")
+    md.append("Counters per dispatch of the tile kernel (`%s...>`), summed over the "
+              "device, averaged over %d dispatches:\n" % (PREFILL, len(ids)))
+    md.append("| counter | value |")
+    md.append("|---|---|")
+    for c in MFMA_COUNTERS:
+        md.append("| %s | %.0f |" % (c, avg[c]))
+    md.append("\n| figure | value |")
+    md.append("|---|---|")
+    md.append("| MFMA flops (MOPS_BF16 x 512) | %.4g |" % flops)
+    md.append("| algorithmic flops 2 M K N | %.4g |" % algo)
+    md.append("| counted / algorithmic | %.4f |" % (flops / algo))
+    md.append("| tile kernel, kernel-trace average (us) | %.2f |" % us)
+    md.append("| achieved bf16 MFMA rate (counted flops / duration, TFLOP/s) | %.1f |"
+              % (flops / us / 1e6))
+    md.append("| fraction of the 2.5 PFLOP/s dense bf16 peak | %.3f |" % (flops / us / 1e6 / 2500))
+    # device facts from the profiler's own agent table
+    agent = [r for r in csv.DictReader(open(find_csv(os.path.join(out, "mfma"),
+                                                     "agent_info.csv")))
+             if r.get("Name", "").startswith("gfx")][0]
+    xcc, simds = int(agent["Num_Xcc"]), int(agent["Simd_Count"])
+    clk_ghz = avg["GRBM_GUI_ACTIVE"] / xcc / (us * 1e3)
+    busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (avg["GRBM_GUI_ACTIVE"] / xcc * simds)
+    md.append("| clock while the kernel ran (GRBM_GUI_ACTIVE / %d XCDs / duration, GHz) | %.3f |"
+              % (xcc, clk_ghz))
+    md.append("| MFMA pipes busy: SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / %d x %d SIMDs) "
+              "| %.3f |\n" % (xcc, simds, busy))
+    md.append("SQ_VALU_MFMA_BUSY_CYCLES is the sum over SIMDs of cycles with an MFMA in "
+              "flight: here exactly 32 per `v_mfma_f32_32x32x16_bf16` (MOPS / 2). The peak "
+              "of 2.5 PFLOP/s assumes %d MHz; the clock counted during this kernel is lower, "
+              "so the busy fraction at the running clock exceeds the fraction of peak.\n"
+              % int(agent["Max_Engine_Clk_Fcompute"]))
+    md.append("The tile kernel excludes the K-piece sum kernel (`%s...>`), which issues no "
+              "MFMA.\n" % PREFILL_SUM)
+    with open(os.path.join(dest, "prefill_m2048_mfma_counters.md"), "w") as f:
+        f.write("\n".join(md))
+    print("prefill: counted MFMA flops %.4g vs algorithmic %.4g; %.1f TFLOP/s over %.2f us"
+          % (flops, algo, flops / us / 1e6, us), flush=True)
 
 
 def summarize_wide(out, dest):
