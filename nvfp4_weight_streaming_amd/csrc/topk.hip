@@ -22,7 +22,9 @@
 // held it shifts its list.  Level 0 reads the logits and writes k candidate
 // keys per unit; while a row has more than one unit of candidates, the next
 // level does the same over them.  The last level writes the indices and
-// re-reads the values from the logits (bit for bit).
+// re-reads the values from the logits (bit for bit).  For k <= 8 and at most
+// 256 units, one wave per row merges level 0's sorted runs instead of
+// further levels (topk_merge_kernel).
 #include "common.h"
 
 namespace nvfp4 {
@@ -162,6 +164,62 @@ __global__ __launch_bounds__(kTopkThreads) void topk_level_kernel(
     }
 }
 
+// The levels after the first, for k <= 8 and at most 256 units: a row's
+// candidates are then u0 runs of k keys, each already sorted descending (lane
+// r of a unit keeps its round-r key), and one wave per row merges them into
+// the answer in k rounds, with no sort: lane l owns runs l, l + 64, l + 128
+// and l + 192, its head is the largest current key of its runs, and each
+// round outputs the wave's largest head and advances the run that held it.
+// One launch instead of one or two further levels, each of which sorted its
+// units again.
+constexpr int kMergeRuns = 4;  // runs per lane
+constexpr int kMergeMaxK = 8;
+__global__ __launch_bounds__(64) void topk_merge_kernel(const float* __restrict__ logits, int ld,
+                                                        const u64* __restrict__ in_keys,
+                                                        int units, int k,
+                                                        int* __restrict__ idx_out,
+                                                        float* __restrict__ val_out) {
+    const int lane = threadIdx.x, m = blockIdx.x;
+    // All loads at once: clamped addresses, runs past `units` and keys past
+    // k masked after.
+    u64 x[kMergeRuns][kMergeMaxK];
+#pragma unroll
+    for (int r = 0; r < kMergeRuns; ++r)
+#pragma unroll
+        for (int j = 0; j < kMergeMaxK; ++j) {
+            const int run = min(lane + 64 * r, units - 1), jj = min(j, k - 1);
+            x[r][j] = in_keys[((size_t)m * units + run) * k + jj];
+        }
+#pragma unroll
+    for (int r = 0; r < kMergeRuns; ++r)
+#pragma unroll
+        for (int j = 0; j < kMergeMaxK; ++j)
+            x[r][j] = (lane + 64 * r < units && j < k) ? x[r][j] : 0;
+    int taken[kMergeRuns] = {0, 0, 0, 0};
+    u64 kept = 0;
+    for (int t = 0; t < k; ++t) {
+        u64 h[kMergeRuns];
+#pragma unroll
+        for (int r = 0; r < kMergeRuns; ++r) {
+            u64 v = 0;  // 0 once the run is exhausted
+#pragma unroll
+            for (int j = 0; j < kMergeMaxK; ++j) v = taken[r] == j ? x[r][j] : v;
+            h[r] = v;
+        }
+        const u64 top = wave_max64(max64(max64(h[0], h[1]), max64(h[2], h[3])));
+        kept = lane == t ? top : kept;
+        // keys are distinct: exactly one run of one lane held `top`
+#pragma unroll
+        for (int r = 0; r < kMergeRuns; ++r) taken[r] += h[r] == top ? 1 : 0;
+    }
+    if (lane < k) {
+        // the row has at least k elements, so kept is a real key
+        const int i = (int)~(unsigned int)(kept & 0xFFFFFFFFu);
+        idx_out[(size_t)m * k + lane] = i;
+        val_out[(size_t)m * k + lane] = logits[(size_t)m * ld + i];
+    }
+}
+
 int topk_levels(int V, int k, int* units0) {
     int n = V, levels = 0, u0 = 0;
     do {
@@ -228,6 +286,12 @@ int nvfp4_topk(const float* logits_dev, int M, int V, int ld, int k, int* idx_de
     hipLaunchKernelGGL((topk_level_kernel<true, false>), dim3(blocks(u0), M), block, 0, s,
                        logits_dev, ld, nullptr, V, k, u0, buf[0], nullptr, nullptr);
     NVFP4_HIP(hipGetLastError());
+    if (k <= kMergeMaxK && u0 <= 64 * kMergeRuns) {
+        hipLaunchKernelGGL(topk_merge_kernel, dim3(M), dim3(64), 0, s, logits_dev, ld, buf[0], u0,
+                           k, idx_dev, val_dev);
+        NVFP4_HIP(hipGetLastError());
+        return NVFP4_OK;
+    }
     int n = u0 * k, cur = 0;
     for (int l = 1; l < levels; ++l) {
         const int u = (n + kTopkUnit - 1) / kTopkUnit;

@@ -55,6 +55,30 @@ def test_topk_matches_oracle(nv, M, V, k, ties):
     _check(x, k, got_idx, got_val, "topk %r ties=%s" % ((M, V, k), ties))
 
 
+@pytest.mark.parametrize("M,V,k", [(2, 262144, 8), (2, 262145, 8), (3, 65536, 2)])
+def test_topk_run_merge_bounds(nv, M, V, k):
+    """After the first level, k <= 8 rows of at most 256 candidate runs are
+    merged by one wave (4 runs per lane): exactly 256 runs, 257 (the level
+    path), and a small k."""
+    x = synth.logits(5, V + k, M, V, ties=True)
+    got_idx, got_val = _run(nv, x, k)
+    _check(x, k, got_idx, got_val, "merge bounds %r" % ((M, V, k),))
+
+
+@pytest.mark.parametrize("k", [1, 5, 8])
+def test_topk_all_winners_in_one_run(nv, k):
+    """The k largest logits all in one 1024-entry unit (one candidate run
+    supplies every output, so it is exhausted), with an equal-valued pair
+    across two units for the last place."""
+    M, V = 3, 152064
+    x = synth.logits(6, 77 + k, M, V)
+    for m in range(M):
+        x[m, 5000:5000 + k] = 1000.0 + np.arange(k, dtype=np.float32)[::-1] * (m + 1)
+        x[m, 90000] = x[m, 5000 + k - 1]  # ties with the k-th value, larger index
+    got_idx, got_val = _run(nv, x, k)
+    _check(x, k, got_idx, got_val, "one run k=%d" % k)
+
+
 @pytest.mark.parametrize("M,V,ld,k", [(3, 5000, 5008, 5), (2, 100, 131, 64), (2, 64, 64, 64)])
 def test_topk_strided_rows(nv, M, V, ld, k):
     x = synth.logits(4, V + ld, M, V, ties=True)
