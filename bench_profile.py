@@ -54,7 +54,7 @@ PASSES = (
 )
 MFMA_COUNTERS = PASSES[4][1][1:]
 VERIFY = "nvfp4::verify_kernel<"
-TOPK = "nvfp4::topk_level_kernel<"
+TOPK = "nvfp4::topk_"  # level and merge kernels
 CALIB_BYTES = 1 << 30
 DECODE = "nvfp4::decode_"  # decode_kernel< and decode_window_kernel<
 PREFILL = "nvfp4::prefill_kernel<"
