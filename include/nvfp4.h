@@ -135,8 +135,8 @@ typedef struct nvfp4_gemm_config {
     int windows; /* SPLITK: windows of `chunks` superblocks per K slice; above 1 a
                     wave streams its slice, issuing the next window's loads
                     before computing the current one (0 or 1: one window) */
-    int verify_waves;   /* verify widths (8 < M <= 64): waves per workgroup, 8 or
-                           16 (0: by shape) */
+    int verify_waves;   /* verify widths (8 < M <= 64): waves per workgroup, 4, 8
+                           or 16 (0: 4 up to 48 rows, 8 above) */
     int verify_windows; /* verify widths: superblocks per K slice (0: by shape) */
 } nvfp4_gemm_config;
 

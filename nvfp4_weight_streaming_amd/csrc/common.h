@@ -66,7 +66,8 @@ struct StreamConfig {
 struct VerifyConfig {
     int enabled;   // max_M > 8
     int rows;      // rows the workspace holds: ceil(min(max_M, 64) / 16) * 16
-    DecodeConfig d;
+    DecodeConfig g[2];  // launch config for up to 48 rows (G <= 3) and for 49..64 (G = 4)
+    DecodeConfig d;     // workspace envelope of both: counter and partial areas, ws_bytes
     size_t ws_off; // offset of its counters and partials in the plan's workspace
 };
 

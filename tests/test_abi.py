@@ -127,7 +127,8 @@ def test_gemm_config_validation(nv):
 
 
 def test_verify_width_config(nv):
-    for bad, word in ((dict(verify_waves=4), "config.verify_waves"),
+    for bad, word in ((dict(verify_waves=2), "config.verify_waves"),
+                      (dict(verify_waves=32), "config.verify_waves"),
                       (dict(verify_windows=-1), "config.verify_windows")):
         with pytest.raises(nv.Nvfp4Error) as e:
             nv.nvfp4_gemm_create(64, 5120, 5120, 1, **bad)

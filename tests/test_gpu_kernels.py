@@ -325,8 +325,9 @@ def test_verify_width_ragged(nv, M, K, N, bf16):
 
 @pytest.mark.parametrize("M,K,N", [(40, 5136, 515), (64, 3072, 300), (20, 12288, 70)])
 @pytest.mark.parametrize("cfg", [dict(verify_waves=16), dict(verify_windows=3),
-                                 dict(verify_waves=16, verify_windows=1)],
-                         ids=["w16", "s3", "w16s1"])
+                                 dict(verify_waves=16, verify_windows=1),
+                                 dict(verify_waves=8), dict(verify_waves=4, verify_windows=2)],
+                         ids=["w16", "s3", "w16s1", "w8", "w4s2"])
 def test_verify_width_configs(nv, M, K, N, cfg):
     """Non-default verify-width plans: 16 waves per workgroup, other slice
     lengths (ragged last slice, one superblock per slice)."""
