@@ -30,7 +30,7 @@
 namespace nvfp4 {
 
 constexpr int kVerifyWavesUpTo48 = 4;   // G <= 3
-constexpr int kVerifyWavesAbove48 = 8;  // G = 4
+constexpr int kVerifyWavesAbove48 = 8;  // G = 4, many column groups
 
 // End of a workgroup: outputs (one slice) or the split-K hand-off (several).
 // acc[gi][j] holds row 16 gi + 4 (lane / 16) + j, column lane % 16 of the
@@ -342,10 +342,10 @@ static void verify_launch_config(int n_tiles, int nsb, int waves, int rows,
     d.ws_bytes = d.counter_bytes + d.partial_bytes;
 }
 
-// Plan: 4 waves per workgroup up to 48 rows, 8 for 49..64 rows (measured over
-// the 64-layer round against 8 throughout: M = 16 -7.6%, M = 40 -3%, M = 64
-// +4.5% with 4); both launch configurations share one workspace area sized
-// for the larger of each part.
+// Plan: 4 waves per workgroup (measured over the 64-layer round against 8
+// throughout: M = 16 -7.6%, M = 40 -3%), except 8 for 49..64 rows when the
+// column groups outnumber the compute units; both launch configurations share
+// one workspace area sized for the larger of each part.
 int make_verify_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, VerifyConfig* v) {
     v->enabled = max_M > NVFP4_DECODE_MAX_M;
     v->ws_off = 0;
@@ -363,8 +363,13 @@ int make_verify_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, Ve
         return set_error(NVFP4_EINVAL, "config.verify_windows: %d < 0", cfg->verify_windows);
     verify_launch_config(n_tiles, nsb, forced ? forced : kVerifyWavesUpTo48, v->rows, cfg,
                          v->g[0]);
-    verify_launch_config(n_tiles, nsb, forced ? forced : kVerifyWavesAbove48, v->rows, cfg,
-                         v->g[1]);
+    // 49..64 rows: 4 waves too, unless the column groups of 4 tiles outnumber
+    // the compute units (gate_up: 8 waves, 7% faster there; qkv, o and down
+    // are 12%, 9% and 3% faster with 4)
+    const bool many = round_up((n_tiles + 3) / 4, 8) >= device_cus();
+    verify_launch_config(n_tiles, nsb,
+                         forced ? forced : many ? kVerifyWavesAbove48 : kVerifyWavesUpTo48,
+                         v->rows, cfg, v->g[1]);
     DecodeConfig& d = v->d;
     d.counter_bytes = std::max(v->g[0].counter_bytes, v->g[1].counter_bytes);
     d.partial_bytes = std::max(v->g[0].partial_bytes, v->g[1].partial_bytes);
