@@ -111,8 +111,10 @@ __device__ __forceinline__ void verify_finish(const f32x4 (&acc)[G], void* __res
 
 // Window length (in 128-k chunks) for G row groups: with 48 or 64 rows a
 // superblock's activations take 50-66 KiB of LDS per buffer, so the window is
-// half a superblock and two workgroups fit on a compute unit.
-constexpr int verify_kbw(int G) { return G >= 3 ? 2 : 4; }
+// half a superblock and two workgroups fit on a compute unit.  At 32 rows the
+// half-superblock window measured 6% faster over the round (more workgroups
+// per compute unit); at 16 rows the whole superblock is 9% faster.
+constexpr int verify_kbw(int G) { return G >= 2 ? 2 : 4; }
 
 // Weights of one window: KBW code chunks (16 B per lane each, 4 MFMA steps
 // apiece) and their KBW scale words (one E4M3 byte per step).
