@@ -171,8 +171,11 @@ def gemm(act_bits: np.ndarray, codes: np.ndarray, scales: np.ndarray, t: float,
 
 
 def dequantize(codes: np.ndarray, scales: np.ndarray, t: float) -> np.ndarray:
-    """The exact dequantised matrix w[n][k] (fp64) via the GEMM with one-hot
-    activations would be slow; this is the element-wise definition instead."""
+    """The dequantised matrix, element by element, in fp64:
+    w[n][k] = E2M1(code of k) * E4M3(scale of block k // 16) * t, with the code
+    of k in the low nibble of byte k // 2 for even k and in the high nibble
+    for odd k ("Models and artifacts", "The artifact": 4-bit values with one
+    scale per 16).  Exact: at most 2 + 4 + 24 significant bits."""
     N = codes.shape[0]
     K = codes.shape[1] * 2
     lib = _load()
@@ -194,7 +197,9 @@ def tolerance(S: np.ndarray) -> np.ndarray:
 
 def tolerance_bf16(y: np.ndarray, S: np.ndarray) -> np.ndarray:
     """Bound for outputs stored as bf16: the fp32 bound before the final
-    rounding plus half a bf16 ulp of the (bounded) value."""
+    rounding plus half a bf16 ulp of the (bounded) value.  bf16 has 8
+    significant bits, so its round-to-nearest store moves a value by at most
+    2^-8 of its magnitude (at the bottom of a binade)."""
     tol = np.ldexp(S, -16)
     return tol + np.ldexp(np.abs(y) + tol, -8)
 

@@ -283,6 +283,88 @@ def test_gemm_zero_scales_give_zero(oracle_mod):
     assert not y.any() and not S.any()
 
 
+# ---- dequantisation -------------------------------------------------------------
+
+def _dequant_pins(dequant, oracle_mod, golden_dir):
+    """w[n][k] element-wise against (1) the exact value from the golden E2M1
+    table, torch's E4M3 decoder and the canonical nibble order (low nibble =
+    even k), and (2) the oracle GEMM with one-hot bf16 activation rows (row k
+    of the identity returns column k of w, one exact product per output).
+    Returns False on the first mismatch."""
+    g = _golden_e2m1(golden_dir)
+    e4 = _torch_e4m3_table()
+    for seed, (K, N) in enumerate([(16, 1), (64, 6), (256, 9), (48, 48), (512, 3)]):
+        codes, scales = synth.random_planes(60 + seed, 8, N, K)
+        t = float(np.float32(np.random.default_rng(seed).uniform(1e-4, 3.0)))
+        w = np.asarray(dequant(codes, scales, t))
+        if w.shape != (N, K):
+            return False
+        for n in range(N):
+            for k in range(K):
+                byte = int(codes[n, k // 2])
+                c = (byte >> 4) if (k & 1) else (byte & 15)
+                exact = Fraction(g[c]) * Fraction(float(e4[int(scales[n, k // 16])])) * Fraction(t)
+                if Fraction(float(w[n, k])) != exact:
+                    return False
+        eye = synth._to_bf16_bits(np.eye(K, dtype=np.float32))
+        y, _ = oracle_mod.gemm(eye, codes, scales, t, threads=2)
+        if not np.array_equal(w, y.T):
+            return False
+    return True
+
+
+def test_dequantize_pins(oracle_mod, golden_dir):
+    assert _dequant_pins(oracle_mod.dequantize, oracle_mod, golden_dir)
+
+
+def _dequant_tiled(oracle_mod, codes, scales, t):
+    """oracle.dequantize with one planted mistake: the block scales laid along
+    K by tiling the row of scales instead of repeating each one 16 times."""
+    N, K = codes.shape[0], codes.shape[1] * 2
+    e2 = np.array([oracle_mod.e2m1_value(c) for c in range(16)])
+    e4 = np.array([oracle_mod.e4m3_value(b) for b in range(256)])
+    c = np.empty((N, K), np.int64)
+    c[:, 0::2] = codes & 15
+    c[:, 1::2] = codes >> 4
+    s = np.tile(scales.astype(np.int64), (1, 16))
+    return e2[c] * e4[s] * float(t)
+
+
+DEQUANT_MUTANTS = {
+    "nibble_order": lambda o, c, s, t: o.dequantize(_swap_nibbles(c), s, t),
+    "block_shift": lambda o, c, s, t: o.dequantize(c, np.roll(s, 1, axis=1), t),
+    "scales_tiled": _dequant_tiled,
+    "sign_ignored": lambda o, c, s, t: o.dequantize((c & 0x77).astype(np.uint8), s, t),
+    "no_tensor_scale": lambda o, c, s, t: o.dequantize(c, s, 1.0),
+    "transposed": lambda o, c, s, t: o.dequantize(c, s, t).T,
+}
+
+
+@pytest.mark.parametrize("name", sorted(DEQUANT_MUTANTS))
+def test_dequantize_planted_mistakes_fail_the_pins(oracle_mod, golden_dir, name):
+    mutant = DEQUANT_MUTANTS[name]
+    assert not _dequant_pins(lambda c, s, t: mutant(oracle_mod, c, s, t), oracle_mod, golden_dir)
+
+
+# ---- acceptance bounds ------------------------------------------------------------
+
+def test_tolerance_bounds(oracle_mod):
+    """tolerance(S) is 2^-16 S.  tolerance_bf16(y, 0) admits the bf16 store of
+    any value (the oracle's pinned fp64 -> bf16 rounding), including a tie at
+    the bottom of a binade (1 + 2^-8 rounds to 1: error 2^-8 of the value),
+    which a 2^-9 allowance would reject."""
+    S = np.array([0.0, 1.0, 3.5e-3, 65.0])
+    assert np.array_equal(oracle_mod.tolerance(S), S / 65536.0)
+    rng = np.random.default_rng(11)
+    y = np.concatenate([rng.standard_normal(2000) * 10.0 ** rng.uniform(-6, 6, 2000),
+                        [1.0 + 2.0 ** -8, -(1.0 + 2.0 ** -8), 2.0 ** -126 * 1.5]])
+    b = oracle_mod.bf16_round(y)
+    stored = (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    err = np.abs(stored - y)
+    assert np.all(err <= oracle_mod.tolerance_bf16(y, np.zeros_like(y)))
+    assert err[-3] > np.ldexp(abs(y[-3]), -9)
+
+
 # ---- planted mistakes must be caught ----------------------------------------
 
 def _swap_nibbles(codes):
