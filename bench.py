@@ -3,7 +3,10 @@
 One step = one replay of the 27B-class decode round: 64 layers x {qkv
 5120x7168, o 6144x5120, gate_up 5120x34816, down 17408x5120} (K x N), every
 matrix streamed once for M lanes, captured in one HIP graph per width.  The
-headline runs M = 8 lanes; the same run also times widths 1..8.
+headline runs M = 8 lanes; the same run also times widths 1..8, the other
+workloads of the same path (single projection, output head, prefill chunk,
+verify widths, top-k, the chained MLP) and a plain streaming read of the same
+bytes (the achievable rate).
 
 Prints one JSON line (rank 0):
   value        = algorithmic bytes of the round (NVFP4 weights + bf16
@@ -11,9 +14,10 @@ Prints one JSON line (rank 0):
   roofline     = the decode kernel: average algorithmic bytes per launch over
                  the round's matrices / average launch duration (the timed
                  region's HIP event time over the round's launches) against
-                 the MI355X HBM peak of 8 TB/s
-  cpu_baseline = the CPU oracle timed on the host's cores on a bounded sample
-                 of the same workload (see cpu_baseline() below)
+                 the MI355X HBM peak of 8 TB/s; `achievable` beside it is a
+                 plain streaming read of the same weight bytes, timed here
+  cpu_baseline = the CPU oracle timed on the host's cores on bounded samples
+                 of the workloads (see cpu_baseline() below)
 
 Inputs are synthetic (seeded N(0, 0.02) fp32 weights quantised on the GPU,
 N(0, 1) bf16 activations) and resident in HBM before the timed region.
@@ -31,12 +35,21 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
 LAYERS = 64
 ROUND_SHAPES = (("qkv", 5120, 7168), ("o", 6144, 5120), ("gate_up", 5120, 34816),
                 ("down", 17408, 5120))
 METRIC = "NVFP4 decode GEMM GB/s & % HBM peak at M=1..8; 27B-class round ms"
 # The prefill chunk timed beside the round: M, K, N (bf16 out).
 PREFILL_SHAPE = (2048, 5120, 17408)
+# The single-projection config: K = N = 5120, bf16 out, widths 1, 2, 4, 8,
+# over this many distinct weight copies chained in one graph (0.94 GB, well
+# above the 256 MB Infinity Cache, so every call streams from HBM).
+PROJ_K = PROJ_N = 5120
+PROJ_COPIES = 64
+# The output head: M = 8, K = 5120, N = 152064, fp32 logits; two weight copies
+# alternate so consecutive calls never find their weights in a cache.
+HEAD_K, HEAD_N = 5120, 152064
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_traffic.json")
@@ -71,47 +84,52 @@ def weight_bytes(K, N):
     return K * N // 2 + K * N // 16
 
 
+def gemm_bytes(M, K, N, out_bytes=2):
+    """Algorithmic bytes of one GEMM: weights once, bf16 activations in, outputs."""
+    return weight_bytes(K, N) + M * K * 2 + M * N * out_bytes
+
+
 def round_bytes(M, layers=LAYERS):
     """Algorithmic bytes of one round: weights once, activations in and bf16
     outputs once."""
-    b = 0
-    for _, K, N in ROUND_SHAPES:
-        b += weight_bytes(K, N) + M * K * 2 + M * N * 2
-    return b * layers
+    return sum(gemm_bytes(M, K, N) for _, K, N in ROUND_SHAPES) * layers
 
 
-def build_round(nv, seed=0, layers=LAYERS, max_M=8, log=None):
-    """Generate, quantise and pack every matrix of the round on the GPU.
-    Returns (round spec list, buffers kept alive, tensor scales)."""
+def build_round(nv, seed=0, layers=LAYERS, max_M=8, log=None, shapes=ROUND_SHAPES):
+    """Generate, quantise and pack every matrix of the round on the GPU (all
+    packed planes in one arena, in round order).  Returns (round spec list,
+    buffers kept alive; keep[0] is the arena)."""
     import torch
     import synth
     specs, keep = [], []
     total = sum(nv.nvfp4_packed_code_bytes(K, N) + nv.nvfp4_packed_scale_bytes(K, N)
-                for _, K, N in ROUND_SHAPES) * layers
+                for _, K, N in shapes) * layers
     arena = torch.empty(total, dtype=torch.uint8, device="cuda")
     keep.append(arena)
     off = 0
     qws = torch.empty(nv.nvfp4_quantize_workspace_bytes(), dtype=torch.uint8, device="cuda")
-    ts_dev = torch.empty(layers * len(ROUND_SHAPES), dtype=torch.float32, device="cuda")
+    ts_dev = torch.empty(layers * len(shapes), dtype=torch.float32, device="cuda")
     t0 = time.time()
     for layer in range(layers):
-        for j, (name, K, N) in enumerate(ROUND_SHAPES):
-            idx = layer * len(ROUND_SHAPES) + j
-            w = synth.weights_device(seed, synth.stream_id(layer, name), N, K)
+        for j, (name, K, N) in enumerate(shapes):
+            idx = layer * len(shapes) + j
+            sid = synth.stream_id(layer, name) if name in synth.PROJECTIONS else 5000 + idx
+            w = synth.weights_device(seed, sid, N, K)
             codes = torch.empty((N, K // 2), dtype=torch.uint8, device="cuda")
             scales = torch.empty((N, K // 16), dtype=torch.uint8, device="cuda")
             nv.nvfp4_quantize(w, K, N, codes, scales, ts_dev[idx:idx + 1], qws)
             cb, sb = nv.nvfp4_packed_code_bytes(K, N), nv.nvfp4_packed_scale_bytes(K, N)
             cpk = arena[off:off + cb]
             spk = arena[off + cb:off + cb + sb]
-            off += cb + sb
             nv.nvfp4_pack(codes, scales, K, N, cpk, spk)
             del w, codes, scales
-            act = synth.activations_device(seed, synth.stream_id(layer, name), max_M, K)
+            act = synth.activations_device(seed, sid, max_M, K)
             out = torch.empty((max_M, N), dtype=torch.bfloat16, device="cuda")
             keep += [act, out]
             specs.append(dict(K=K, N=N, codes=cpk, scales=spk, tensor_scale=0.0, act=act,
-                              out=out, out_dtype=nv.OUT_BF16, name=name, layer=layer))
+                              out=out, out_dtype=nv.OUT_BF16, name=name, layer=layer,
+                              arena_off=off, packed_bytes=cb + sb))
+            off += cb + sb
         if log and layer % 16 == 15:
             torch.cuda.synchronize()
             log("  built layers 0..%d (%.1f s)" % (layer, time.time() - t0))
@@ -129,46 +147,112 @@ def synth_act(spec, rows, seed=0):
                                     spec["K"])
 
 
-def cpu_baseline(layers=None, lanes=8, threads=None):
-    """The CPU oracle, as it stands, on a bounded sample of the round: the
-    first `layers` layers' four matrices in full (default four layers, 335.5 M
-    weights each), M = 8 lanes.  Drawing and quantising the sample (with the
-    oracle's quantiser, rows split over threads) is not timed; the oracle GEMM
-    is.  Returns (GB/s of NVFP4 weights processed, threads, sample
-    description, seconds)."""
-    from concurrent.futures import ThreadPoolExecutor
+# ---- CPU baseline: the oracle as it stands, on the host's cores -----------------
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_planes(pool, threads, sid, N, K, rows=None):
+    """Canonical planes of a synthetic weight matrix quantised by the oracle
+    (the tensor scale over the whole matrix; rows [0, rows) quantised)."""
     import numpy as np
+    import oracle
+    import synth
+    W = synth.weights(0, sid, N, K)
+    t = oracle.tensor_scale(W)
+    R = N if rows is None else rows
+    bounds = [R * i // threads for i in range(threads + 1)]
+    parts = list(pool.map(lambda ab: oracle.quantize_rows(W[ab[0]:ab[1]], t),
+                          zip(bounds[:-1], bounds[1:])))
+    del W
+    return (np.concatenate([c for c, _ in parts]), np.concatenate([s for _, s in parts]), t)
+
+
+def cpu_baseline(threads=None, round_layers=None):
+    """The CPU oracle (fp64, exact dequantisation), as it stands, timed on the
+    host's cores on bounded samples of each workload.  Drawing and quantising
+    inputs (with the oracle's quantiser, rows split over threads) is not
+    timed; the oracle GEMM is.  Returns a dict: the headline sample (layers
+    0..round_layers-1 of the round in full at M = 8, GB/s of weight bytes),
+    and per-config seconds and rates:
+      tiny       M = 1, K = 256, N = 512, in full
+      projection M = 1, 2, 4, 8, K = N = 5120, in full
+      head       M = 8, K = 5120, the first N/8 = 19008 of the 152064 rows
+      prefill    8 of the 2048 rows, K = 5120, N = 17408 in full
+    Rates for sampled configs are per unit of work, so they scale to the full
+    config (the oracle's cost is linear in rows and in weights)."""
+    from concurrent.futures import ThreadPoolExecutor
     import oracle
     import synth
     if threads is None:
         threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    if layers is None:
-        layers = int(os.environ.get("NVFP4_CPU_SAMPLE_LAYERS", "4"))
+    if round_layers is None:
+        round_layers = int(os.environ.get("NVFP4_CPU_SAMPLE_LAYERS", "2"))
     oracle.build()
-    dt, nbytes = 0.0, 0
+    per = {}
+
+    def timed(act, planes):
+        c, s, t = planes
+        t0 = time.perf_counter()
+        oracle.gemm(act, c, s, t, threads=threads)
+        return time.perf_counter() - t0
+
     with ThreadPoolExecutor(threads) as pool:
-        for layer in range(layers):
+        # the round sample (the headline metric's unit: GB/s of weight bytes)
+        dt, nbytes = 0.0, 0
+        for layer in range(round_layers):
             for name, K, N in ROUND_SHAPES:
                 sid = synth.stream_id(layer, name)
-                W = synth.weights(0, sid, N, K)
-                t = oracle.tensor_scale(W)
-                bounds = [N * i // threads for i in range(threads + 1)]
-                parts = list(pool.map(lambda ab: oracle.quantize_rows(W[ab[0]:ab[1]], t),
-                                      zip(bounds[:-1], bounds[1:])))
-                del W
-                codes = np.concatenate([c for c, _ in parts])
-                scales = np.concatenate([s for _, s in parts])
-                del parts
-                act = synth.activations(0, sid, lanes, K)
-                t0 = time.perf_counter()
-                oracle.gemm(act, codes, scales, t, threads=threads)
-                dt += time.perf_counter() - t0
+                planes = _oracle_planes(pool, threads, sid, N, K)
+                dt += timed(synth.activations(0, sid, 8, K), planes)
                 nbytes += weight_bytes(K, N)
-    desc = ("oracle GEMM (fp64, exact dequantisation) over layer%s 0%s of the round in full "
-            "(qkv, o, gate_up, down), M=%d lanes: %d weight bytes in %.2f s"
-            % ("s" if layers > 1 else "", "..%d" % (layers - 1) if layers > 1 else "", lanes,
-               nbytes, dt))
-    return nbytes / dt / 1e9, threads, desc, dt
+                del planes
+        head_value = nbytes / dt / 1e9
+        per["round_sample"] = {
+            "layers": round_layers, "M": 8, "seconds": round(dt, 3),
+            "weight_bytes": nbytes, "GB_s": round(head_value, 5),
+            "est_full_round_s": round(dt * LAYERS / round_layers, 1)}
+        # tiny
+        planes = _oracle_planes(pool, threads, 0, 512, 256)
+        s = timed(synth.activations(0, 0, 1, 256), planes)
+        per["tiny"] = {"M": 1, "K": 256, "N": 512, "seconds": round(s, 6)}
+        # projection
+        planes = _oracle_planes(pool, threads, 100, PROJ_N, PROJ_K)
+        proj = {}
+        for M in (1, 2, 4, 8):
+            s = timed(synth.activations(0, 100, M, PROJ_K), planes)
+            proj[str(M)] = {"seconds": round(s, 4),
+                            "GB_s": round(gemm_bytes(M, PROJ_K, PROJ_N) / s / 1e9, 5)}
+        per["projection"] = proj
+        # output head, first N/8 rows
+        rows = HEAD_N // 8
+        planes = _oracle_planes(pool, threads, 9002, HEAD_N, HEAD_K, rows=rows)
+        s = timed(synth.activations(0, 9002, 8, HEAD_K), planes)
+        per["head"] = {"M": 8, "rows": rows, "of_rows": HEAD_N, "seconds": round(s, 3),
+                       "GB_s": round(weight_bytes(HEAD_K, rows) / s / 1e9, 5),
+                       "est_full_s": round(s * HEAD_N / rows, 2)}
+        del planes
+        # prefill chunk, 8 of its 2048 rows of activations
+        PM, PK, PN = PREFILL_SHAPE
+        planes = _oracle_planes(pool, threads, 9001, PN, PK)
+        s = timed(synth.activations(0, 9001, 8, PK), planes)
+        per["prefill"] = {"M_sampled": 8, "of_M": PM, "K": PK, "N": PN, "seconds": round(s, 3),
+                          "GFLOP_s": round(2.0 * 8 * PK * PN / s / 1e9, 3),
+                          "est_full_s": round(s * PM / 8, 1)}
+        del planes
+    desc = ("oracle GEMM (fp64, exact dequantisation) over layers 0..%d of the round in full "
+            "(qkv, o, gate_up, down), M=8 lanes: %d weight bytes in %.2f s"
+            % (round_layers - 1, nbytes, dt))
+    return {"value": round(head_value, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": desc, "cpu_model": _cpu_model(), "per_config": per}
 
 
 def main():
@@ -179,7 +263,7 @@ def main():
     ap.add_argument("--layers", type=int, default=LAYERS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true",
-                    help="skip the M=1..8 sweep (profiling runs: keep only M=8 launches)")
+                    help="time only the M=8 round and the prefill chunk (profiling runs)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (for scaling memory counters)")
     ap.add_argument("--quiet", action="store_true")
@@ -196,56 +280,48 @@ def main():
 
     import torch
     import nvfp4_weight_streaming_amd as nv
+    import synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     nv.lib()
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()  # default priority
     log("building the round (%d layers) ..." % args.layers)
-    plans, wss = {}, []
     with torch.cuda.stream(stream):
         specs, keep = build_round(nv, layers=args.layers, log=log)
-        for mode in (nv.ROUND_PERSISTENT, nv.ROUND_PER_MATRIX, nv.ROUND_CHAIN):
-            ws_bytes = nv.nvfp4_round_workspace_bytes(specs, 8, mode=mode)
-            ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
-            wss.append(ws)
-            plans[mode] = nv.nvfp4_round_create(specs, 8, ws, ws_bytes, stream, mode=mode)
+        ws_bytes = nv.nvfp4_round_workspace_bytes(specs, 8)
+        ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+        plan = nv.nvfp4_round_create(specs, 8, ws, ws_bytes, stream)
     torch.cuda.synchronize()
-    nodes = {m: nv.nvfp4_round_graph_nodes(p, 8) for m, p in plans.items()}
-    log("round graphs: persistent %d node(s), per-matrix %d nodes, chained %d node(s) per width"
-        % (nodes[nv.ROUND_PERSISTENT], nodes[nv.ROUND_PER_MATRIX], nodes[nv.ROUND_CHAIN]))
+    nodes = nv.nvfp4_round_graph_nodes(plan, 8)
+    log("round graph: %d kernel nodes per width" % nodes)
 
-    def time_round(plan, M, steps, warmup):
-        """Mean device time per replay (ms): one HIP event pair around each
-        replay, all on the stream the graph runs on."""
+    def time_events(fn, reps, warmup=2):
+        """Mean device time per call (ms): one HIP event pair on `stream`
+        around `reps` back-to-back calls."""
         for _ in range(warmup):
-            nv.nvfp4_round_run(plan, M, stream)
+            fn()
         stream.synchronize()
-        evs = []
-        for _ in range(steps):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            nv.nvfp4_round_run(plan, M, stream)
-            b.record(stream)
-            evs.append((a, b))
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
         torch.cuda.synchronize()
-        return sum(a.elapsed_time(b) for a, b in evs) / steps
+        return a.elapsed_time(b) / reps
 
-    headline = plans[nv.ROUND_PER_MATRIX]
-    persistent = plans[nv.ROUND_PERSISTENT]
-    # Headline: M = 8 lanes, the default round (one graph of per-matrix decode
-    # kernels).  The timed region is the K replays bracketed by device
-    # synchronisation.
+    # Headline: M = 8 lanes.  The timed region is the K replays between two
+    # events on the replay stream, bracketed by device synchronisation.
     for _ in range(args.warmup):
-        nv.nvfp4_round_run(headline, 8, stream)
+        nv.nvfp4_round_run(plan, 8, stream)
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(args.steps):
-        nv.nvfp4_round_run(headline, 8, stream)
+        nv.nvfp4_round_run(plan, 8, stream)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
@@ -255,11 +331,8 @@ def main():
     log("M=8 round: %.3f ms, %.1f GB/s (%.1f%% of 8 TB/s)" % (ms8, gbs8, 100 * gbs8 / HBM_PEAK_GBS))
 
     # Prefill chunk (M = 2048, K = 5120, N = 17408, bf16 out): the bf16 MFMA
-    # kernel over dequantised tiles.  Timed right after the headline, before
-    # the minutes of round sweeps below: timed after them, the same kernel
-    # took 378-399 us instead of 334-345 us (the chip then runs it at a lower
-    # clock; the counter pass shows 2.06 GHz even when timed early).
-    import synth
+    # kernel over dequantised tiles.  Timed right after the headline: after
+    # minutes of sustained load the chip runs it at a lower clock.
     PM, PK, PN = PREFILL_SHAPE
     with torch.cuda.stream(stream):
         wp = synth.weights_device(0, 9001, PN, PK)
@@ -268,42 +341,121 @@ def main():
         pact = synth.activations_device(0, 9001, PM, PK)
         pout = torch.empty((PM, PN), dtype=torch.bfloat16, device="cuda")
         pg = nv.Gemm(PM, PK, PN, nv.OUT_BF16)
-        for _ in range(2):
-            pg(ppw, pact, pout, stream=stream)
-        stream.synchronize()
-        # back-to-back calls between one pair of events (throughput, as a
-        # chunk loop issues them)
-        n_pre = max(3, args.steps // 4)
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(n_pre):
-            pg(ppw, pact, pout, stream=stream)
-        b.record(stream)
-        torch.cuda.synchronize()
-    p_us = a.elapsed_time(b) / n_pre * 1e3
+    p_us = time_events(lambda: pg(ppw, pact, pout, stream=stream), max(3, args.steps // 4)) * 1e3
     p_tflops = 2.0 * PM * PK * PN / (p_us * 1e-6) / 1e12
     log("prefill M=%d K=%d N=%d: %.1f us, %.1f TFLOP/s (%.1f%% of 2.5 PF bf16)"
-        % (PM, PK, PN, p_us, p_tflops, 100 * p_tflops / 2500.0))
+        % (PM, PK, PN, p_us, p_tflops, 100 * p_tflops / BF16_MFMA_PEAK_TFLOPS))
     prefill = {"M": PM, "K": PK, "N": PN, "us": round(p_us, 2), "TFLOP_s": round(p_tflops, 1),
-               "frac_bf16_mfma_peak": round(p_tflops / 2500.0, 4)}
+               "frac_bf16_mfma_peak": round(p_tflops / BF16_MFMA_PEAK_TFLOPS, 4)}
     del ppw, pact, pout, pg
 
-    sweep, sweep_ps, sweep_ch = {}, {}, {}
+    # Achievable: a plain streaming read of the same weight bytes, (a) as one
+    # read of the whole arena and (b) as a graph of 256 reads, one per matrix
+    # with that matrix's byte size, the shape of the round graph.
+    arena = keep[0]
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    big_ms = time_events(lambda: nv.nvfp4_stream_read(arena, arena.numel(), sink, stream), 5)
+    big_gbs = arena.numel() / (big_ms * 1e-3) / 1e9
+    rg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(rg, stream=stream):
+        for s in specs:
+            nv.nvfp4_stream_read(arena[s["arena_off"]:], s["packed_bytes"], sink)
+    def replay_reads():
+        with torch.cuda.stream(stream):
+            rg.replay()
+    graph_ms = time_events(replay_reads, 10)
+    wbytes = sum(s["packed_bytes"] for s in specs)
+    graph_gbs = wbytes / (graph_ms * 1e-3) / 1e9
+    log("achievable: one read of the %.2f GB arena %.3f ms (%.1f GB/s); graph of %d reads "
+        "%.3f ms (%.1f GB/s)" % (arena.numel() / 1e9, big_ms, big_gbs, len(specs), graph_ms,
+                                 graph_gbs))
+    del rg
+    achievable = {"single_read_GB_s": round(big_gbs, 1), "single_read_ms": round(big_ms, 4),
+                  "graph_of_reads_ms": round(graph_ms, 4), "graph_of_reads_GB_s": round(graph_gbs, 1),
+                  "graph_nodes": len(specs),
+                  "what": "nvfp4_stream_read over the round's packed weights: one read of the "
+                          "whole arena, and a graph of one read per matrix"}
+
+    sweep = {}
     for M in ([] if args.no_sweep else range(1, 9)):
-        for mode, tab in ((nv.ROUND_PER_MATRIX, sweep), (nv.ROUND_PERSISTENT, sweep_ps),
-                          (nv.ROUND_CHAIN, sweep_ch)):
-            ms = time_round(plans[mode], M, max(5, args.steps // 2), 2)
-            gbs = round_bytes(M, args.layers) / (ms * 1e-3) / 1e9
-            tab[str(M)] = {"round_ms": round(ms, 4), "GB_s": round(gbs, 1),
-                           "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
-        log("M=%d: per-matrix graph %.3f ms (%.1f GB/s), persistent %.3f ms, chained %.3f ms "
-            "(%.1f GB/s)" % (M, sweep[str(M)]["round_ms"], sweep[str(M)]["GB_s"],
-                             sweep_ps[str(M)]["round_ms"], sweep_ch[str(M)]["round_ms"],
-                             sweep_ch[str(M)]["GB_s"]))
-    for mode in (nv.ROUND_PERSISTENT, nv.ROUND_CHAIN):
-        flags = nv.nvfp4_round_status(plans[mode])
-        assert flags == 0, "round form %d: a wait timed out (flags %d)" % (mode, flags)
+        ms = time_events(lambda: nv.nvfp4_round_run(plan, M, stream), max(5, args.steps // 2))
+        gbs = round_bytes(M, args.layers) / (ms * 1e-3) / 1e9
+        sweep[str(M)] = {"round_ms": round(ms, 4), "GB_s": round(gbs, 1),
+                         "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        log("M=%d round: %.3f ms (%.1f GB/s, %.1f%%)" % (M, ms, gbs, 100 * gbs / HBM_PEAK_GBS))
+
+    # Single projection (K = N = 5120, bf16 out) over PROJ_COPIES distinct
+    # weight copies chained in one graph: the per-GEMM mean at M = 1, 2, 4, 8.
+    projection = {}
+    if not args.no_sweep:
+        with torch.cuda.stream(stream):
+            pspecs, pkeep = build_round(nv, layers=PROJ_COPIES, shapes=(("proj", PROJ_K, PROJ_N),))
+            pws_b = nv.nvfp4_round_workspace_bytes(pspecs, 8)
+            pws = torch.zeros(max(pws_b, 16), dtype=torch.uint8, device="cuda")
+            pplan = nv.nvfp4_round_create(pspecs, 8, pws, pws_b, stream)
+        torch.cuda.synchronize()
+        for M in (1, 2, 4, 8):
+            ms = time_events(lambda: nv.nvfp4_round_run(pplan, M, stream), max(5, args.steps // 2))
+            us = ms * 1e3 / PROJ_COPIES
+            gbs = gemm_bytes(M, PROJ_K, PROJ_N) / (us * 1e-6) / 1e9
+            projection[str(M)] = {"us_per_gemm": round(us, 3), "GB_s": round(gbs, 1),
+                                  "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+            log("projection M=%d K=N=5120: %.2f us per GEMM (%.1f GB/s) over %d copies"
+                % (M, us, gbs, PROJ_COPIES))
+        nv.nvfp4_round_destroy(pplan)
+        del pspecs, pkeep, pws
+
+    # Output head (M = 8, K = 5120, N = 152064, fp32 logits), two weight copies
+    # alternating, back-to-back calls between one pair of events.
+    with torch.cuda.stream(stream):
+        hpws = []
+        for c in range(2):
+            wh = synth.weights_device(0, 9002 + 10 * c, HEAD_N, HEAD_K)
+            hpws.append(nv.PackedWeight.quantize(wh, stream=stream))
+            del wh
+        hact = synth.activations_device(0, 9002, 8, HEAD_K)
+        hout = torch.empty((8, HEAD_N), dtype=torch.float32, device="cuda")
+        hg = nv.Gemm(8, HEAD_K, HEAD_N, nv.OUT_F32)
+    n_head = max(6, args.steps) // 2 * 2
+    flip = [0]
+
+    def head_call():
+        hg(hpws[flip[0]], hact, hout, stream=stream)
+        flip[0] ^= 1
+    h_us = time_events(head_call, n_head) * 1e3
+    h_bytes = gemm_bytes(8, HEAD_K, HEAD_N, out_bytes=4)
+    h_gbs = h_bytes / (h_us * 1e-6) / 1e9
+    log("output head M=8 K=%d N=%d (fp32 out): %.1f us, %.1f GB/s (%.1f%% of 8 TB/s, %.1f%% of "
+        "the single-read rate)" % (HEAD_K, HEAD_N, h_us, h_gbs, 100 * h_gbs / HBM_PEAK_GBS,
+                                   100 * h_gbs / big_gbs))
+    head = {"M": 8, "K": HEAD_K, "N": HEAD_N, "out": "fp32", "us": round(h_us, 2),
+            "algorithmic_bytes": h_bytes, "GB_s": round(h_gbs, 1),
+            "frac_hbm_peak": round(h_gbs / HBM_PEAK_GBS, 4),
+            "frac_of_achievable": round(h_gbs / big_gbs, 4), "weight_copies": 2}
+
+    # Top-k over the vocabulary, the step after the head: on the head's own
+    # logits (k = 1, the greedy argmax, and k = 8), and on 7 rows of a
+    # 248320-entry vocabulary (the size class of the pages' drafter top-k).
+    def time_topk(logits, k, reps=20):
+        M, V = logits.shape
+        idx = torch.empty((M, k), dtype=torch.int32, device="cuda")
+        val = torch.empty((M, k), dtype=torch.float32, device="cuda")
+        wsb = nv.nvfp4_topk_workspace_bytes(M, V, k)
+        tws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+        return time_events(lambda: nv.nvfp4_topk(logits, M, V, V, k, idx, val, tws, wsb, stream),
+                           reps, warmup=3) * 1e3
+    topk = {}
+    if not args.no_sweep:
+        for k in (1, 8):
+            us = time_topk(hout, k)
+            topk["head_M8_V%d_k%d" % (HEAD_N, k)] = {"us": round(us, 2)}
+            log("top-k of the head's logits (M=8, V=%d, k=%d): %.2f us" % (HEAD_N, k, us))
+        lg = torch.from_numpy(synth.logits(0, 9003, 7, 248320)).cuda()
+        us = time_topk(lg, 7)
+        topk["M7_V248320_k7"] = {"us": round(us, 2)}
+        log("top-k M=7 V=248320 k=7: %.2f us" % us)
+        del lg
+    del hpws, hact, hout, hg
 
     # Chained MLP: the same round with each down matrix reading the SwiGLU of
     # its layer's gate_up output (one more graph node per layer), so the
@@ -322,7 +474,7 @@ def main():
             cplan = nv.nvfp4_round_create(cspecs, 8, cws, cws_bytes, stream)
         torch.cuda.synchronize()
         for M in (1, 8):
-            ms = time_round(cplan, M, max(5, args.steps // 2), 2)
+            ms = time_events(lambda: nv.nvfp4_round_run(cplan, M, stream), max(5, args.steps // 2))
             gbs = round_bytes(M, args.layers) / (ms * 1e-3) / 1e9
             chained[str(M)] = {"round_ms": round(ms, 4), "GB_s": round(gbs, 1),
                                "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
@@ -334,7 +486,7 @@ def main():
 
     # Verify widths (speculative decoding checks up to 7 drafts per lane in the
     # same pass: up to 8 x 8 = 64 rows): the same weights, 64-row activation
-    # and output buffers, a per-matrix round with one graph per width 1..64.
+    # and output buffers, a round with one graph per width 1..64.
     verify = {}
     if not args.no_sweep:
         t_v = time.time()
@@ -350,7 +502,7 @@ def main():
         torch.cuda.synchronize()
         log("verify-width round (widths 1..64) built in %.1f s" % (time.time() - t_v))
         for M in (16, 32, 64):
-            ms = time_round(vplan, M, max(5, args.steps // 2), 2)
+            ms = time_events(lambda: nv.nvfp4_round_run(vplan, M, stream), max(5, args.steps // 2))
             gbs = round_bytes(M, args.layers) / (ms * 1e-3) / 1e9
             verify[str(M)] = {"round_ms": round(ms, 4), "GB_s": round(gbs, 1),
                               "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
@@ -363,75 +515,11 @@ def main():
     # decode kernels, one per matrix, in sequence on `stream`, so its average
     # launch duration is the timed region's event time over the launches (it
     # includes the short gaps between graph nodes, so it is an upper bound).
-    launches = nodes[nv.ROUND_PER_MATRIX]
-    dk_us = ms8 * 1e3 / launches
-    avg_bytes = bytes8 / launches
+    dk_us = ms8 * 1e3 / nodes
+    avg_bytes = bytes8 / nodes
     achieved = avg_bytes / (dk_us * 1e-6) / 1e9
-    log("decode kernel: %.2f us average launch, %.0f bytes average, %.1f GB/s"
-        % (dk_us, avg_bytes, achieved))
-
-
-    # Output head (M = 8, K = 5120, N = 152064, fp32 logits): one decode launch
-    # per call, default plan; back-to-back calls between one pair of events.
-    HK, HN = 5120, 152064
-    with torch.cuda.stream(stream):
-        wh = synth.weights_device(0, 9002, HN, HK)
-        hpw = nv.PackedWeight.quantize(wh, stream=stream)
-        del wh
-        hact = synth.activations_device(0, 9002, 8, HK)
-        hout = torch.empty((8, HN), dtype=torch.float32, device="cuda")
-        hg = nv.Gemm(8, HK, HN, nv.OUT_F32)
-        for _ in range(3):
-            hg(hpw, hact, hout, stream=stream)
-        stream.synchronize()
-        n_head = max(5, args.steps)
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(n_head):
-            hg(hpw, hact, hout, stream=stream)
-        b.record(stream)
-        torch.cuda.synchronize()
-    h_us = a.elapsed_time(b) / n_head * 1e3
-    h_bytes = weight_bytes(HK, HN) + 8 * HK * 2 + 8 * HN * 4
-    h_gbs = h_bytes / (h_us * 1e-6) / 1e9
-    log("output head M=8 K=%d N=%d (fp32 out): %.1f us, %.1f GB/s (%.1f%% of 8 TB/s)"
-        % (HK, HN, h_us, h_gbs, 100 * h_gbs / HBM_PEAK_GBS))
-    head = {"M": 8, "K": HK, "N": HN, "out": "fp32", "us": round(h_us, 2),
-            "algorithmic_bytes": h_bytes, "GB_s": round(h_gbs, 1),
-            "frac_hbm_peak": round(h_gbs / HBM_PEAK_GBS, 4)}
-
-    # Top-k over the vocabulary, the step after the head: on the head's own
-    # logits (k = 1, the greedy argmax, and k = 8), and on 7 rows of a
-    # 248320-entry vocabulary (the size class of the pages' drafter top-k).
-    def time_topk(logits, k, reps=20):
-        M, V = logits.shape
-        idx = torch.empty((M, k), dtype=torch.int32, device="cuda")
-        val = torch.empty((M, k), dtype=torch.float32, device="cuda")
-        wsb = nv.nvfp4_topk_workspace_bytes(M, V, k)
-        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
-        with torch.cuda.stream(stream):
-            for _ in range(3):
-                nv.nvfp4_topk(logits, M, V, V, k, idx, val, ws, wsb, stream)
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(reps):
-                nv.nvfp4_topk(logits, M, V, V, k, idx, val, ws, wsb, stream)
-            b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps * 1e3
-    import synth
-    topk = {}
-    for k in (1, 8):
-        us = time_topk(hout, k)
-        topk["head_M8_V%d_k%d" % (HN, k)] = {"us": round(us, 2)}
-        log("top-k of the head's logits (M=8, V=%d, k=%d): %.2f us" % (HN, k, us))
-    lg = torch.from_numpy(synth.logits(0, 9003, 7, 248320)).cuda()
-    us = time_topk(lg, 7)
-    topk["M7_V248320_k7"] = {"us": round(us, 2)}
-    log("top-k M=7 V=248320 k=7: %.2f us" % us)
-    del hpw, hact, hout, hg, lg
+    log("decode kernel: %.2f us average launch, %.0f bytes average, %.1f GB/s (%.1f%% of the "
+        "graph-of-reads rate)" % (dk_us, avg_bytes, achieved, 100 * achieved / graph_gbs))
 
     if args.calibration_copy:
         # A plain copy kernel of known size: 1 GiB read, 1 GiB written.
@@ -441,15 +529,14 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    nv.nvfp4_round_destroy(plan)
     cpu = None
     if not args.no_cpu_baseline:
-        v, thr, desc, dt = cpu_baseline()
-        cpu = {"value": round(v, 5), "unit": "GB/s", "cores": thr, "kind": "oracle",
-               "sample": desc}
-        log("cpu baseline: %.4f GB/s on %d threads (%.1f s)" % (v, thr, dt))
+        t_c = time.time()
+        cpu = cpu_baseline()
+        log("cpu baseline: %.4f GB/s on %d threads (%s); leg took %.1f s"
+            % (cpu["value"], cpu["cores"], cpu["cpu_model"], time.time() - t_c))
 
-    for p in plans.values():
-        nv.nvfp4_round_destroy(p)
     tr = measured_traffic()
     traffic = None
     if tr is not None:
@@ -476,28 +563,29 @@ def main():
             "lanes": 8,
             "round_weight_bytes": sum(weight_bytes(K, N) for _, K, N in ROUND_SHAPES) * args.layers,
             "round_bytes_m8": bytes8,
-            "graph_kernel_nodes": nodes[nv.ROUND_PER_MATRIX],
+            "graph_kernel_nodes": nodes,
             "parallelism": "single GPU",
         },
         "frac_hbm_peak": round(gbs8 / HBM_PEAK_GBS, 4),
         "round_ms_m1_to_m8": {k: v["round_ms"] for k, v in sweep.items()},
         "round_sweep": sweep,
-        "round_sweep_persistent_kernel": sweep_ps,
-        "round_sweep_chained": sweep_ch,
+        "projection": projection,
         "verify_width_rounds": verify,
         "chained_mlp_rounds": chained,
         "roofline": {
             "bound": "hbm",
-            "kernel": "nvfp4::decode_window_kernel<WAVES, 1, true> (split-K decode, slices streamed "
-                      "in windows of one superblock, bf16 out), M=8",
+            "kernel": "nvfp4::decode_window_kernel (split-K decode, slices streamed in windows, "
+                      "bf16 out), M=8",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "avg_launch_us": round(dk_us, 3),
             "avg_algorithmic_bytes_per_launch": round(avg_bytes),
-            "launches_per_round": 4 * args.layers,
+            "launches_per_round": nodes,
             "traffic": traffic,
+            "achievable": achievable,
+            "frac_of_graph_of_reads": round(achieved / graph_gbs, 4),
         },
         "prefill_chunk": prefill,
         "output_head": head,

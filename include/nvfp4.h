@@ -116,24 +116,15 @@ int nvfp4_quantize(const float* w_dev, int K, int N, uint8_t* codes_dev, uint8_t
 
 typedef struct nvfp4_gemm_plan* nvfp4_gemm;
 
-/* Decode kernels (M <= 8). */
-enum nvfp4_kernel {
-    NVFP4_KERNEL_AUTO = 0,
-    NVFP4_KERNEL_STREAM = 1, /* full-K column groups, per-wave weight ring */
-    NVFP4_KERNEL_SPLITK = 2  /* K split over workgroups, last one reduces (default) */
-};
-
 /* Optional kernel configuration for nvfp4_gemm_create_ex; 0 fields mean
  * "choose automatically". */
 typedef struct nvfp4_gemm_config {
-    int split_k; /* SPLITK: number of K slices (workgroups per column group) */
-    int waves;   /* SPLITK: waves per workgroup (column tiles of 16), 4 or 8 */
-    int chunks;  /* SPLITK: K values per slice in units of 512, 1..4 (when
+    int split_k; /* decode: number of K slices (workgroups per column group) */
+    int waves;   /* decode: waves per workgroup (column tiles of 16), 4 or 8 */
+    int chunks;  /* decode: K values per slice in units of 512, 1..4 (when
                     split_k is 0) */
-    int kernel;  /* nvfp4_kernel */
-    int tiles;   /* STREAM: column tiles of 16 per workgroup, 2, 4 or 8 */
-    int windows; /* SPLITK: windows of `chunks` superblocks per K slice; above 1 a
-                    wave streams its slice, issuing the next window's loads
+    int windows; /* decode: windows of `chunks` superblocks per K slice; above 1
+                    a wave streams its slice, issuing the next window's loads
                     before computing the current one (0 or 1: one window) */
     int verify_waves;   /* verify widths (8 < M <= 64): waves per workgroup, 4, 8
                            or 16 (0: 4 up to 48 rows, 8 above) */
@@ -193,7 +184,7 @@ enum nvfp4_act_op {
 };
 
 /* One matrix of a round.  act_dev holds max_M rows of K bf16 values, out_dev
- * max_M rows of N outputs.  act_op: nvfp4_act_op (PER_MATRIX rounds only). */
+ * max_M rows of N outputs.  act_op: nvfp4_act_op. */
 typedef struct nvfp4_layer {
     int K, N;
     const uint8_t* codes_dev;  /* packed */
@@ -207,67 +198,32 @@ typedef struct nvfp4_layer {
 
 typedef struct nvfp4_round_plan* nvfp4_round;
 
-/* Forms of a round (see nvfp4_round_create_ex). */
-enum nvfp4_round_mode {
-    NVFP4_ROUND_PERSISTENT = 0, /* one persistent kernel walks every matrix */
-    NVFP4_ROUND_PER_MATRIX = 1, /* one decode kernel per matrix */
-    NVFP4_ROUND_CHAIN = 2       /* one launch whose workgroups run the matrices in order */
-};
-
-/* Workspace a round over these layers needs in the given form (the default
- * form is NVFP4_ROUND_PER_MATRIX). */
+/* Workspace a round over these layers needs (one split-K counter region and
+ * one partial-sum region, shared by the matrices, which run one after the
+ * other). */
 int nvfp4_round_workspace_bytes(const nvfp4_layer* layers, int n_layers, int max_M,
                                 size_t* workspace_bytes);
-int nvfp4_round_workspace_bytes_ex(const nvfp4_layer* layers, int n_layers, int max_M, int mode,
-                                   size_t* workspace_bytes);
 
-/* Capture one HIP graph per width M = 1..max_M, each running the n_layers
- * GEMMs in list order, as the reference engine replays one graph per batch
- * width.  max_M <= 64 for PER_MATRIX (widths above 8, the verify widths of
- * speculative decoding, launch the verify-width kernel), <= 8 for the other
- * forms.  Matrix i+1 starts computing only once every output of matrix
- * i is written (the order of a forward pass in which each matrix consumes the
- * previous one's result).
- *   PER_MATRIX : the graph holds one decode (or verify-width) kernel launch
- *                per matrix.
- *   PERSISTENT : the graph holds one kernel whose resident workgroups walk
- *                every matrix; the next matrix's weights are fetched while the
- *                previous matrix finishes (no launch boundary between them).
- *                Outputs are written with device-coherent stores.  Its waits
- *                are bounded: a wait that times out raises a flag read by
- *                nvfp4_round_status (the results are then not valid).  The
- *                grid assumes it has the device to itself while it runs.
- *   CHAIN      : the graph holds one launch whose workgroups are the
- *                decode workgroups of every matrix, in list order ("Ignis"
- *                README, "Lineage": "Credits" -- the round's decode kernels
- *                are chained so that each GEMM's start overlaps the previous
- *                one's drain).  A workgroup issues its weight loads, then
- *                waits until the previous matrix is complete, then reads its
- *                activations.  Outputs are written with device-coherent
- *                stores; activations that overlap an earlier matrix's output
- *                are read with device-coherent loads.  Waits are bounded as in
- *                PERSISTENT.  Needs workgroups spread evenly over the 8 XCDs
- *                (checked here: NVFP4_EUNSUPPORTED otherwise).  The workspace
- *                holds a split-K region per matrix (about 10.5 MB per layer of
- *                the 27B-class round).
+/* Capture one HIP graph per width M = 1..max_M (max_M <= 64), each running
+ * the n_layers GEMMs in list order: the reference engine replays one CUDA
+ * graph per batch width ("Ignis" README, "What sets it apart", "The decode
+ * round").  The graph of width M holds one kernel launch per matrix (the
+ * decode kernel for M <= 8, the verify-width kernel for the widths of
+ * speculative verification above 8: "Ignis" README, "Speculative decoding
+ * (DFlash2)"), plus one SwiGLU launch before each matrix whose act_op asks for
+ * it.  Launches are ordered on one stream, so matrix i+1 starts only once
+ * every output of matrix i is written, the order of a forward pass in which
+ * each matrix consumes the previous one's result.
  * The layer array is copied; the device buffers it names must stay valid
- * while the plan lives.  The workspace (nvfp4_round_workspace_bytes_ex
- * bytes, 16-byte aligned) is zeroed and written here, then owned by the plan
- * until it is destroyed.  Synchronises `stream`.  nvfp4_round_create is the
- * PER_MATRIX form (measured faster on MI355X for the 27B-class round). */
+ * while the plan lives.  The workspace (nvfp4_round_workspace_bytes bytes,
+ * 16-byte aligned) is zeroed here, then owned by the plan until it is
+ * destroyed.  Synchronises `stream` (graph capture and upload).
+ * Errors: EINVAL names the layer and field; EHIP carries the runtime's
+ * message (nothing is left allocated). */
 int nvfp4_round_create(nvfp4_round* plan, const nvfp4_layer* layers, int n_layers, int max_M,
                        void* workspace_dev, size_t workspace_bytes, void* stream);
-int nvfp4_round_create_ex(nvfp4_round* plan, const nvfp4_layer* layers, int n_layers, int max_M,
-                          int mode, void* workspace_dev, size_t workspace_bytes, void* stream);
-/* Error flags raised by the replays since the last call (bit 0: a wait timed
- * out), then cleared; after a time-out the plan's counters are also re-zeroed
- * so later replays are valid again.  Synchronises the device.  Always 0 for
- * PER_MATRIX. */
-int nvfp4_round_status(nvfp4_round plan, unsigned int* flags);
-/* Bound on the polling rounds of each wait of a PERSISTENT or CHAIN round (default
- * 2^16, tens of milliseconds).  Synchronises the device. */
-int nvfp4_round_set_spin_limit(nvfp4_round plan, unsigned int limit);
-/* Replay the graph of width M (1..max_M) on `stream`. */
+/* Replay the graph of width M (1..max_M) on `stream`.  Asynchronous.
+ * ESTATE for a destroyed or foreign handle, EINVAL for M out of range. */
 int nvfp4_round_run(nvfp4_round plan, int M, void* stream);
 /* Number of kernel nodes in the graph of width M (0 on error). */
 int nvfp4_round_graph_nodes(nvfp4_round plan, int M);
@@ -300,6 +256,18 @@ int nvfp4_swiglu(const uint16_t* gate_up_dev, int M, int F, uint16_t* out_dev, v
 size_t nvfp4_topk_workspace_bytes(int M, int V, int k);
 int nvfp4_topk(const float* logits_dev, int M, int V, int ld, int k, int* idx_dev,
                float* val_dev, void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/* ---- measurement ------------------------------------------------------------- */
+
+/* Read `bytes` bytes of buf_dev once with the streaming load shape of the
+ * decode kernels' weight stream and no arithmetic: the achievable read rate
+ * that the round, which streams the weights at the card's memory bandwidth
+ * ("Ignis" README, "What sets it apart", "The decode round"), is measured
+ * against.  buf_dev 16-byte aligned, bytes a positive multiple of 16;
+ * sink_dev: one device word, written only if the folded value of the data
+ * equals an improbable constant (it keeps the loads).  Asynchronous on
+ * `stream`; EINVAL names a bad argument before anything is launched. */
+int nvfp4_stream_read(const void* buf_dev, size_t bytes, unsigned int* sink_dev, void* stream);
 
 #ifdef __cplusplus
 }

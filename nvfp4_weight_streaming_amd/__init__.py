@@ -30,13 +30,11 @@ EXPORTS = (
     "nvfp4_quantize_workspace_bytes", "nvfp4_quantize",
     "nvfp4_gemm_create", "nvfp4_gemm_create_ex", "nvfp4_gemm_destroy", "nvfp4_gemm_run",
     "nvfp4_workspace_clear",
-    "nvfp4_round_workspace_bytes", "nvfp4_round_workspace_bytes_ex", "nvfp4_round_create",
-    "nvfp4_round_create_ex", "nvfp4_round_status", "nvfp4_round_set_spin_limit",
-    "nvfp4_round_run", "nvfp4_round_graph_nodes", "nvfp4_round_destroy",
-    "nvfp4_topk_workspace_bytes", "nvfp4_topk", "nvfp4_swiglu",
+    "nvfp4_round_workspace_bytes", "nvfp4_round_create", "nvfp4_round_run",
+    "nvfp4_round_graph_nodes", "nvfp4_round_destroy",
+    "nvfp4_topk_workspace_bytes", "nvfp4_topk", "nvfp4_swiglu", "nvfp4_stream_read",
 )
 TOPK_MAX_K = 64
-ROUND_PERSISTENT, ROUND_PER_MATRIX, ROUND_CHAIN = 0, 1, 2
 
 
 class Nvfp4Error(RuntimeError):
@@ -52,11 +50,8 @@ _STATUS = {OK: "ok", EINVAL: "EINVAL", EUNSUPPORTED: "EUNSUPPORTED", EHIP: "EHIP
 
 class GemmConfig(ctypes.Structure):
     _fields_ = [("split_k", ctypes.c_int), ("waves", ctypes.c_int), ("chunks", ctypes.c_int),
-                ("kernel", ctypes.c_int), ("tiles", ctypes.c_int), ("windows", ctypes.c_int),
-                ("verify_waves", ctypes.c_int), ("verify_windows", ctypes.c_int)]
-
-
-KERNEL_AUTO, KERNEL_STREAM, KERNEL_SPLITK = 0, 1, 2
+                ("windows", ctypes.c_int), ("verify_waves", ctypes.c_int),
+                ("verify_windows", ctypes.c_int)]
 
 
 class Layer(ctypes.Structure):
@@ -103,11 +98,7 @@ def lib():
         L.nvfp4_gemm_run.argtypes = [vp, i, i, i, vp, vp, c.c_float, vp, vp, vp, vp]
         L.nvfp4_workspace_clear.argtypes = [vp, sz, vp]
         L.nvfp4_round_workspace_bytes.argtypes = [c.POINTER(Layer), i, i, c.POINTER(sz)]
-        L.nvfp4_round_workspace_bytes_ex.argtypes = [c.POINTER(Layer), i, i, i, c.POINTER(sz)]
         L.nvfp4_round_create.argtypes = [c.POINTER(vp), c.POINTER(Layer), i, i, vp, sz, vp]
-        L.nvfp4_round_create_ex.argtypes = [c.POINTER(vp), c.POINTER(Layer), i, i, i, vp, sz, vp]
-        L.nvfp4_round_status.argtypes = [vp, c.POINTER(c.c_uint)]
-        L.nvfp4_round_set_spin_limit.argtypes = [vp, c.c_uint]
         L.nvfp4_round_run.argtypes = [vp, i, vp]
         L.nvfp4_round_graph_nodes.argtypes = [vp, i]
         L.nvfp4_round_destroy.argtypes = [vp]
@@ -116,6 +107,7 @@ def lib():
         L.nvfp4_topk_workspace_bytes.restype = sz
         L.nvfp4_topk.argtypes = [vp, i, i, i, i, vp, vp, vp, sz, vp]
         L.nvfp4_swiglu.argtypes = [vp, i, i, vp, vp]
+        L.nvfp4_stream_read.argtypes = [vp, sz, vp, vp]
         for name in EXPORTS:
             getattr(L, name)
         _lib = L
@@ -184,6 +176,10 @@ def nvfp4_swiglu(gate_up, M, F, out, stream=None):
     _check(lib().nvfp4_swiglu(_ptr(gate_up), M, F, _ptr(out), _stream(stream)))
 
 
+def nvfp4_stream_read(buf, nbytes, sink, stream=None):
+    _check(lib().nvfp4_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)))
+
+
 def nvfp4_topk_workspace_bytes(M, V, k) -> int:
     return lib().nvfp4_topk_workspace_bytes(M, V, k)
 
@@ -205,14 +201,13 @@ def topk(logits, k, stream=None):
     return idx, val
 
 
-def nvfp4_gemm_create(max_M, K, N, out_dtype, split_k=0, waves=0, chunks=0, kernel=0, tiles=0,
-                      windows=0, verify_waves=0, verify_windows=0):
+def nvfp4_gemm_create(max_M, K, N, out_dtype, split_k=0, waves=0, chunks=0, windows=0,
+                      verify_waves=0, verify_windows=0):
     """Returns (plan handle, workspace bytes)."""
     h = ctypes.c_void_p()
     ws = ctypes.c_size_t()
-    if split_k or waves or chunks or kernel or tiles or windows or verify_waves or verify_windows:
-        cfg = GemmConfig(split_k, waves, chunks, kernel, tiles, windows, verify_waves,
-                         verify_windows)
+    if split_k or waves or chunks or windows or verify_waves or verify_windows:
+        cfg = GemmConfig(split_k, waves, chunks, windows, verify_waves, verify_windows)
         _check(lib().nvfp4_gemm_create_ex(ctypes.byref(h), max_M, K, N, out_dtype,
                                           ctypes.byref(cfg), ctypes.byref(ws)))
     else:
@@ -245,37 +240,18 @@ def _layers(layers):
     return arr
 
 
-def nvfp4_round_workspace_bytes(layers, max_M, mode=None) -> int:
+def nvfp4_round_workspace_bytes(layers, max_M) -> int:
     ws = ctypes.c_size_t()
-    if mode is None:
-        _check(lib().nvfp4_round_workspace_bytes(_layers(layers), len(layers), max_M,
-                                                 ctypes.byref(ws)))
-    else:
-        _check(lib().nvfp4_round_workspace_bytes_ex(_layers(layers), len(layers), max_M, mode,
-                                                    ctypes.byref(ws)))
+    _check(lib().nvfp4_round_workspace_bytes(_layers(layers), len(layers), max_M,
+                                             ctypes.byref(ws)))
     return ws.value
 
 
-def nvfp4_round_create(layers, max_M, workspace, workspace_bytes, stream=None, mode=None):
+def nvfp4_round_create(layers, max_M, workspace, workspace_bytes, stream=None):
     h = ctypes.c_void_p()
-    if mode is None:
-        _check(lib().nvfp4_round_create(ctypes.byref(h), _layers(layers), len(layers), max_M,
-                                        _ptr(workspace), workspace_bytes, _stream(stream)))
-    else:
-        _check(lib().nvfp4_round_create_ex(ctypes.byref(h), _layers(layers), len(layers), max_M,
-                                           mode, _ptr(workspace), workspace_bytes,
-                                           _stream(stream)))
+    _check(lib().nvfp4_round_create(ctypes.byref(h), _layers(layers), len(layers), max_M,
+                                    _ptr(workspace), workspace_bytes, _stream(stream)))
     return h.value
-
-
-def nvfp4_round_status(plan) -> int:
-    f = ctypes.c_uint()
-    _check(lib().nvfp4_round_status(plan, ctypes.byref(f)))
-    return f.value
-
-
-def nvfp4_round_set_spin_limit(plan, limit: int):
-    _check(lib().nvfp4_round_set_spin_limit(plan, limit))
 
 
 def nvfp4_round_run(plan, M, stream=None):
@@ -338,12 +314,12 @@ class PackedWeight:
 class Gemm:
     """A plan plus its workspace: ``Gemm(max_M, K, N, out_dtype)(w, act, out)``."""
 
-    def __init__(self, max_M, K, N, out_dtype=OUT_BF16, split_k=0, waves=0, chunks=0, kernel=0,
-                 tiles=0, windows=0, device="cuda", verify_waves=0, verify_windows=0):
+    def __init__(self, max_M, K, N, out_dtype=OUT_BF16, split_k=0, waves=0, chunks=0,
+                 windows=0, device="cuda", verify_waves=0, verify_windows=0):
         import torch
         self.plan, self.ws_bytes = nvfp4_gemm_create(max_M, K, N, out_dtype, split_k, waves,
-                                                     chunks, kernel, tiles, windows,
-                                                     verify_waves, verify_windows)
+                                                     chunks, windows, verify_waves,
+                                                     verify_windows)
         self.K, self.N, self.max_M, self.out_dtype = K, N, max_M, out_dtype
         self.workspace = None
         if self.ws_bytes:

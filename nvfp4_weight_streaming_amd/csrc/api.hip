@@ -95,17 +95,6 @@ int run_gemm(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_
     if (M > NVFP4_DECODE_MAX_M && p->ver.enabled)
         return launch_verify(p, M, codes, scales, ts, act, out, ws, off.ver_counters,
                              off.ver_partial, s);
-    if (p->str.enabled) {
-        // Rows beyond 8 (when no prefill kernel applies) run as further passes.
-        const size_t esz = p->out_dtype == NVFP4_OUT_BF16 ? 2 : 4;
-        for (int m0 = 0; m0 < M; m0 += NVFP4_DECODE_MAX_M) {
-            const int mm = M - m0 < NVFP4_DECODE_MAX_M ? M - m0 : NVFP4_DECODE_MAX_M;
-            int st = stream_launch_gemm(p, mm, codes, scales, ts, act + (size_t)m0 * p->K,
-                                        (char*)out + (size_t)m0 * p->N * esz, s);
-            if (st) return st;
-        }
-        return NVFP4_OK;
-    }
     return launch_decode(p, M, codes, scales, ts, act, out, ws, partial_off, s);
 }
 
@@ -153,16 +142,7 @@ static int create_plan(nvfp4_gemm* plan, int max_M, int K, int N, int out_dtype,
     p->out_dtype = out_dtype;
     p->Kp = padded_k(K);
     p->Np = padded_n(N);
-    const int kernel = cfg ? cfg->kernel : NVFP4_KERNEL_AUTO;
-    int st = NVFP4_OK;
-    if (kernel < NVFP4_KERNEL_AUTO || kernel > NVFP4_KERNEL_SPLITK)
-        st = set_error(NVFP4_EINVAL, "config.kernel: %d is not AUTO, STREAM or SPLITK", kernel);
-    const int tiles = cfg ? cfg->tiles : 0;
-    if (!st && tiles != 0 && tiles != 2 && tiles != 4 && tiles != 8)
-        st = set_error(NVFP4_EINVAL, "config.tiles: %d is not 2, 4 or 8", tiles);
-    p->str.enabled = kernel == NVFP4_KERNEL_STREAM;
-    p->str.tiles = tiles;
-    if (!st) st = make_decode_config(K, N, max_M, cfg, &p->dec);
+    int st = make_decode_config(K, N, max_M, cfg, &p->dec);
     if (!st) st = make_verify_config(K, N, max_M, cfg, &p->ver);
     if (!st) st = make_prefill_config(max_M, K, N, &p->pre);
     if (st != NVFP4_OK) {
@@ -173,7 +153,7 @@ static int create_plan(nvfp4_gemm* plan, int max_M, int K, int N, int out_dtype,
     // [decode counters, partials][verify counters, partials][prefill partials]:
     // the counters must stay zero between runs, so no area overlaps another.
     auto align = [](size_t v) { return (v + 255) & ~(size_t)255; };
-    const size_t dec_ws = p->str.enabled ? 0 : p->dec.ws_bytes;
+    const size_t dec_ws = p->dec.ws_bytes;
     p->ver.ws_off = align(dec_ws);
     size_t end = p->ver.d.ws_bytes ? p->ver.ws_off + p->ver.d.ws_bytes : dec_ws;
     p->pre.ws_off = align(end);

@@ -56,12 +56,6 @@ struct DecodeConfig {
     size_t ws_bytes;    // counter_bytes + partial_bytes
 };
 
-struct StreamDesc;
-struct StreamConfig {
-    int enabled;  // the streaming kernel serves M <= 8
-    int tiles;    // forced column tiles per workgroup (0: by shape)
-};
-
 // Verify widths (8 < M <= 64): the decode layout for 16 G rows, G = ceil(M / 16).
 struct VerifyConfig {
     int enabled;   // max_M > 8
@@ -84,7 +78,6 @@ struct nvfp4_gemm_plan {
     int max_M, K, N, out_dtype;
     int Kp, Np;
     nvfp4::DecodeConfig dec;
-    nvfp4::StreamConfig str;
     nvfp4::VerifyConfig ver;
     nvfp4::PrefillConfig pre;
     size_t ws_bytes;
@@ -115,38 +108,6 @@ int launch_prefill(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const 
                    float ts, const uint16_t* act, void* out, void* ws, hipStream_t s);
 int launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 int launch_swiglu(const uint16_t* gate_up, uint16_t* out, int M, int F, hipStream_t s);
-
-// Streaming kernel (stream.hip).
-void stream_fill_desc(StreamDesc* d, int K, int N, const void* codes, const void* scales,
-                      const uint16_t* act, void* out, float ts, int out_dtype, int T_override);
-int stream_launch_gemm(const nvfp4_gemm_plan* p, int M, const uint8_t* codes,
-                       const uint8_t* scales, float ts, const uint16_t* act, void* out,
-                       hipStream_t s);
-int stream_round_grid(int* grid);
-// Persistent round: writes the descriptors (with the task rotation for `grid`)
-// into the workspace.  Layout, in bytes.
-struct StreamRoundLayout {
-    size_t done_off, status_off, desc_off, flags_off, total;
-};
-size_t stream_round_layout(int n, StreamRoundLayout* out);
-int stream_round_write_descs(const nvfp4_layer* L, int n, int grid, void* ws,
-                             const StreamRoundLayout& lay, hipStream_t s);
-int stream_launch_round(int n, int M, int grid, void* ws, const StreamRoundLayout& lay,
-                        hipStream_t s);
-
-// Chained round (chain.hip): every matrix of a round in one launch.  Layout of
-// its workspace, in bytes: status, per-XCD ticket counters, per-matrix done
-// counters, completion flags, then (written once by the plan) one record per
-// ticket, then one counter + partial-sum region per matrix.
-struct ChainLayout {
-    int n;
-    size_t per_xcd;  // workgroups (tickets) per XCD
-    size_t status_off, tickets_off, done_off, flags_off, desc_off, regions_off, total;
-};
-size_t chain_round_layout(const nvfp4_layer* L, int n, ChainLayout* out);
-int chain_round_write(const nvfp4_layer* L, int n, int max_M, void* ws, const ChainLayout& y);
-int chain_check_dispatch(void* ws, const ChainLayout& y);
-int chain_launch_round(int M, void* ws, const ChainLayout& y, hipStream_t s);
 
 // Shared validation of a GEMM run against its plan.
 int validate_run(const nvfp4_gemm_plan* p, int M, int K, int N, const void* codes,

@@ -4,15 +4,14 @@
 // from one captured graph per batch width (widths 1..8) rather than issued
 // launch by launch.  Here a round is a list of weight matrices run in list
 // order, each with its own activation input and output; the graph of width M
-// runs every matrix for M lanes, and nvfp4_round_run replays it.  Two forms:
-//   NVFP4_ROUND_PERSISTENT - the graph holds one persistent kernel that walks
-//     all matrices, each starting only when the previous one is final, with
-//     the weight stream running on across the boundary (stream.hip);
-//   NVFP4_ROUND_PER_MATRIX - the graph holds one decode kernel per matrix on
-//     one stream;
-//   NVFP4_ROUND_CHAIN - the graph holds one launch of the chained kernel
-//     (chain.hip), whose workgroups run the matrices in order, each one's
-//     weight loads issued before the previous matrix is complete.
+// holds one decode kernel per matrix (the verify-width kernel above 8 rows),
+// one after the other on one stream, and nvfp4_round_run replays it.
+//
+// One kernel per matrix, not one launch for the round: on MI355X a graph's
+// kernel boundary costs about 1.5 us, while telling every workgroup of the
+// next matrix, on all eight XCDs, that the previous one is complete costs
+// several device-scope round trips (about 6 us per matrix measured for a
+// single-launch chain of plain reads with the round's byte sizes).
 #include <new>
 #include <vector>
 
@@ -21,10 +20,6 @@
 struct nvfp4_round_plan {
     uint32_t magic;
     int max_M;
-    int mode;
-    int grid;    // persistent form: resident workgroups
-    nvfp4::StreamRoundLayout lay;
-    nvfp4::ChainLayout chain;
     std::vector<nvfp4_layer> layers;
     std::vector<nvfp4_gemm_plan*> plans;
     void* ws;
@@ -36,11 +31,6 @@ struct nvfp4_round_plan {
 };
 
 namespace nvfp4 {
-
-// Polling rounds before a wait of the persistent round gives up (each round
-// is one coherent load plus a short sleep, about a microsecond: tens of
-// milliseconds in all, far above any one matrix's time).
-constexpr unsigned int kDefaultSpinLimit = 1u << 16;
 
 static void free_round(nvfp4_round_plan* r) {
     for (int i = 0; i < NVFP4_VERIFY_MAX_M; ++i) {
@@ -82,12 +72,6 @@ static int validate_layers(const nvfp4_layer* L, int n, int max_M) {
     return NVFP4_OK;
 }
 
-static bool any_act_op(const nvfp4_layer* L, int n) {
-    for (int i = 0; i < n; ++i)
-        if (L[i].act_op != NVFP4_ACT_INPUT) return true;
-    return false;
-}
-
 }  // namespace nvfp4
 
 using namespace nvfp4;
@@ -117,54 +101,12 @@ static int round_layout(const nvfp4_layer* layers, int n_layers, int max_M, size
     return NVFP4_OK;
 }
 
-// The single-launch forms serve decode widths only; the per-matrix form
-// also the verify widths (its graphs launch the verify-width kernel).
-static int check_mode(int mode, int max_M) {
-    if (mode != NVFP4_ROUND_PERSISTENT && mode != NVFP4_ROUND_PER_MATRIX &&
-        mode != NVFP4_ROUND_CHAIN)
-        return set_error(NVFP4_EINVAL,
-                         "mode: %d is not PERSISTENT (0), PER_MATRIX (1) or CHAIN (2)", mode);
-    if (mode != NVFP4_ROUND_PER_MATRIX && max_M > NVFP4_DECODE_MAX_M)
-        return set_error(NVFP4_EINVAL, "max_M: %d above %d, the largest of the %s form", max_M,
-                         NVFP4_DECODE_MAX_M,
-                         mode == NVFP4_ROUND_PERSISTENT ? "PERSISTENT" : "CHAIN");
-    return NVFP4_OK;
-}
-
-// Workspace offsets of a plan's status words and of its synchronisation state
-// (re-zeroed after a time-out), for the forms that have them.
-static bool sync_state(const nvfp4_round_plan* r, size_t* status_off) {
-    if (r->mode == NVFP4_ROUND_PERSISTENT) {
-        *status_off = r->lay.status_off;
-        return true;
-    }
-    if (r->mode == NVFP4_ROUND_CHAIN) {
-        *status_off = r->chain.status_off;
-        return true;
-    }
-    return false;
-}
-
-int nvfp4_round_workspace_bytes_ex(const nvfp4_layer* layers, int n_layers, int max_M, int mode,
-                                   size_t* workspace_bytes) {
+int nvfp4_round_workspace_bytes(const nvfp4_layer* layers, int n_layers, int max_M,
+                                size_t* workspace_bytes) {
     clear_error();
     int st = validate_layers(layers, n_layers, max_M);
     if (st) return st;
-    st = check_mode(mode, max_M);
-    if (st) return st;
-    if (mode != NVFP4_ROUND_PER_MATRIX && any_act_op(layers, n_layers))
-        return set_error(NVFP4_EUNSUPPORTED, "layers[].act_op: only the PER_MATRIX form chains");
     if (!workspace_bytes) return set_error(NVFP4_EINVAL, "workspace_bytes: NULL");
-    if (mode == NVFP4_ROUND_PERSISTENT) {
-        StreamRoundLayout lay;
-        *workspace_bytes = stream_round_layout(n_layers, &lay);
-        return NVFP4_OK;
-    }
-    if (mode == NVFP4_ROUND_CHAIN) {
-        ChainLayout y;
-        *workspace_bytes = chain_round_layout(layers, n_layers, &y);
-        return NVFP4_OK;
-    }
     size_t c = 0, p = 0;
     st = round_layout(layers, n_layers, max_M, &c, &p);
     if (st) return st;
@@ -172,37 +114,17 @@ int nvfp4_round_workspace_bytes_ex(const nvfp4_layer* layers, int n_layers, int 
     return NVFP4_OK;
 }
 
-int nvfp4_round_workspace_bytes(const nvfp4_layer* layers, int n_layers, int max_M,
-                                size_t* workspace_bytes) {
-    return nvfp4_round_workspace_bytes_ex(layers, n_layers, max_M, NVFP4_ROUND_PER_MATRIX,
-                                          workspace_bytes);
-}
-
-int nvfp4_round_create_ex(nvfp4_round* plan, const nvfp4_layer* layers, int n_layers, int max_M,
-                          int mode, void* workspace, size_t workspace_bytes, void* stream) {
+int nvfp4_round_create(nvfp4_round* plan, const nvfp4_layer* layers, int n_layers, int max_M,
+                       void* workspace, size_t workspace_bytes, void* stream) {
     clear_error();
     if (!plan) return set_error(NVFP4_EINVAL, "plan: NULL");
     *plan = nullptr;
     int st = validate_layers(layers, n_layers, max_M);
     if (st) return st;
-    st = check_mode(mode, max_M);
-    if (st) return st;
-    if (mode != NVFP4_ROUND_PER_MATRIX && any_act_op(layers, n_layers))
-        return set_error(NVFP4_EUNSUPPORTED, "layers[].act_op: only the PER_MATRIX form chains");
     size_t need_c = 0, need_p = 0;
-    StreamRoundLayout lay{};
-    ChainLayout chain{};
-    if (mode == NVFP4_ROUND_PERSISTENT) {
-        stream_round_layout(n_layers, &lay);
-    } else if (mode == NVFP4_ROUND_CHAIN) {
-        chain_round_layout(layers, n_layers, &chain);
-    } else {
-        st = round_layout(layers, n_layers, max_M, &need_c, &need_p);
-        if (st) return st;
-    }
-    const size_t need = mode == NVFP4_ROUND_PERSISTENT ? lay.total
-                        : mode == NVFP4_ROUND_CHAIN    ? chain.total
-                                                       : need_c + need_p;
+    st = round_layout(layers, n_layers, max_M, &need_c, &need_p);
+    if (st) return st;
+    const size_t need = need_c + need_p;
     if (workspace_bytes < need)
         return set_error(NVFP4_EINVAL, "workspace_bytes: %zu < %zu needed", workspace_bytes, need);
     if (need && !workspace) return set_error(NVFP4_EINVAL, "workspace: NULL");
@@ -212,9 +134,6 @@ int nvfp4_round_create_ex(nvfp4_round* plan, const nvfp4_layer* layers, int n_la
     if (!r) return set_error(NVFP4_EINVAL, "plan: out of host memory");
     r->magic = kRoundMagic;
     r->max_M = max_M;
-    r->mode = mode;
-    r->lay = lay;
-    r->chain = chain;
     r->layers.assign(layers, layers + n_layers);
     r->ws = workspace;
     r->ws_bytes = workspace_bytes;
@@ -245,25 +164,6 @@ int nvfp4_round_create_ex(nvfp4_round* plan, const nvfp4_layer* layers, int n_la
         e = hipStreamSynchronize(user);
         if (e != hipSuccess) st = hip_fail(e, "hipStreamSynchronize");
     }
-    if (!st && mode == NVFP4_ROUND_PERSISTENT) {
-        st = stream_round_grid(&r->grid);
-        if (!st) st = stream_round_write_descs(layers, n_layers, r->grid, workspace, lay, user);
-        if (!st) {
-            const unsigned int limit = kDefaultSpinLimit;
-            e = hipMemcpy((char*)workspace + lay.status_off + 4, &limit, 4, hipMemcpyHostToDevice);
-            if (e != hipSuccess) st = hip_fail(e, "hipMemcpy(spin limit)");
-        }
-    }
-    if (!st && mode == NVFP4_ROUND_CHAIN) {
-        st = chain_round_write(layers, n_layers, max_M, workspace, chain);
-        if (!st) {
-            const unsigned int limit = kDefaultSpinLimit;
-            e = hipMemcpy((char*)workspace + chain.status_off + 4, &limit, 4,
-                          hipMemcpyHostToDevice);
-            if (e != hipSuccess) st = hip_fail(e, "hipMemcpy(spin limit)");
-        }
-        if (!st) st = chain_check_dispatch(workspace, chain);
-    }
     for (int M = 1; M <= max_M && !st; ++M) {
         e = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal);
         if (e != hipSuccess) {
@@ -271,21 +171,15 @@ int nvfp4_round_create_ex(nvfp4_round* plan, const nvfp4_layer* layers, int n_la
             break;
         }
         int lst = NVFP4_OK;
-        if (mode == NVFP4_ROUND_PERSISTENT) {
-            lst = stream_launch_round(n_layers, M, r->grid, workspace, lay, cap);
-        } else if (mode == NVFP4_ROUND_CHAIN) {
-            lst = chain_launch_round(M, workspace, chain, cap);
-        } else {
-            for (int i = 0; i < n_layers && !lst; ++i) {
-                const nvfp4_layer& l = r->layers[i];
-                if (l.act_op == NVFP4_ACT_SWIGLU_PREV)
-                    lst = launch_swiglu((const uint16_t*)r->layers[i - 1].out_dev,
-                                        const_cast<uint16_t*>(l.act_dev), M, l.K, cap);
-                if (lst) break;
-                lst = run_gemm(r->plans[i], M, l.codes_dev, l.scales_dev, l.tensor_scale,
-                               l.act_dev, l.out_dev, workspace,
-                               RunOffsets{r->partial_off, 0, r->partial_off}, cap);
-            }
+        for (int i = 0; i < n_layers && !lst; ++i) {
+            const nvfp4_layer& l = r->layers[i];
+            if (l.act_op == NVFP4_ACT_SWIGLU_PREV)
+                lst = launch_swiglu((const uint16_t*)r->layers[i - 1].out_dev,
+                                    const_cast<uint16_t*>(l.act_dev), M, l.K, cap);
+            if (lst) break;
+            lst = run_gemm(r->plans[i], M, l.codes_dev, l.scales_dev, l.tensor_scale, l.act_dev,
+                           l.out_dev, workspace, RunOffsets{r->partial_off, 0, r->partial_off},
+                           cap);
         }
         hipGraph_t g = nullptr;
         e = hipStreamEndCapture(cap, &g);
@@ -323,52 +217,6 @@ int nvfp4_round_create_ex(nvfp4_round* plan, const nvfp4_layer* layers, int n_la
         return st;
     }
     *plan = r;
-    return NVFP4_OK;
-}
-
-int nvfp4_round_create(nvfp4_round* plan, const nvfp4_layer* layers, int n_layers, int max_M,
-                       void* workspace, size_t workspace_bytes, void* stream) {
-    return nvfp4_round_create_ex(plan, layers, n_layers, max_M, NVFP4_ROUND_PER_MATRIX, workspace,
-                                 workspace_bytes, stream);
-}
-
-int nvfp4_round_status(nvfp4_round plan, unsigned int* flags) {
-    clear_error();
-    if (!plan || plan->magic != kRoundMagic) return set_error(NVFP4_ESTATE, "plan: invalid handle");
-    if (!flags) return set_error(NVFP4_EINVAL, "flags: NULL");
-    *flags = 0;
-    size_t status_off = 0;
-    if (!sync_state(plan, &status_off)) return NVFP4_OK;
-    void* p = (char*)plan->ws + status_off;
-    NVFP4_HIP(hipDeviceSynchronize());
-    NVFP4_HIP(hipMemcpy(flags, p, 4, hipMemcpyDeviceToHost));
-    const unsigned int zero = 0;
-    NVFP4_HIP(hipMemcpy(p, &zero, 4, hipMemcpyHostToDevice));
-    if (*flags && plan->mode == NVFP4_ROUND_CHAIN) {
-        // Tickets, done counters, flags and every matrix's split-K counters
-        // (the ticket records between them stay).
-        const ChainLayout& y = plan->chain;
-        NVFP4_HIP(hipMemset((char*)plan->ws + y.tickets_off, 0, y.desc_off - y.tickets_off));
-        NVFP4_HIP(hipMemset((char*)plan->ws + y.regions_off, 0, y.total - y.regions_off));
-        NVFP4_HIP(hipDeviceSynchronize());
-    } else if (*flags) {
-        // A replay that timed out may have left completion counters behind:
-        // zero them (the descriptors after them stay) so the plan is usable.
-        NVFP4_HIP(hipMemset((char*)plan->ws + plan->lay.done_off, 0, plan->lay.status_off));
-        NVFP4_HIP(hipMemset((char*)plan->ws + plan->lay.flags_off, 0,
-                            plan->lay.total - plan->lay.flags_off));
-        NVFP4_HIP(hipDeviceSynchronize());
-    }
-    return NVFP4_OK;
-}
-
-int nvfp4_round_set_spin_limit(nvfp4_round plan, unsigned int limit) {
-    clear_error();
-    if (!plan || plan->magic != kRoundMagic) return set_error(NVFP4_ESTATE, "plan: invalid handle");
-    size_t status_off = 0;
-    if (!sync_state(plan, &status_off)) return NVFP4_OK;
-    NVFP4_HIP(hipDeviceSynchronize());
-    NVFP4_HIP(hipMemcpy((char*)plan->ws + status_off + 4, &limit, 4, hipMemcpyHostToDevice));
     return NVFP4_OK;
 }
 

@@ -14,6 +14,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+import oracle  # noqa: E402  (the acceptance bounds)
+
 
 def require_gpu():
     import torch
@@ -51,17 +53,44 @@ def pack(nv, codes_dev, scales_dev, K, N, t):
     return nv.PackedWeight.from_canonical(codes_dev, scales_dev, t, K, N)
 
 
-def run(nv, pw, act_dev, out_dtype, M=None, split_k=0, waves=0, chunks=0, kernel=0, tiles=0,
-        max_M=None, windows=0, verify_waves=0, verify_windows=0):
+# Elements of a canary region placed right after an output buffer, and the
+# bit patterns it holds (quiet NaNs no kernel writes): a store past the end of
+# [M][N] (a ragged tile, a wrong row stride) changes them.
+CANARY_ELEMS = 4096
+_CANARY = {2: 0x7FA5, 4: 0x7FA5A5A5}
+
+
+def canary_out(M, N, dtype):
+    """An [M][N] output tensor (NaN-poisoned) followed in memory by a canary
+    region.  Returns (out, assert_canary) where assert_canary(what) checks
+    that the region is untouched."""
+    import torch
+    n = M * N
+    buf = torch.empty(n + CANARY_ELEMS, dtype=dtype, device="cuda")
+    buf[:n].fill_(float("nan"))
+    ity = torch.int16 if buf.element_size() == 2 else torch.int32
+    pattern = _CANARY[buf.element_size()]
+    buf.view(ity)[n:] = pattern
+
+    def assert_canary(what=""):
+        tail = buf.view(ity)[n:]
+        bad = int((tail != pattern).sum().item())
+        assert bad == 0, "%s: %d canary elements after the output were overwritten" % (what, bad)
+
+    return buf[:n].view(M, N), assert_canary
+
+
+def run(nv, pw, act_dev, out_dtype, M=None, split_k=0, waves=0, chunks=0, max_M=None,
+        windows=0, verify_waves=0, verify_windows=0):
     import torch
     M = act_dev.shape[0] if M is None else M
     g = nv.Gemm(max_M or M, pw.K, pw.N, out_dtype, split_k=split_k, waves=waves, chunks=chunks,
-                kernel=kernel, tiles=tiles, windows=windows, verify_waves=verify_waves,
-                verify_windows=verify_windows)
+                windows=windows, verify_waves=verify_waves, verify_windows=verify_windows)
     dt = torch.float32 if out_dtype == nv.OUT_F32 else torch.bfloat16
-    out = torch.full((M, pw.N), float("nan"), dtype=dt, device="cuda")  # poison
+    out, assert_canary = canary_out(M, pw.N, dt)
     g(pw, act_dev, out, M=M)
     torch.cuda.synchronize()
+    assert_canary("M=%d K=%d N=%d" % (M, pw.K, pw.N))
     return out, g
 
 
@@ -72,9 +101,7 @@ def check(out, y, S, bf16: bool, what=""):
     assert o.shape == y.shape, (o.shape, y.shape)
     assert np.all(np.isfinite(o)), "non-finite output %s" % what
     err = np.abs(o - y)
-    tol = np.ldexp(S, -16)
-    if bf16:
-        tol = tol + np.ldexp(np.abs(y) + tol, -8)
+    tol = oracle.tolerance_bf16(y, S) if bf16 else oracle.tolerance(S)
     bad = err > tol
     if bad.any():
         i = np.argwhere(bad)[0]

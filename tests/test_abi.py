@@ -93,37 +93,23 @@ def test_gemm_config_validation(nv):
     with pytest.raises(nv.Nvfp4Error) as e:
         nv.nvfp4_gemm_create(8, 5120, 5120, 1, split_k=0, waves=3)
     assert "waves" in e.value.message
-    SPLITK = nv.KERNEL_SPLITK
-    plan, ws = nv.nvfp4_gemm_create(8, 5120, 5120, 1, split_k=5, waves=8, kernel=SPLITK)
+    plan, ws = nv.nvfp4_gemm_create(8, 5120, 5120, 1, split_k=5, waves=8)
     assert ws > 0
     nv.nvfp4_gemm_destroy(plan)
-    plan, ws = nv.nvfp4_gemm_create(8, 2048, 5120, 1, split_k=1, waves=4, kernel=SPLITK)
+    plan, ws = nv.nvfp4_gemm_create(8, 2048, 5120, 1, split_k=1, waves=4)
     assert ws == 0  # no K split: no partials, no counters
     nv.nvfp4_gemm_destroy(plan)
     # a workgroup holds at most 4 x 512 values of K, so K = 5120 needs 3 slices
     with pytest.raises(nv.Nvfp4Error) as e:
-        nv.nvfp4_gemm_create(8, 5120, 5120, 1, split_k=1, kernel=SPLITK)
+        nv.nvfp4_gemm_create(8, 5120, 5120, 1, split_k=1)
     assert e.value.message.startswith("config.split_k")
     for bad in (0 - 1, 5):
         with pytest.raises(nv.Nvfp4Error) as e:
-            nv.nvfp4_gemm_create(8, 5120, 5120, 1, chunks=bad, kernel=SPLITK)
+            nv.nvfp4_gemm_create(8, 5120, 5120, 1, chunks=bad)
         assert e.value.message.startswith("config.chunks")
-    plan, ws = nv.nvfp4_gemm_create(8, 5120, 5120, 1, chunks=4, kernel=SPLITK)
+    plan, ws = nv.nvfp4_gemm_create(8, 5120, 5120, 1, chunks=4)
     assert ws > 0
     nv.nvfp4_gemm_destroy(plan)
-    # the streaming kernel needs no workspace
-    for tiles in (0, 2, 4, 8):
-        plan, ws = nv.nvfp4_gemm_create(8, 5120, 5120, 1, tiles=tiles, kernel=nv.KERNEL_STREAM)
-        assert ws == 0
-        nv.nvfp4_gemm_destroy(plan)
-    for bad_kernel in (-1, 3):
-        with pytest.raises(nv.Nvfp4Error) as e:
-            nv.nvfp4_gemm_create(8, 5120, 5120, 1, kernel=bad_kernel)
-        assert e.value.message.startswith("config.kernel")
-    for bad_tiles in (1, 3, 16):
-        with pytest.raises(nv.Nvfp4Error) as e:
-            nv.nvfp4_gemm_create(8, 5120, 5120, 1, tiles=bad_tiles)
-        assert e.value.message.startswith("config.tiles")
 
 
 def test_verify_width_config(nv):
@@ -180,7 +166,7 @@ FAKE = 1 << 20  # a 16-byte-aligned non-null address; never dereferenced
     (dict(workspace=None), "workspace", 1), (dict(workspace=FAKE + 4), "workspace", 1)])
 def test_gemm_run_validates_before_any_gpu_call(nv, kw, word, status):
     # a split-K plan: it needs a workspace, so every argument is checked
-    plan, ws = nv.nvfp4_gemm_create(8, 5120, 5120, 1, kernel=nv.KERNEL_SPLITK)
+    plan, ws = nv.nvfp4_gemm_create(8, 5120, 5120, 1)
     assert ws > 0
     args = dict(M=4, K=5120, N=5120, codes=FAKE, scales=FAKE, act=FAKE, out=FAKE,
                 workspace=FAKE)
@@ -230,18 +216,12 @@ def test_round_validation(nv):
         with pytest.raises(nv.Nvfp4Error) as e:
             nv.nvfp4_round_workspace_bytes(layers, 8)
         assert e.value.message.startswith(word), e.value.message
-    # per-matrix rounds take the verify widths too; the single-launch forms
-    # only decode widths
+    # rounds take the verify widths too (up to 64 rows)
     assert nv.nvfp4_round_workspace_bytes([good] * 2, 64) >= 0
     with pytest.raises(nv.Nvfp4Error) as e:
         nv.nvfp4_round_workspace_bytes([good], 65)
     assert e.value.message.startswith("max_M")
-    for mode in (nv.ROUND_PERSISTENT, nv.ROUND_CHAIN):
-        with pytest.raises(nv.Nvfp4Error) as e:
-            nv.nvfp4_round_workspace_bytes([good], 9, mode=mode)
-        assert e.value.message.startswith("max_M"), e.value.message
-    # chaining: SwiGLU of the previous output needs a previous bf16 matrix of N = 2 K,
-    # and only the per-matrix form takes it
+    # chaining: SwiGLU of the previous output needs a previous bf16 matrix of N = 2 K
     gu = dict(good, K=256, N=64)
     dn = dict(good, K=32, N=256, act_op=nv.ACT_SWIGLU_PREV)
     assert nv.nvfp4_round_workspace_bytes([gu, dn], 8) >= 0
@@ -251,9 +231,6 @@ def test_round_validation(nv):
         with pytest.raises(nv.Nvfp4Error) as e:
             nv.nvfp4_round_workspace_bytes(layers, 8)
         assert e.value.message.startswith(word), e.value.message
-    with pytest.raises(nv.Nvfp4Error) as e:
-        nv.nvfp4_round_workspace_bytes([gu, dn], 8, mode=nv.ROUND_CHAIN)
-    assert e.value.status == nv.EUNSUPPORTED
     L = nv.lib()
     for args, word in (((FAKE, 0, 4, FAKE, None), "M"), ((FAKE, 2, 0, FAKE, None), "F"),
                        ((None, 2, 4, FAKE, None), "gate_up"), ((FAKE, 2, 4, None, None), "out"),
@@ -262,3 +239,42 @@ def test_round_validation(nv):
         assert nv.last_error().startswith(word), nv.last_error()
     assert L.nvfp4_round_run(None, 1, None) == nv.ESTATE
     assert nv.nvfp4_round_graph_nodes(None, 1) == 0
+
+
+def test_stream_read_validates(nv):
+    L = nv.lib()
+    sink = 0x10000
+    for args, word in (((None, 1024, sink, None), "buf"), ((FAKE + 8, 1024, sink, None), "buf"),
+                       ((FAKE, 0, sink, None), "bytes"), ((FAKE, 1000, sink, None), "bytes"),
+                       ((FAKE, 1024, None, None), "sink"), ((FAKE, 1024, sink + 2, None), "sink")):
+        assert L.nvfp4_stream_read(*args) == nv.EINVAL
+        assert nv.last_error().startswith(word), nv.last_error()
+
+
+def _gpu_visible():
+    import torch
+    return torch.cuda.is_available()
+
+
+@pytest.mark.skipif("_gpu_visible()",
+                    reason="forces a HIP runtime failure by launching with no device present; "
+                           "with a GPU the same calls would run")
+def test_hip_failure_is_returned_as_ehip(nv):
+    """With no device, valid requests reach the HIP runtime, which fails: each
+    entry point returns NVFP4_EHIP (it never aborts) and the message names the
+    failing HIP call and carries the runtime's text."""
+    L = nv.lib()
+    sink = 0x10000
+    st = L.nvfp4_stream_read(FAKE, 1 << 20, sink, None)
+    assert st == nv.EHIP, (st, nv.last_error())
+    msg = nv.last_error()
+    assert "hip" in msg.lower() and "(" in msg, msg
+    st = L.nvfp4_workspace_clear(FAKE, 4096, None)
+    assert st == nv.EHIP, (st, nv.last_error())
+    plan, ws = nv.nvfp4_gemm_create(8, 256, 16, 0)
+    try:
+        st = L.nvfp4_gemm_run(plan, 1, 256, 16, FAKE, FAKE, ctypes.c_float(1.0), FAKE, FAKE,
+                              FAKE if ws else None, None)
+        assert st == nv.EHIP, (st, nv.last_error())
+    finally:
+        nv.nvfp4_gemm_destroy(plan)

@@ -171,15 +171,14 @@ RAGGED = [(1, 16, 1), (3, 48, 17), (8, 512, 16), (5, 1040, 100), (8, 2576, 33),
 
 @pytest.mark.parametrize("M,K,N", RAGGED)
 @pytest.mark.parametrize("bf16", [False, True])
-@pytest.mark.parametrize("kernel", [1, 2])
-def test_random_planes_ragged(nv, M, K, N, bf16, kernel):
+def test_random_planes_ragged(nv, M, K, N, bf16):
     """Every code and every finite scale byte (subnormal ones included),
-    shapes with ragged K and N tails, both decode kernels."""
+    shapes with ragged K and N tails, default plans."""
     codes, scales = synth.random_planes(M * 7 + K, N, N, K)
     t = float(np.float32(np.random.default_rng(K + N).uniform(1e-4, 1e-2)))
     act = synth.activations(M + K, N, M, K)
     pw = pack(nv, dev(codes), dev(scales), K, N, t)
-    out, _ = run(nv, pw, dev_bf16(act), nv.OUT_BF16 if bf16 else nv.OUT_F32, kernel=kernel)
+    out, _ = run(nv, pw, dev_bf16(act), nv.OUT_BF16 if bf16 else nv.OUT_F32)
     y, S = oracle.gemm(act, codes, scales, t)
     check(out, y, S, bf16=bf16, what="ragged %r" % ((M, K, N),))
 
@@ -195,7 +194,7 @@ def test_streamed_slices_ragged(nv, M, K, N, cfg):
     t = 1.5e-3
     act = synth.activations(M + 3, K + N, M, K)
     pw = pack(nv, dev(codes), dev(scales), K, N, t)
-    out, _ = run(nv, pw, dev_bf16(act), nv.OUT_F32, kernel=2, **cfg)
+    out, _ = run(nv, pw, dev_bf16(act), nv.OUT_F32, **cfg)
     y, S = oracle.gemm(act, codes, scales, t)
     check(out, y, S, bf16=False, what="streamed %r %r" % ((M, K, N), cfg))
 
@@ -236,10 +235,9 @@ def test_projection_5120_full(nv, M):
     check(out32, y, S, bf16=False, what="projection f32 M=%d" % M)
 
 
-CONFIGS = ([dict(kernel=2, chunks=c, waves=w) for w in (4, 8) for c in (1, 2, 3, 4)] +
-           [dict(kernel=1, tiles=t) for t in (2, 4, 8)] +
+CONFIGS = ([dict(chunks=c, waves=w) for w in (4, 8) for c in (1, 2, 3, 4)] +
            # streamed slices: several windows of `chunks` superblocks per workgroup
-           [dict(kernel=2, chunks=c, waves=w, windows=n)
+           [dict(chunks=c, waves=w, windows=n)
             for (w, c, n) in ((4, 1, 3), (4, 2, 2), (8, 2, 3), (8, 1, 5), (4, 2, 6), (8, 3, 2))])
 
 
@@ -372,6 +370,37 @@ def test_verify_width_boundary_to_prefill(nv):
         out, _ = run(nv, pw, dev_bf16(act[:m]), nv.OUT_F32, max_M=65)
         y, S = oracle.gemm(act[:m], codes, scales, 0.002)
         check(out, y, S, bf16=False, what="M=%d" % m)
+
+
+# Default verify-width plans at the shapes that reach each branch of the plan:
+# gate_up (K 5120, N 34816: more column groups than compute units -> two K
+# slices; 8 waves per workgroup at 49..64 rows), down (K 17408, N 5120: fewer
+# groups than units -> slices sized to one workgroup per unit) and a matrix
+# wide enough for no K split at all (N >= 65536 with 4 tiles per group).
+VERIFY_FULL = [(5120, 34816), (17408, 5120), (1024, 65552)]
+
+
+@pytest.mark.parametrize("K,N", VERIFY_FULL)
+def test_verify_width_default_plans_full_shapes(nv, K, N):
+    import torch
+    codes, scales = synth.random_planes(K + 3, N + 1, N, K)
+    t = 2.5e-3
+    act = synth.activations(K + 4, N + 2, 64, K)
+    pw = pack(nv, dev(codes), dev(scales), K, N, t)
+    g = nv.Gemm(64, K, N, nv.OUT_BF16)
+    rng = np.random.default_rng(N)
+    cols = set(rng.choice(N, 48, replace=False).tolist())
+    cols |= {0, 15, 16, 63, 64, N // 2, N - 65, N - 64, N - 17, N - 16, N - 1}
+    cols = np.array(sorted(cols))
+    sel = torch.from_numpy(cols).cuda()
+    y_all, S_all = oracle.gemm(act, codes[cols], scales[cols], t)
+    a = dev_bf16(act)
+    for M in (16, 40, 64):
+        out = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+        g(pw, a[:M], out, M=M)
+        torch.cuda.synchronize()
+        check(out[:, sel], y_all[:M], S_all[:M], bf16=True, what="verify M=%d K=%d N=%d" % (M, K, N))
+        assert not torch.isnan(out).any().item(), "unwritten outputs at M=%d" % M
 
 
 # ---- prefill (M > 8: dequantised tiles, bf16 MFMA) ------------------------------

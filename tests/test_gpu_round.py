@@ -2,19 +2,18 @@
 
 A round of 12 matrices (3 layers x the four projections of the 27B-class
 structure, at the real K and 1/16 of the real N) is replayed at every width
-M = 1..8 in each of the three forms (persistent, per-matrix, chained) and
-every matrix's output is compared with the oracle.  Replays are repeated with
-eager GEMM work between them, each checked, and the outputs are poisoned
-before every replay so a skipped node shows.  A second round feeds outputs
-into later matrices' activations (overwriting buffers that earlier matrices
-read) to check the ordering and visibility guarantees of the one-launch
-forms."""
+M = 1..8 and every matrix's output is compared with the oracle.  Replays are
+repeated with eager GEMM work between them, each checked, and the outputs are
+poisoned before every replay so a skipped node shows; a canary region after
+each output must stay untouched.  A second round feeds outputs into later
+matrices' activations (overwriting buffers that earlier matrices read) to
+check the ordering of the graph's launches."""
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from tests.gpu_util import bf16_bits, check, dev, dev_bf16, host, pack, require_gpu
+from tests.gpu_util import bf16_bits, canary_out, check, dev, dev_bf16, host, pack, require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -36,20 +35,17 @@ def small_round():
             out_dtype = nv.OUT_F32 if (layer + j) % 3 == 0 else nv.OUT_BF16
             dt = torch.float32 if out_dtype == nv.OUT_F32 else torch.bfloat16
             pw = pack(nv, dev(codes), dev(scales), K, N, t)
+            out, canary = canary_out(8, N, dt)
             specs.append(dict(K=K, N=N, codes=pw.codes, scales=pw.scales, tensor_scale=t,
-                              act=dev_bf16(act), out=torch.empty((8, N), dtype=dt, device="cuda"),
-                              out_dtype=out_dtype, pw=pw))
+                              act=dev_bf16(act), out=out, out_dtype=out_dtype, pw=pw,
+                              canary=canary))
             ref.append((y, S))
-    plans = {}
-    keep = []
-    for mode in (nv.ROUND_PERSISTENT, nv.ROUND_PER_MATRIX, nv.ROUND_CHAIN):
-        ws_bytes = nv.nvfp4_round_workspace_bytes(specs, 8, mode=mode)
-        ws = torch.full((max(ws_bytes, 16),), 0x5A, dtype=torch.uint8, device="cuda")  # create zeroes it
-        plans[mode] = nv.nvfp4_round_create(specs, 8, ws, ws_bytes, mode=mode)
-        keep.append(ws)
-    yield nv, plans, specs, ref
-    for p in plans.values():
-        nv.nvfp4_round_destroy(p)
+    ws_bytes = nv.nvfp4_round_workspace_bytes(specs, 8)
+    ws = torch.full((max(ws_bytes, 16),), 0x5A, dtype=torch.uint8, device="cuda")  # create zeroes it
+    plan = nv.nvfp4_round_create(specs, 8, ws, ws_bytes)
+    yield nv, plan, specs, ref
+    nv.nvfp4_round_destroy(plan)
+    del ws
 
 
 def _poison(specs):
@@ -61,36 +57,28 @@ def _check_all(nv, specs, ref, M, what):
     for i, (s, (y, S)) in enumerate(zip(specs, ref)):
         check(s["out"][:M], y[:M], S[:M], bf16=s["out_dtype"] == nv.OUT_BF16,
               what="%s matrix %d" % (what, i))
-
-
-MODES = (0, 1, 2)  # persistent, per-matrix, chained
+        s["canary"]("%s matrix %d" % (what, i))
 
 
 def test_graph_nodes(small_round):
-    nv, plans, specs, _ = small_round
+    nv, plan, specs, _ = small_round
     for M in range(1, 9):
-        assert nv.nvfp4_round_graph_nodes(plans[nv.ROUND_PER_MATRIX], M) == len(specs)
-        assert nv.nvfp4_round_graph_nodes(plans[nv.ROUND_PERSISTENT], M) == 1
-        assert nv.nvfp4_round_graph_nodes(plans[nv.ROUND_CHAIN], M) == 1
+        assert nv.nvfp4_round_graph_nodes(plan, M) == len(specs)
 
 
-@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("M", range(1, 9))
-def test_round_every_width(small_round, M, mode):
+def test_round_every_width(small_round, M):
     import torch
-    nv, plans, specs, ref = small_round
+    nv, plan, specs, ref = small_round
     _poison(specs)
-    nv.nvfp4_round_run(plans[mode], M)
+    nv.nvfp4_round_run(plan, M)
     torch.cuda.synchronize()
-    _check_all(nv, specs, ref, M, "mode %d width %d" % (mode, M))
-    assert nv.nvfp4_round_status(plans[mode]) == 0
+    _check_all(nv, specs, ref, M, "width %d" % M)
 
 
-@pytest.mark.parametrize("mode", MODES)
-def test_replays_with_eager_work_between(small_round, mode):
+def test_replays_with_eager_work_between(small_round):
     import torch
-    nv, plans, specs, ref = small_round
-    plan = plans[mode]
+    nv, plan, specs, ref = small_round
     s0 = specs[2]
     g = nv.Gemm(8, s0["K"], s0["N"], s0["out_dtype"])
     scratch = torch.empty_like(s0["out"])
@@ -109,64 +97,21 @@ def test_replays_with_eager_work_between(small_round, mode):
         torch.cuda.synchronize()
 
 
-def test_all_forms_back_to_back(small_round):
-    """The forms replayed one after the other on the same buffers each match
-    the oracle.  The chained and per-matrix forms slice K alike for K < 16384,
-    so there they agree bit for bit."""
-    import torch
-    nv, plans, specs, ref = small_round
-    outs = {}
-    for mode in MODES:
-        _poison(specs)
-        nv.nvfp4_round_run(plans[mode], 8)
-        torch.cuda.synchronize()
-        _check_all(nv, specs, ref, 8, "mode %d" % mode)
-        outs[mode] = [host(s["out"]).copy() for s in specs]
-    assert len(outs) == 3
-    for i, s in enumerate(specs):
-        if s["K"] < 16384:
-            assert np.array_equal(outs[1][i].view(np.uint8), outs[2][i].view(np.uint8)), i
-
-
-@pytest.mark.parametrize("mode", (0, 2))
-def test_forced_wait_timeout_is_reported_and_recovers(small_round, mode):
-    """A spin limit of 0 makes every cross-matrix wait give up at once (the
-    kernel still exits); the flag is reported, the counters re-armed, and the
-    next replay with the normal limit is correct again."""
-    import torch
-    nv, plans, specs, ref = small_round
-    plan = plans[mode]
-    nv.nvfp4_round_set_spin_limit(plan, 0)
-    for _ in range(3):
-        nv.nvfp4_round_run(plan, 8)
-    torch.cuda.synchronize()
-    flags = nv.nvfp4_round_status(plan)
-    nv.nvfp4_round_set_spin_limit(plan, 1 << 16)
-    assert flags in (0, 1)  # with no real wait needed the flag may stay clear
-    _poison(specs)
-    nv.nvfp4_round_run(plan, 8)
-    torch.cuda.synchronize()
-    _check_all(nv, specs, ref, 8, "after time-out")
-    assert nv.nvfp4_round_status(plan) == 0
-
-
 def test_round_invalid_width(small_round):
-    nv, plans, _, _ = small_round
-    for plan in plans.values():
-        with pytest.raises(nv.Nvfp4Error) as e:
-            nv.nvfp4_round_run(plan, 9)
-        assert e.value.message.startswith("M")
+    nv, plan, _, _ = small_round
+    with pytest.raises(nv.Nvfp4Error) as e:
+        nv.nvfp4_round_run(plan, 9)
+    assert e.value.message.startswith("M")
 
 
-def test_chain_outputs_feed_later_matrices():
+def test_round_outputs_feed_later_matrices():
     """Outputs of a round feed later matrices' activations, and buffers that
-    earlier matrices read are overwritten and read again within the launch:
+    earlier matrices read are overwritten and read again within the replay:
         m0: A -> B   m1: B -> A   m2: A -> C (fp32)   m3: A -> D
         m4: D -> B   m5: B -> E (fp32)
-    Every replay starts from A = X0 and poisoned B..E.  The chained form must
-    equal the per-matrix form (kernel boundaries between matrices) bit for bit
-    on every output, and the matrices whose inputs are still in place at the
-    end (m2..m5) must match the oracle on those inputs."""
+    Every replay starts from A = X0 and poisoned B..E.  Replays must repeat
+    bit for bit, and the matrices whose inputs are still in place at the end
+    (m2..m5) must match the oracle on those inputs."""
     import torch
     nv = require_gpu()
     dims = [(1024, 1536, "A", "B", nv.OUT_BF16), (1536, 1024, "B", "A", nv.OUT_BF16),
@@ -196,33 +141,28 @@ def test_chain_outputs_feed_later_matrices():
         for k in "BCDE":
             bufs[k].fill_(float("nan"))
 
-    results, keep = {}, []
-    for mode in (nv.ROUND_PER_MATRIX, nv.ROUND_CHAIN):
-        wsb = nv.nvfp4_round_workspace_bytes(specs, 8, mode=mode)
-        ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda")
-        keep.append(ws)
-        plan = nv.nvfp4_round_create(specs, 8, ws, wsb, mode=mode)
-        try:
-            for M in (8, 3, 8):
-                reset()
-                nv.nvfp4_round_run(plan, M)
-                torch.cuda.synchronize()
-                snap = {k: host(v).copy() for k, v in bufs.items()}
-                results.setdefault(M, {})[mode] = snap
-                assert nv.nvfp4_round_status(plan) == 0
-        finally:
-            nv.nvfp4_round_destroy(plan)
-    for M, by_mode in results.items():
-        a, b = by_mode[nv.ROUND_PER_MATRIX], by_mode[nv.ROUND_CHAIN]
-        for k in bufs:
-            assert np.array_equal(a[k][:M].view(np.uint8), b[k][:M].view(np.uint8)), (M, k)
+    wsb = nv.nvfp4_round_workspace_bytes(specs, 8)
+    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    plan = nv.nvfp4_round_create(specs, 8, ws, wsb)
+    snaps = []
+    try:
+        for M in (8, 3, 8):
+            reset()
+            nv.nvfp4_round_run(plan, M)
+            torch.cuda.synchronize()
+            snaps.append((M, {k: host(v).copy() for k, v in bufs.items()}))
+    finally:
+        nv.nvfp4_round_destroy(plan)
+    (_, a), (_, b) = snaps[0], snaps[2]
+    for k in bufs:
+        assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
     # Oracle on the inputs left in place (width 8).
     for i in (2, 3, 4, 5):
         s = specs[i]
         codes, scales, t = planes[i]
         act = bf16_bits(s["act"])
         y, S = oracle.gemm(act, codes, scales, t)
-        check(s["out"], y, S, bf16=s["out_dtype"] == nv.OUT_BF16, what="chained m%d" % i)
+        check(s["out"], y, S, bf16=s["out_dtype"] == nv.OUT_BF16, what="fed-forward m%d" % i)
 
 
 # ---- verify widths (per-matrix round with max_M = 64) ----------------------------
@@ -243,9 +183,10 @@ def verify_round():
         out_dtype = nv.OUT_F32 if j % 2 == 0 else nv.OUT_BF16
         dt = torch.float32 if out_dtype == nv.OUT_F32 else torch.bfloat16
         pw = pack(nv, dev(codes), dev(scales), K, N, t)
+        out, canary = canary_out(64, N, dt)
         specs.append(dict(K=K, N=N, codes=pw.codes, scales=pw.scales, tensor_scale=t,
-                          act=dev_bf16(act), out=torch.empty((64, N), dtype=dt, device="cuda"),
-                          out_dtype=out_dtype, pw=pw))
+                          act=dev_bf16(act), out=out, out_dtype=out_dtype, pw=pw,
+                          canary=canary))
         ref.append((y, S))
     ws_bytes = nv.nvfp4_round_workspace_bytes(specs, 64)
     ws = torch.full((max(ws_bytes, 16),), 0x5A, dtype=torch.uint8, device="cuda")

@@ -1,12 +1,12 @@
 """GPU parity of the SwiGLU step (bit for bit against the oracle) and of a
-round that chains gate_up -> SwiGLU -> down (against the same steps run as
-separate calls)."""
+round that chains gate_up -> SwiGLU -> down (against the oracle, and bit for
+bit against the same steps run as separate calls)."""
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from tests.gpu_util import dev, dev_bf16, host, pack, require_gpu, bf16_bits
+from tests.gpu_util import bf16_bits, check, dev, dev_bf16, host, pack, require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -43,25 +43,32 @@ def test_swiglu_matches_oracle(nv, M, F):
 
 def test_chained_mlp_round(nv):
     """Two layers of x -> gate_up -> SwiGLU -> down, the down matrices reading
-    the round-made SwiGLU of the gate_up outputs; every replay (widths 1, 5, 8)
-    must equal the same steps run as separate calls, bit for bit."""
+    the round-made SwiGLU of the gate_up outputs.  Every replay (widths 1, 5,
+    8) is checked against the oracle step by step: gate_up against
+    oracle.gemm, the round-made activations bit for bit against oracle.swiglu
+    of the gate_up output the round wrote, and down against oracle.gemm of
+    those activations (bf16 bound).  It must also equal the same steps run as
+    separate calls, bit for bit."""
     import torch
     K, F = 512, 1024
-    specs, mats = [], []
+    specs, mats, planes = [], [], []
     for layer in range(2):
         for j, (k, n) in enumerate(((K, 2 * F), (F, K))):
             codes, scales = synth.random_planes(40 + layer, j, n, k)
             t = 2e-3 if j == 0 else 5e-4
             pw = pack(nv, dev(codes), dev(scales), k, n, t)
             if j == 0:
-                act = dev_bf16(synth.activations(41 + layer, 0, 8, k))
+                x = synth.activations(41 + layer, 0, 8, k)
+                act = dev_bf16(x)
             else:
+                x = None
                 act = torch.zeros((8, k), dtype=torch.bfloat16, device="cuda")  # round-made
             out = torch.empty((8, n), dtype=torch.bfloat16, device="cuda")
             specs.append(dict(K=k, N=n, codes=pw.codes, scales=pw.scales, tensor_scale=t,
                               act=act, out=out, out_dtype=nv.OUT_BF16,
                               act_op=nv.ACT_SWIGLU_PREV if j == 1 else nv.ACT_INPUT))
             mats.append(pw)
+            planes.append((codes, scales, t, x))
     ws_bytes = nv.nvfp4_round_workspace_bytes(specs, 8)
     ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     plan = nv.nvfp4_round_create(specs, 8, ws, ws_bytes)
@@ -74,6 +81,17 @@ def test_chained_mlp_round(nv):
             torch.cuda.synchronize()
             for layer in range(2):
                 gu_s, dn_s = specs[2 * layer], specs[2 * layer + 1]
+                # the oracle, step by step
+                gc, gs, gt, gx = planes[2 * layer]
+                dc, ds, dt, _ = planes[2 * layer + 1]
+                y, S = oracle.gemm(gx[:M], gc, gs, gt)
+                check(gu_s["out"][:M], y, S, bf16=True, what="gate_up M=%d" % M)
+                gu_bits = bf16_bits(gu_s["out"][:M])
+                h = oracle.swiglu(gu_bits)
+                assert np.array_equal(bf16_bits(dn_s["act"][:M]), h), (M, layer)
+                y, S = oracle.gemm(h, dc, ds, dt)
+                check(dn_s["out"][:M], y, S, bf16=True, what="down M=%d" % M)
+                # the same steps as separate calls
                 g_ref = torch.empty((M, 2 * F), dtype=torch.bfloat16, device="cuda")
                 nv.Gemm(M, K, 2 * F, nv.OUT_BF16)(mats[2 * layer], gu_s["act"][:M], g_ref)
                 h_ref = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
