@@ -129,6 +129,14 @@ typedef struct nvfp4_gemm_config {
     int verify_waves;   /* verify widths (8 < M <= 64): waves per workgroup, 4, 8
                            or 16 (0: 4 up to 48 rows, 8 above) */
     int verify_windows; /* verify widths: superblocks per K slice (0: by shape) */
+    int tile_max_m;     /* widths M <= tile_max_m (at most 4) run the kernel with one
+                           workgroup per 16-column tile over all of K, its waves
+                           splitting K and adding in LDS (no workspace); 0: by shape
+                           (up to 4 for matrices of fewer than 4 x compute-unit
+                           tiles, 2 for wider ones, none when K needs more than 12
+                           waves); -1: never */
+    int tile_superblocks; /* that kernel: superblocks of 512 k per wave, 1..3 (0: by
+                             shape) */
 } nvfp4_gemm_config;
 
 /* Create a plan for GEMMs of shape (M <= max_M) x K x N with the given output

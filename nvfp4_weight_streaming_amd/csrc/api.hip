@@ -95,6 +95,7 @@ int run_gemm(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_
     if (M > NVFP4_DECODE_MAX_M && p->ver.enabled)
         return launch_verify(p, M, codes, scales, ts, act, out, ws, off.ver_counters,
                              off.ver_partial, s);
+    if (M <= p->tile.max_m) return launch_tile(p, M, codes, scales, ts, act, out, s);
     return launch_decode(p, M, codes, scales, ts, act, out, ws, partial_off, s);
 }
 
@@ -143,6 +144,7 @@ static int create_plan(nvfp4_gemm* plan, int max_M, int K, int N, int out_dtype,
     p->Kp = padded_k(K);
     p->Np = padded_n(N);
     int st = make_decode_config(K, N, max_M, cfg, &p->dec);
+    if (!st) st = make_tile_config(K, N, max_M, cfg, &p->tile);
     if (!st) st = make_verify_config(K, N, max_M, cfg, &p->ver);
     if (!st) st = make_prefill_config(max_M, K, N, &p->pre);
     if (st != NVFP4_OK) {

@@ -65,6 +65,14 @@ struct VerifyConfig {
     size_t ws_off; // offset of its counters and partials in the plan's workspace
 };
 
+// Narrow widths (M <= 4): one workgroup per column tile over all of K, its
+// waves splitting K and adding their sums in LDS (decode_tile_kernel).
+struct TileConfig {
+    int max_m;  // largest M routed to the tile kernel (0: none)
+    int sbw;    // superblocks of 512 k per wave (1..3)
+    int waves;  // waves per workgroup: ceil(K superblocks / sbw), 1..16
+};
+
 struct PrefillConfig {
     int enabled;
     size_t ws_off;    // partial sums of K-split tiles: offset in the workspace
@@ -78,6 +86,7 @@ struct nvfp4_gemm_plan {
     int max_M, K, N, out_dtype;
     int Kp, Np;
     nvfp4::DecodeConfig dec;
+    nvfp4::TileConfig tile;
     nvfp4::VerifyConfig ver;
     nvfp4::PrefillConfig pre;
     size_t ws_bytes;
@@ -93,6 +102,7 @@ int device_cus();
 int xcd_mapping_verified();
 int make_verify_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, VerifyConfig* out);
 int make_decode_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, DecodeConfig* out);
+int make_tile_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, TileConfig* out);
 int make_prefill_config(int max_M, int K, int N, PrefillConfig* out);
 
 // Launchers (no validation: callers validated).  Return NVFP4_OK or EHIP.
@@ -101,6 +111,8 @@ int make_prefill_config(int max_M, int K, int N, PrefillConfig* out);
 int launch_decode(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
                   float ts, const uint16_t* act, void* out, void* ws, size_t partial_off,
                   hipStream_t s);
+int launch_tile(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
+                float ts, const uint16_t* act, void* out, hipStream_t s);
 int launch_verify(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
                   float ts, const uint16_t* act, void* out, void* ws, size_t counters_off,
                   size_t partial_off, hipStream_t s);

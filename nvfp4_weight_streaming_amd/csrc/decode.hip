@@ -320,6 +320,191 @@ __global__ __launch_bounds__(WAVES * 64) void decode_window_kernel(
                                ng, split, nt, &s_last);
 }
 
+// ---- narrow widths: one workgroup per column tile ------------------------------------
+
+// M <= 4 lanes.  With few activation rows a workgroup can afford the whole of
+// K's activations (at most 4 x K bf16), so one workgroup owns one 16-column
+// tile over all of K and its waves split K: wave p streams superblocks
+// [p SBW, p SBW + SBW), issuing all of its weight loads and its activation
+// rows (direct-to-LDS copies, into its own LDS rows) at once, then computes
+// with the split-A MFMA of the decode kernel.  The waves' sums meet in LDS
+// and are added in wave order, so there is no split-K hand-off between
+// workgroups, no workspace and no atomic.  Lanes whose A-operand row is not a
+// live activation row read a zero row.
+//
+// Measured in 64-node graphs on MI355X at M = 1 against the split-K kernel:
+// qkv (5120 x 7168) 6.65 us against 8.15, o (6144 x 5120) 6.57 against 7.71,
+// gate_up (5120 x 34816) 18.7 against 20.1, the output head at plain-read
+// speed (64.0 us; a plain read of its bytes 64.2).  It loses at M = 8, where
+// every workgroup re-stages 80 KB of activations per tile, and for long K
+// (down, 34 superblocks), whose waves per workgroup leave one workgroup per
+// compute unit.
+template <int SBW, int MR, bool BF16>
+__global__ __launch_bounds__(1024) void decode_tile_kernel(
+    const uint4* __restrict__ codes, const uint4* __restrict__ scales,
+    const uint16_t* __restrict__ act, void* __restrict__ out, float ts, int M, int K, int N,
+    int nsb) {
+    constexpr int kRow = SBW * kSuperK + kLdsPad;  // bf16 elements per staged row
+    extern __shared__ __attribute__((aligned(16))) __bf16 tile_lds[];
+    const int waves = blockDim.x >> 6;
+    // The wave index is uniform; saying so keeps the activation resources scalar.
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
+    const int nt = blockIdx.x;
+    const int col = lane & 15, g = lane >> 4;
+    __bf16* zero = tile_lds;                                // one row of zeros
+    __bf16* rows = tile_lds + kRow + wave * MR * kRow;      // this wave's MR rows
+    float* red = (float*)(tile_lds + kRow + waves * MR * kRow);  // [waves][8][16]
+    for (int o = threadIdx.x; o < kRow / 8; o += blockDim.x)
+        *(uint4*)(zero + 8 * o) = make_uint4(0, 0, 0, 0);
+
+    // Every wave has at least one superblock (waves = ceil(nsb / SBW)); the
+    // last one may have fewer than SBW and re-reads its last (unused) one.
+    const int sb0 = wave * SBW;
+    const int ns = min(SBW, nsb - sb0);
+    const uint4* cp = codes + ((size_t)nt * nsb + sb0) * 256 + lane;
+    const uint4* sp = scales + ((size_t)nt * nsb + sb0) * 32 + col * 2 + (g >> 1);
+    Chunk w[SBW];
+#pragma unroll
+    for (int c = 0; c < SBW; ++c) {
+        const int cc = min(c, ns - 1);
+        load_chunk(w[c], cp + 256 * cc, sp + 32 * cc);
+    }
+    // Activation rows r < M of this wave's K range, one 1 KiB copy per row
+    // and superblock; each row's resource ends at the row's end, so values
+    // past K read as zero.
+#pragma unroll
+    for (int r = 0; r < MR; ++r) {
+        if (r < M) {
+#pragma unroll
+            for (int c = 0; c < SBW; ++c) {
+                if (c < ns) {
+                    const int k = (sb0 + c) * kSuperK;
+                    const uint16_t* row = act + (size_t)r * K + k;
+                    const int bytes = (K - k) * (int)sizeof(uint16_t);
+                    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                        const_cast<uint16_t*>(row), 0, bytes, 0x00020000);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rs, (__attribute__((address_space(3))) void*)(rows + r * kRow + c * kSuperK),
+                        16, lane * 16, 0, 0, 0);
+                }
+            }
+        }
+    }
+    __syncthreads();  // the zero row is written
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's weights and rows have landed
+
+    const int m = col & 7;
+    const bool live = ((col >> 3) == (g >> 1)) && (m < M);
+    const __bf16* ap = live ? (rows + m * kRow + 8 * g) : (zero + 8 * g);
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < SBW; ++c)
+        if (c < ns) chunk_steps(acc, w[c], ap + c * kSuperK);
+
+    // Lanes g and g+2 hold the same (row, column) for the two block halves.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] += __shfl_xor(acc[j], 32, 64);
+    if (lane < 32) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) red[(wave * 8 + 4 * g + j) * kTileN + col] = acc[j];
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < M * kTileN) {
+        const int mm = threadIdx.x / kTileN, c = threadIdx.x - mm * kTileN;
+        float sum = 0.f;
+        for (int p = 0; p < waves; ++p) sum += red[(p * 8 + mm) * kTileN + c];
+        const int n = nt * kTileN + c;
+        if (n < N) store_out<BF16>(out, (size_t)mm * N + n, sum * ts);
+    }
+}
+
+static size_t tile_lds_bytes(int sbw, int mr, int waves) {
+    const size_t row = (size_t)sbw * kSuperK + kLdsPad;
+    return (row + (size_t)waves * mr * row) * 2 + (size_t)waves * 8 * kTileN * sizeof(float);
+}
+
+int make_tile_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, TileConfig* t) {
+    *t = TileConfig{};
+    const int n_tiles = padded_n(N) / kTileN;
+    const int nsb = padded_k(K) / kSuperK;
+    const int forced_m = cfg ? cfg->tile_max_m : 0;
+    const int forced_sbw = cfg ? cfg->tile_superblocks : 0;
+    if (forced_m < -1 || forced_m > 4)
+        return set_error(NVFP4_EINVAL, "config.tile_max_m: %d outside [-1, 4]", forced_m);
+    if (forced_sbw < 0 || forced_sbw > 3)
+        return set_error(NVFP4_EINVAL, "config.tile_superblocks: %d outside [0, 3]", forced_sbw);
+    if (forced_m == -1) return NVFP4_OK;
+    // Defaults measured on MI355X over the round's shapes and the output
+    // head: one superblock per wave while the tiles alone give each compute
+    // unit fewer than 4 workgroups (qkv, o), two for wider matrices (gate_up,
+    // the head); M up to 4 and up to 2 respectively; no tile kernel when K
+    // would need more than 12 waves per workgroup (down).
+    const bool wide = n_tiles >= 4 * device_cus();
+    const int sbw = forced_sbw ? forced_sbw : (wide ? 2 : 1);
+    const int waves = (nsb + sbw - 1) / sbw;
+    if (waves > 16) {
+        if (forced_m > 0)
+            return set_error(NVFP4_EINVAL, "config.tile_max_m: K = %d needs %d waves of %d "
+                             "superblocks, more than 16", K, waves, sbw);
+        return NVFP4_OK;
+    }
+    int max_m = forced_m ? forced_m : (waves > 12 ? 0 : wide ? 2 : 4);
+    if (max_m > max_M) max_m = max_M;
+    if (max_m > 0 && tile_lds_bytes(sbw, max_m <= 1 ? 1 : max_m <= 2 ? 2 : 4, waves) > 160 * 1024)
+        return set_error(NVFP4_EINVAL, "config.tile_superblocks: %d with %d waves needs more "
+                         "LDS than a compute unit has", sbw, waves);
+    t->max_m = max_m;
+    t->sbw = sbw;
+    t->waves = waves;
+    return NVFP4_OK;
+}
+
+template <int SBW, int MR, bool BF16>
+static int launch_tile_t(const nvfp4_gemm_plan* p, int M, const uint8_t* codes,
+                         const uint8_t* scales, float ts, const uint16_t* act, void* out,
+                         hipStream_t s) {
+    const TileConfig& t = p->tile;
+    const size_t lds = tile_lds_bytes(SBW, MR, t.waves);
+    if (lds > 64 * 1024) {
+        // above the default limit of dynamic LDS per workgroup
+        NVFP4_HIP(hipFuncSetAttribute((const void*)decode_tile_kernel<SBW, MR, BF16>,
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+    }
+    hipLaunchKernelGGL((decode_tile_kernel<SBW, MR, BF16>), dim3(p->Np / kTileN),
+                       dim3(t.waves * 64), lds, s, (const uint4*)codes, (const uint4*)scales, act,
+                       out, ts, M, p->K, p->N, p->Kp / kSuperK);
+    NVFP4_HIP(hipGetLastError());
+    return NVFP4_OK;
+}
+
+template <int SBW, bool BF16>
+static int launch_tile_m(const nvfp4_gemm_plan* p, int M, const uint8_t* codes,
+                         const uint8_t* scales, float ts, const uint16_t* act, void* out,
+                         hipStream_t s) {
+    if (M <= 1) return launch_tile_t<SBW, 1, BF16>(p, M, codes, scales, ts, act, out, s);
+    if (M <= 2) return launch_tile_t<SBW, 2, BF16>(p, M, codes, scales, ts, act, out, s);
+    return launch_tile_t<SBW, 4, BF16>(p, M, codes, scales, ts, act, out, s);
+}
+
+template <bool BF16>
+static int launch_tile_s(const nvfp4_gemm_plan* p, int M, const uint8_t* codes,
+                         const uint8_t* scales, float ts, const uint16_t* act, void* out,
+                         hipStream_t s) {
+    switch (p->tile.sbw) {
+        case 1: return launch_tile_m<1, BF16>(p, M, codes, scales, ts, act, out, s);
+        case 2: return launch_tile_m<2, BF16>(p, M, codes, scales, ts, act, out, s);
+        default: return launch_tile_m<3, BF16>(p, M, codes, scales, ts, act, out, s);
+    }
+}
+
+int launch_tile(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
+                float ts, const uint16_t* act, void* out, hipStream_t s) {
+    return p->out_dtype == NVFP4_OUT_BF16
+               ? launch_tile_s<true>(p, M, codes, scales, ts, act, out, s)
+               : launch_tile_s<false>(p, M, codes, scales, ts, act, out, s);
+}
+
 // ---- device facts ----------------------------------------------------------------
 
 int device_cus() {

@@ -112,6 +112,26 @@ def test_gemm_config_validation(nv):
     nv.nvfp4_gemm_destroy(plan)
 
 
+def test_tile_kernel_config(nv):
+    for bad, word in ((dict(tile_max_m=5), "config.tile_max_m"),
+                      (dict(tile_max_m=-2), "config.tile_max_m"),
+                      (dict(tile_superblocks=4), "config.tile_superblocks"),
+                      (dict(tile_superblocks=-1), "config.tile_superblocks"),
+                      # K = 17408: 34 superblocks, 34 waves of one
+                      (dict(tile_max_m=2, tile_superblocks=1), "config.tile_max_m")):
+        K = 17408 if bad.get("tile_superblocks") == 1 else 5120
+        with pytest.raises(nv.Nvfp4Error) as e:
+            nv.nvfp4_gemm_create(8, K, 5120, 1, **bad)
+        assert e.value.status == nv.EINVAL and e.value.message.startswith(word), e.value.message
+    # the tile kernel needs no workspace: a plan that routes every width to it has none
+    plan, ws = nv.nvfp4_gemm_create(4, 5120, 5120, 1, tile_max_m=4)
+    assert ws >= 0
+    nv.nvfp4_gemm_destroy(plan)
+    for sbw in (1, 2, 3):
+        plan, ws = nv.nvfp4_gemm_create(2, 2048, 100, 0, tile_max_m=2, tile_superblocks=sbw)
+        nv.nvfp4_gemm_destroy(plan)
+
+
 def test_verify_width_config(nv):
     for bad, word in ((dict(verify_waves=2), "config.verify_waves"),
                       (dict(verify_waves=32), "config.verify_waves"),

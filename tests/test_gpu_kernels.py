@@ -235,6 +235,59 @@ def test_projection_5120_full(nv, M):
     check(out32, y, S, bf16=False, what="projection f32 M=%d" % M)
 
 
+# ---- narrow widths: one workgroup per column tile over all of K ------------------
+
+# Ragged K (inside a superblock, one superblock, below 512) and N (inside a
+# tile), K needing 1..16 waves of 1..3 superblocks.
+TILE = [(256, 512), (16, 3), (528, 40), (5120, 130), (6144, 33), (2576, 515), (17408, 20),
+        (1040, 16)]
+
+
+@pytest.mark.parametrize("K,N", TILE)
+@pytest.mark.parametrize("sbw", [1, 2, 3])
+def test_tile_kernel_forced(nv, K, N, sbw):
+    """The tile kernel forced for M = 1..4 (both output dtypes) against the
+    oracle; shapes whose K needs more than 16 waves of sbw superblocks are
+    refused at plan time."""
+    import math
+    if math.ceil(-(-K // 512) / sbw) > 16:
+        with pytest.raises(nv.Nvfp4Error):
+            nv.Gemm(4, K, N, nv.OUT_F32, tile_max_m=4, tile_superblocks=sbw)
+        return
+    codes, scales = synth.random_planes(K + sbw, N + 17, N, K)
+    t = float(np.float32(np.random.default_rng(K * N + sbw).uniform(1e-4, 1e-2)))
+    act = synth.activations(K + 7, N + sbw, 4, K)
+    pw = pack(nv, dev(codes), dev(scales), K, N, t)
+    for M in (1, 2, 3, 4):
+        y, S = oracle.gemm(act[:M], codes, scales, t)
+        for bf16 in (False, True):
+            out, _ = run(nv, pw, dev_bf16(act[:M]), nv.OUT_BF16 if bf16 else nv.OUT_F32,
+                         tile_max_m=4, tile_superblocks=sbw)
+            check(out, y, S, bf16=bf16, what="tile K=%d N=%d sbw=%d M=%d" % (K, N, sbw, M))
+
+
+def test_tile_kernel_repeats_bitwise_and_shares_a_plan_with_split_k(nv):
+    """One plan serves M <= 4 with the tile kernel and M = 5..8 with the
+    split-K kernel; repeated runs are bit-identical."""
+    import torch
+    K, N = 5120, 7168  # qkv: tile kernel up to M = 4 by default
+    codes, scales = synth.random_planes(31, 32, N, K)
+    t = 1.0e-3
+    act = synth.activations(31, 33, 8, K)
+    pw = pack(nv, dev(codes), dev(scales), K, N, t)
+    g = nv.Gemm(8, K, N, nv.OUT_F32)
+    a = dev_bf16(act)
+    for m in (1, 4, 5, 8, 2, 1):
+        out = torch.full((m, N), float("nan"), dtype=torch.float32, device="cuda")
+        g(pw, a[:m], out, M=m)
+        again = torch.full_like(out, float("nan"))
+        g(pw, a[:m], again, M=m)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out).view(np.uint32), host(again).view(np.uint32)), m
+        y, S = oracle.gemm(act[:m], codes, scales, t)
+        check(out, y, S, bf16=False, what="M=%d of a shared plan" % m)
+
+
 CONFIGS = ([dict(chunks=c, waves=w) for w in (4, 8) for c in (1, 2, 3, 4)] +
            # streamed slices: several windows of `chunks` superblocks per workgroup
            [dict(chunks=c, waves=w, windows=n)
