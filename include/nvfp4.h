@@ -177,6 +177,20 @@ int nvfp4_gemm_run(nvfp4_gemm plan, int M, int K, int N, const uint8_t* codes_de
                    const uint8_t* scales_dev, float tensor_scale, const uint16_t* act_dev,
                    void* out_dev, void* workspace_dev, void* stream);
 
+/* nvfp4_gemm_run for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same kernels, with the split-K counters and partial sums in a static 16 MiB
+ * device array per GPU (held until the process ends) instead of a caller
+ * workspace.  Arguments as nvfp4_gemm_run, without the workspace.  A run that
+ * needs more than 16 MiB of that state (a large prefill chunk) returns
+ * NVFP4_EUNSUPPORTED and launches nothing.  The first call on a device
+ * zero-fills the array with one kernel on `stream`.  Every call on a GPU uses
+ * that GPU's one array: calls that overlap on one GPU (other streams, other
+ * threads) race and must be serialised by the caller.  Allocates nothing. */
+int nvfp4_gemm_run_noalloc(nvfp4_gemm plan, int M, int K, int N, const uint8_t* codes_dev,
+                           const uint8_t* scales_dev, float tensor_scale, const uint16_t* act_dev,
+                           void* out_dev, void* stream);
+
 /* Zero a workspace with a fill kernel (safe inside graph capture). */
 int nvfp4_workspace_clear(void* workspace_dev, size_t bytes, void* stream);
 

@@ -29,6 +29,7 @@ EXPORTS = (
     "nvfp4_packed_code_bytes", "nvfp4_packed_scale_bytes", "nvfp4_pack", "nvfp4_unpack",
     "nvfp4_quantize_workspace_bytes", "nvfp4_quantize",
     "nvfp4_gemm_create", "nvfp4_gemm_create_ex", "nvfp4_gemm_destroy", "nvfp4_gemm_run",
+    "nvfp4_gemm_run_noalloc",
     "nvfp4_workspace_clear",
     "nvfp4_round_workspace_bytes", "nvfp4_round_create", "nvfp4_round_run",
     "nvfp4_round_graph_nodes", "nvfp4_round_destroy",
@@ -97,6 +98,7 @@ def lib():
         L.nvfp4_gemm_destroy.argtypes = [vp]
         L.nvfp4_gemm_destroy.restype = None
         L.nvfp4_gemm_run.argtypes = [vp, i, i, i, vp, vp, c.c_float, vp, vp, vp, vp]
+        L.nvfp4_gemm_run_noalloc.argtypes = [vp, i, i, i, vp, vp, c.c_float, vp, vp, vp]
         L.nvfp4_workspace_clear.argtypes = [vp, sz, vp]
         L.nvfp4_round_workspace_bytes.argtypes = [c.POINTER(Layer), i, i, c.POINTER(sz)]
         L.nvfp4_round_create.argtypes = [c.POINTER(vp), c.POINTER(Layer), i, i, vp, sz, vp]
@@ -228,6 +230,12 @@ def nvfp4_gemm_run(plan, M, K, N, codes, scales, tensor_scale, act, out, workspa
     _check(lib().nvfp4_gemm_run(plan, M, K, N, _ptr(codes), _ptr(scales),
                                 ctypes.c_float(tensor_scale), _ptr(act), _ptr(out),
                                 _ptr(workspace), _stream(stream)))
+
+
+def nvfp4_gemm_run_noalloc(plan, M, K, N, codes, scales, tensor_scale, act, out, stream=None):
+    _check(lib().nvfp4_gemm_run_noalloc(plan, M, K, N, _ptr(codes), _ptr(scales),
+                                        ctypes.c_float(tensor_scale), _ptr(act), _ptr(out),
+                                        _stream(stream)))
 
 
 def nvfp4_workspace_clear(workspace, nbytes, stream=None):

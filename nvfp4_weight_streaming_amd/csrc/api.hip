@@ -8,6 +8,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "common.h"
@@ -83,7 +84,8 @@ int validate_run(const nvfp4_gemm_plan* p, int M, int K, int N, const void* code
 }
 
 RunOffsets gemm_offsets(const nvfp4_gemm_plan* p) {
-    return RunOffsets{p->dec.counter_bytes, p->ver.ws_off, p->ver.ws_off + p->ver.d.counter_bytes};
+    return RunOffsets{p->dec.counter_bytes, p->ver.ws_off, p->ver.ws_off + p->ver.d.counter_bytes,
+                      p->pre.ws_off};
 }
 
 int run_gemm(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
@@ -91,7 +93,7 @@ int run_gemm(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_
              hipStream_t s) {
     const size_t partial_off = off.dec_partial;
     if (M > NVFP4_VERIFY_MAX_M && p->pre.enabled)
-        return launch_prefill(p, M, codes, scales, ts, act, out, ws, s);
+        return launch_prefill(p, M, codes, scales, ts, act, out, ws, off.pre_partial, s);
     if (M > NVFP4_DECODE_MAX_M && p->ver.enabled)
         return launch_verify(p, M, codes, scales, ts, act, out, ws, off.ver_counters,
                              off.ver_partial, s);
@@ -191,6 +193,87 @@ int nvfp4_gemm_run(nvfp4_gemm plan, int M, int K, int N, const uint8_t* codes_de
     if (st != NVFP4_OK) return st;
     return run_gemm(plan, M, codes_dev, scales_dev, tensor_scale, act_dev, out_dev,
                     workspace_dev, gemm_offsets(plan), (hipStream_t)stream);
+}
+
+// ---- GEMM runs that allocate nothing ----------------------------------------------
+
+// For callers that cannot allocate device memory (graph capture, serving loops,
+// harnesses that forbid it): the split-K counters and partial sums live in a
+// file-scope device array, one copy per GPU, instead of a caller workspace.
+// The array's name is a host-side stand-in: host code uses only the device
+// address hipGetSymbolAddress returns, looked up once per device with that
+// device current.  Every call on a GPU shares that GPU's copy; calls that
+// overlap on one GPU race.
+}  // extern "C"
+
+namespace nvfp4 {
+// Layout: [split-K counters of every plan: kScratchCounters][partial sums].
+// All plans share one counter region, which every run leaves zeroed again,
+// so the region stays zero from one call to the next whatever plans
+// alternate; partial sums need no initial value.
+constexpr size_t kScratchBytes = (size_t)16 << 20;  // 16 MiB per GPU
+constexpr size_t kScratchCounters = (size_t)64 << 10;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64];
+
+// The device address of this device's scratch, zero-filled by a kernel on
+// `s` the first time it is used on the device.
+static int scratch_for_current_device(hipStream_t s, void** ptr) {
+    int dev = 0;
+    NVFP4_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= 64) return set_error(NVFP4_EUNSUPPORTED, "device %d: above 63", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        NVFP4_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        const int st = launch_fill_zero(p, kScratchBytes, s);
+        if (st) return st;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return NVFP4_OK;
+}
+
+// Counter and partial-sum bytes a run of M rows needs in that layout.
+static void noalloc_need(const nvfp4_gemm_plan* p, int M, size_t* counters, size_t* partials) {
+    *counters = *partials = 0;
+    if (M > NVFP4_VERIFY_MAX_M && p->pre.enabled) {
+        *partials = prefill_ws_bytes(M, p->K, p->N);
+    } else if (M > NVFP4_DECODE_MAX_M && p->ver.enabled) {
+        *counters = p->ver.d.counter_bytes;
+        *partials = p->ver.d.partial_bytes;
+    } else if (M > p->tile.max_m) {
+        *counters = p->dec.counter_bytes;
+        *partials = p->dec.partial_bytes;
+    }
+}
+}  // namespace nvfp4
+
+extern "C" {
+
+int nvfp4_gemm_run_noalloc(nvfp4_gemm plan, int M, int K, int N, const uint8_t* codes_dev,
+                           const uint8_t* scales_dev, float tensor_scale, const uint16_t* act_dev,
+                           void* out_dev, void* stream) {
+    clear_error();
+    // Validate everything first (the scratch stands in for the workspace), so
+    // that nothing is launched on error.
+    int st = validate_run(plan, M, K, N, codes_dev, scales_dev, act_dev, out_dev, (void*)256);
+    if (st != NVFP4_OK) return st;
+    size_t nc = 0, np = 0;
+    noalloc_need(plan, M, &nc, &np);
+    if (nc > kScratchCounters || np > kScratchBytes - kScratchCounters)
+        return set_error(NVFP4_EUNSUPPORTED, "M: %d needs %zu bytes of split-K counters and %zu of "
+                         "partial sums, above the static scratch (%zu and %zu bytes; use "
+                         "nvfp4_gemm_run with a workspace)", M, nc, np, kScratchCounters,
+                         kScratchBytes - kScratchCounters);
+    void* ws = nullptr;
+    st = scratch_for_current_device((hipStream_t)stream, &ws);
+    if (st) return st;
+    const RunOffsets off{kScratchCounters, 0, kScratchCounters, kScratchCounters};
+    return run_gemm(plan, M, codes_dev, scales_dev, tensor_scale, act_dev, out_dev, ws, off,
+                    (hipStream_t)stream);
 }
 
 int nvfp4_workspace_clear(void* workspace_dev, size_t bytes, void* stream) {

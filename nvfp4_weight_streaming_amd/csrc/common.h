@@ -104,6 +104,8 @@ int make_verify_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, Ve
 int make_decode_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, DecodeConfig* out);
 int make_tile_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, TileConfig* out);
 int make_prefill_config(int max_M, int K, int N, PrefillConfig* out);
+// Bytes of K-piece partial sums a prefill run of M rows uses (after pre.ws_off).
+size_t prefill_ws_bytes(int M, int K, int N);
 
 // Launchers (no validation: callers validated).  Return NVFP4_OK or EHIP.
 // ws: the workspace; partial_off: byte offset of the partial sums in it (the
@@ -116,8 +118,11 @@ int launch_tile(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uin
 int launch_verify(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
                   float ts, const uint16_t* act, void* out, void* ws, size_t counters_off,
                   size_t partial_off, hipStream_t s);
+// pre_off: byte offset of the K pieces' partial sums in ws (the plan's own
+// pre.ws_off, or another place a caller lays out).
 int launch_prefill(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
-                   float ts, const uint16_t* act, void* out, void* ws, hipStream_t s);
+                   float ts, const uint16_t* act, void* out, void* ws, size_t pre_off,
+                   hipStream_t s);
 int launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 int launch_swiglu(const uint16_t* gate_up, uint16_t* out, int M, int F, hipStream_t s);
 
@@ -130,6 +135,7 @@ struct RunOffsets {
     size_t dec_partial;   // decode partials (its counters start at 0)
     size_t ver_counters;  // verify-width counters
     size_t ver_partial;   // verify-width partials
+    size_t pre_partial;   // prefill K pieces' partial sums
 };
 RunOffsets gemm_offsets(const nvfp4_gemm_plan* p);
 int run_gemm(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,

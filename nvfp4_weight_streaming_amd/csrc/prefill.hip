@@ -489,13 +489,19 @@ int make_prefill_config(int max_M, int K, int N, PrefillConfig* out) {
     return NVFP4_OK;
 }
 
+size_t prefill_ws_bytes(int M, int K, int N) {
+    const PrefillSplit s = prefill_split(M, K, N, device_cus());
+    return (size_t)s.n_tail * s.splits * kPTileFloats * sizeof(float);
+}
+
 int launch_prefill(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
-                   float ts, const uint16_t* act, void* out, void* ws, hipStream_t s) {
+                   float ts, const uint16_t* act, void* out, void* ws, size_t pre_off,
+                   hipStream_t s) {
     const int n_tiles = p->Np / kTileN, nsb = p->Kp / kSuperK;
     const int mblocks = (M + kPTile - 1) / kPTile;
     const PrefillSplit sp = prefill_split(M, p->K, p->N, device_cus());
     const int pieces = sp.n_tail * sp.splits;
-    float* part = pieces ? (float*)((char*)ws + p->pre.ws_off) : nullptr;
+    float* part = pieces ? (float*)((char*)ws + pre_off) : nullptr;
     const dim3 grid((unsigned)(sp.tiles - sp.n_tail + pieces));
     const bool bf16 = p->out_dtype == NVFP4_OUT_BF16;
     if (bf16)

@@ -178,7 +178,8 @@ int nvfp4_round_create(nvfp4_round* plan, const nvfp4_layer* layers, int n_layer
                                     const_cast<uint16_t*>(l.act_dev), M, l.K, cap);
             if (lst) break;
             lst = run_gemm(r->plans[i], M, l.codes_dev, l.scales_dev, l.tensor_scale, l.act_dev,
-                           l.out_dev, workspace, RunOffsets{r->partial_off, 0, r->partial_off},
+                           l.out_dev, workspace,
+                           RunOffsets{r->partial_off, 0, r->partial_off, r->partial_off},
                            cap);
         }
         hipGraph_t g = nullptr;
