@@ -425,13 +425,25 @@ def main():
     h_us = time_events(head_call, n_head) * 1e3
     h_bytes = gemm_bytes(8, HEAD_K, HEAD_N, out_bytes=4)
     h_gbs = h_bytes / (h_us * 1e-6) / 1e9
+
+    # A plain read of the head's own weight bytes (one read of each packed
+    # copy's codes and scales, alternating), the floor for this kernel.
+    def head_read():
+        hp = hpws[flip[0]]
+        nv.nvfp4_stream_read(hp.codes, hp.codes.numel(), sink, stream)
+        nv.nvfp4_stream_read(hp.scales, hp.scales.numel(), sink, stream)
+        flip[0] ^= 1
+    hr_us = time_events(head_read, n_head) * 1e3
     log("output head M=8 K=%d N=%d (fp32 out): %.1f us, %.1f GB/s (%.1f%% of 8 TB/s, %.1f%% of "
-        "the single-read rate)" % (HEAD_K, HEAD_N, h_us, h_gbs, 100 * h_gbs / HBM_PEAK_GBS,
-                                   100 * h_gbs / big_gbs))
+        "the single-read rate); a plain read of its weights %.1f us" % (
+            HEAD_K, HEAD_N, h_us, h_gbs, 100 * h_gbs / HBM_PEAK_GBS, 100 * h_gbs / big_gbs,
+            hr_us))
     head = {"M": 8, "K": HEAD_K, "N": HEAD_N, "out": "fp32", "us": round(h_us, 2),
             "algorithmic_bytes": h_bytes, "GB_s": round(h_gbs, 1),
             "frac_hbm_peak": round(h_gbs / HBM_PEAK_GBS, 4),
-            "frac_of_achievable": round(h_gbs / big_gbs, 4), "weight_copies": 2}
+            "frac_of_achievable": round(h_gbs / big_gbs, 4), "weight_copies": 2,
+            "plain_read_of_weights_us": round(hr_us, 2),
+            "time_over_plain_read": round(h_us / hr_us, 4)}
 
     # Top-k over the vocabulary, the step after the head: on the head's own
     # logits (k = 1, the greedy argmax, and k = 8), and on 7 rows of a
