@@ -54,12 +54,16 @@ PASSES = (
 )
 MFMA_COUNTERS = PASSES[4][1][1:]
 VERIFY = "nvfp4::verify_kernel<"
+TILE = "nvfp4::decode_tile_kernel<"
 TOPK = "nvfp4::topk_"  # level and merge kernels
 CALIB_BYTES = 1 << 30
 DECODE = "nvfp4::decode_"  # decode_kernel< and decode_window_kernel<
 PREFILL = "nvfp4::prefill_kernel<"
 PREFILL_SUM = "nvfp4::prefill_reduce_kernel<"
 COPY = "__amd_rocclr_copyBuffer"
+# The achievable leg's one read of the whole weight arena: non-temporal
+# 16-byte loads, the load type of the decode kernel's weight stream.
+STREAM_READ_BIG = "nvfp4::stream_read_kernel"
 
 
 def rocprof_cmd(flags, out_dir, args=BENCH_ARGS):
@@ -205,12 +209,15 @@ def summarize(out, dest):
         keys = {meta[k] for k in dec_ids[:4]}  # the round's four shapes (not the head)
         dec_v = [per[k] for k in dec_ids if meta[k] in keys]
         cal = max(v for k, v in per.items() if COPY in meta[k][0])
-        return dec_v, cal, len(dec_v)
+        big = [v for k, v in per.items() if STREAM_READ_BIG in meta[k][0]]
+        return dec_v, cal, len(dec_v), (sum(big) / len(big) if big else float("nan"))
 
-    f_dec, f_cal, nf = counter("fetch")
-    w_dec, w_cal, nw = counter("write")
+    f_dec, f_cal, nf, f_big = counter("fetch")
+    w_dec, w_cal, nw, _ = counter("write")
     f_factor = CALIB_BYTES / (f_cal * 1024)
     w_factor = CALIB_BYTES / (w_cal * 1024)
+    arena = line["config"]["round_weight_bytes"]
+    f_factor_nt = arena / (f_big * 1024)
     fetch_b = sum(f_dec) / nf * 1024 * f_factor
     write_b = sum(w_dec) / nw * 1024 * w_factor
     md = []
@@ -225,6 +232,11 @@ def summarize(out, dest):
     md.append("|---|---|---|---|")
     md.append("| FETCH_SIZE | %.0f | %d | %.4f |" % (f_cal, CALIB_BYTES // 1024, f_factor))
     md.append("| WRITE_SIZE | %.0f | %d | %.4f |\n" % (w_cal, CALIB_BYTES // 1024, w_factor))
+    md.append("Cross-check of the FETCH_SIZE factor on the decode kernel's own load type: "
+              "the same runs read the round's whole packed weight arena once with "
+              "`nvfp4_stream_read` (non-temporal 16-byte loads, as the decode kernel's weight "
+              "stream), %d bytes: FETCH_SIZE reads %.0f KiB, a factor of %.4f against %.4f "
+              "for the copy.\n" % (arena, f_big, f_factor_nt, f_factor))
     md.append("| per decode launch (average over %d launches) | bytes |" % nf)
     md.append("|---|---|")
     md.append("| FETCH_SIZE x factor | %.0f |" % fetch_b)
@@ -241,6 +253,7 @@ def summarize(out, dest):
                    "algorithmic_bytes_per_launch": algo,
                    "launches": nf,
                    "fetch_scale": round(f_factor, 4), "write_scale": round(w_factor, 4),
+                   "fetch_scale_nt_read": round(f_factor_nt, 4),
                    "workload": "M = 8 27B-class round, all 256 decode launches per replay"},
                   f, indent=1)
         f.write("\n")
@@ -325,7 +338,7 @@ def summarize_wide(out, dest):
                                               "kernel_trace.csv"))))
     trace.sort(key=lambda r: int(r["Start_Timestamp"]))
     dur = lambda r: int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
-    md = ["# Verify-width rounds and top-k over the vocabulary: kernel trace\n"]
+    md = ["# Verify-width rounds, narrow widths and top-k over the vocabulary: kernel trace\n"]
     md.append("Command (from the repository root, with `TMPDIR=/tmp`, run in /tmp):\n")
     md.append("    python3 bench_profile.py --out OUT\n")
     md.append("which runs, for this pass:\n")
@@ -350,6 +363,25 @@ def summarize_wide(out, dest):
         md.append("| %d | %s | %.4f | %.2f | %.2f | %.2f | %.2f |"
                   % (M, vr.get(str(M), {}).get("round_ms", "-"),
                      sum(map(dur, seg)) / (len(seg) / per_round) / 1e6, *avg))
+    md.append("\n## Narrow widths (M <= 4): the one-tile-per-workgroup kernel, per launch shape\n")
+    md.append("From the same run's width sweep (M = 1..4 rounds), the projection (K = N = 5120, "
+              "64 copies, M = 1, 2, 4) and the chained-MLP round (M = 1).  MR is the template's "
+              "staged-row count (1, 2 or 4 rows).\n")
+    md.append("| kernel (SBW, MR, bf16) | column tiles | waves per workgroup | matrix | launches | "
+              "average (us) |")
+    md.append("|---|---|---|---|---|---|")
+    tiles_name = {448: "qkv 5120x7168", 2176: "gate_up 5120x34816", 9504: "head 5120x152064"}
+    tgroups = collections.OrderedDict()
+    for r in trace:
+        if TILE in r["Kernel_Name"]:
+            wg = int(r["Workgroup_Size_X"])
+            key = (short(r["Kernel_Name"]), int(r["Grid_Size_X"]) // wg, wg // 64)
+            tgroups.setdefault(key, []).append(dur(r))
+    for (name, nt, waves), ds in tgroups.items():
+        label = tiles_name.get(nt, "o 6144x5120" if (nt, waves) == (320, 12) else
+                               "projection 5120x5120" if (nt, waves) == (320, 10) else "?")
+        md.append("| %s | %d | %d | %s | %d | %.2f |" % (name.replace("nvfp4::", ""), nt, waves,
+                                                          label, len(ds), sum(ds) / len(ds) / 1e3))
     md.append("\n## Top-k levels (per launch)\n")
     md.append("| kernel | grid X x Y (threads x rows) | launches | average (us) |")
     md.append("|---|---|---|---|")
