@@ -140,7 +140,9 @@ typedef struct nvfp4_gemm_config {
 } nvfp4_gemm_config;
 
 /* Create a plan for GEMMs of shape (M <= max_M) x K x N with the given output
- * dtype.  Validates K % 16 == 0, K >= 16, N >= 1, max_M >= 1, out_dtype.
+ * dtype.  Validates K % 16 == 0, K >= 16, N >= 1, max_M >= 1, out_dtype;
+ * returns NVFP4_EUNSUPPORTED for K >= 2^24, and for K >= 2^22 when max_M > 64
+ * (the kernels above 8 rows address activations with 32-bit byte offsets).
  * The first plan made on a device also runs a one-off check of the device's
  * workgroup-to-XCD dispatch order (one tiny kernel and a synchronisation);
  * split-K plans use the cheaper in-L2 hand-off of partial sums only if it
@@ -171,7 +173,11 @@ void nvfp4_gemm_destroy(nvfp4_gemm plan);
  * and, when the 256 x 256 output tiles leave a last partial round on the
  * device's compute units, a second kernel that adds the fp32 partial sums of
  * those tiles' K pieces.  The workspace holds, in this order, the decode,
- * verify and prefill areas the plan's max_M needs.  Asynchronous; no
+ * verify and prefill areas the plan's max_M needs.  For M > 8 and K not a
+ * multiple of 512, every activation value must be finite: those kernels read
+ * the tail of a row's last K window from the start of the next row and
+ * multiply it by the zero weights past K (an infinity or NaN there would turn
+ * into NaN sums of another row).  Rows of M <= 8 end at K.  Asynchronous; no
  * synchronisation. */
 int nvfp4_gemm_run(nvfp4_gemm plan, int M, int K, int N, const uint8_t* codes_dev,
                    const uint8_t* scales_dev, float tensor_scale, const uint16_t* act_dev,

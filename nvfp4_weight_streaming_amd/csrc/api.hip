@@ -130,7 +130,14 @@ static int create_plan(nvfp4_gemm* plan, int max_M, int K, int N, int out_dtype,
     if (K < 16 || K % 16 != 0) return set_error(NVFP4_EINVAL, "K: %d is not a positive multiple of 16", K);
     if (N < 1) return set_error(NVFP4_EINVAL, "N: %d < 1", N);
     if (max_M < 1) return set_error(NVFP4_EINVAL, "max_M: %d < 1", max_M);
-    if (K > (1 << 24)) return set_error(NVFP4_EUNSUPPORTED, "K: %d above 2^24", K);
+    // The verify-width and prefill kernels address activations with 32-bit
+    // byte offsets: 64 rows of K bf16 values (verify widths), and a block of
+    // 256 rows (prefill), must stay below 2^31 bytes.
+    if (K >= (1 << 24)) return set_error(NVFP4_EUNSUPPORTED, "K: %d not below 2^24", K);
+    if (max_M > NVFP4_VERIFY_MAX_M && K >= (1 << 22))
+        return set_error(NVFP4_EUNSUPPORTED, "K: %d not below 2^22 with max_M = %d above %d "
+                         "(32-bit activation offsets of the prefill kernel)", K, max_M,
+                         NVFP4_VERIFY_MAX_M);
     if (N > (1 << 26)) return set_error(NVFP4_EUNSUPPORTED, "N: %d above 2^26", N);
     if (max_M > (1 << 20)) return set_error(NVFP4_EUNSUPPORTED, "max_M: %d above 2^20", max_M);
     if (out_dtype != NVFP4_OUT_F32 && out_dtype != NVFP4_OUT_BF16)

@@ -89,6 +89,19 @@ def test_gemm_create_null_outputs(nv):
     assert "workspace_bytes" in nv.last_error()
 
 
+def test_gemm_create_size_limits(nv):
+    """Shapes whose activation byte offsets would pass 2^31 in the kernels
+    above 8 rows (64 rows of K values; 256-row prefill blocks) are refused."""
+    for args in ((8, 1 << 24, 16, 1), (64, (1 << 24) + 16, 16, 1), (65, 1 << 22, 16, 1),
+                 (2048, (1 << 22) + 512, 16, 1)):
+        with pytest.raises(nv.Nvfp4Error) as e:
+            nv.nvfp4_gemm_create(*args)
+        assert e.value.status == nv.EUNSUPPORTED and e.value.message.startswith("K"), args
+    for args in ((64, (1 << 24) - 16, 16, 1), (65, (1 << 22) - 16, 16, 1)):
+        plan, _ = nv.nvfp4_gemm_create(*args)
+        nv.nvfp4_gemm_destroy(plan)
+
+
 def test_gemm_config_validation(nv):
     with pytest.raises(nv.Nvfp4Error) as e:
         nv.nvfp4_gemm_create(8, 5120, 5120, 1, split_k=0, waves=3)
