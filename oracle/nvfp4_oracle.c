@@ -200,13 +200,6 @@ void oracle_gemm_cols(int M, int K, int N, const uint8_t* codes, const uint8_t* 
     }
 }
 
-/* Same, for a list of selected rows: y[i][m] for column cols[i]. */
-void oracle_gemm_selected(int M, int K, const uint8_t* codes_rows, const uint8_t* scales_rows,
-                          float t, const uint16_t* act, int count, double* y, double* S) {
-    /* codes_rows / scales_rows hold `count` canonical rows back to back. */
-    oracle_gemm_cols(M, K, count, codes_rows, scales_rows, t, act, 0, count, y, S);
-}
-
 /* Threaded driver: splits the columns into `threads` contiguous ranges; each
  * output is still computed by oracle_gemm_cols exactly as above. */
 typedef struct {
