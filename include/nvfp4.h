@@ -190,7 +190,9 @@ int nvfp4_gemm_run(nvfp4_gemm plan, int M, int K, int N, const uint8_t* codes_de
  * workspace.  Arguments as nvfp4_gemm_run, without the workspace.  A run that
  * needs more than 16 MiB of that state (a large prefill chunk) returns
  * NVFP4_EUNSUPPORTED and launches nothing.  The first call on a device
- * zero-fills the array with one kernel on `stream`.  Every call on a GPU uses
+ * zero-fills the array with one kernel on `stream`, so it must be made
+ * outside stream capture (under capture it returns NVFP4_ESTATE and launches
+ * nothing); later calls may be captured.  Every call on a GPU uses
  * that GPU's one array: calls that overlap on one GPU (other streams, other
  * threads) race and must be serialised by the caller.  Allocates nothing. */
 int nvfp4_gemm_run_noalloc(nvfp4_gemm plan, int M, int K, int N, const uint8_t* codes_dev,

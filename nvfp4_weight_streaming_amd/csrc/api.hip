@@ -226,13 +226,21 @@ static std::mutex g_scratch_mu;
 static void* g_scratch_ptr[64];
 
 // The device address of this device's scratch, zero-filled by a kernel on
-// `s` the first time it is used on the device.
+// `s` the first time it is used on the device.  That first use must not be
+// under stream capture: the fill would only be recorded into the caller's
+// graph, while later calls would take the scratch as already cleared.
 static int scratch_for_current_device(hipStream_t s, void** ptr) {
     int dev = 0;
     NVFP4_HIP(hipGetDevice(&dev));
     if (dev < 0 || dev >= 64) return set_error(NVFP4_EUNSUPPORTED, "device %d: above 63", dev);
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     if (!g_scratch_ptr[dev]) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        NVFP4_HIP(hipStreamIsCapturing(s, &cs));
+        if (cs != hipStreamCaptureStatusNone)
+            return set_error(NVFP4_ESTATE, "stream: the first call on device %d is under stream "
+                             "capture; make one call outside capture first (it clears the "
+                             "static scratch)", dev);
         void* p = nullptr;
         NVFP4_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
         const int st = launch_fill_zero(p, kScratchBytes, s);

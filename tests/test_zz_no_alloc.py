@@ -73,3 +73,81 @@ def test_noalloc_refuses_a_run_beyond_the_scratch():
     assert st == nv.EUNSUPPORTED, (st, nv.last_error())
     assert "static scratch" in nv.last_error(), nv.last_error()
     assert torch.isnan(out).all().item()  # nothing ran
+
+
+_CAPTURE_CHILD = r'''
+import ctypes, sys
+sys.path.insert(0, sys.argv[1])
+import numpy as np
+import torch
+import nvfp4_weight_streaming_amd as nv
+import synth
+from tests.gpu_util import dev, dev_bf16, host, pack
+
+M, K, N = 8, 2048, 300
+codes, scales = synth.random_planes(91, 92, N, K)
+pw = pack(nv, dev(codes), dev(scales), K, N, 0.003)
+act = dev_bf16(synth.activations(93, 94, M, K))
+g = nv.Gemm(8, K, N, nv.OUT_F32, tile_max_m=-1)
+L = nv.lib()
+side = torch.cuda.Stream()
+
+
+def call(out, stream):
+    return L.nvfp4_gemm_run_noalloc(g.plan, M, K, N, pw.codes.data_ptr(), pw.scales.data_ptr(),
+                                    ctypes.c_float(pw.tensor_scale), act.data_ptr(),
+                                    out.data_ptr(), stream.cuda_stream)
+
+
+def nan_out():
+    return torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+
+
+torch.cuda.synchronize()
+# 1. The first call on the device, under capture: refused, nothing recorded.
+first = nan_out()
+graph0 = torch.cuda.CUDAGraph()
+with torch.cuda.graph(graph0, stream=side):
+    first.zero_()
+    st = call(first, side)
+print("first call under capture:", st, nv.last_error(), flush=True)
+assert st == nv.ESTATE and "capture" in nv.last_error(), (st, nv.last_error())
+# 2. An eager call sets the scratch up.
+ref = nan_out()
+st = call(ref, torch.cuda.current_stream())
+assert st == nv.OK, (st, nv.last_error())
+torch.cuda.synchronize()
+assert not torch.isnan(ref).any().item()
+# 3. Later calls may be captured: every replay equals the eager result bit for
+# bit, with eager calls on the same scratch between the replays.
+got = nan_out()
+graph = torch.cuda.CUDAGraph()
+with torch.cuda.graph(graph, stream=side):
+    st = call(got, side)
+assert st == nv.OK, (st, nv.last_error())
+for r in range(3):
+    got.fill_(float("nan"))
+    graph.replay()
+    torch.cuda.synchronize()
+    assert np.array_equal(host(got).view(np.uint32), host(ref).view(np.uint32)), r
+    between = nan_out()
+    assert call(between, torch.cuda.current_stream()) == nv.OK
+    torch.cuda.synchronize()
+    assert np.array_equal(host(between).view(np.uint32), host(ref).view(np.uint32)), r
+print("ok", flush=True)
+'''
+
+
+def test_noalloc_first_call_under_capture_is_refused_and_later_captures_replay():
+    """In a fresh process (the scratch not yet set up on the device): a first
+    call made under stream capture is refused (its clearing of the scratch
+    would only be recorded); after one eager call, captured calls replay
+    bit-identically to eager ones."""
+    import os
+    import subprocess
+    import sys
+    require_gpu()
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _CAPTURE_CHILD, root], cwd=root,
+                       capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), (r.stdout[-2000:], r.stderr[-3000:])
