@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_util import bf16_bits, check, dev, dev_bf16, host, pack, require_gpu, run
+from tests.gpu_util import canary_out, bf16_bits, check, dev, dev_bf16, host, pack, require_gpu, run
 
 pytestmark = pytest.mark.gpu
 
@@ -411,6 +411,33 @@ def test_verify_width_rows_share_one_plan_and_repeat_bitwise(nv):
         assert np.array_equal(host(out).view(np.uint32), host(again).view(np.uint32)), m
         y, S = oracle.gemm(act[:m], codes, scales, t)
         check(out, y, S, bf16=False, what="M=%d of a max_M=64 plan" % m)
+
+
+@pytest.mark.parametrize("K,N", [(16, 1), (16, 17), (32, 1), (528, 1)])
+def test_smallest_shapes_through_every_kernel(nv, K, N):
+    """The smallest K (one 16-value block) and N (one column) through every
+    kernel one plan routes to: the tile kernel (M <= 4), split-K decode (5..8,
+    and 1..8 with the tile kernel off), verify widths (9..64) and prefill
+    (65, 300), both output dtypes, each against the oracle."""
+    import torch
+    codes, scales = synth.random_planes(K * 3 + N, K + 5, N, K)
+    t = 2.0e-3
+    act = synth.activations(K + N, 9, 300, K)
+    pw = pack(nv, dev(codes), dev(scales), K, N, t)
+    a = dev_bf16(act)
+    for tile in (0, -1):
+        for dt, tdt in ((nv.OUT_F32, torch.float32), (nv.OUT_BF16, torch.bfloat16)):
+            g = nv.Gemm(300, K, N, dt, tile_max_m=tile)
+            for m in (1, 4, 5, 8, 9, 17, 40, 64, 65, 300):
+                if tile == -1 and m > 8:
+                    continue
+                out, assert_canary = canary_out(m, N, tdt)
+                g(pw, a[:m], out, M=m)
+                torch.cuda.synchronize()
+                assert_canary("K=%d N=%d M=%d" % (K, N, m))
+                y, S = oracle.gemm(act[:m], codes, scales, t)
+                check(out, y, S, bf16=dt == nv.OUT_BF16,
+                      what="K=%d N=%d M=%d tile=%d" % (K, N, m, tile))
 
 
 def test_verify_width_boundary_to_prefill(nv):
