@@ -176,7 +176,38 @@ def _oracle_planes(pool, threads, sid, N, K, rows=None):
     return (np.concatenate([c for c, _ in parts]), np.concatenate([s for _, s in parts]), t)
 
 
-def cpu_baseline(threads=None, round_layers=None):
+def _gpu_parity(gpu, planes, act_bits, M, K, N, out_dtype, y, S, rows=None):
+    """Runs the library's GEMM (default plan for M rows) on the oracle's own
+    planes and activations, and returns, over the first `rows` rows: max
+    |out - y| / S, the largest fraction of the acceptance bound used (fp32
+    outputs 2^-16 S; bf16 outputs that plus the store's rounding), and whether
+    every output is within the bound."""
+    import numpy as np
+    import oracle
+    nv, torch, stream = gpu
+    c, s, t = planes
+    rows = M if rows is None else rows
+    with torch.cuda.stream(stream):
+        pw = nv.PackedWeight.from_canonical(torch.from_numpy(c).cuda(), torch.from_numpy(s).cuda(),
+                                            t, K, N, stream)
+        act = torch.from_numpy(np.ascontiguousarray(act_bits).view(np.int16)).cuda()
+        act = act.view(torch.bfloat16)
+        g = nv.Gemm(M, K, N, out_dtype)
+        dt = torch.float32 if out_dtype == nv.OUT_F32 else torch.bfloat16
+        out = torch.empty((M, N), dtype=dt, device="cuda")
+        g(pw, act, out, M=M, stream=stream)
+    torch.cuda.synchronize()
+    o = out[:rows].float().cpu().numpy().astype(np.float64)
+    y, S = y[:rows], S[:rows]
+    err = np.abs(o - y)
+    bound = oracle.tolerance(S) if out_dtype == nv.OUT_F32 else oracle.tolerance_bf16(y, S)
+    tiny = np.finfo(np.float64).tiny
+    ratio = float((err / np.maximum(S, tiny)).max())
+    used = float((err / np.maximum(bound, tiny)).max())
+    return ratio, used, bool(np.all(err <= bound))
+
+
+def cpu_baseline(threads=None, round_layers=None, gpu=None):
     """The CPU oracle (fp64, exact dequantisation), as it stands, timed on the
     host's cores on bounded samples of each workload.  Drawing and quantising
     inputs (with the oracle's quantiser, rows split over threads) is not
@@ -188,7 +219,11 @@ def cpu_baseline(threads=None, round_layers=None):
       head       M = 8, K = 5120, the first N/8 = 19008 of the 152064 rows
       prefill    8 of the 2048 rows, K = 5120, N = 17408 in full
     Rates for sampled configs are per unit of work, so they scale to the full
-    config (the oracle's cost is linear in rows and in weights)."""
+    config (the oracle's cost is linear in rows and in weights).
+    With `gpu` = (nv, torch, stream), every oracle result except the head's
+    is also compared with the library's output on the same planes and
+    activations (default plans; the prefill chunk run at all 2048 rows):
+    `max_err_over_S` and `within_bound` in each config's entry."""
     from concurrent.futures import ThreadPoolExecutor
     import oracle
     import synth
@@ -202,57 +237,92 @@ def cpu_baseline(threads=None, round_layers=None):
     def timed(act, planes):
         c, s, t = planes
         t0 = time.perf_counter()
-        oracle.gemm(act, c, s, t, threads=threads)
-        return time.perf_counter() - t0
+        y, S = oracle.gemm(act, c, s, t, threads=threads)
+        return time.perf_counter() - t0, y, S
+
+    checks = []
+
+    def parity(entry, planes, act, M, K, N, out_dtype, y, S, rows=None):
+        if gpu is None:
+            return
+        ratio, used, ok = _gpu_parity(gpu, planes, act, M, K, N, out_dtype, y, S, rows)
+        entry["max_err_over_S"] = float("%.3g" % ratio)
+        entry["max_err_over_bound"] = float("%.3g" % used)
+        entry["within_bound"] = ok
+        checks.append(ok)
+
+    nv = gpu[0] if gpu is not None else None
 
     with ThreadPoolExecutor(threads) as pool:
         # the round sample (the headline metric's unit: GB/s of weight bytes)
         dt, nbytes = 0.0, 0
+        worst, worst_used, all_ok = 0.0, 0.0, True
         for layer in range(round_layers):
             for name, K, N in ROUND_SHAPES:
                 sid = synth.stream_id(layer, name)
                 planes = _oracle_planes(pool, threads, sid, N, K)
-                dt += timed(synth.activations(0, sid, 8, K), planes)
+                act = synth.activations(0, sid, 8, K)
+                sec, y, S = timed(act, planes)
+                dt += sec
                 nbytes += weight_bytes(K, N)
-                del planes
+                if gpu is not None:
+                    m = {}
+                    parity(m, planes, act, 8, K, N, nv.OUT_BF16, y, S)
+                    worst = max(worst, m["max_err_over_S"])
+                    worst_used = max(worst_used, m["max_err_over_bound"])
+                    all_ok = all_ok and m["within_bound"]
+                del planes, y, S
         head_value = nbytes / dt / 1e9
         per["round_sample"] = {
             "layers": round_layers, "M": 8, "seconds": round(dt, 3),
             "weight_bytes": nbytes, "GB_s": round(head_value, 5),
             "est_full_round_s": round(dt * LAYERS / round_layers, 1)}
+        if gpu is not None:
+            per["round_sample"]["max_err_over_S"] = worst
+            per["round_sample"]["max_err_over_bound"] = worst_used
+            per["round_sample"]["within_bound"] = all_ok
         # tiny
         planes = _oracle_planes(pool, threads, 0, 512, 256)
-        s = timed(synth.activations(0, 0, 1, 256), planes)
-        per["tiny"] = {"M": 1, "K": 256, "N": 512, "seconds": round(s, 6)}
+        act = synth.activations(0, 0, 1, 256)
+        sec, y, S = timed(act, planes)
+        per["tiny"] = {"M": 1, "K": 256, "N": 512, "seconds": round(sec, 6)}
+        parity(per["tiny"], planes, act, 1, 256, 512, nv and nv.OUT_F32, y, S)
         # projection
         planes = _oracle_planes(pool, threads, 100, PROJ_N, PROJ_K)
         proj = {}
         for M in (1, 2, 4, 8):
-            s = timed(synth.activations(0, 100, M, PROJ_K), planes)
-            proj[str(M)] = {"seconds": round(s, 4),
-                            "GB_s": round(gemm_bytes(M, PROJ_K, PROJ_N) / s / 1e9, 5)}
+            act = synth.activations(0, 100, M, PROJ_K)
+            sec, y, S = timed(act, planes)
+            proj[str(M)] = {"seconds": round(sec, 4),
+                            "GB_s": round(gemm_bytes(M, PROJ_K, PROJ_N) / sec / 1e9, 5)}
+            parity(proj[str(M)], planes, act, M, PROJ_K, PROJ_N, nv and nv.OUT_BF16, y, S)
         per["projection"] = proj
         # output head, first N/8 rows
         rows = HEAD_N // 8
         planes = _oracle_planes(pool, threads, 9002, HEAD_N, HEAD_K, rows=rows)
-        s = timed(synth.activations(0, 9002, 8, HEAD_K), planes)
-        per["head"] = {"M": 8, "rows": rows, "of_rows": HEAD_N, "seconds": round(s, 3),
-                       "GB_s": round(weight_bytes(HEAD_K, rows) / s / 1e9, 5),
-                       "est_full_s": round(s * HEAD_N / rows, 2)}
-        del planes
-        # prefill chunk, 8 of its 2048 rows of activations
+        sec, y, S = timed(synth.activations(0, 9002, 8, HEAD_K), planes)
+        per["head"] = {"M": 8, "rows": rows, "of_rows": HEAD_N, "seconds": round(sec, 3),
+                       "GB_s": round(weight_bytes(HEAD_K, rows) / sec / 1e9, 5),
+                       "est_full_s": round(sec * HEAD_N / rows, 2)}
+        del planes, y, S
+        # prefill chunk, the first 8 of its 2048 rows of activations
         PM, PK, PN = PREFILL_SHAPE
         planes = _oracle_planes(pool, threads, 9001, PN, PK)
-        s = timed(synth.activations(0, 9001, 8, PK), planes)
-        per["prefill"] = {"M_sampled": 8, "of_M": PM, "K": PK, "N": PN, "seconds": round(s, 3),
-                          "GFLOP_s": round(2.0 * 8 * PK * PN / s / 1e9, 3),
-                          "est_full_s": round(s * PM / 8, 1)}
-        del planes
+        act = synth.activations(0, 9001, PM, PK)
+        sec, y, S = timed(act[:8], planes)
+        per["prefill"] = {"M_sampled": 8, "of_M": PM, "K": PK, "N": PN, "seconds": round(sec, 3),
+                          "GFLOP_s": round(2.0 * 8 * PK * PN / sec / 1e9, 3),
+                          "est_full_s": round(sec * PM / 8, 1)}
+        parity(per["prefill"], planes, act, PM, PK, PN, nv and nv.OUT_BF16, y, S, rows=8)
+        del planes, y, S
     desc = ("oracle GEMM (fp64, exact dequantisation) over layers 0..%d of the round in full "
             "(qkv, o, gate_up, down), M=8 lanes: %d weight bytes in %.2f s"
             % (round_layers - 1, nbytes, dt))
-    return {"value": round(head_value, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": desc, "cpu_model": _cpu_model(), "per_config": per}
+    res = {"value": round(head_value, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": desc, "cpu_model": _cpu_model(), "per_config": per}
+    if gpu is not None:
+        res["gpu_outputs_within_bound"] = all(checks) and per["round_sample"]["within_bound"]
+    return res
 
 
 def main():
@@ -329,6 +399,19 @@ def main():
     bytes8 = round_bytes(8, args.layers)
     gbs8 = bytes8 / (ms8 * 1e-3) / 1e9
     log("M=8 round: %.3f ms, %.1f GB/s (%.1f%% of 8 TB/s)" % (ms8, gbs8, 100 * gbs8 / HBM_PEAK_GBS))
+    # The same K replays again, one event between consecutive ones: the spread
+    # of single replays (median, minimum, maximum) beside the mean above.
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for i in range(args.steps):
+        nv.nvfp4_round_run(plan, 8, stream)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    each = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    replays = {"median_ms": round(each[len(each) // 2], 4), "min_ms": round(each[0], 4),
+               "max_ms": round(each[-1], 4), "replays": args.steps}
+    log("M=8 round, single replays: median %.3f ms, min %.3f, max %.3f"
+        % (replays["median_ms"], replays["min_ms"], replays["max_ms"]))
 
     # Prefill chunk (M = 2048, K = 5120, N = 17408, bf16 out): the bf16 MFMA
     # kernel over dequantised tiles.  Timed right after the headline: after
@@ -545,7 +628,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         t_c = time.time()
-        cpu = cpu_baseline()
+        cpu = cpu_baseline(gpu=(nv, torch, stream))
         log("cpu baseline: %.4f GB/s on %d threads (%s); leg took %.1f s"
             % (cpu["value"], cpu["cores"], cpu["cpu_model"], time.time() - t_c))
 
@@ -579,6 +662,7 @@ def main():
             "parallelism": "single GPU",
         },
         "frac_hbm_peak": round(gbs8 / HBM_PEAK_GBS, 4),
+        "round_m8_single_replays": replays,
         "round_ms_m1_to_m8": {k: v["round_ms"] for k, v in sweep.items()},
         "round_sweep": sweep,
         "projection": projection,
