@@ -60,7 +60,7 @@ struct DecodeConfig {
 struct VerifyConfig {
     int enabled;   // max_M > 8
     int rows;      // rows the workspace holds: ceil(min(max_M, 64) / 16) * 16
-    DecodeConfig g[2];  // launch config for up to 48 rows (G <= 3) and for 49..64 (G = 4)
+    DecodeConfig g[4];  // launch config for G = 1..4 row groups of 16 (up to the plan's rows)
     DecodeConfig d;     // workspace envelope of both: counter and partial areas, ws_bytes
     size_t ws_off; // offset of its counters and partials in the plan's workspace
 };

@@ -29,8 +29,8 @@
 
 namespace nvfp4 {
 
-constexpr int kVerifyWavesUpTo48 = 4;   // G <= 3
-constexpr int kVerifyWavesAbove48 = 8;  // G = 4, many column groups
+constexpr int kVerifyWaves = 4;       // waves per workgroup by default
+constexpr int kVerifyWavesWide = 8;   // G = 4 with many column groups; long K at G = 2, 3
 
 // End of a workgroup: outputs (one slice) or the split-K hand-off (several).
 // acc[gi][j] holds row 16 gi + 4 (lane / 16) + j, column lane % 16 of the
@@ -307,7 +307,8 @@ __global__ __launch_bounds__(WAVES * 64) void verify_kernel(
 // below (no split for column groups that alone give every compute unit 4
 // workgroups), a workspace for `rows` rows.
 static void verify_launch_config(int n_tiles, int nsb, int waves, int rows,
-                                 const nvfp4_gemm_config* cfg, DecodeConfig& d) {
+                                 const nvfp4_gemm_config* cfg, int slice_sb,
+                                 DecodeConfig& d) {
     d = DecodeConfig{};
     const int n_groups = (n_tiles + waves - 1) / waves;
     const int ng8 = round_up(n_groups, 8);
@@ -321,6 +322,8 @@ static void verify_launch_config(int n_tiles, int nsb, int waves, int rows,
     int windows;
     if (cfg && cfg->verify_windows)
         windows = cfg->verify_windows;
+    else if (slice_sb)
+        windows = slice_sb;
     else if (wide)
         windows = nsb;
     else if (ng8 < cus) {
@@ -344,15 +347,24 @@ static void verify_launch_config(int n_tiles, int nsb, int waves, int rows,
     d.ws_bytes = d.counter_bytes + d.partial_bytes;
 }
 
-// Plan: 4 waves per workgroup (measured over the 64-layer round against 8
-// throughout: M = 16 -7.6%, M = 40 -3%), except 8 for 49..64 rows when the
-// column groups outnumber the compute units; both launch configurations share
-// one workspace area sized for the larger of each part.
+// Plan, per count G of 16-row groups: 4 waves per workgroup (measured over the
+// 64-layer round against 8 throughout: M = 16 -7.6%, M = 40 -3%), except
+//  - 8 for 49..64 rows when the column groups of 4 tiles outnumber the
+//    compute units (gate_up: 7% faster there; qkv, o and down are 12%, 9%
+//    and 3% faster with 4);
+//  - 8, with K slices of 6 superblocks, for 17..48 rows of a long K (>= 32
+//    superblocks: down), as the M <= 8 kernel's long-K plan (down, repeats
+//    interleaved in one process: M = 17 18.2 us against 20.6, M = 32 19.4
+//    against 21.4, M = 48 24.4 against 25.0; at 16 and 64 rows the 4-wave
+//    plan stays faster).
+// The launch configurations share one workspace area sized for the larger
+// of each part.
 int make_verify_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, VerifyConfig* v) {
     v->enabled = max_M > NVFP4_DECODE_MAX_M;
     v->ws_off = 0;
     v->rows = 0;
-    v->g[0] = v->g[1] = v->d = DecodeConfig{};
+    for (DecodeConfig& g : v->g) g = DecodeConfig{};
+    v->d = DecodeConfig{};
     if (!v->enabled) return NVFP4_OK;
     const int m = max_M < NVFP4_VERIFY_MAX_M ? max_M : NVFP4_VERIFY_MAX_M;
     v->rows = (m + 15) / 16 * 16;
@@ -363,18 +375,18 @@ int make_verify_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, Ve
         return set_error(NVFP4_EINVAL, "config.verify_waves: %d is not 4, 8 or 16", forced);
     if (cfg && cfg->verify_windows < 0)
         return set_error(NVFP4_EINVAL, "config.verify_windows: %d < 0", cfg->verify_windows);
-    verify_launch_config(n_tiles, nsb, forced ? forced : kVerifyWavesUpTo48, v->rows, cfg,
-                         v->g[0]);
-    // 49..64 rows: 4 waves too, unless the column groups of 4 tiles outnumber
-    // the compute units (gate_up: 8 waves, 7% faster there; qkv, o and down
-    // are 12%, 9% and 3% faster with 4)
     const bool many = round_up((n_tiles + 3) / 4, 8) >= device_cus();
-    verify_launch_config(n_tiles, nsb,
-                         forced ? forced : many ? kVerifyWavesAbove48 : kVerifyWavesUpTo48,
-                         v->rows, cfg, v->g[1]);
+    const bool long_k = nsb >= 32;
     DecodeConfig& d = v->d;
-    d.counter_bytes = std::max(v->g[0].counter_bytes, v->g[1].counter_bytes);
-    d.partial_bytes = std::max(v->g[0].partial_bytes, v->g[1].partial_bytes);
+    for (int G = 1; G <= v->rows / 16; ++G) {
+        const bool long_mid = long_k && (G == 2 || G == 3);
+        const int waves = forced ? forced
+                          : (G == 4 && many) || long_mid ? kVerifyWavesWide : kVerifyWaves;
+        verify_launch_config(n_tiles, nsb, waves, v->rows, cfg, !forced && long_mid ? 6 : 0,
+                             v->g[G - 1]);
+        d.counter_bytes = std::max(d.counter_bytes, v->g[G - 1].counter_bytes);
+        d.partial_bytes = std::max(d.partial_bytes, v->g[G - 1].partial_bytes);
+    }
     d.ws_bytes = d.counter_bytes + d.partial_bytes;
     return NVFP4_OK;
 }
@@ -383,7 +395,7 @@ int launch_verify(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const u
                   float ts, const uint16_t* act, void* out, void* ws, size_t counters_off,
                   size_t partial_off, hipStream_t s) {
     const int G = (M + 15) / 16;
-    const DecodeConfig& d = p->ver.g[G == 4 ? 1 : 0];
+    const DecodeConfig& d = p->ver.g[G - 1];
     unsigned int* counters = d.splits > 1 ? (unsigned int*)((char*)ws + counters_off) : nullptr;
     float* partial = d.splits > 1 ? (float*)((char*)ws + partial_off) : nullptr;
     const bool bf16 = p->out_dtype == NVFP4_OUT_BF16;

@@ -455,8 +455,9 @@ def test_verify_width_boundary_to_prefill(nv):
 # Default verify-width plans at the shapes that reach each branch of the plan:
 # gate_up (K 5120, N 34816: more column groups than compute units -> two K
 # slices; 8 waves per workgroup at 49..64 rows), down (K 17408, N 5120: fewer
-# groups than units -> slices sized to one workgroup per unit) and a matrix
-# wide enough for no K split at all (N >= 65536 with 4 tiles per group).
+# groups than units -> slices sized to one workgroup per unit at 16 and 64
+# rows; long K -> 8 waves and slices of 6 superblocks at 17..48 rows) and a
+# matrix wide enough for no K split at all (N >= 65536 with 4 tiles per group).
 VERIFY_FULL = [(5120, 34816), (17408, 5120), (1024, 65552)]
 
 
@@ -475,7 +476,7 @@ def test_verify_width_default_plans_full_shapes(nv, K, N):
     sel = torch.from_numpy(cols).cuda()
     y_all, S_all = oracle.gemm(act, codes[cols], scales[cols], t)
     a = dev_bf16(act)
-    for M in (16, 40, 64):
+    for M in (16, 32, 40, 64):
         out = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
         g(pw, a[:M], out, M=M)
         torch.cuda.synchronize()
