@@ -126,9 +126,10 @@ typedef struct nvfp4_gemm_config {
     int windows; /* decode: windows of `chunks` superblocks per K slice; above 1
                     a wave streams its slice, issuing the next window's loads
                     before computing the current one (0 or 1: one window) */
-    int verify_waves;   /* verify widths (8 < M <= 64): waves per workgroup, 4, 8
-                           or 16 (0: 4 up to 48 rows, 8 above) */
-    int verify_windows; /* verify widths: superblocks per K slice (0: by shape) */
+    int verify_waves;   /* verify widths (8 < M <= 64): waves (column tiles) per
+                           workgroup, 4, 8 or 16 (0: by shape) */
+    int verify_windows; /* verify widths: superblocks of 512 k per K slice of a
+                           column group (0: by shape) */
     int tile_max_m;     /* widths M <= tile_max_m (at most 4) run the kernel with one
                            workgroup per 16-column tile over all of K, its waves
                            splitting K and adding in LDS (no workspace); 0: by shape
@@ -137,6 +138,11 @@ typedef struct nvfp4_gemm_config {
                            waves); -1: never */
     int tile_superblocks; /* that kernel: superblocks of 512 k per wave, 1..3 (0: by
                              shape) */
+    int verify_ranges;  /* verify widths: 1..4 workgroups per compute unit taking
+                           equal ranges of their XCD's superblocks, a range
+                           running on from one column group into the next, in
+                           place of per-group K slices (0: by shape; not with
+                           verify_windows) */
 } nvfp4_gemm_config;
 
 /* Create a plan for GEMMs of shape (M <= max_M) x K x N with the given output

@@ -53,7 +53,7 @@ class GemmConfig(ctypes.Structure):
     _fields_ = [("split_k", ctypes.c_int), ("waves", ctypes.c_int), ("chunks", ctypes.c_int),
                 ("windows", ctypes.c_int), ("verify_waves", ctypes.c_int),
                 ("verify_windows", ctypes.c_int), ("tile_max_m", ctypes.c_int),
-                ("tile_superblocks", ctypes.c_int)]
+                ("tile_superblocks", ctypes.c_int), ("verify_ranges", ctypes.c_int)]
 
 
 class Layer(ctypes.Structure):
@@ -205,14 +205,15 @@ def topk(logits, k, stream=None):
 
 
 def nvfp4_gemm_create(max_M, K, N, out_dtype, split_k=0, waves=0, chunks=0, windows=0,
-                      verify_waves=0, verify_windows=0, tile_max_m=0, tile_superblocks=0):
+                      verify_waves=0, verify_windows=0, tile_max_m=0, tile_superblocks=0,
+                      verify_ranges=0):
     """Returns (plan handle, workspace bytes)."""
     h = ctypes.c_void_p()
     ws = ctypes.c_size_t()
     if (split_k or waves or chunks or windows or verify_waves or verify_windows or tile_max_m
-            or tile_superblocks):
+            or tile_superblocks or verify_ranges):
         cfg = GemmConfig(split_k, waves, chunks, windows, verify_waves, verify_windows,
-                         tile_max_m, tile_superblocks)
+                         tile_max_m, tile_superblocks, verify_ranges)
         _check(lib().nvfp4_gemm_create_ex(ctypes.byref(h), max_M, K, N, out_dtype,
                                           ctypes.byref(cfg), ctypes.byref(ws)))
     else:
@@ -327,12 +328,12 @@ class Gemm:
 
     def __init__(self, max_M, K, N, out_dtype=OUT_BF16, split_k=0, waves=0, chunks=0,
                  windows=0, device="cuda", verify_waves=0, verify_windows=0, tile_max_m=0,
-                 tile_superblocks=0):
+                 tile_superblocks=0, verify_ranges=0):
         import torch
         self.plan, self.ws_bytes = nvfp4_gemm_create(max_M, K, N, out_dtype, split_k, waves,
                                                      chunks, windows, verify_waves,
                                                      verify_windows, tile_max_m,
-                                                     tile_superblocks)
+                                                     tile_superblocks, verify_ranges)
         self.K, self.N, self.max_M, self.out_dtype = K, N, max_M, out_dtype
         self.workspace = None
         if self.ws_bytes:

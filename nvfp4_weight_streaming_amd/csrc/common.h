@@ -48,6 +48,9 @@ struct DecodeConfig {
     int n_groups;       // column groups of `waves` tiles
     int grid;           // workgroups launched (n_groups padded to 8, times splits)
     int l2_local;       // split-K partials stay in one XCD's L2 (mapping verified)
+    int per_xcd;        // verify widths: workgroups per XCD (equal ranges of its windows)
+    int slots;          // verify widths: partial-sum slots per column group
+    int lds_pad;        // verify widths: dynamic LDS bytes requested beyond the kernel's own
     // Workspace layout: [counters: counter_bytes][partial sums: partial_bytes].
     // Counters come first so that, when several plans share one workspace (a
     // round), no plan's partial sums ever overlap any plan's counters.

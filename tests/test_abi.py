@@ -148,7 +148,10 @@ def test_tile_kernel_config(nv):
 def test_verify_width_config(nv):
     for bad, word in ((dict(verify_waves=2), "config.verify_waves"),
                       (dict(verify_waves=32), "config.verify_waves"),
-                      (dict(verify_windows=-1), "config.verify_windows")):
+                      (dict(verify_windows=-1), "config.verify_windows"),
+                      (dict(verify_ranges=-1), "config.verify_ranges"),
+                      (dict(verify_ranges=5), "config.verify_ranges"),
+                      (dict(verify_ranges=1, verify_windows=2), "config.verify_ranges")):
         with pytest.raises(nv.Nvfp4Error) as e:
             nv.nvfp4_gemm_create(64, 5120, 5120, 1, **bad)
         assert e.value.message.startswith(word), e.value.message

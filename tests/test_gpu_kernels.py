@@ -377,11 +377,16 @@ def test_verify_width_ragged(nv, M, K, N, bf16):
 @pytest.mark.parametrize("M,K,N", [(40, 5136, 515), (64, 3072, 300), (20, 12288, 70)])
 @pytest.mark.parametrize("cfg", [dict(verify_waves=16), dict(verify_windows=3),
                                  dict(verify_waves=16, verify_windows=1),
-                                 dict(verify_waves=8), dict(verify_waves=4, verify_windows=2)],
-                         ids=["w16", "s3", "w16s1", "w8", "w4s2"])
+                                 dict(verify_waves=8), dict(verify_waves=4, verify_windows=2),
+                                 dict(verify_ranges=1), dict(verify_ranges=2, verify_waves=4),
+                                 dict(verify_ranges=3, verify_waves=16)],
+                         ids=["w16", "s3", "w16s1", "w8", "w4s2", "r1", "r2w4", "r3w16"])
 def test_verify_width_configs(nv, M, K, N, cfg):
     """Non-default verify-width plans: 16 waves per workgroup, other slice
-    lengths (ragged last slice, one superblock per slice)."""
+    lengths (ragged last slice, one superblock per slice), and equal ranges
+    of each XCD's superblocks forced on shapes with a single column group,
+    with groups on only some XCDs, and with every group split over many
+    workgroups."""
     codes, scales = synth.random_planes(M + 71, K, N, K)
     t = 1.25e-3
     act = synth.activations(M + 72, N, M, K)
@@ -452,23 +457,28 @@ def test_verify_width_boundary_to_prefill(nv):
         check(out, y, S, bf16=False, what="M=%d" % m)
 
 
-# Default verify-width plans at the shapes that reach each branch of the plan:
-# gate_up (K 5120, N 34816: more column groups than compute units -> two K
-# slices; 8 waves per workgroup at 49..64 rows), down (K 17408, N 5120: fewer
-# groups than units -> slices sized to one workgroup per unit at 16 and 64
-# rows; long K -> 8 waves and slices of 6 superblocks at 17..48 rows) and a
-# matrix wide enough for no K split at all (N >= 65536 with 4 tiles per group).
-VERIFY_FULL = [(5120, 34816), (17408, 5120), (1024, 65552)]
+# Default verify-width plans at full-size shapes that reach each branch of
+# the plan: gate_up (K 5120, N 34816: more 4-tile groups than compute units ->
+# above 16 rows one 8-wave workgroup per unit over equal ranges of its XCD's
+# superblocks, 34 groups per XCD and about 10.6 superblocks per range; at 16
+# rows two K slices per group), down (K 17408, N 5120: per-group slices sized
+# to one workgroup per unit; long K -> 8 waves and slices of 6 superblocks at
+# 17..48 rows) and a matrix wide enough for no K split at 16 rows and ranges
+# of about two whole groups above (N = 65552, K = 1024).
+# Last: equal ranges of 4-tile groups on a matrix wide enough that a range
+# holds whole groups and runs on into the next.
+VERIFY_FULL = [(5120, 34816, {}), (17408, 5120, {}), (1024, 65552, {}),
+               (1024, 20000, dict(verify_ranges=1, verify_waves=4))]
 
 
-@pytest.mark.parametrize("K,N", VERIFY_FULL)
-def test_verify_width_default_plans_full_shapes(nv, K, N):
+@pytest.mark.parametrize("K,N,cfg", VERIFY_FULL)
+def test_verify_width_default_plans_full_shapes(nv, K, N, cfg):
     import torch
     codes, scales = synth.random_planes(K + 3, N + 1, N, K)
     t = 2.5e-3
     act = synth.activations(K + 4, N + 2, 64, K)
     pw = pack(nv, dev(codes), dev(scales), K, N, t)
-    g = nv.Gemm(64, K, N, nv.OUT_BF16)
+    g = nv.Gemm(64, K, N, nv.OUT_BF16, **cfg)
     rng = np.random.default_rng(N)
     cols = set(rng.choice(N, 48, replace=False).tolist())
     cols |= {0, 15, 16, 63, 64, N // 2, N - 65, N - 64, N - 17, N - 16, N - 1}
