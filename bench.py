@@ -528,6 +528,34 @@ def main():
             "plain_read_of_weights_us": round(hr_us, 2),
             "time_over_plain_read": round(h_us / hr_us, 4)}
 
+    # Greedy sampling after the head: the argmax fused into the head's run
+    # (nvfp4_gemm_run_argmax), against the head followed by the top-k kernel
+    # with k = 1 (same plan, same weight copies).
+    hidx = torch.empty(8, dtype=torch.int32, device="cuda")
+    area_b = nv.nvfp4_gemm_argmax_area_bytes(hg.plan)
+    area = torch.empty(area_b, dtype=torch.uint8, device="cuda")
+
+    def head_argmax():
+        hp = hpws[flip[0]]
+        nv.nvfp4_gemm_run_argmax(hg.plan, 8, HEAD_K, HEAD_N, hp.codes, hp.scales, hp.tensor_scale,
+                                 hact, hout, hidx, hg.workspace, area, area_b, stream)
+        flip[0] ^= 1
+    ha_us = time_events(head_argmax, n_head) * 1e3
+    k1_idx = torch.empty((8, 1), dtype=torch.int32, device="cuda")
+    k1_val = torch.empty((8, 1), dtype=torch.float32, device="cuda")
+    k1_wsb = nv.nvfp4_topk_workspace_bytes(8, HEAD_N, 1)
+    k1_ws = torch.empty(max(k1_wsb, 16), dtype=torch.uint8, device="cuda")
+
+    def head_then_topk():
+        head_call()
+        nv.nvfp4_topk(hout, 8, HEAD_N, HEAD_N, 1, k1_idx, k1_val, k1_ws, k1_wsb, stream)
+    ht_us = time_events(head_then_topk, n_head) * 1e3
+    log("output head + greedy argmax: fused %.1f us; head then top-k (k=1) %.1f us"
+        % (ha_us, ht_us))
+    head["with_argmax_fused_us"] = round(ha_us, 2)
+    head["then_topk_k1_us"] = round(ht_us, 2)
+    del area, hidx, k1_idx, k1_val, k1_ws
+
     # Top-k over the vocabulary, the step after the head: on the head's own
     # logits (k = 1, the greedy argmax, and k = 8), and on 7 rows of a
     # 248320-entry vocabulary (the size class of the pages' drafter top-k).

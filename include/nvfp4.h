@@ -189,6 +189,35 @@ int nvfp4_gemm_run(nvfp4_gemm plan, int M, int K, int N, const uint8_t* codes_de
                    const uint8_t* scales_dev, float tensor_scale, const uint16_t* act_dev,
                    void* out_dev, void* workspace_dev, void* stream);
 
+/* Bytes of the area nvfp4_gemm_run_argmax needs for this plan (one slot of
+ * 8 row keys per column group of the decode kernel); 0 for an invalid handle
+ * or a bf16 plan. */
+size_t nvfp4_gemm_argmax_area_bytes(nvfp4_gemm plan);
+
+/* The output head's step with greedy sampling fused in ("Ignis" README,
+ * "Speculative decoding (DFlash2)": a top-k over the vocabulary follows the
+ * head; here k = 1): runs nvfp4_gemm_run for 1 <= M <= min(8, max_M) rows of
+ * an fp32 plan, always with the decode kernel (not the narrow-width one), and
+ * also writes argmax_dev[m] = the column of the largest logit of row m, equal
+ * values resolved to the smaller column and -0.0 equal to +0.0: the index
+ * nvfp4_topk with k = 1 returns for the same logits, which are written to
+ * logits_dev [M][N] as nvfp4_gemm_run writes them with the decode kernel
+ * (for M <= 4 a plan may route nvfp4_gemm_run to the narrow-width kernel,
+ * whose sums can differ in the last bits).  The workgroup that writes a
+ * column group's logits also stores the group's row maxima; a second, small
+ * kernel takes the maximum over the groups.  NaN logits are out of contract.
+ *   argmax_dev  : int32 [M]
+ *   area_dev    : area_bytes >= nvfp4_gemm_argmax_area_bytes(plan) bytes,
+ *                 16-byte aligned, any content (every word read is written
+ *                 first in the same call); owned by the call while it runs.
+ * EINVAL for a bf16 plan, M outside [1, min(8, max_M)], a short area, or a
+ * NULL or misaligned pointer, before anything is launched.  Asynchronous; no
+ * synchronisation. */
+int nvfp4_gemm_run_argmax(nvfp4_gemm plan, int M, int K, int N, const uint8_t* codes_dev,
+                          const uint8_t* scales_dev, float tensor_scale, const uint16_t* act_dev,
+                          float* logits_dev, int* argmax_dev, void* workspace_dev,
+                          void* area_dev, size_t area_bytes, void* stream);
+
 /* nvfp4_gemm_run for callers that cannot allocate device memory (code under
  * graph capture, tight serving loops, harnesses that forbid allocation): the
  * same kernels, with the split-K counters and partial sums in a static 16 MiB

@@ -29,7 +29,7 @@ EXPORTS = (
     "nvfp4_packed_code_bytes", "nvfp4_packed_scale_bytes", "nvfp4_pack", "nvfp4_unpack",
     "nvfp4_quantize_workspace_bytes", "nvfp4_quantize",
     "nvfp4_gemm_create", "nvfp4_gemm_create_ex", "nvfp4_gemm_destroy", "nvfp4_gemm_run",
-    "nvfp4_gemm_run_noalloc",
+    "nvfp4_gemm_run_noalloc", "nvfp4_gemm_argmax_area_bytes", "nvfp4_gemm_run_argmax",
     "nvfp4_workspace_clear",
     "nvfp4_round_workspace_bytes", "nvfp4_round_create", "nvfp4_round_run",
     "nvfp4_round_graph_nodes", "nvfp4_round_destroy",
@@ -99,6 +99,10 @@ def lib():
         L.nvfp4_gemm_destroy.restype = None
         L.nvfp4_gemm_run.argtypes = [vp, i, i, i, vp, vp, c.c_float, vp, vp, vp, vp]
         L.nvfp4_gemm_run_noalloc.argtypes = [vp, i, i, i, vp, vp, c.c_float, vp, vp, vp]
+        L.nvfp4_gemm_run_argmax.argtypes = [vp, i, i, i, vp, vp, c.c_float, vp, vp, vp, vp, vp,
+                                            sz, vp]
+        L.nvfp4_gemm_argmax_area_bytes.argtypes = [vp]
+        L.nvfp4_gemm_argmax_area_bytes.restype = sz
         L.nvfp4_workspace_clear.argtypes = [vp, sz, vp]
         L.nvfp4_round_workspace_bytes.argtypes = [c.POINTER(Layer), i, i, c.POINTER(sz)]
         L.nvfp4_round_create.argtypes = [c.POINTER(vp), c.POINTER(Layer), i, i, vp, sz, vp]
@@ -181,6 +185,18 @@ def nvfp4_swiglu(gate_up, M, F, out, stream=None):
 
 def nvfp4_stream_read(buf, nbytes, sink, stream=None):
     _check(lib().nvfp4_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)))
+
+
+def nvfp4_gemm_argmax_area_bytes(plan) -> int:
+    return lib().nvfp4_gemm_argmax_area_bytes(plan)
+
+
+def nvfp4_gemm_run_argmax(plan, M, K, N, codes, scales, tensor_scale, act, logits, argmax,
+                          workspace, area, area_bytes, stream=None):
+    _check(lib().nvfp4_gemm_run_argmax(plan, M, K, N, _ptr(codes), _ptr(scales),
+                                       tensor_scale, _ptr(act), _ptr(logits),
+                                       _ptr(argmax), _ptr(workspace), _ptr(area), area_bytes,
+                                       _stream(stream)))
 
 
 def nvfp4_topk_workspace_bytes(M, V, k) -> int:

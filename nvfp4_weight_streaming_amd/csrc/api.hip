@@ -202,6 +202,35 @@ int nvfp4_gemm_run(nvfp4_gemm plan, int M, int K, int N, const uint8_t* codes_de
                     workspace_dev, gemm_offsets(plan), (hipStream_t)stream);
 }
 
+size_t nvfp4_gemm_argmax_area_bytes(nvfp4_gemm plan) {
+    if (!plan || plan->magic != kGemmMagic || plan->out_dtype != NVFP4_OUT_F32) return 0;
+    return ((size_t)plan->dec.n_groups * 8 * sizeof(unsigned long long) + 255) / 256 * 256;
+}
+
+int nvfp4_gemm_run_argmax(nvfp4_gemm plan, int M, int K, int N, const uint8_t* codes_dev,
+                          const uint8_t* scales_dev, float tensor_scale, const uint16_t* act_dev,
+                          float* logits_dev, int* argmax_dev, void* workspace_dev,
+                          void* area_dev, size_t area_bytes, void* stream) {
+    clear_error();
+    int st = validate_run(plan, M, K, N, codes_dev, scales_dev, act_dev, logits_dev,
+                          workspace_dev);
+    if (st != NVFP4_OK) return st;
+    if (plan->out_dtype != NVFP4_OUT_F32)
+        return set_error(NVFP4_EINVAL, "plan: bf16 outputs; the argmax run needs fp32 logits");
+    if (M > NVFP4_DECODE_MAX_M)
+        return set_error(NVFP4_EINVAL, "M: %d above %d for the argmax run", M, NVFP4_DECODE_MAX_M);
+    if (!argmax_dev) return set_error(NVFP4_EINVAL, "argmax: NULL");
+    if (((uintptr_t)argmax_dev & 3) != 0) return set_error(NVFP4_EINVAL, "argmax: not 4-byte aligned");
+    if (!area_dev) return set_error(NVFP4_EINVAL, "area: NULL");
+    if (!aligned16(area_dev)) return set_error(NVFP4_EINVAL, "area: not 16-byte aligned");
+    const size_t need = nvfp4_gemm_argmax_area_bytes(plan);
+    if (area_bytes < need)
+        return set_error(NVFP4_EINVAL, "area: %zu bytes, the plan needs %zu", area_bytes, need);
+    return launch_decode_argmax(plan, M, codes_dev, scales_dev, tensor_scale, act_dev,
+                                logits_dev, workspace_dev, gemm_offsets(plan).dec_partial,
+                                area_dev, argmax_dev, (hipStream_t)stream);
+}
+
 // ---- GEMM runs that allocate nothing ----------------------------------------------
 
 // For callers that cannot allocate device memory (graph capture, serving loops,

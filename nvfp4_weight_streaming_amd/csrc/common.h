@@ -116,6 +116,9 @@ size_t prefill_ws_bytes(int M, int K, int N);
 int launch_decode(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
                   float ts, const uint16_t* act, void* out, void* ws, size_t partial_off,
                   hipStream_t s);
+int launch_decode_argmax(const nvfp4_gemm_plan* p, int M, const uint8_t* codes,
+                         const uint8_t* scales, float ts, const uint16_t* act, float* out,
+                         void* ws, size_t partial_off, void* area, int* argmax, hipStream_t s);
 int launch_tile(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
                 float ts, const uint16_t* act, void* out, hipStream_t s);
 int launch_verify(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,

@@ -32,14 +32,73 @@
 
 namespace nvfp4 {
 
+// Argmax of each output row, fused into the output head's run (the step
+// after the head: "Ignis" README, "Speculative decoding (DFlash2)", top-k over
+// the vocabulary; k = 1 here).  Logit v at column n becomes the key
+// (ord(v) << 32) | ~n of the top-k kernel: a larger key is a larger value, or
+// an equal one at a smaller column (-0 equals +0).  The one workgroup that
+// writes a column group's outputs folds their keys into LDS per row and
+// stores the group's 8 row keys to its slot of the caller's area (plain
+// stores, no atomics); argmax_merge_kernel then takes each row's maximum over
+// the slots.  Measured at M = 8, N = 152064: the head with its argmax 75.8 us,
+// the head alone 69.9, the head followed by the top-k kernel with k = 1 76.0:
+// the second launch costs what the top-k launch did.  (A first form folded
+// the keys into per-XCD words with L2 atomics and elected the last group by
+// counters, with no second launch: every workgroup then waited for two atomic
+// round trips, and the head with its argmax took 80.3 us against 76.5.)
+struct ArgmaxRef {
+    unsigned long long* area;    // [groups][8] row keys; null: no argmax
+    unsigned long long* s_keys;  // LDS, 8 words
+};
+
+__device__ __forceinline__ unsigned long long argmax_key(float v, int n) {
+    unsigned int b = __float_as_uint(v);
+    if (b == 0x80000000u) b = 0u;  // -0 -> +0
+    const unsigned int o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return ((unsigned long long)o << 32) | (unsigned int)(~n);
+}
+
+// After a group's outputs are written and their keys folded into s_keys.
+__device__ __forceinline__ void argmax_group_done(const ArgmaxRef& am, int ng) {
+    __syncthreads();  // every output's key is in s_keys
+    if (threadIdx.x < 8) am.area[(size_t)ng * 8 + threadIdx.x] = am.s_keys[threadIdx.x];
+}
+
+// Row m's argmax from the n_groups slots of the area (workgroup m, 256
+// threads).  (One workgroup of 1024 threads reading whole slots and keeping
+// all 8 rows measured slower: 78.7 us for the head with its argmax against
+// 75.8.)
+__global__ __launch_bounds__(256) void argmax_merge_kernel(const unsigned long long* __restrict__ area,
+                                                           int n_groups, int* __restrict__ out) {
+    __shared__ unsigned long long s_best[4];
+    const int m = blockIdx.x;
+    unsigned long long best = 0;
+    for (int g = threadIdx.x; g < n_groups; g += 256) {
+        const unsigned long long k = area[(size_t)g * 8 + m];
+        best = k > best ? k : best;
+    }
+    for (int o = 32; o >= 1; o >>= 1) {
+        const unsigned long long k = __shfl_xor(best, o, 64);
+        best = k > best ? k : best;
+    }
+    if ((threadIdx.x & 63) == 0) s_best[threadIdx.x >> 6] = best;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < 4; ++w) best = s_best[w] > best ? s_best[w] : best;
+        out[m] = (int)~(unsigned int)best;
+    }
+}
+
 // The end of a workgroup: the two row halves of each lane's sums are added,
-// then the outputs (one slice) or the split-K hand-off (several).
+// then the outputs (one slice) or the split-K hand-off (several), and the
+// argmax step when asked for.
 template <int WAVES, bool BF16>
 __device__ __forceinline__ void decode_finish(float (&acc)[4], void* __restrict__ out,
                                               float* __restrict__ partial,
                                               unsigned int* __restrict__ counters, float ts,
                                               int M, int N, int splits, int n_tiles, int l2_local,
-                                              int ng, int split, int nt, int* s_last) {
+                                              int ng, int split, int nt, int* s_last,
+                                              const ArgmaxRef& am) {
     constexpr int kThreads = WAVES * 64;
     constexpr int kCols = WAVES * kTileN;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -48,6 +107,18 @@ __device__ __forceinline__ void decode_finish(float (&acc)[4], void* __restrict_
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] += __shfl_xor(acc[j], 32, 64);
     const bool mine = lane < 32 && ng * WAVES + wave < n_tiles;
+    const bool amax = am.area != nullptr;  // (uniform)
+    if (amax) {
+        if (threadIdx.x < 8) am.s_keys[threadIdx.x] = 0;
+        __syncthreads();
+    }
+    // Output (mm, n) = v: stored, and its key folded into the row's LDS word.
+    auto emit = [&](int mm, int n, float v) {
+        store_out<BF16>(out, (size_t)mm * N + n, v);
+        if (amax)
+            __hip_atomic_fetch_max(&am.s_keys[mm], argmax_key(v, n), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
 
     if (splits == 1) {
         if (mine) {
@@ -55,9 +126,10 @@ __device__ __forceinline__ void decode_finish(float (&acc)[4], void* __restrict_
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int mm = 4 * g + j;
-                if (mm < M && n < N) store_out<BF16>(out, (size_t)mm * N + n, acc[j] * ts);
+                if (mm < M && n < N) emit(mm, n, acc[j] * ts);
             }
         }
+        if (amax) argmax_group_done(am, ng);
         return;
     }
 
@@ -85,8 +157,14 @@ __device__ __forceinline__ void decode_finish(float (&acc)[4], void* __restrict_
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0) {
+        // (agent scope is a read-modify-write in this XCD's L2; without the
+        // verified mapping the contributors may sit on several XCDs, so the
+        // counter is then device-coherent)
         const unsigned int old =
-            __hip_atomic_fetch_add(&counters[ng], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            l2_local ? __hip_atomic_fetch_add(&counters[ng], 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT)
+                     : __hip_atomic_fetch_add(&counters[ng], 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_SYSTEM);
         *s_last = (old == (unsigned int)(splits - 1));
     }
     __syncthreads();
@@ -103,10 +181,15 @@ __device__ __forceinline__ void decode_finish(float (&acc)[4], void* __restrict_
         const int idx = threadIdx.x + r * kThreads;
         const int mm = idx / kCols, c = idx - mm * kCols;
         const int n = ng * kCols + c;
-        if (idx < M * kCols && n < N) store_out<BF16>(out, (size_t)mm * N + n, sum[r] * ts);
+        if (idx < M * kCols && n < N) emit(mm, n, sum[r] * ts);
     }
-    if (threadIdx.x == 0)  // leave the counter zeroed for the next run
-        __hip_atomic_store(&counters[ng], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) {  // leave the counter zeroed for the next run
+        if (l2_local)
+            __hip_atomic_store(&counters[ng], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+            __hip_atomic_store(&counters[ng], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    if (amax) argmax_group_done(am, ng);
 }
 
 // One workgroup = WAVES column tiles (one per wave) x one K slice of up to
@@ -120,11 +203,12 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
     const uint4* __restrict__ codes, const uint4* __restrict__ scales,
     const uint16_t* __restrict__ act, void* __restrict__ out, float* __restrict__ partial,
     unsigned int* __restrict__ counters, float ts, int M, int K, int N, int nsb, int splits,
-    int n_groups, int n_tiles, int l2_local) {
+    int n_groups, int n_tiles, int l2_local, unsigned long long* __restrict__ amax_area) {
     constexpr int kThreads = WAVES * 64;
     constexpr int kStride = NCH * kSuperK + kLdsPad;          // LDS row, bf16 elements
     __shared__ __attribute__((aligned(16))) __bf16 lds[9 * kStride];
     __shared__ int s_last;
+    __shared__ unsigned long long s_keys[8];
 
     const int b = blockIdx.x;
     const int xcd = b & 7, q = b >> 3;
@@ -168,7 +252,8 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
         if (c < nch) chunk_steps(acc, w[c], ap + c * kSuperK);
 
     decode_finish<WAVES, BF16>(acc, out, partial, counters, ts, M, N, splits, n_tiles, l2_local,
-                               ng, split, nt, &s_last);
+                               ng, split, nt, &s_last,
+                               ArgmaxRef{amax_area, s_keys});
 }
 
 // ---- long slices ------------------------------------------------------------------
@@ -199,7 +284,8 @@ __global__ __launch_bounds__(WAVES * 64) void decode_window_kernel(
     const uint4* __restrict__ codes, const uint4* __restrict__ scales,
     const uint16_t* __restrict__ act, void* __restrict__ out, float* __restrict__ partial,
     unsigned int* __restrict__ counters, float ts, int M, int K, int N, int nsb, int splits,
-    int n_groups, int n_tiles, int l2_local, int windows) {
+    int n_groups, int n_tiles, int l2_local, int windows,
+    unsigned long long* __restrict__ amax_area) {
     constexpr int kThreads = WAVES * 64;
     constexpr int kStride = NCH * kSuperK + kLdsPad;  // LDS row, bf16 elements
     constexpr int kSeg = 8 * NCH / WAVES;  // activation segments (1 KiB) per wave per window
@@ -211,6 +297,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_window_kernel(
     __shared__ __attribute__((aligned(16))) __bf16 lds0[9 * kStride];
     __shared__ __attribute__((aligned(16))) __bf16 lds1[9 * kStride];
     __shared__ int s_last;
+    __shared__ unsigned long long s_keys[8];
 
     const int b = blockIdx.x;
     const int xcd = b & 7, q = b >> 3;
@@ -317,7 +404,8 @@ __global__ __launch_bounds__(WAVES * 64) void decode_window_kernel(
         step(w, No{}, wa, wb, lds0, lds1);
     }
     decode_finish<WAVES, BF16>(acc, out, partial, counters, ts, M, N, splits, n_tiles, l2_local,
-                               ng, split, nt, &s_last);
+                               ng, split, nt, &s_last,
+                               ArgmaxRef{amax_area, s_keys});
 }
 
 // ---- narrow widths: one workgroup per column tile ------------------------------------
@@ -634,10 +722,15 @@ int make_decode_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, De
     return NVFP4_OK;
 }
 
+// The argmax step's area for a launch (null: none).
+struct ArgmaxArgs {
+    unsigned long long* area;
+};
+
 template <int WAVES, int NCH, bool BF16>
 static int launch_t(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
                     float ts, const uint16_t* act, void* out, void* ws, size_t partial_off,
-                    hipStream_t s) {
+                    const ArgmaxArgs& am, hipStream_t s) {
     const DecodeConfig& d = p->dec;
     unsigned int* counters = (unsigned int*)ws;
     float* partial = ws ? (float*)((char*)ws + partial_off) : nullptr;
@@ -645,12 +738,12 @@ static int launch_t(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const
         hipLaunchKernelGGL((decode_window_kernel<WAVES, NCH, BF16>), dim3(d.grid),
                            dim3(WAVES * 64), 0, s, (const uint4*)codes, (const uint4*)scales, act,
                            out, partial, counters, ts, M, p->K, p->N, p->Kp / kSuperK, d.splits,
-                           d.n_groups, p->Np / kTileN, d.l2_local, d.windows);
+                           d.n_groups, p->Np / kTileN, d.l2_local, d.windows, am.area);
     else
         hipLaunchKernelGGL((decode_kernel<WAVES, NCH, BF16>), dim3(d.grid), dim3(WAVES * 64), 0,
                            s, (const uint4*)codes, (const uint4*)scales, act, out, partial,
                            counters, ts, M, p->K, p->N, p->Kp / kSuperK, d.splits, d.n_groups,
-                           p->Np / kTileN, d.l2_local);
+                           p->Np / kTileN, d.l2_local, am.area);
     NVFP4_HIP(hipGetLastError());
     return NVFP4_OK;
 }
@@ -658,37 +751,55 @@ static int launch_t(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const
 template <int WAVES, bool BF16>
 static int launch_c(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
                     float ts, const uint16_t* act, void* out, void* ws, size_t po,
-                    hipStream_t s) {
+                    const ArgmaxArgs& am, hipStream_t s) {
     switch (p->dec.chunks) {
-        case 1: return launch_t<WAVES, 1, BF16>(p, M, codes, scales, ts, act, out, ws, po, s);
-        case 2: return launch_t<WAVES, 2, BF16>(p, M, codes, scales, ts, act, out, ws, po, s);
-        case 3: return launch_t<WAVES, 3, BF16>(p, M, codes, scales, ts, act, out, ws, po, s);
-        default: return launch_t<WAVES, 4, BF16>(p, M, codes, scales, ts, act, out, ws, po, s);
+        case 1: return launch_t<WAVES, 1, BF16>(p, M, codes, scales, ts, act, out, ws, po, am, s);
+        case 2: return launch_t<WAVES, 2, BF16>(p, M, codes, scales, ts, act, out, ws, po, am, s);
+        case 3: return launch_t<WAVES, 3, BF16>(p, M, codes, scales, ts, act, out, ws, po, am, s);
+        default: return launch_t<WAVES, 4, BF16>(p, M, codes, scales, ts, act, out, ws, po, am, s);
     }
 }
 
 template <bool BF16>
 static int launch_w(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
                     float ts, const uint16_t* act, void* out, void* ws, size_t po,
-                    hipStream_t s) {
-    if (p->dec.waves == 8) return launch_c<8, BF16>(p, M, codes, scales, ts, act, out, ws, po, s);
-    return launch_c<4, BF16>(p, M, codes, scales, ts, act, out, ws, po, s);
+                    const ArgmaxArgs& am, hipStream_t s) {
+    if (p->dec.waves == 8)
+        return launch_c<8, BF16>(p, M, codes, scales, ts, act, out, ws, po, am, s);
+    return launch_c<4, BF16>(p, M, codes, scales, ts, act, out, ws, po, am, s);
 }
 
 int launch_decode(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
                   float ts, const uint16_t* act, void* out, void* ws, size_t partial_off,
                   hipStream_t s) {
     const size_t esz = p->out_dtype == NVFP4_OUT_BF16 ? 2 : 4;
+    const ArgmaxArgs none{nullptr};
     // Rows beyond 8 (when no prefill kernel applies) run as further weight passes.
     for (int m0 = 0; m0 < M; m0 += NVFP4_DECODE_MAX_M) {
         const int mm = M - m0 < NVFP4_DECODE_MAX_M ? M - m0 : NVFP4_DECODE_MAX_M;
         const uint16_t* a = act + (size_t)m0 * p->K;
         void* o = (char*)out + (size_t)m0 * p->N * esz;
         int st = p->out_dtype == NVFP4_OUT_BF16
-                     ? launch_w<true>(p, mm, codes, scales, ts, a, o, ws, partial_off, s)
-                     : launch_w<false>(p, mm, codes, scales, ts, a, o, ws, partial_off, s);
+                     ? launch_w<true>(p, mm, codes, scales, ts, a, o, ws, partial_off, none, s)
+                     : launch_w<false>(p, mm, codes, scales, ts, a, o, ws, partial_off, none, s);
         if (st) return st;
     }
+    return NVFP4_OK;
+}
+
+// M <= 8 rows of an fp32 plan through the decode kernel (never the narrow-width
+// tile kernel), each column group's row keys to its slot of `area`, then the
+// merge kernel: row m's argmax to argmax[m].
+int launch_decode_argmax(const nvfp4_gemm_plan* p, int M, const uint8_t* codes,
+                         const uint8_t* scales, float ts, const uint16_t* act, float* out,
+                         void* ws, size_t partial_off, void* area, int* argmax,
+                         hipStream_t s) {
+    const ArgmaxArgs am{(unsigned long long*)area};
+    const int st = launch_w<false>(p, M, codes, scales, ts, act, out, ws, partial_off, am, s);
+    if (st) return st;
+    hipLaunchKernelGGL(argmax_merge_kernel, dim3(M), dim3(256), 0, s,
+                       (const unsigned long long*)area, p->dec.n_groups, argmax);
+    NVFP4_HIP(hipGetLastError());
     return NVFP4_OK;
 }
 

@@ -103,14 +103,24 @@ __device__ __forceinline__ void verify_finish(const f32x4 (&acc)[G], void* __res
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0) {
+        // (agent scope is a read-modify-write in this XCD's L2; without the
+        // verified mapping the contributors may sit on several XCDs, so the
+        // counter is then device-coherent)
         const unsigned int old =
-            __hip_atomic_fetch_add(&counters[ng], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            l2_local ? __hip_atomic_fetch_add(&counters[ng], 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT)
+                     : __hip_atomic_fetch_add(&counters[ng], 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_SYSTEM);
         *s_last = (old == (unsigned int)(nc - 1));
     }
     __syncthreads();
     if (!*s_last) return;
-    if (threadIdx.x == 0)  // leave the counter zeroed for the next run
-        __hip_atomic_store(&counters[ng], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) {  // leave the counter zeroed for the next run
+        if (l2_local)
+            __hip_atomic_store(&counters[ng], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+            __hip_atomic_store(&counters[ng], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
     if (!mine) return;
     // The slots in contributor order (this workgroup's own from registers):
     // the same sum whichever contributor arrives last.  Loads of kB slots are

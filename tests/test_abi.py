@@ -145,6 +145,35 @@ def test_tile_kernel_config(nv):
         nv.nvfp4_gemm_destroy(plan)
 
 
+def test_gemm_run_argmax_validation(nv):
+    """Errors the fused argmax run raises before launching anything."""
+    f32, _ = nv.nvfp4_gemm_create(8, 5120, 1000, nv.OUT_F32)
+    bf, _ = nv.nvfp4_gemm_create(8, 5120, 1000, nv.OUT_BF16)
+    wide, _ = nv.nvfp4_gemm_create(16, 5120, 1000, nv.OUT_F32)
+    # one slot of 8 row keys per 4-tile column group (1000 columns: 16 groups)
+    need = nv.nvfp4_gemm_argmax_area_bytes(f32)
+    assert need >= 16 * 64 and nv.nvfp4_gemm_argmax_area_bytes(bf) == 0
+    p16, ok4 = 0x10000, 0x10004  # aligned stand-ins: nothing is dereferenced before validation
+    base = dict(K=5120, N=1000, codes=p16, scales=p16, tensor_scale=1.0, act=p16, logits=p16,
+                argmax=ok4, workspace=p16, area=p16, area_bytes=need)
+    cases = [(bf, 8, {}, "plan"), (f32, 0, {}, "M"), (wide, 9, {}, "M"),
+             (f32, 8, dict(argmax=None), "argmax"), (f32, 8, dict(argmax=0x10002), "argmax"),
+             (f32, 8, dict(area=None), "area"), (f32, 8, dict(area=0x10008), "area"),
+             (f32, 8, dict(area_bytes=need - 16), "area"), (f32, 8, dict(K=4096), "K")]
+    try:
+        for plan, M, over, word in cases:
+            a = dict(base, **over)
+            with pytest.raises(nv.Nvfp4Error) as e:
+                nv.nvfp4_gemm_run_argmax(plan, M, a["K"], a["N"], a["codes"], a["scales"],
+                                         a["tensor_scale"], a["act"], a["logits"], a["argmax"],
+                                         a["workspace"], a["area"], a["area_bytes"], stream=0)
+            assert e.value.status == nv.EINVAL and e.value.message.startswith(word), \
+                (M, over, e.value.message)
+    finally:
+        for p in (f32, bf, wide):
+            nv.nvfp4_gemm_destroy(p)
+
+
 def test_verify_width_config(nv):
     for bad, word in ((dict(verify_waves=2), "config.verify_waves"),
                       (dict(verify_waves=32), "config.verify_waves"),
