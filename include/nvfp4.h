@@ -66,6 +66,18 @@ enum nvfp4_out_dtype { NVFP4_OUT_F32 = 0, NVFP4_OUT_BF16 = 1 };
  * M goes to the prefill kernel. */
 #define NVFP4_VERIFY_MAX_M 64
 
+/* Prefill schedules (nvfp4_gemm_config.prefill_schedule) for M > 64, whose
+ * 256 x 256 output tiles are spread over the compute units: */
+enum nvfp4_prefill_schedule {
+    NVFP4_PREFILL_AUTO = 0,     /* stream-K when the tiles outnumber the compute
+                                   units and are not a multiple of them, else pieces */
+    NVFP4_PREFILL_PIECES = 1,   /* whole tiles; the tiles of a last partial round cut
+                                   along K into pieces, added by a second kernel */
+    NVFP4_PREFILL_STREAM_K = 2  /* (where it applies) every compute unit takes an
+                                   equal run of the tiles' K stages laid end to end; a
+                                   tile shared by two units is finished by the later */
+};
+
 /* Largest k of nvfp4_topk. */
 #define NVFP4_TOPK_MAX_K 64
 
@@ -143,6 +155,7 @@ typedef struct nvfp4_gemm_config {
                            running on from one column group into the next, in
                            place of per-group K slices (0: by shape; not with
                            verify_windows) */
+    int prefill_schedule; /* M > 64: an nvfp4_prefill_schedule */
 } nvfp4_gemm_config;
 
 /* Create a plan for GEMMs of shape (M <= max_M) x K x N with the given output
@@ -175,11 +188,15 @@ void nvfp4_gemm_destroy(nvfp4_gemm plan);
  *                           if the plan needs none
  * (K, N) must equal the plan's, 1 <= M <= max_M.  M <= 8 uses the decode
  * kernel and 8 < M <= 64 the verify-width decode kernel (each one pass over
- * the weights for all M rows); larger M uses the bf16 MFMA prefill kernel,
- * and, when the 256 x 256 output tiles leave a last partial round on the
- * device's compute units, a second kernel that adds the fp32 partial sums of
- * those tiles' K pieces.  The workspace holds, in this order, the decode,
- * verify and prefill areas the plan's max_M needs.  For M > 8 and K not a
+ * the weights for all M rows); larger M uses the bf16 MFMA prefill kernel.
+ * When its 256 x 256 output tiles outnumber the device's compute units and
+ * are not a multiple of them, it runs the stream-K schedule (one workgroup
+ * per compute unit, equal runs of K stages; the two fp32 partial sums of a
+ * shared tile meet in the workspace and the later contributor adds them);
+ * with fewer tiles than compute units, a last partial round's tiles are cut
+ * along K and a second kernel adds their pieces (NVFP4_PREFILL_PIECES asks
+ * for that schedule in every case).  The workspace holds, in this order, the
+ * decode, verify and prefill areas the plan's max_M needs.  For M > 8 and K not a
  * multiple of 512, every activation value must be finite: those kernels read
  * the tail of a row's last K window from the start of the next row and
  * multiply it by the zero weights past K (an infinity or NaN there would turn
@@ -223,8 +240,11 @@ int nvfp4_gemm_run_argmax(nvfp4_gemm plan, int M, int K, int N, const uint8_t* c
  * same kernels, with the split-K counters and partial sums in a static 16 MiB
  * device array per GPU (held until the process ends) instead of a caller
  * workspace.  Arguments as nvfp4_gemm_run, without the workspace.  A run that
- * needs more than 16 MiB of that state (a large prefill chunk) returns
- * NVFP4_EUNSUPPORTED and launches nothing.  The first call on a device
+ * needs more than 16 MiB of that state (a large prefill chunk; every
+ * stream-K prefill run, whose hand-off slots take 512 KiB per pair of
+ * neighbouring compute units: a plan made with NVFP4_PREFILL_PIECES needs
+ * none where its tiles fill whole rounds) returns NVFP4_EUNSUPPORTED and
+ * launches nothing.  The first call on a device
  * zero-fills the array with one kernel on `stream`, so it must be made
  * outside stream capture (under capture it returns NVFP4_ESTATE and launches
  * nothing); later calls may be captured.  Every call on a GPU uses

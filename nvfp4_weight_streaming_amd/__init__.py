@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
 
 OK, EINVAL, EUNSUPPORTED, EHIP, ESTATE = 0, 1, 2, 3, 4
 OUT_F32, OUT_BF16 = 0, 1
+PREFILL_AUTO, PREFILL_PIECES, PREFILL_STREAM_K = 0, 1, 2
 DECODE_MAX_M = 8
 VERIFY_MAX_M = 64
 
@@ -53,7 +54,8 @@ class GemmConfig(ctypes.Structure):
     _fields_ = [("split_k", ctypes.c_int), ("waves", ctypes.c_int), ("chunks", ctypes.c_int),
                 ("windows", ctypes.c_int), ("verify_waves", ctypes.c_int),
                 ("verify_windows", ctypes.c_int), ("tile_max_m", ctypes.c_int),
-                ("tile_superblocks", ctypes.c_int), ("verify_ranges", ctypes.c_int)]
+                ("tile_superblocks", ctypes.c_int), ("verify_ranges", ctypes.c_int),
+                ("prefill_schedule", ctypes.c_int)]
 
 
 class Layer(ctypes.Structure):
@@ -222,14 +224,14 @@ def topk(logits, k, stream=None):
 
 def nvfp4_gemm_create(max_M, K, N, out_dtype, split_k=0, waves=0, chunks=0, windows=0,
                       verify_waves=0, verify_windows=0, tile_max_m=0, tile_superblocks=0,
-                      verify_ranges=0):
+                      verify_ranges=0, prefill_schedule=0):
     """Returns (plan handle, workspace bytes)."""
     h = ctypes.c_void_p()
     ws = ctypes.c_size_t()
     if (split_k or waves or chunks or windows or verify_waves or verify_windows or tile_max_m
-            or tile_superblocks or verify_ranges):
+            or tile_superblocks or verify_ranges or prefill_schedule):
         cfg = GemmConfig(split_k, waves, chunks, windows, verify_waves, verify_windows,
-                         tile_max_m, tile_superblocks, verify_ranges)
+                         tile_max_m, tile_superblocks, verify_ranges, prefill_schedule)
         _check(lib().nvfp4_gemm_create_ex(ctypes.byref(h), max_M, K, N, out_dtype,
                                           ctypes.byref(cfg), ctypes.byref(ws)))
     else:
@@ -344,12 +346,13 @@ class Gemm:
 
     def __init__(self, max_M, K, N, out_dtype=OUT_BF16, split_k=0, waves=0, chunks=0,
                  windows=0, device="cuda", verify_waves=0, verify_windows=0, tile_max_m=0,
-                 tile_superblocks=0, verify_ranges=0):
+                 tile_superblocks=0, verify_ranges=0, prefill_schedule=0):
         import torch
         self.plan, self.ws_bytes = nvfp4_gemm_create(max_M, K, N, out_dtype, split_k, waves,
                                                      chunks, windows, verify_waves,
                                                      verify_windows, tile_max_m,
-                                                     tile_superblocks, verify_ranges)
+                                                     tile_superblocks, verify_ranges,
+                                                     prefill_schedule)
         self.K, self.N, self.max_M, self.out_dtype = K, N, max_M, out_dtype
         self.workspace = None
         if self.ws_bytes:

@@ -85,7 +85,7 @@ int validate_run(const nvfp4_gemm_plan* p, int M, int K, int N, const void* code
 
 RunOffsets gemm_offsets(const nvfp4_gemm_plan* p) {
     return RunOffsets{p->dec.counter_bytes, p->ver.ws_off, p->ver.ws_off + p->ver.d.counter_bytes,
-                      p->pre.ws_off};
+                      p->pre.ws_off, p->pre.ws_off + p->pre.counter_bytes};
 }
 
 int run_gemm(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
@@ -93,7 +93,8 @@ int run_gemm(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_
              hipStream_t s) {
     const size_t partial_off = off.dec_partial;
     if (M > NVFP4_VERIFY_MAX_M && p->pre.enabled)
-        return launch_prefill(p, M, codes, scales, ts, act, out, ws, off.pre_partial, s);
+        return launch_prefill(p, M, codes, scales, ts, act, out, ws, off.pre_counters,
+                              off.pre_partial, p->pre.schedule, s);
     if (M > NVFP4_DECODE_MAX_M && p->ver.enabled)
         return launch_verify(p, M, codes, scales, ts, act, out, ws, off.ver_counters,
                              off.ver_partial, s);
@@ -155,13 +156,13 @@ static int create_plan(nvfp4_gemm* plan, int max_M, int K, int N, int out_dtype,
     int st = make_decode_config(K, N, max_M, cfg, &p->dec);
     if (!st) st = make_tile_config(K, N, max_M, cfg, &p->tile);
     if (!st) st = make_verify_config(K, N, max_M, cfg, &p->ver);
-    if (!st) st = make_prefill_config(max_M, K, N, &p->pre);
+    if (!st) st = make_prefill_config(max_M, K, N, cfg, &p->pre);
     if (st != NVFP4_OK) {
         p->magic = 0;
         delete p;
         return st;
     }
-    // [decode counters, partials][verify counters, partials][prefill partials]:
+    // [decode counters, partials][verify counters, partials][prefill counters, partials]:
     // the counters must stay zero between runs, so no area overlaps another.
     auto align = [](size_t v) { return (v + 255) & ~(size_t)255; };
     const size_t dec_ws = p->dec.ws_bytes;
@@ -284,7 +285,7 @@ static int scratch_for_current_device(hipStream_t s, void** ptr) {
 static void noalloc_need(const nvfp4_gemm_plan* p, int M, size_t* counters, size_t* partials) {
     *counters = *partials = 0;
     if (M > NVFP4_VERIFY_MAX_M && p->pre.enabled) {
-        *partials = prefill_ws_bytes(M, p->K, p->N);
+        prefill_ws_need(p, M, p->pre.schedule, counters, partials);
     } else if (M > NVFP4_DECODE_MAX_M && p->ver.enabled) {
         *counters = p->ver.d.counter_bytes;
         *partials = p->ver.d.partial_bytes;
@@ -315,7 +316,7 @@ int nvfp4_gemm_run_noalloc(nvfp4_gemm plan, int M, int K, int N, const uint8_t* 
     void* ws = nullptr;
     st = scratch_for_current_device((hipStream_t)stream, &ws);
     if (st) return st;
-    const RunOffsets off{kScratchCounters, 0, kScratchCounters, kScratchCounters};
+    const RunOffsets off{kScratchCounters, 0, kScratchCounters, 0, kScratchCounters};
     return run_gemm(plan, M, codes_dev, scales_dev, tensor_scale, act_dev, out_dev, ws, off,
                     (hipStream_t)stream);
 }

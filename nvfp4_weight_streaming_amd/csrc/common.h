@@ -78,8 +78,11 @@ struct TileConfig {
 
 struct PrefillConfig {
     int enabled;
-    size_t ws_off;    // partial sums of K-split tiles: offset in the workspace
-    size_t ws_bytes;  // and their size (0: no M the plan serves splits)
+    int schedule;          // NVFP4_PREFILL_*: 0 by shape
+    int cus;               // compute units the schedule and workspace are laid out for
+    size_t ws_off;         // [counters][partial sums] of split tiles: offset in the workspace
+    size_t counter_bytes;  // the counters' share (stream-K hand-offs; zero between runs)
+    size_t ws_bytes;       // and the whole area (0: no M the plan serves splits)
 };
 
 }  // namespace nvfp4
@@ -106,9 +109,8 @@ int xcd_mapping_verified();
 int make_verify_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, VerifyConfig* out);
 int make_decode_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, DecodeConfig* out);
 int make_tile_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, TileConfig* out);
-int make_prefill_config(int max_M, int K, int N, PrefillConfig* out);
-// Bytes of K-piece partial sums a prefill run of M rows uses (after pre.ws_off).
-size_t prefill_ws_bytes(int M, int K, int N);
+int make_prefill_config(int max_M, int K, int N, const nvfp4_gemm_config* cfg,
+                        PrefillConfig* out);
 
 // Launchers (no validation: callers validated).  Return NVFP4_OK or EHIP.
 // ws: the workspace; partial_off: byte offset of the partial sums in it (the
@@ -127,8 +129,12 @@ int launch_verify(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const u
 // pre_off: byte offset of the K pieces' partial sums in ws (the plan's own
 // pre.ws_off, or another place a caller lays out).
 int launch_prefill(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
-                   float ts, const uint16_t* act, void* out, void* ws, size_t pre_off,
-                   hipStream_t s);
+                   float ts, const uint16_t* act, void* out, void* ws, size_t ctr_off,
+                   size_t pre_off, int schedule, hipStream_t s);
+// Counter and partial-sum bytes a prefill run of M rows uses with `schedule`
+// (an NVFP4_PREFILL_* value; a plan runs its own, pre.schedule).
+void prefill_ws_need(const nvfp4_gemm_plan* p, int M, int schedule, size_t* counters,
+                     size_t* partials);
 int launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 int launch_swiglu(const uint16_t* gate_up, uint16_t* out, int M, int F, hipStream_t s);
 
@@ -141,7 +147,8 @@ struct RunOffsets {
     size_t dec_partial;   // decode partials (its counters start at 0)
     size_t ver_counters;  // verify-width counters
     size_t ver_partial;   // verify-width partials
-    size_t pre_partial;   // prefill K pieces' partial sums
+    size_t pre_counters;  // prefill stream-K counters
+    size_t pre_partial;   // prefill partial sums (stream-K slots or K pieces)
 };
 RunOffsets gemm_offsets(const nvfp4_gemm_plan* p);
 int run_gemm(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,

@@ -121,7 +121,7 @@ struct PrefillB {
     int coff[kB], soff[kB];
 
     __device__ __forceinline__ void init(const uint8_t* codes, const uint8_t* scales, int nsb,
-                                         int n_tiles, int nt0) {
+                                         int n_tiles, int nt0, int tid) {
         const size_t tiles = (size_t)(n_tiles - nt0);
         rc = prefill_rsrc(codes + (size_t)nt0 * nsb * kCodeBytesPerSuper,
                           tiles * nsb * kCodeBytesPerSuper);
@@ -129,7 +129,7 @@ struct PrefillB {
                           tiles * nsb * kScaleBytesPerSuper);
 #pragma unroll
         for (int i = 0; i < kB; ++i) {
-            const int u = threadIdx.x + NW * 64 * i;
+            const int u = tid + NW * 64 * i;
             const int t = u >> 6, ls = u & 63;
             const int col = ls & 15, p = (ls >> 4) >> 1;
             coff[i] = t * nsb * kCodeBytesPerSuper + ls * 16;
@@ -161,10 +161,10 @@ struct PStage {
     // Piece q (0 .. 2 kB - 1) of the dequantised store: lane slot q / 2, word
     // q % 2 (8 values).
     template <int Q>
-    __device__ __forceinline__ void store_piece(__bf16* lb, int kt) const {
+    __device__ __forceinline__ void store_piece(__bf16* lb, int kt, int tid) const {
         constexpr int i = Q / 2, w = Q % 2;
         const int h = (kt * kPBK % 128) / 64;
-        const int u = threadIdx.x + NW * 64 * i;
+        const int u = tid + NW * 64 * i;
         const int ls = u & 63;
         const int col = (u >> 6) * 16 + (ls & 15), g = ls >> 4;
         const int sw = (int)(s[i] >> (16 * h));
@@ -172,11 +172,11 @@ struct PStage {
         *(uint4*)(lb + swz(col, 4 * w + g)) = dequant8(w ? c[i].y : c[i].x, sc);
     }
 
-    __device__ __forceinline__ void store(__bf16* lb, int kt) const {
+    __device__ __forceinline__ void store(__bf16* lb, int kt, int tid) const {
         const int h = (kt * kPBK % 128) / 64;
 #pragma unroll
         for (int i = 0; i < kB; ++i) {
-            const int u = threadIdx.x + NW * 64 * i;
+            const int u = tid + NW * 64 * i;
             const int ls = u & 63;
             const int col = (u >> 6) * 16 + (ls & 15), g = ls >> 4;
             const int sw = (int)(s[i] >> (16 * h));
@@ -197,11 +197,11 @@ struct PStage {
 // multiplies of step ks.
 template <int BM, int BN, int NW, int Q>
 __device__ __forceinline__ void prefill_store_share(const PStage<BN, NW>& nx, __bf16* lbn,
-                                                    int ktn, int ks) {
+                                                    int ktn, int ks, int tid) {
     constexpr int kPieces = 2 * PStage<BN, NW>::kB;
     // pieces ks * kPieces / 4 .. (ks + 1) * kPieces / 4 - 1
     if constexpr (Q < kPieces) {
-        if (Q * 4 / kPieces == ks) nx.template store_piece<Q>(lbn, ktn);
+        if (Q * 4 / kPieces == ks) nx.template store_piece<Q>(lbn, ktn, tid);
     }
 }
 
@@ -219,7 +219,7 @@ template <int BM, int BN, int NW>
 __device__ __forceinline__ void prefill_mma(
     f32x16 (&acc)[ptiles_i(BM, NW)][ptiles_j(BN)], const __bf16* la,
     const __bf16* lb, const PStage<BN, NW>& nx, __bf16* lbn, int ktn, int wm, int wn, int r32,
-    int half) {
+    int half, int tid) {
     constexpr int TI = PTiles<BM, BN, NW>::TI, TJ = PTiles<BM, BN, NW>::TJ;
     constexpr int WM = PTiles<BM, BN, NW>::WM;
     bf16x8 av[2][TI], bv[2][TJ];
@@ -244,40 +244,39 @@ __device__ __forceinline__ void prefill_mma(
             for (int j = 0; j < TJ; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[buf][i], bv[buf][j],
                                                                     acc[i][j], 0, 0, 0);
-        prefill_store_share<BM, BN, NW, 0>(nx, lbn, ktn, ks);
-        prefill_store_share<BM, BN, NW, 1>(nx, lbn, ktn, ks);
-        prefill_store_share<BM, BN, NW, 2>(nx, lbn, ktn, ks);
-        prefill_store_share<BM, BN, NW, 3>(nx, lbn, ktn, ks);
+        prefill_store_share<BM, BN, NW, 0>(nx, lbn, ktn, ks, tid);
+        prefill_store_share<BM, BN, NW, 1>(nx, lbn, ktn, ks, tid);
+        prefill_store_share<BM, BN, NW, 2>(nx, lbn, ktn, ks, tid);
+        prefill_store_share<BM, BN, NW, 3>(nx, lbn, ktn, ks, tid);
     }
     __builtin_amdgcn_s_setprio(0);
 }
 
-// One BM x BN block tile over K stages kt0 .. kt1 - 1; wave w owns rows
-// (w / 4) * BM / (NW / 4) and columns (w % 4) * BN/4, as TI x TJ MFMA tiles
-// of 32 x 32 (PTiles).  With part == nullptr the tile covers all of K and stores
-// acc * ts to out; otherwise it stores its raw accumulators to part (BM * BN
-// floats, in register order: float4 ((((w TI + i) TJ + j) 4 + r / 4) 64 +
-// lane) holds elements r .. r + 3 of lane's MFMA tile (i, j)).
-template <int BM, int BN, int NW, bool BF16>
-__device__ __forceinline__ void prefill_tile(PrefillLds& L, const uint8_t* __restrict__ codes,
-                                             const uint8_t* __restrict__ scales,
-                                             const uint16_t* __restrict__ act,
-                                             void* __restrict__ out, float* __restrict__ part,
-                                             float ts, int M, int K, int N, int nsb, int n_tiles,
-                                             int m0, int n0, int kt0, int kt1) {
+// This wave's share of the BM x BN block tile at (m0, n0) over K stages
+// kt0 .. kt1 - 1 (kt1 > kt0), accumulated into acc from zero; wave w owns
+// rows (w / 4) * BM / (NW / 4) and columns (w % 4) * BN/4, as TI x TJ MFMA
+// tiles of 32 x 32 (PTiles).  On return, re-reads of the last stage may still
+// be in flight into L (the prefetch runs two stages past the end): a caller
+// that reuses L waits for them and for every wave first.  tid is the thread
+// index (a caller looping over tiles passes it opaque, so that the addresses
+// derived from it are not computed once before that loop and held).
+template <int BM, int BN, int NW>
+__device__ __forceinline__ void prefill_accumulate(
+    f32x16 (&acc)[ptiles_i(BM, NW)][ptiles_j(BN)], PrefillLds& L,
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+    const uint16_t* __restrict__ act, int M, int K, int nsb, int n_tiles, int m0, int n0,
+    int kt0, int kt1, int tid) {
     constexpr int TI = PTiles<BM, BN, NW>::TI, TJ = PTiles<BM, BN, NW>::TJ;
-    constexpr int WM = PTiles<BM, BN, NW>::WM;
     // loads per thread per stage: weights (a code and a scale load per lane
     // slot) and activation copies
     constexpr int kWL = 2 * PStage<BN, NW>::kB, kAL = PrefillA<BM, NW>::kL;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = tid >> 6, lane = tid & 63;
     const int wm = wave >> 2, wn = wave & 3;
     const int nt0 = n0 / kTileN;
     const int nks = kt1 - kt0;
     // absolute stage of relative stage u, clamped to the last one
     auto at = [&](int u) { return kt0 + min(u, nks - 1); };
 
-    f32x16 acc[TI][TJ];
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -293,12 +292,12 @@ __device__ __forceinline__ void prefill_tile(PrefillLds& L, const uint8_t* __res
     PrefillA<BM, NW> A;
     A.init(act, M, K, m0, wave, lane);
     PrefillB<BN, NW> B;
-    B.init(codes, scales, nsb, n_tiles, nt0);
+    B.init(codes, scales, nsb, n_tiles, nt0, tid);
     PStage<BN, NW> st0, st1;
     A.copy(L.a[0], at(0), wave);
     st0.load(B, at(0));
     __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));
-    st0.store(L.b[0], at(0));
+    st0.store(L.b[0], at(0), tid);
     // The loads in flight when the loop starts are issued in the order the
     // loop itself leaves them at the end of each stage (weights of stage 1,
     // activation copy of stage 1, weights of stage 2), so the compiler's own
@@ -323,7 +322,7 @@ __device__ __forceinline__ void prefill_tile(PrefillLds& L, const uint8_t* __res
         A.copy(L.a[(u + 2) % 3], at(u + 2), wave);
         __builtin_amdgcn_sched_barrier(0);
         prefill_mma<BM, BN, NW>(acc, L.a[u % 3], L.b[u & 1], next, L.b[(u + 1) & 1], at(u + 1),
-                                wm, wn, r32, half);
+                                wm, wn, r32, half, tid);
         __builtin_amdgcn_sched_barrier(0);
         next.load(B, at(u_next));
         __builtin_amdgcn_sched_barrier(0);
@@ -345,23 +344,24 @@ __device__ __forceinline__ void prefill_tile(PrefillLds& L, const uint8_t* __res
         stage(u + 1, st1, u + 4);
     }
     if (u < nks) stage(u, st0, u + 3);
+}
 
-    if (part) {
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-#pragma unroll
-            for (int j = 0; j < TJ; ++j)
-#pragma unroll
-                for (int rq = 0; rq < 4; ++rq) {
-                    const int v = (((wave * TI + i) * TJ + j) * 4 + rq) * 64 + lane;
-                    *(float4*)(part + 4 * v) =
-                        make_float4(acc[i][j][4 * rq], acc[i][j][4 * rq + 1],
-                                    acc[i][j][4 * rq + 2], acc[i][j][4 * rq + 3]);
-                }
-        return;
-    }
-    // Epilogue: element r of a 32 x 32 tile in lane l is
-    // (row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32).
+// Epilogue of a whole tile: element r of a 32 x 32 MFMA tile in lane l is
+// (row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32); acc * ts to out.
+template <int BM, int BN, int NW, bool BF16>
+__device__ __forceinline__ void prefill_store_tile(
+    const f32x16 (&acc)[ptiles_i(BM, NW)][ptiles_j(BN)], void* __restrict__ out, float ts, int M,
+    int N, int m0, int n0) {
+    constexpr int TI = PTiles<BM, BN, NW>::TI, TJ = PTiles<BM, BN, NW>::TJ;
+    constexpr int WM = PTiles<BM, BN, NW>::WM;
+    // (the thread index made opaque here: in a loop over tiles the compiler
+    // would otherwise compute these addresses once, before the loop, and
+    // hold them in registers through the multiplies)
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int wave = tid >> 6, lane = tid & 63;
+    const int wm = wave >> 2, wn = wave & 3;
+    const int r32 = lane & 31, half = lane >> 5;
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -373,6 +373,45 @@ __device__ __forceinline__ void prefill_tile(PrefillLds& L, const uint8_t* __res
                 if (m < M && n < N) store_out<BF16>(out, (size_t)m * N + n, acc[i][j][r] * ts);
             }
         }
+}
+
+// Raw accumulators of a K piece to part (BM * BN floats, in register order:
+// float4 ((((w TI + i) TJ + j) 4 + r / 4) 64 + lane) holds elements r .. r + 3
+// of lane's MFMA tile (i, j) of wave w).
+template <int BM, int BN, int NW>
+__device__ __forceinline__ void prefill_store_piece(
+    const f32x16 (&acc)[ptiles_i(BM, NW)][ptiles_j(BN)], float* __restrict__ part) {
+    constexpr int TI = PTiles<BM, BN, NW>::TI, TJ = PTiles<BM, BN, NW>::TJ;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const int v = (((wave * TI + i) * TJ + j) * 4 + rq) * 64 + lane;
+                *(float4*)(part + 4 * v) = make_float4(acc[i][j][4 * rq], acc[i][j][4 * rq + 1],
+                                                       acc[i][j][4 * rq + 2], acc[i][j][4 * rq + 3]);
+            }
+}
+
+// One block tile over K stages kt0 .. kt1 - 1, in a workgroup of its own.
+// With part == nullptr the tile covers all of K and stores acc * ts to out;
+// otherwise it stores its raw accumulators to part (prefill_store_piece).
+template <int BM, int BN, int NW, bool BF16>
+__device__ __forceinline__ void prefill_tile(PrefillLds& L, const uint8_t* __restrict__ codes,
+                                             const uint8_t* __restrict__ scales,
+                                             const uint16_t* __restrict__ act,
+                                             void* __restrict__ out, float* __restrict__ part,
+                                             float ts, int M, int K, int N, int nsb, int n_tiles,
+                                             int m0, int n0, int kt0, int kt1) {
+    f32x16 acc[ptiles_i(BM, NW)][ptiles_j(BN)];
+    prefill_accumulate<BM, BN, NW>(acc, L, codes, scales, act, M, K, nsb, n_tiles, m0, n0, kt0,
+                                   kt1, threadIdx.x);
+    if (part)
+        prefill_store_piece<BM, BN, NW>(acc, part);
+    else
+        prefill_store_tile<BM, BN, NW, BF16>(acc, out, ts, M, N, m0, n0);
 }
 
 constexpr int kPTile = 256;                      // block tile edge (rows and outputs)
@@ -404,6 +443,163 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(
         prefill_tile<kPTile, kPTile, kPWaves, BF16>(L, codes, scales, act, out, nullptr, ts, M,
                                                     K, N, nsb, n_tiles, (t % mblocks) * kPTile,
                                                     (t / mblocks) * kPTile, 0, nk);
+    }
+}
+
+// ---- stream-K schedule ----------------------------------------------------------
+//
+// With more tiles than compute units, and not a multiple of them, the tiles'
+// K stages are laid end to end (tile after tile, W = tiles * nk in all) and
+// workgroup r of C (one per compute unit) takes the stages r W / C ..
+// (r + 1) W / C - 1: every unit gets the same number of stages, with no last
+// partial round.  A run holds at least one tile's nk stages, so a tile is
+// shared by at most two workgroups: r, whose run ends inside it (its head,
+// stages 0 .. h - 1), and r + 1 (its tail, h .. nk - 1), which meet at
+// boundary r.  A workgroup runs its head first, then its tail, then its
+// whole tiles, so the hand-offs of shared tiles happen early and spread over
+// the run while other workgroups compute.
+
+// Cache policy of the hand-off's stores and loads between XCDs: device scope
+// (sc1), so that they bypass the XCDs' non-coherent cached copies.
+constexpr int kPDeviceScope = 16;
+constexpr int kPWaveFloats = 32 * 32 * PTiles<256, 256, kPWaves>::TI * PTiles<256, 256, kPWaves>::TJ;
+
+// Hand-off of a shared tile, wave by wave (wave w of both contributors owns
+// the same outputs): the wave stores its accumulators to its slot (role 0:
+// head, 1: tail) and, once the stores have completed, increments its counter
+// at boundary bi.  With both contributors on one XCD (LOCAL) the slots and
+// the counter live in that XCD's L2: plain stores and loads, an agent-scope
+// atomic.  Otherwise the stores and loads are device-scope and the counter
+// system-scope (coherent across XCDs).  The wave that finds the other's increment already there adds the
+// other's slot to its accumulators, stores the outputs and zeroes the
+// counter again.  The sum is own + other: the same float whichever wave
+// comes second (addition commutes), so the outputs do not depend on the
+// order of arrival.  Slots: float4 ((i TJ + j) 4 + r / 4) 64 + lane of
+// slot (2 bi + role) NW + w holds elements r .. r + 3 of lane's MFMA tile.
+template <int BM, int BN, int NW, bool BF16, bool LOCAL>
+__device__ __forceinline__ void prefill_handoff(f32x16 (&acc)[ptiles_i(BM, NW)][ptiles_j(BN)],
+                                                float* __restrict__ slots,
+                                                unsigned int* __restrict__ counters, int bi,
+                                                int role, void* __restrict__ out, float ts, int M,
+                                                int N, int m0, int n0) {
+    constexpr int TI = PTiles<BM, BN, NW>::TI, TJ = PTiles<BM, BN, NW>::TJ;
+    constexpr int kF = 32 * 32 * TI * TJ;  // floats per wave
+    constexpr int kAux = LOCAL ? 0 : kPDeviceScope;
+    // (the wave index through a scalar register: the slot addresses are
+    // uniform, so the buffer resources stay scalar)
+    // (the thread index opaque, as in prefill_store_tile)
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    float* mine = slots + ((size_t)(2 * bi + role) * NW + wave) * kF;
+    const float* other = slots + ((size_t)(2 * bi + (role ^ 1)) * NW + wave) * kF;
+    const __amdgpu_buffer_rsrc_t rm = prefill_rsrc(mine, (size_t)kF * 4);
+    const __amdgpu_buffer_rsrc_t ro = prefill_rsrc(other, (size_t)kF * 4);
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const int v = ((i * TJ + j) * 4 + rq) * 64 + lane;
+                const u32x4 x = {__float_as_uint(acc[i][j][4 * rq]),
+                                 __float_as_uint(acc[i][j][4 * rq + 1]),
+                                 __float_as_uint(acc[i][j][4 * rq + 2]),
+                                 __float_as_uint(acc[i][j][4 * rq + 3])};
+                __builtin_amdgcn_raw_buffer_store_b128(x, rm, 16 * v, 0, kAux);
+            }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    unsigned int* ctr = counters + (size_t)bi * NW + wave;
+    unsigned int old = 0;
+    if (lane == 0)
+        old = LOCAL ? __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                    : __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    old = __builtin_amdgcn_readlane(old, 0);
+    asm volatile("" ::: "memory");
+    if (old == 0) return;  // the other wave comes second and finishes
+    // The other's slot in batches of kBatch MFMA tiles (their loads in flight
+    // together), within the registers the accumulators leave.
+    constexpr int kBatch = 2;
+#pragma unroll
+    for (int b0 = 0; b0 < TI * TJ; b0 += kBatch) {
+        u32x4 x[kBatch * 4];
+#pragma unroll
+        for (int q = 0; q < kBatch * 4; ++q)
+            x[q] = __builtin_amdgcn_raw_buffer_load_b128(ro, 16 * ((b0 * 4 + q) * 64 + lane), 0,
+                                                         kAux);
+#pragma unroll
+        for (int q = 0; q < kBatch * 4; ++q) {
+            const int i = (b0 + q / 4) / TJ, j = (b0 + q / 4) % TJ, rq = q % 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][4 * rq + e] += __uint_as_float(x[q][e]);
+        }
+        asm volatile("" ::: "memory");
+    }
+    if (lane == 0) {
+        if (LOCAL)
+            __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+            __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    prefill_store_tile<BM, BN, NW, BF16>(acc, out, ts, M, N, m0, n0);
+}
+
+// Stream tile t covers rows (t / nblocks) * 256 and outputs (t % nblocks) *
+// 256.  Run r's parts in order: the head of tile hi / nk (if the run ends
+// inside a tile), the tail of tile lo / nk (if it starts inside one), then
+// the whole tiles between.  Slots: 2 NW kPWaveFloats floats per boundary;
+// counters: NW per boundary, zero between runs.
+template <bool BF16>
+__global__ __launch_bounds__(kPThreads) void prefill_sk_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+    const uint16_t* __restrict__ act, void* __restrict__ out, float* __restrict__ slots,
+    unsigned int* __restrict__ counters, float ts, int M, int K, int N, int nsb, int n_tiles,
+    int nblocks, int tiles, int l2_local) {
+    __shared__ __attribute__((aligned(16))) PrefillLds L;
+    const int nk = (K + kPBK - 1) / kPBK;
+    const long long W = (long long)tiles * nk;
+    const int C = (int)gridDim.x;
+    // Run r of workgroup b: with C a multiple of 8, the C / 8 workgroups of
+    // one XCD (b % 8) take consecutive runs, and the stream holds the tiles
+    // row block by row block, so an XCD works on the same rows of
+    // activations (kept in its L2) across its column blocks.
+    const int r = C % 8 ? (int)blockIdx.x : (int)(blockIdx.x % 8) * (C / 8) + (int)blockIdx.x / 8;
+    // (l2_local: workgroup b verified to run on XCD b % 8, and C % 8 == 0)
+    const long long lo = W * r / C, hi = W * (r + 1) / C;
+    const int h = (int)(hi % nk), a = (int)(lo % nk);
+    const int t_head = (int)(hi / nk), t_tail = (int)(lo / nk);
+    const int t_first = (int)((lo + nk - 1) / nk);  // first whole tile
+    const int nh = h > 0, na = a > 0;  // a head part, a tail part
+    const int n_parts = nh + na + (t_head - t_first);
+    f32x16 acc[PTiles<kPTile, kPTile, kPWaves>::TI][PTiles<kPTile, kPTile, kPWaves>::TJ];
+    for (int q = 0; q < n_parts; ++q) {
+        // part q is of kind 0 (head), 1 (tail) or 2 (whole tile q - nh - na)
+        const int kind = q < nh ? 0 : q < nh + na ? 1 : 2;
+        const int t = kind == 0 ? t_head : kind == 1 ? t_tail : t_first + (q - nh - na);
+        const int kt0 = kind == 1 ? a : 0, kt1 = kind == 0 ? h : nk;
+        const int m0 = (t / nblocks) * kPTile, n0 = (t % nblocks) * kPTile;
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        prefill_accumulate<kPTile, kPTile, kPWaves>(acc, L, codes, scales, act, M, K, nsb,
+                                                    n_tiles, m0, n0, kt0, kt1, tid);
+        // The part ended with a barrier after every wave's last LDS reads;
+        // this wave's re-reads past the end (into its own rows and columns
+        // of L) must land before the next part's first copies.  Waiting here,
+        // before the epilogue, leaves the epilogue's stores in flight.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (kind == 2) {
+            prefill_store_tile<kPTile, kPTile, kPWaves, BF16>(acc, out, ts, M, N, m0, n0);
+        } else {
+            // boundary bi between runs bi and bi + 1: on one XCD (its L2)
+            // unless bi + 1 starts the next XCD's segment
+            const int bi = kind == 0 ? r : r - 1;
+            if (l2_local && (bi + 1) % (C / 8) != 0)
+                prefill_handoff<kPTile, kPTile, kPWaves, BF16, true>(acc, slots, counters, bi,
+                                                                     kind, out, ts, M, N, m0, n0);
+            else
+                prefill_handoff<kPTile, kPTile, kPWaves, BF16, false>(
+                    acc, slots, counters, bi, kind, out, ts, M, N, m0, n0);
+        }
     }
 }
 
@@ -454,17 +650,25 @@ __global__ __launch_bounds__(kPReduceThreads) void prefill_reduce_kernel(
         if (m + r < M) store_out<BF16>(out, (size_t)(m + r) * N + n, e[r] * ts);
 }
 
-// Tiles beyond whole rounds (one tile per compute unit at a time) are split
-// along K when at least two pieces each fit: n_tail tiles, S pieces each.
+// How a run of M rows is laid out over the compute units.  With more tiles
+// than units, and not a multiple of them, the stream-K schedule (unless the
+// plan asks for pieces); otherwise the tiles beyond whole rounds (one tile
+// per compute unit at a time) are split along K when at least two pieces
+// each fit: n_tail tiles, S pieces each.
 struct PrefillSplit {
     int tiles, n_tail, splits;
+    bool stream;
 };
 
-static PrefillSplit prefill_split(int M, int K, int N, int cus) {
+static PrefillSplit prefill_split(int M, int K, int N, int cus, int schedule) {
     const int mblocks = (M + kPTile - 1) / kPTile, nblocks = (N + kPTile - 1) / kPTile;
     const int nk = (K + kPBK - 1) / kPBK;
-    PrefillSplit s{mblocks * nblocks, 0, 1};
+    PrefillSplit s{mblocks * nblocks, 0, 1, false};
     const int left = s.tiles % cus;
+    if (schedule != NVFP4_PREFILL_PIECES && s.tiles > cus && left) {
+        s.stream = true;
+        return s;
+    }
     const int S = left ? min(cus / left, nk / kPMinPieceStages) : 1;
     if (S >= 2) {
         s.n_tail = left;
@@ -473,37 +677,78 @@ static PrefillSplit prefill_split(int M, int K, int N, int cus) {
     return s;
 }
 
-int make_prefill_config(int max_M, int K, int N, PrefillConfig* out) {
+// Workspace of a run: [counters][partial sums] (stream-K: a counter per wave
+// and two slots per boundary between workgroups; pieces: no counters, the
+// pieces' partial sums).
+static void prefill_need(const PrefillSplit& s, int cus, size_t* counters, size_t* partials) {
+    if (s.stream) {
+        *counters = ((size_t)(cus - 1) * kPWaves * sizeof(unsigned int) + 255) & ~(size_t)255;
+        *partials = (size_t)(cus - 1) * 2 * kPWaves * kPWaveFloats * sizeof(float);
+    } else {
+        *counters = 0;
+        *partials = (size_t)s.n_tail * s.splits * kPTileFloats * sizeof(float);
+    }
+}
+
+int make_prefill_config(int max_M, int K, int N, const nvfp4_gemm_config* cfg,
+                        PrefillConfig* out) {
     out->enabled = max_M > NVFP4_VERIFY_MAX_M;
     out->ws_off = 0;
     out->ws_bytes = 0;
+    out->counter_bytes = 0;
+    out->schedule = cfg ? cfg->prefill_schedule : 0;
+    out->cus = device_cus();
+    if (out->schedule < 0 || out->schedule > NVFP4_PREFILL_STREAM_K)
+        return set_error(NVFP4_EINVAL, "config.prefill_schedule: %d outside [0, %d]",
+                         out->schedule, NVFP4_PREFILL_STREAM_K);
     if (!out->enabled) return NVFP4_OK;
-    // The largest partial-sum area over every M the plan serves (the split
-    // depends on M only through the row blocks).
-    const int cus = device_cus();
+    // The largest counter and partial-sum areas over every M the plan serves
+    // (the layout depends on M only through the row blocks).
+    size_t part = 0;
     for (int mb = 1; mb <= (max_M + kPTile - 1) / kPTile; ++mb) {
-        const PrefillSplit s = prefill_split(mb * kPTile, K, N, cus);
-        const size_t bytes = (size_t)s.n_tail * s.splits * kPTileFloats * sizeof(float);
-        if (bytes > out->ws_bytes) out->ws_bytes = bytes;
+        size_t c = 0, p = 0;
+        prefill_need(prefill_split(mb * kPTile, K, N, out->cus, out->schedule), out->cus, &c, &p);
+        if (c > out->counter_bytes) out->counter_bytes = c;
+        if (p > part) part = p;
     }
+    out->ws_bytes = out->counter_bytes + part;
     return NVFP4_OK;
 }
 
-size_t prefill_ws_bytes(int M, int K, int N) {
-    const PrefillSplit s = prefill_split(M, K, N, device_cus());
-    return (size_t)s.n_tail * s.splits * kPTileFloats * sizeof(float);
+void prefill_ws_need(const nvfp4_gemm_plan* p, int M, int schedule, size_t* counters,
+                     size_t* partials) {
+    prefill_need(prefill_split(M, p->K, p->N, p->pre.cus, schedule), p->pre.cus, counters,
+                 partials);
 }
 
 int launch_prefill(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const uint8_t* scales,
-                   float ts, const uint16_t* act, void* out, void* ws, size_t pre_off,
-                   hipStream_t s) {
+                   float ts, const uint16_t* act, void* out, void* ws, size_t ctr_off,
+                   size_t pre_off, int schedule, hipStream_t s) {
     const int n_tiles = p->Np / kTileN, nsb = p->Kp / kSuperK;
     const int mblocks = (M + kPTile - 1) / kPTile;
-    const PrefillSplit sp = prefill_split(M, p->K, p->N, device_cus());
+    const PrefillSplit sp = prefill_split(M, p->K, p->N, p->pre.cus, schedule);
+    const bool bf16 = p->out_dtype == NVFP4_OUT_BF16;
+    if (sp.stream) {
+        // one workgroup per compute unit (the plan's count, which sized the
+        // workspace); the kernel needs more tiles than workgroups
+        float* slots = (float*)((char*)ws + pre_off);
+        unsigned int* counters = (unsigned int*)((char*)ws + ctr_off);
+        const dim3 grid((unsigned)p->pre.cus);
+        const int l2_local = p->pre.cus % 8 == 0 && xcd_mapping_verified();
+        if (bf16)
+            hipLaunchKernelGGL(prefill_sk_kernel<true>, grid, dim3(kPThreads), 0, s, codes,
+                               scales, act, out, slots, counters, ts, M, p->K, p->N, nsb, n_tiles,
+                               sp.tiles / mblocks, sp.tiles, l2_local);
+        else
+            hipLaunchKernelGGL(prefill_sk_kernel<false>, grid, dim3(kPThreads), 0, s, codes,
+                               scales, act, out, slots, counters, ts, M, p->K, p->N, nsb, n_tiles,
+                               sp.tiles / mblocks, sp.tiles, l2_local);
+        NVFP4_HIP(hipGetLastError());
+        return NVFP4_OK;
+    }
     const int pieces = sp.n_tail * sp.splits;
     float* part = pieces ? (float*)((char*)ws + pre_off) : nullptr;
     const dim3 grid((unsigned)(sp.tiles - sp.n_tail + pieces));
-    const bool bf16 = p->out_dtype == NVFP4_OUT_BF16;
     if (bf16)
         hipLaunchKernelGGL(prefill_kernel<true>, grid, dim3(kPThreads), 0, s, codes, scales, act,
                            out, part, ts, M, p->K, p->N, nsb, n_tiles, mblocks, sp.tiles,

@@ -179,7 +179,7 @@ int nvfp4_round_create(nvfp4_round* plan, const nvfp4_layer* layers, int n_layer
             if (lst) break;
             lst = run_gemm(r->plans[i], M, l.codes_dev, l.scales_dev, l.tensor_scale, l.act_dev,
                            l.out_dev, workspace,
-                           RunOffsets{r->partial_off, 0, r->partial_off, r->partial_off},
+                           RunOffsets{r->partial_off, 0, r->partial_off, 0, r->partial_off},
                            cap);
         }
         hipGraph_t g = nullptr;

@@ -82,13 +82,13 @@ def canary_out(M, N, dtype):
 
 def run(nv, pw, act_dev, out_dtype, M=None, split_k=0, waves=0, chunks=0, max_M=None,
         windows=0, verify_waves=0, verify_windows=0, tile_max_m=0, tile_superblocks=0,
-        verify_ranges=0):
+        verify_ranges=0, prefill_schedule=0):
     import torch
     M = act_dev.shape[0] if M is None else M
     g = nv.Gemm(max_M or M, pw.K, pw.N, out_dtype, split_k=split_k, waves=waves, chunks=chunks,
                 windows=windows, verify_waves=verify_waves, verify_windows=verify_windows,
                 tile_max_m=tile_max_m, tile_superblocks=tile_superblocks,
-                verify_ranges=verify_ranges)
+                verify_ranges=verify_ranges, prefill_schedule=prefill_schedule)
     dt = torch.float32 if out_dtype == nv.OUT_F32 else torch.bfloat16
     out, assert_canary = canary_out(M, pw.N, dt)
     g(pw, act_dev, out, M=M)

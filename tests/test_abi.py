@@ -192,6 +192,31 @@ def test_verify_width_config(nv):
     nv.nvfp4_gemm_destroy(p64)
 
 
+def test_prefill_schedule_config_and_workspace(nv):
+    """prefill_schedule outside 0..2 is refused.  With the device's compute
+    units taken as 256 when no GPU answers (the plan's own count otherwise),
+    a prefill chunk of 544 tiles gets the stream-K area: counters, then two
+    slots of 256 x 256 fp32 sums per pair of neighbouring workgroups; the
+    pieces schedule instead holds its last round's K pieces."""
+    for bad in (-1, 3):
+        with pytest.raises(nv.Nvfp4Error) as e:
+            nv.nvfp4_gemm_create(2048, 5120, 17408, 1, prefill_schedule=bad)
+        assert e.value.message.startswith("config.prefill_schedule"), e.value.message
+    p, ws = nv.nvfp4_gemm_create(2048, 5120, 17408, 1)
+    pp, wsp = nv.nvfp4_gemm_create(2048, 5120, 17408, 1, prefill_schedule=nv.PREFILL_PIECES)
+    ps, wss = nv.nvfp4_gemm_create(2048, 5120, 17408, 1, prefill_schedule=nv.PREFILL_STREAM_K)
+    try:
+        assert ws == wss
+        if not _gpu_visible():
+            cus = 256
+            slots = (cus - 1) * 2 * 256 * 256 * 4
+            counters = ((cus - 1) * 8 * 4 + 255) // 256 * 256
+            assert ws - wsp == slots + counters - 32 * 8 * 256 * 256 * 4
+    finally:
+        for h in (p, pp, ps):
+            nv.nvfp4_gemm_destroy(h)
+
+
 def test_topk_validation_and_workspace(nv):
     L = nv.lib()
     assert nv.nvfp4_topk_workspace_bytes(8, 1024, 8) == 0       # one unit per row

@@ -496,8 +496,9 @@ def test_verify_width_default_plans_full_shapes(nv, K, N, cfg):
 
 # ---- prefill (M > 8: dequantised tiles, bf16 MFMA) ------------------------------
 
-# All but the last split their tiles along K (fp32 partial sums and a second
-# kernel); K = 256 is too short to split (4 stages of 64).
+# At most one tile per compute unit: all but the last split their tiles along K
+# (fp32 partial sums and a second kernel); K = 256 is too short to split (4
+# stages of 64).
 @pytest.mark.parametrize("M,K,N", [(9, 512, 64), (64, 1024, 256), (300, 1040, 530),
                                    (513, 2048, 300), (256, 5120, 272), (40, 256, 1000)])
 @pytest.mark.parametrize("bf16", [False, True])
@@ -531,11 +532,103 @@ def test_prefill_and_decode_share_a_workspace(nv):
         check(out, y, S, bf16=False, what="M=%d after the other path" % m)
 
 
+# ---- prefill, stream-K schedule (more tiles than compute units) ----------------
+
+def _stream_k_shape(nv, M, N):
+    """True when the device runs (M, N) with the stream-K schedule."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles = ((M + 255) // 256) * ((N + 255) // 256)
+    return tiles > cus and tiles % cus != 0
+
+
+def _quarter_cols(N, seed):
+    """A random column in every 64-column quarter of each 256-column block:
+    with every row, that samples every wave's outputs of every tile (a wave
+    owns one quarter of a tile's columns), the shared tiles' included."""
+    rng = np.random.default_rng(seed)
+    cols = {q + int(rng.integers(0, min(64, N - q))) for q in range(0, N, 64)}
+    return np.array(sorted(cols | {0, N - 1}))
+
+
+def _sk_case(nv, M, K, N, seed):
+    codes, scales = synth.random_planes(seed, M + N, N, K)
+    t = float(np.float32(np.random.default_rng(seed).uniform(1e-4, 1e-2)))
+    act = synth.activations(seed + 1, K + N, M, K)
+    pw = pack(nv, dev(codes), dev(scales), K, N, t)
+    cols = _quarter_cols(N, seed)
+    y, S = oracle.gemm(act, codes[cols], scales[cols], t)
+    return pw, dev_bf16(act), cols, y, S
+
+
+# Ragged M, N and K (K = 1040: a partial last stage; K = 16: one stage, so no
+# tile is shared); 258 to 354 tiles on 256 compute units.
+SK_SHAPES = [(300, 1040, 33000), (100, 2048, 66000), (600, 512, 30000), (300, 16, 40000)]
+
+
+@pytest.mark.parametrize("M,K,N", SK_SHAPES)
+@pytest.mark.parametrize("bf16", [False, True])
+def test_prefill_stream_k_sampled(nv, M, K, N, bf16):
+    import torch
+    assert _stream_k_shape(nv, M, N)
+    pw, a, cols, y, S = _sk_case(nv, M, K, N, M + K + N)
+    out, _ = run(nv, pw, a, nv.OUT_BF16 if bf16 else nv.OUT_F32)  # (canaries checked)
+    check(out[:, torch.from_numpy(cols).cuda()], y, S, bf16=bf16,
+          what="stream-K prefill %r" % ((M, K, N),))
+
+
+def test_prefill_stream_k_deterministic_and_pieces_schedule(nv):
+    """Repeated stream-K runs are bit-identical (a shared tile's sum does not
+    depend on which contributor comes second); the pieces schedule, asked for
+    by the plan, meets the same bound on the same shape."""
+    import torch
+    M, K, N = 300, 1040, 33000
+    pw, a, cols, y, S = _sk_case(nv, M, K, N, 5)
+    c = torch.from_numpy(cols).cuda()
+    g = nv.Gemm(M, K, N, nv.OUT_F32)
+    outs = []
+    for _ in range(3):
+        out = torch.full((M, N), float("nan"), device="cuda")
+        g(pw, a, out)
+        torch.cuda.synchronize()
+        outs.append(out)
+    for o in outs[1:]:
+        assert np.array_equal(host(o).view(np.uint32), host(outs[0]).view(np.uint32))
+    check(outs[0][:, c], y, S, bf16=False, what="stream-K")
+    out, _ = run(nv, pw, a, nv.OUT_F32, prefill_schedule=nv.PREFILL_PIECES)
+    check(out[:, c], y, S, bf16=False, what="pieces schedule")
+
+
+def test_prefill_stream_k_fresh_slots_and_shared_workspace(nv):
+    """One plan runs stream-K prefill on one weight matrix, decode, stream-K on
+    another matrix, then the first again: the hand-off slots hold the previous
+    run's sums when a run starts, and every run must read only its own; the
+    counters must come back to zero for the decode kernel too."""
+    import torch
+    M, K, N = 600, 512, 30000
+    cases = [_sk_case(nv, M, K, N, s) for s in (11, 12)]
+    g = nv.Gemm(M, K, N, nv.OUT_F32)
+    first = None
+    for step, (ci, m) in enumerate([(0, M), (0, 8), (1, M), (0, M), (1, 5)]):
+        pw, a, cols, y, S = cases[ci]
+        c = torch.from_numpy(cols).cuda()
+        out = torch.full((m, N), float("nan"), device="cuda")
+        g(pw, a[:m], out, M=m)
+        torch.cuda.synchronize()
+        check(out[:, c], y[:m], S[:m], bf16=False, what="step %d (matrix %d, M = %d)" % (step, ci, m))
+        if m == M and ci == 0:
+            o = host(out)
+            if first is None:
+                first = o
+            else:
+                assert np.array_equal(o.view(np.uint32), first.view(np.uint32))
+
+
 def test_prefill_chunk_config_sampled(nv):
     """The prefill-chunk config: M = 2048, K = 5120, N = 17408, quantised
-    N(0, 0.02) weights, bf16 out; every row, sampled columns (some of them in
-    the last four column blocks, whose tiles are split along K on a
-    256-CU device)."""
+    N(0, 0.02) weights, bf16 out; every row, sampled columns (544 tiles: the
+    stream-K schedule on a 256-CU device, 224 of the tiles shared between two
+    workgroups)."""
     import torch
     M, K, N = 2048, 5120, 17408
     W = synth.weights(0, 300, N, K)
