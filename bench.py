@@ -424,13 +424,20 @@ def main():
         pact = synth.activations_device(0, 9001, PM, PK)
         pout = torch.empty((PM, PN), dtype=torch.bfloat16, device="cuda")
         pg = nv.Gemm(PM, PK, PN, nv.OUT_BF16)
+        # the other schedule, for comparison: whole tiles plus the last
+        # partial round's tiles cut along K and a sum kernel
+        pg_pieces = nv.Gemm(PM, PK, PN, nv.OUT_BF16, prefill_schedule=nv.PREFILL_PIECES)
     p_us = time_events(lambda: pg(ppw, pact, pout, stream=stream), max(3, args.steps // 4)) * 1e3
     p_tflops = 2.0 * PM * PK * PN / (p_us * 1e-6) / 1e12
     log("prefill M=%d K=%d N=%d: %.1f us, %.1f TFLOP/s (%.1f%% of 2.5 PF bf16)"
         % (PM, PK, PN, p_us, p_tflops, 100 * p_tflops / BF16_MFMA_PEAK_TFLOPS))
+    pp_us = time_events(lambda: pg_pieces(ppw, pact, pout, stream=stream),
+                        max(3, args.steps // 4)) * 1e3
+    log("prefill, pieces schedule: %.1f us" % pp_us)
     prefill = {"M": PM, "K": PK, "N": PN, "us": round(p_us, 2), "TFLOP_s": round(p_tflops, 1),
-               "frac_bf16_mfma_peak": round(p_tflops / BF16_MFMA_PEAK_TFLOPS, 4)}
-    del ppw, pact, pout, pg
+               "frac_bf16_mfma_peak": round(p_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+               "schedule": "stream-K (default plan)", "pieces_schedule_us": round(pp_us, 2)}
+    del ppw, pact, pout, pg, pg_pieces
 
     # Achievable: a plain streaming read of the same weight bytes, (a) as one
     # read of the whole arena and (b) as a graph of 256 reads, one per matrix

@@ -18,7 +18,8 @@ short text summaries to profiles/:
                                     bench run with few steps)
   prefill_m2048_mfma_counters.md    the prefill tile kernel's counted MFMA flops,
                                     rate against the bf16 peak, clock and MFMA
-                                    busy fraction (one more counter pass)
+                                    busy fraction, LDS bank conflicts and VALU
+                                    activity (two more counter passes)
 
 Usage (on a machine with the GPU):  python3 bench_profile.py --out DIR
 `--summarize-only` rebuilds the summaries from DIR without profiling.
@@ -51,15 +52,34 @@ PASSES = (
     # MFMA work and busy cycles of the prefill chunk (the same runs time it)
     ("mfma", ["--pmc", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES",
               "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"], 300, BENCH_ARGS),
+    # ... and its LDS and VALU activity
+    ("lds", ["--pmc", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_ACTIVE_INST_LDS",
+             "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_COEXEC_CYCLES",
+             "GRBM_GUI_ACTIVE"], 300, BENCH_ARGS),
 )
 MFMA_COUNTERS = PASSES[4][1][1:]
+LDS_COUNTERS = PASSES[5][1][1:]
 VERIFY = "nvfp4::verify_kernel<"
 TILE = "nvfp4::decode_tile_kernel<"
 TOPK = "nvfp4::topk_"  # level and merge kernels
 CALIB_BYTES = 1 << 30
 DECODE = "nvfp4::decode_"  # decode_kernel< and decode_window_kernel<
-PREFILL = "nvfp4::prefill_kernel<"
+# The prefill chunk's kernels: the default plan's stream-K kernel (timed
+# first), then the pieces schedule's tile kernel and K-piece sum kernel.
+PREFILL_SK = "nvfp4::prefill_sk_kernel<"
+PREFILL_PIECES = "nvfp4::prefill_kernel<"
 PREFILL_SUM = "nvfp4::prefill_reduce_kernel<"
+
+
+def default_prefill(names):
+    """Name prefix of the default plan's prefill kernel among the run's
+    kernel names: the stream-K kernel when the device ran it, else the
+    pieces schedule's tile kernel."""
+    return PREFILL_SK if any(PREFILL_SK in n for n in names) else PREFILL_PIECES
+
+
+def is_prefill(name, which):
+    return which in name
 COPY = "__amd_rocclr_copyBuffer"
 # The achievable leg's one read of the whole weight arena: non-temporal
 # 16-byte loads, the load type of the decode kernel's weight stream.
@@ -122,7 +142,9 @@ def summarize(out, dest):
     round_keys = {(r["Kernel_Name"], r["Grid_Size_X"]) for r in dec[:4]}
     head = [r for r in dec if (r["Kernel_Name"], r["Grid_Size_X"]) not in round_keys]
     dec = [r for r in dec if (r["Kernel_Name"], r["Grid_Size_X"]) in round_keys]
-    pre = [r for r in trace if PREFILL in r["Kernel_Name"]]
+    which = default_prefill([r["Kernel_Name"] for r in trace])
+    pre = [r for r in trace if is_prefill(r["Kernel_Name"], which)]
+    pcs = [r for r in trace if which != PREFILL_PIECES and PREFILL_PIECES in r["Kernel_Name"]]
     dur = lambda r: int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
     dec_avg_us = sum(map(dur, dec)) / len(dec) / 1e3
     pre_avg_us = sum(map(dur, pre)) / len(pre) / 1e3 if pre else float("nan")
@@ -163,9 +185,19 @@ def summarize(out, dest):
               % (algo, roof["achieved"], algo / (dec_avg_us * 1e-6) / 1e9))
     md.append("| M = 8 round (ms) | %.4f | %.4f (sum of kernel durations / replays) |"
               % (line["ms_per_step"], sum(map(dur, dec)) / (len(dec) / per_round) / 1e6))
-    md.append("| prefill chunk (us): tile kernel + K-piece sum kernel | %.2f | %.2f + %.2f "
-              "= %.2f |" % (line["prefill_chunk"]["us"], pre_avg_us, psum_avg_us,
-                            pre_avg_us + psum_avg_us))
+    if which == PREFILL_PIECES:
+        md.append("| prefill chunk (us): tile kernel + K-piece sum kernel | %.2f | %.2f + %.2f "
+                  "= %.2f |" % (line["prefill_chunk"]["us"], pre_avg_us, psum_avg_us,
+                                pre_avg_us + psum_avg_us))
+    else:
+        md.append("| prefill chunk, default plan (us): stream-K kernel | %.2f | %.2f |"
+                  % (line["prefill_chunk"]["us"], pre_avg_us))
+        if pcs:
+            pcs_us = sum(map(dur, pcs)) / len(pcs) / 1e3
+            md.append("| prefill chunk, pieces schedule (us): tile kernel + K-piece sum kernel "
+                      "| %.2f | %.2f + %.2f = %.2f |"
+                      % (line["prefill_chunk"].get("pieces_schedule_us", float("nan")), pcs_us,
+                         psum_avg_us, pcs_us + psum_avg_us))
     if "output_head" in line:
         md.append("| output head, M = 8, K = 5120, N = 152064, fp32 out (us) | %.2f | %.2f |"
                   % (line["output_head"]["us"], head_avg_us))
@@ -278,11 +310,12 @@ def summarize_mfma(out, dest):
         k = int(r["Dispatch_Id"])
         per[k][r["Counter_Name"]] += float(r["Counter_Value"])
         name[k] = r["Kernel_Name"]
-    ids = sorted(k for k in per if PREFILL in name[k])
+    which = default_prefill(name.values())
+    ids = sorted(k for k in per if is_prefill(name[k], which))
     avg = {c: sum(per[k][c] for k in ids) / len(ids) for c in MFMA_COUNTERS}
     trace = list(csv.DictReader(open(find_csv(os.path.join(out, "trace"), "kernel_trace.csv"))))
     durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace
-            if PREFILL in r["Kernel_Name"]]
+            if is_prefill(r["Kernel_Name"], which)]
     us = sum(durs) / len(durs) / 1e3
     M, K, N = bench.PREFILL_SHAPE
     algo = 2.0 * M * K * N
@@ -292,8 +325,8 @@ def summarize_mfma(out, dest):
               "of its own via `python3 bench_profile.py --out OUT`:\n")
     md.append("    " + shown(rocprof_cmd(PASSES[4][1], "OUT/mfma")))
     md.append("    " + shown(rocprof_cmd(PASSES[0][1], "OUT/trace")) + "\n")
-    md.append("Counters per dispatch of the tile kernel (`%s...>`), summed over the "
-              "device, averaged over %d dispatches:\n" % (PREFILL, len(ids)))
+    md.append("Counters per dispatch of the default plan's kernel (`%s...>`), summed over "
+              "the device, averaged over its %d dispatches:\n" % (which, len(ids)))
     md.append("| counter | value |")
     md.append("|---|---|")
     for c in MFMA_COUNTERS:
@@ -323,12 +356,54 @@ def summarize_mfma(out, dest):
               "of 2.5 PFLOP/s assumes %d MHz; the clock counted during this kernel is lower, "
               "so the busy fraction at the running clock exceeds the fraction of peak.\n"
               % int(agent["Max_Engine_Clk_Fcompute"]))
-    md.append("The tile kernel excludes the K-piece sum kernel (`%s...>`), which issues no "
-              "MFMA.\n" % PREFILL_SUM)
+    md.append("The bench also times the pieces schedule (`%s...>` and its K-piece sum "
+              "`%s...>`) on the same data; its dispatches are not in these averages.\n"
+              % (PREFILL_PIECES, PREFILL_SUM))
+    if os.path.isdir(os.path.join(out, "lds")):
+        md += lds_table(out, avg, xcc, simds, int(agent["Cu_Count"]) if "Cu_Count" in agent
+                        else simds // 4)
     with open(os.path.join(dest, "prefill_m2048_mfma_counters.md"), "w") as f:
         f.write("\n".join(md))
     print("prefill: counted MFMA flops %.4g vs algorithmic %.4g; %.1f TFLOP/s over %.2f us"
           % (flops, algo, flops / us / 1e6, us), flush=True)
+
+
+def lds_table(out, mfma_avg, xcc, simds, cus):
+    """LDS and VALU activity of the prefill tile kernel from the "lds" pass,
+    with the derived figures by the expressions rocprofv3 -L gives for them
+    (LDSBankConflict, LdsBankConflict, VALUBusy)."""
+    rows = list(csv.DictReader(open(find_csv(os.path.join(out, "lds"),
+                                             "counter_collection.csv"))))
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    name = {}
+    for r in rows:
+        k = int(r["Dispatch_Id"])
+        per[k][r["Counter_Name"]] += float(r["Counter_Value"])
+        name[k] = r["Kernel_Name"]
+    which = default_prefill(name.values())
+    ids = sorted(k for k in per if is_prefill(name[k], which))
+    avg = {c: sum(per[k][c] for k in ids) / len(ids) for c in LDS_COUNTERS}
+    gui = avg["GRBM_GUI_ACTIVE"] / xcc  # GRBM_GUI_ACTIVE of one XCD (the max over them)
+    md = ["## LDS and VALU activity (a counter pass of its own)\n",
+          "    " + shown(rocprof_cmd(PASSES[5][1], "OUT/lds")) + "\n",
+          "| counter | value |", "|---|---|"]
+    for c in LDS_COUNTERS:
+        md.append("| %s | %.0f |" % (c, avg[c]))
+    bank, idx = avg["SQ_LDS_BANK_CONFLICT"], avg["SQ_LDS_IDX_ACTIVE"]
+    md += ["\n| figure | value |", "|---|---|",
+           "| LDS bank-conflict cycles per conflict-free LDS cycle (LdsBankConflict: "
+           "BANK_CONFLICT / (IDX_ACTIVE - BANK_CONFLICT)) | %.3f |" % (bank / (idx - bank)),
+           "| share of the kernel's time the LDS is stalled by bank conflicts "
+           "(LDSBankConflict: 100 BANK_CONFLICT / GRBM_GUI_ACTIVE / %d CUs, %%) | %.1f |"
+           % (cus, 100.0 * bank / gui / cus),
+           "| VALUBusy (100 ACTIVE_INST_VALU / %d CUs / GRBM_GUI_ACTIVE, %%) | %.1f |"
+           % (cus, 100.0 * avg["SQ_ACTIVE_INST_VALU"] / cus / gui),
+           "| cycles an MFMA and a VALU instruction issued together, per MFMA-busy cycle "
+           "(VALU_MFMA_COEXEC / VALU_MFMA_BUSY of the MFMA pass) | %.3f |"
+           % (avg["SQ_VALU_MFMA_COEXEC_CYCLES"] / mfma_avg["SQ_VALU_MFMA_BUSY_CYCLES"])]
+    md.append("\nThe two passes are separate runs of the same command; each average is "
+              "over the default plan's kernel dispatches in its run.\n")
+    return md
 
 
 def summarize_wide(out, dest):
