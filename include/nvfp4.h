@@ -69,19 +69,26 @@ enum nvfp4_out_dtype { NVFP4_OUT_F32 = 0, NVFP4_OUT_BF16 = 1 };
 /* Prefill schedules (nvfp4_gemm_config.prefill_schedule) for M > 64, whose
  * 256 x 256 output tiles are spread over the compute units: */
 enum nvfp4_prefill_schedule {
-    NVFP4_PREFILL_AUTO = 0,     /* stream-K when the tiles outnumber the compute
-                                   units and are not a multiple of them, else pieces */
+    NVFP4_PREFILL_AUTO = 0,     /* stream-K where it applies (see nvfp4_gemm_run),
+                                   else pieces */
     NVFP4_PREFILL_PIECES = 1,   /* whole tiles; the tiles of a last partial round cut
                                    along K into pieces, added by a second kernel */
     NVFP4_PREFILL_STREAM_K = 2  /* (where it applies) every compute unit takes an
                                    equal run of the tiles' K stages laid end to end; a
-                                   tile shared by two units is finished by the later */
+                                   tile shared by two or three units is finished by the
+                                   last */
 };
 
 /* Largest k of nvfp4_topk. */
 #define NVFP4_TOPK_MAX_K 64
 
 /* ---- status ----------------------------------------------------------------- */
+
+/* Errors stay with the call that raised them: the credits of the pages' engine
+ * ("Lineage", "Credits") list a per-request error boundary among its kernel
+ * work, and here each entry point reports its own failure through its return
+ * value and this thread's last-error text, launching nothing on a refused call
+ * and leaving other plans, rounds and threads untouched. */
 
 /* Static text of a status code. */
 const char* nvfp4_status_string(int status);
@@ -189,13 +196,15 @@ void nvfp4_gemm_destroy(nvfp4_gemm plan);
  * (K, N) must equal the plan's, 1 <= M <= max_M.  M <= 8 uses the decode
  * kernel and 8 < M <= 64 the verify-width decode kernel (each one pass over
  * the weights for all M rows); larger M uses the bf16 MFMA prefill kernel.
- * When its 256 x 256 output tiles outnumber the device's compute units and
- * are not a multiple of them, it runs the stream-K schedule (one workgroup
- * per compute unit, equal runs of K stages; the two fp32 partial sums of a
- * shared tile meet in the workspace and the later contributor adds them);
- * with fewer tiles than compute units, a last partial round's tiles are cut
- * along K and a second kernel adds their pieces (NVFP4_PREFILL_PIECES asks
- * for that schedule in every case).  The workspace holds, in this order, the
+ * When its 256 x 256 output tiles are not a multiple of the device's compute
+ * units, it runs the stream-K schedule (one workgroup per compute unit,
+ * equal runs of K stages; the fp32 partial sums of a tile shared by two or
+ * three runs meet in the workspace and the last contributor adds them in run
+ * order), provided each run holds at least half a tile and, below one tile
+ * per unit, at most 3/4 of the units would hold a tile.  Otherwise whole
+ * tiles, and a last partial round's tiles cut along K with a second kernel
+ * adding their pieces (NVFP4_PREFILL_PIECES asks for that schedule in every
+ * case).  The workspace holds, in this order, the
  * decode, verify and prefill areas the plan's max_M needs.  For M > 8 and K not a
  * multiple of 512, every activation value must be finite: those kernels read
  * the tail of a row's last K window from the start of the next row and
@@ -241,9 +250,9 @@ int nvfp4_gemm_run_argmax(nvfp4_gemm plan, int M, int K, int N, const uint8_t* c
  * device array per GPU (held until the process ends) instead of a caller
  * workspace.  Arguments as nvfp4_gemm_run, without the workspace.  A run that
  * needs more than 16 MiB of that state (a large prefill chunk; every
- * stream-K prefill run, whose hand-off slots take 512 KiB per pair of
- * neighbouring compute units: a plan made with NVFP4_PREFILL_PIECES needs
- * none where its tiles fill whole rounds) returns NVFP4_EUNSUPPORTED and
+ * stream-K prefill run, whose hand-off slots take 512 KiB per compute unit:
+ * a plan made with NVFP4_PREFILL_PIECES needs none where its tiles fill whole
+ * rounds) returns NVFP4_EUNSUPPORTED and
  * launches nothing.  The first call on a device
  * zero-fills the array with one kernel on `stream`, so it must be made
  * outside stream capture (under capture it returns NVFP4_ESTATE and launches

@@ -277,12 +277,12 @@ __device__ __forceinline__ void prefill_accumulate(
     // absolute stage of relative stage u, clamped to the last one
     auto at = [&](int u) { return kt0 + min(u, nks - 1); };
 
+    // (whole zero vectors: element-wise zeroing would read the previous
+    // values, keeping a previous tile's accumulators alive into this one)
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < TJ; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+        for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16{};
 
     // Activations run two stages ahead in three LDS buffers (relative stage
     // u in buffer u % 3); weights run two stages ahead in registers (st0 /
@@ -448,107 +448,143 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(
 
 // ---- stream-K schedule ----------------------------------------------------------
 //
-// With more tiles than compute units, and not a multiple of them, the tiles'
-// K stages are laid end to end (tile after tile, W = tiles * nk in all) and
-// workgroup r of C (one per compute unit) takes the stages r W / C ..
+// The tiles' K stages are laid end to end (tile after tile, W = tiles * nk in
+// all) and workgroup r of C (one per compute unit) takes the stages r W / C ..
 // (r + 1) W / C - 1: every unit gets the same number of stages, with no last
-// partial round.  A run holds at least one tile's nk stages, so a tile is
-// shared by at most two workgroups: r, whose run ends inside it (its head,
-// stages 0 .. h - 1), and r + 1 (its tail, h .. nk - 1), which meet at
-// boundary r.  A workgroup runs its head first, then its tail, then its
-// whole tiles, so the hand-offs of shared tiles happen early and spread over
-// the run while other workgroups compute.
+// partial round.  The host takes this schedule when every run holds at least
+// half a tile's stages (and one), so a tile is shared by at most three
+// consecutive runs.  A run's parts are the last tile it touches if it only
+// starts there (its head), the first tile if it does not take all of it (its
+// tail), then its whole tiles, in that order, so the hand-offs of shared tiles
+// happen early and spread over the run while other workgroups compute.
 
 // Cache policy of the hand-off's stores and loads between XCDs: device scope
 // (sc1), so that they bypass the XCDs' non-coherent cached copies.
 constexpr int kPDeviceScope = 16;
 constexpr int kPWaveFloats = 32 * 32 * PTiles<256, 256, kPWaves>::TI * PTiles<256, 256, kPWaves>::TJ;
+constexpr int kPMaxShare = 3;  // runs sharing one tile, at most
 
-// Hand-off of a shared tile, wave by wave (wave w of both contributors owns
-// the same outputs): the wave stores its accumulators to its slot (role 0:
-// head, 1: tail) and, once the stores have completed, increments its counter
-// at boundary bi.  With both contributors on one XCD (LOCAL) the slots and
-// the counter live in that XCD's L2: plain stores and loads, an agent-scope
-// atomic.  Otherwise the stores and loads are device-scope and the counter
-// system-scope (coherent across XCDs).  The wave that finds the other's increment already there adds the
-// other's slot to its accumulators, stores the outputs and zeroes the
-// counter again.  The sum is own + other: the same float whichever wave
-// comes second (addition commutes), so the outputs do not depend on the
-// order of arrival.  Slots: float4 ((i TJ + j) 4 + r / 4) 64 + lane of
-// slot (2 bi + role) NW + w holds elements r .. r + 3 of lane's MFMA tile.
+// Scalar byte offset of float4 group g (64 lanes) of a slot.
+__device__ __forceinline__ int sk_soff(int g) { return 1024 * g; }
+
+// The run holding stage s: the largest q with W q / C <= s.
+__device__ __forceinline__ int sk_run_of(long long s, long long W, int C) {
+    return (int)(((s + 1) * C - 1) / W);
+}
+
+// Slot of run q's part in tile t: 2 q for the tile holding the run's first
+// stage, 2 q + 1 for its last tile.
+__device__ __forceinline__ int sk_slot(int q, int t, long long W, int C, int nk) {
+    return 2 * q + (t == (int)(W * q / C / nk) ? 0 : 1);
+}
+
+// Hand-off of a shared tile, wave by wave (wave w of every contributor owns
+// the same outputs): the wave stores its accumulators to its slot and, once
+// the stores have completed, increments the tile's counter.  The wave that
+// finds the other n - 1 increments already there adds the n slots in run
+// order, so the sum is the same float whichever contributor comes last,
+// zeroes the counter again and stores the outputs.  (The outputs are stored
+// here rather than by the caller: a store after the hand-off, reached from
+// both outcomes, would keep the accumulators alive through the loads.)  With every contributor on one XCD
+// (LOCAL) the slots and the counter live in that XCD's L2: plain stores and
+// loads, an agent-scope atomic.  Otherwise the stores and loads are
+// device-scope and the counter system-scope (coherent across XCDs).  Slots:
+// float4 ((i TJ + j) 4 + r / 4) 64 + lane of slot s, wave w (at (s NW + w)
+// kPWaveFloats floats) holds elements r .. r + 3 of lane's MFMA tile (i, j).
 template <int BM, int BN, int NW, bool BF16, bool LOCAL>
 __device__ __forceinline__ void prefill_handoff(f32x16 (&acc)[ptiles_i(BM, NW)][ptiles_j(BN)],
                                                 float* __restrict__ slots,
-                                                unsigned int* __restrict__ counters, int bi,
-                                                int role, void* __restrict__ out, float ts, int M,
-                                                int N, int m0, int n0) {
+                                                unsigned int* __restrict__ counters, int ctr,
+                                                int mine, int n, const int (&slot)[kPMaxShare],
+                                                void* __restrict__ out, float ts, int M, int N,
+                                                int m0, int n0) {
     constexpr int TI = PTiles<BM, BN, NW>::TI, TJ = PTiles<BM, BN, NW>::TJ;
     constexpr int kF = 32 * 32 * TI * TJ;  // floats per wave
     constexpr int kAux = LOCAL ? 0 : kPDeviceScope;
-    // (the wave index through a scalar register: the slot addresses are
-    // uniform, so the buffer resources stay scalar)
     // (the thread index opaque, as in prefill_store_tile)
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    float* mine = slots + ((size_t)(2 * bi + role) * NW + wave) * kF;
-    const float* other = slots + ((size_t)(2 * bi + (role ^ 1)) * NW + wave) * kF;
-    const __amdgpu_buffer_rsrc_t rm = prefill_rsrc(mine, (size_t)kF * 4);
-    const __amdgpu_buffer_rsrc_t ro = prefill_rsrc(other, (size_t)kF * 4);
+    auto rsrc_of = [&](int s) {
+        return prefill_rsrc(slots + ((size_t)s * NW + wave) * kF, (size_t)kF * 4);
+    };
+    const __amdgpu_buffer_rsrc_t rm = rsrc_of(mine);
+    // float4 v of a slot at byte 16 lane + sk_soff(v / 64): the lane's part
+    // in a vector register, the rest in the instruction's scalar offset (so
+    // no per-float4 address registers are held)
+    const int voff = 16 * lane;
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
 #pragma unroll
             for (int rq = 0; rq < 4; ++rq) {
-                const int v = ((i * TJ + j) * 4 + rq) * 64 + lane;
                 const u32x4 x = {__float_as_uint(acc[i][j][4 * rq]),
                                  __float_as_uint(acc[i][j][4 * rq + 1]),
                                  __float_as_uint(acc[i][j][4 * rq + 2]),
                                  __float_as_uint(acc[i][j][4 * rq + 3])};
-                __builtin_amdgcn_raw_buffer_store_b128(x, rm, 16 * v, 0, kAux);
+                __builtin_amdgcn_raw_buffer_store_b128(x, rm, voff, sk_soff((i * TJ + j) * 4 + rq),
+                                                       kAux);
             }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    unsigned int* ctr = counters + (size_t)bi * NW + wave;
+    unsigned int* c = counters + (size_t)ctr * NW + wave;
     unsigned int old = 0;
     if (lane == 0)
-        old = LOCAL ? __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                    : __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        old = LOCAL ? __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                    : __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     old = __builtin_amdgcn_readlane(old, 0);
     asm volatile("" ::: "memory");
-    if (old == 0) return;  // the other wave comes second and finishes
-    // The other's slot in batches of kBatch MFMA tiles (their loads in flight
-    // together), within the registers the accumulators leave.
+    if (old != (unsigned int)(n - 1)) return;  // a later contributor finishes
+    // All n slots in run order, this wave's own included (stored and waited
+    // for above: the same values as its registers), so no term depends on
+    // which contributor is adding; the sums go straight to the outputs, in
+    // batches of kBatch MFMA tiles whose loads are in flight together.
+    const __amdgpu_buffer_rsrc_t r0 = rsrc_of(slot[0]), r1 = rsrc_of(slot[1]);
+    const __amdgpu_buffer_rsrc_t r2 = rsrc_of(slot[n == 3 ? 2 : 1]);
+    constexpr int WM = PTiles<BM, BN, NW>::WM;
+    const int wm = wave >> 2, wn = wave & 3, r32 = lane & 31, half = lane >> 5;
     constexpr int kBatch = 2;
+    int vo = voff;
 #pragma unroll
     for (int b0 = 0; b0 < TI * TJ; b0 += kBatch) {
-        u32x4 x[kBatch * 4];
-#pragma unroll
-        for (int q = 0; q < kBatch * 4; ++q)
-            x[q] = __builtin_amdgcn_raw_buffer_load_b128(ro, 16 * ((b0 * 4 + q) * 64 + lane), 0,
-                                                         kAux);
+        u32x4 x0[kBatch * 4], x1[kBatch * 4], x2[kBatch * 4];
 #pragma unroll
         for (int q = 0; q < kBatch * 4; ++q) {
-            const int i = (b0 + q / 4) / TJ, j = (b0 + q / 4) % TJ, rq = q % 4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][j][4 * rq + e] += __uint_as_float(x[q][e]);
+            const int so = sk_soff(b0 * 4 + q);
+            x0[q] = __builtin_amdgcn_raw_buffer_load_b128(r0, vo, so, kAux);
+            x1[q] = __builtin_amdgcn_raw_buffer_load_b128(r1, vo, so, kAux);
+            if (n == 3) x2[q] = __builtin_amdgcn_raw_buffer_load_b128(r2, vo, so, kAux);
         }
-        asm volatile("" ::: "memory");
+        float last = 0.f;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int i = (b0 + u) / TJ, j = (b0 + u) % TJ;
+            const int nn = n0 + wn * (BN / 4) + 32 * j + r32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int q = 4 * u + r / 4, e = r % 4;
+                float sum = __uint_as_float(x0[q][e]) + __uint_as_float(x1[q][e]);
+                if (n == 3) sum += __uint_as_float(x2[q][e]);
+                const int m = m0 + wm * (BM / WM) + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+                if (m < M && nn < N) store_out<BF16>(out, (size_t)m * N + nn, sum * ts);
+                last = sum;
+            }
+        }
+        // the next batch's offset depends on this batch's sums, so its loads
+        // are not issued (and held in registers) before these are done
+        asm volatile("" : "+v"(vo) : "v"(last));
     }
     if (lane == 0) {
         if (LOCAL)
-            __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         else
-            __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
-    prefill_store_tile<BM, BN, NW, BF16>(acc, out, ts, M, N, m0, n0);
 }
 
 // Stream tile t covers rows (t / nblocks) * 256 and outputs (t % nblocks) *
-// 256.  Run r's parts in order: the head of tile hi / nk (if the run ends
-// inside a tile), the tail of tile lo / nk (if it starts inside one), then
-// the whole tiles between.  Slots: 2 NW kPWaveFloats floats per boundary;
-// counters: NW per boundary, zero between runs.
+// 256.  Run r covers stages lo .. hi - 1: tiles ta = lo / nk .. tb = (hi - 1)
+// / nk, of which ta from stage ka = lo - ta nk and tb up to kb = hi - tb nk.
 template <bool BF16>
 __global__ __launch_bounds__(kPThreads) void prefill_sk_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
@@ -563,20 +599,23 @@ __global__ __launch_bounds__(kPThreads) void prefill_sk_kernel(
     // one XCD (b % 8) take consecutive runs, and the stream holds the tiles
     // row block by row block, so an XCD works on the same rows of
     // activations (kept in its L2) across its column blocks.
-    const int r = C % 8 ? (int)blockIdx.x : (int)(blockIdx.x % 8) * (C / 8) + (int)blockIdx.x / 8;
     // (l2_local: workgroup b verified to run on XCD b % 8, and C % 8 == 0)
+    const int r = C % 8 ? (int)blockIdx.x : (int)(blockIdx.x % 8) * (C / 8) + (int)blockIdx.x / 8;
     const long long lo = W * r / C, hi = W * (r + 1) / C;
-    const int h = (int)(hi % nk), a = (int)(lo % nk);
-    const int t_head = (int)(hi / nk), t_tail = (int)(lo / nk);
-    const int t_first = (int)((lo + nk - 1) / nk);  // first whole tile
-    const int nh = h > 0, na = a > 0;  // a head part, a tail part
-    const int n_parts = nh + na + (t_head - t_first);
+    const int ta = (int)(lo / nk), tb = (int)((hi - 1) / nk);
+    const int ka = (int)(lo - (long long)ta * nk), kb = (int)(hi - (long long)tb * nk);
+    const int sh_b = ta != tb && kb != nk;              // a head in tile tb
+    const int sh_a = ka != 0 || (ta == tb && kb != nk);  // a shared part in tile ta
+    const int tw0 = ta + sh_a, n_whole = tb - sh_b - tw0 + 1;
+    const int n_parts = sh_b + sh_a + (n_whole > 0 ? n_whole : 0);
     f32x16 acc[PTiles<kPTile, kPTile, kPWaves>::TI][PTiles<kPTile, kPTile, kPWaves>::TJ];
     for (int q = 0; q < n_parts; ++q) {
-        // part q is of kind 0 (head), 1 (tail) or 2 (whole tile q - nh - na)
-        const int kind = q < nh ? 0 : q < nh + na ? 1 : 2;
-        const int t = kind == 0 ? t_head : kind == 1 ? t_tail : t_first + (q - nh - na);
-        const int kt0 = kind == 1 ? a : 0, kt1 = kind == 0 ? h : nk;
+        // part q is of kind 0 (head of tb), 1 (the part of ta) or 2 (whole
+        // tile tw0 + q - sh_b - sh_a)
+        const int kind = q < sh_b ? 0 : q < sh_b + sh_a ? 1 : 2;
+        const int t = kind == 0 ? tb : kind == 1 ? ta : tw0 + (q - sh_b - sh_a);
+        const int kt0 = kind == 1 ? ka : 0;
+        const int kt1 = kind == 0 || (kind == 1 && ta == tb) ? kb : nk;
         const int m0 = (t / nblocks) * kPTile, n0 = (t % nblocks) * kPTile;
         int tid = threadIdx.x;
         asm volatile("" : "+v"(tid));
@@ -590,15 +629,26 @@ __global__ __launch_bounds__(kPThreads) void prefill_sk_kernel(
         if (kind == 2) {
             prefill_store_tile<kPTile, kPTile, kPWaves, BF16>(acc, out, ts, M, N, m0, n0);
         } else {
-            // boundary bi between runs bi and bi + 1: on one XCD (its L2)
-            // unless bi + 1 starts the next XCD's segment
-            const int bi = kind == 0 ? r : r - 1;
-            if (l2_local && (bi + 1) % (C / 8) != 0)
-                prefill_handoff<kPTile, kPTile, kPWaves, BF16, true>(acc, slots, counters, bi,
-                                                                     kind, out, ts, M, N, m0, n0);
+            // the runs rf .. rf + n - 1 share tile t; its counter belongs to
+            // run rf's slot there
+            // (uniform values through scalar registers: the slot addresses
+            // make buffer resources, which must be scalar)
+            const int rf = __builtin_amdgcn_readfirstlane(sk_run_of((long long)t * nk, W, C));
+            const int n = __builtin_amdgcn_readfirstlane(
+                sk_run_of((long long)(t + 1) * nk - 1, W, C) - rf + 1);
+            int slot[kPMaxShare];
+#pragma unroll
+            for (int i = 0; i < kPMaxShare; ++i)
+                slot[i] = __builtin_amdgcn_readfirstlane(i < n ? sk_slot(rf + i, t, W, C, nk)
+                                                               : sk_slot(rf, t, W, C, nk));
+            const int mine = __builtin_amdgcn_readfirstlane(sk_slot(r, t, W, C, nk));
+            const bool local = l2_local && rf / (C / 8) == (rf + n - 1) / (C / 8);
+            if (local)
+                prefill_handoff<kPTile, kPTile, kPWaves, BF16, true>(
+                    acc, slots, counters, slot[0], mine, n, slot, out, ts, M, N, m0, n0);
             else
                 prefill_handoff<kPTile, kPTile, kPWaves, BF16, false>(
-                    acc, slots, counters, bi, kind, out, ts, M, N, m0, n0);
+                    acc, slots, counters, slot[0], mine, n, slot, out, ts, M, N, m0, n0);
         }
     }
 }
@@ -650,11 +700,11 @@ __global__ __launch_bounds__(kPReduceThreads) void prefill_reduce_kernel(
         if (m + r < M) store_out<BF16>(out, (size_t)(m + r) * N + n, e[r] * ts);
 }
 
-// How a run of M rows is laid out over the compute units.  With more tiles
-// than units, and not a multiple of them, the stream-K schedule (unless the
-// plan asks for pieces); otherwise the tiles beyond whole rounds (one tile
-// per compute unit at a time) are split along K when at least two pieces
-// each fit: n_tail tiles, S pieces each.
+// How a run of M rows is laid out over the compute units.  With tiles not a
+// multiple of the units, the stream-K schedule when each unit's run holds at
+// least half a tile's stages (unless the plan asks for pieces); otherwise the
+// tiles beyond whole rounds (one tile per compute unit at a time) are split
+// along K when at least two pieces each fit: n_tail tiles, S pieces each.
 struct PrefillSplit {
     int tiles, n_tail, splits;
     bool stream;
@@ -665,7 +715,14 @@ static PrefillSplit prefill_split(int M, int K, int N, int cus, int schedule) {
     const int nk = (K + kPBK - 1) / kPBK;
     PrefillSplit s{mblocks * nblocks, 0, 1, false};
     const int left = s.tiles % cus;
-    if (schedule != NVFP4_PREFILL_PIECES && s.tiles > cus && left) {
+    // stream-K when every run holds at least half a tile's stages (and one):
+    // then at most three runs share a tile.  Below one tile per unit only
+    // when at most 3/4 of the units would have a tile: with more, its hand-offs
+    // and part boundaries cost more than the idle units (measured at 224 of
+    // 256: 11% slower; at 160 of 256: 8-17% faster).
+    const long long per_run = (long long)s.tiles * nk / cus;
+    const bool fills = s.tiles > cus || 4 * s.tiles <= 3 * cus;
+    if (schedule != NVFP4_PREFILL_PIECES && left && fills && per_run >= max(1, (nk + 1) / 2)) {
         s.stream = true;
         return s;
     }
@@ -677,13 +734,13 @@ static PrefillSplit prefill_split(int M, int K, int N, int cus, int schedule) {
     return s;
 }
 
-// Workspace of a run: [counters][partial sums] (stream-K: a counter per wave
-// and two slots per boundary between workgroups; pieces: no counters, the
-// pieces' partial sums).
+// Workspace of a run: [counters][partial sums] (stream-K: two slots per run,
+// and a counter per slot and wave; pieces: no counters, the pieces' partial
+// sums).
 static void prefill_need(const PrefillSplit& s, int cus, size_t* counters, size_t* partials) {
     if (s.stream) {
-        *counters = ((size_t)(cus - 1) * kPWaves * sizeof(unsigned int) + 255) & ~(size_t)255;
-        *partials = (size_t)(cus - 1) * 2 * kPWaves * kPWaveFloats * sizeof(float);
+        *counters = ((size_t)2 * cus * kPWaves * sizeof(unsigned int) + 255) & ~(size_t)255;
+        *partials = (size_t)2 * cus * kPWaves * kPWaveFloats * sizeof(float);
     } else {
         *counters = 0;
         *partials = (size_t)s.n_tail * s.splits * kPTileFloats * sizeof(float);
@@ -730,7 +787,7 @@ int launch_prefill(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const 
     const bool bf16 = p->out_dtype == NVFP4_OUT_BF16;
     if (sp.stream) {
         // one workgroup per compute unit (the plan's count, which sized the
-        // workspace); the kernel needs more tiles than workgroups
+        // workspace and chose the schedule)
         float* slots = (float*)((char*)ws + pre_off);
         unsigned int* counters = (unsigned int*)((char*)ws + ctr_off);
         const dim3 grid((unsigned)p->pre.cus);

@@ -196,8 +196,8 @@ def test_prefill_schedule_config_and_workspace(nv):
     """prefill_schedule outside 0..2 is refused.  With the device's compute
     units taken as 256 when no GPU answers (the plan's own count otherwise),
     a prefill chunk of 544 tiles gets the stream-K area: counters, then two
-    slots of 256 x 256 fp32 sums per pair of neighbouring workgroups; the
-    pieces schedule instead holds its last round's K pieces."""
+    slots of 256 x 256 fp32 sums per workgroup's run; the pieces schedule
+    instead holds its last round's K pieces (32 tiles x 8 pieces)."""
     for bad in (-1, 3):
         with pytest.raises(nv.Nvfp4Error) as e:
             nv.nvfp4_gemm_create(2048, 5120, 17408, 1, prefill_schedule=bad)
@@ -209,8 +209,8 @@ def test_prefill_schedule_config_and_workspace(nv):
         assert ws == wss
         if not _gpu_visible():
             cus = 256
-            slots = (cus - 1) * 2 * 256 * 256 * 4
-            counters = ((cus - 1) * 8 * 4 + 255) // 256 * 256
+            slots = 2 * cus * 256 * 256 * 4          # two 256 x 256 fp32 slots per run
+            counters = (2 * cus * 8 * 4 + 255) // 256 * 256  # per slot and wave
             assert ws - wsp == slots + counters - 32 * 8 * 256 * 256 * 4
     finally:
         for h in (p, pp, ps):

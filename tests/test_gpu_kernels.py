@@ -534,12 +534,16 @@ def test_prefill_and_decode_share_a_workspace(nv):
 
 # ---- prefill, stream-K schedule (more tiles than compute units) ----------------
 
-def _stream_k_shape(nv, M, N):
-    """True when the device runs (M, N) with the stream-K schedule."""
+def _stream_k_shape(nv, M, K, N):
+    """True when the device runs (M, K, N) with the stream-K schedule: tiles
+    not a multiple of the compute units, and every unit's run at least half
+    a tile's K stages (and one)."""
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     tiles = ((M + 255) // 256) * ((N + 255) // 256)
-    return tiles > cus and tiles % cus != 0
+    nk = (K + 63) // 64
+    fills = tiles > cus or 4 * tiles <= 3 * cus
+    return tiles % cus != 0 and fills and tiles * nk // cus >= max(1, (nk + 1) // 2)
 
 
 def _quarter_cols(N, seed):
@@ -562,19 +566,55 @@ def _sk_case(nv, M, K, N, seed):
 
 
 # Ragged M, N and K (K = 1040: a partial last stage; K = 16: one stage, so no
-# tile is shared); 258 to 354 tiles on 256 compute units.
-SK_SHAPES = [(300, 1040, 33000), (100, 2048, 66000), (600, 512, 30000), (300, 16, 40000)]
+# tile is shared); 258 to 354 tiles on 256 compute units, and fewer tiles than
+# units (136 and 188: runs shorter than a tile, up to three sharing one).
+SK_SHAPES = [(300, 1040, 33000), (100, 2048, 66000), (600, 512, 30000), (300, 16, 40000),
+             (512, 1040, 17408), (300, 2048, 24000)]
 
 
 @pytest.mark.parametrize("M,K,N", SK_SHAPES)
 @pytest.mark.parametrize("bf16", [False, True])
 def test_prefill_stream_k_sampled(nv, M, K, N, bf16):
     import torch
-    assert _stream_k_shape(nv, M, N)
+    assert _stream_k_shape(nv, M, K, N)
     pw, a, cols, y, S = _sk_case(nv, M, K, N, M + K + N)
     out, _ = run(nv, pw, a, nv.OUT_BF16 if bf16 else nv.OUT_F32)  # (canaries checked)
     check(out[:, torch.from_numpy(cols).cuda()], y, S, bf16=bf16,
           what="stream-K prefill %r" % ((M, K, N),))
+
+
+def _half_block_rows(M, seed):
+    """Two random rows of every 256-row block, one in each half (a wave owns
+    one half of a tile's rows), plus the first and last rows."""
+    rng = np.random.default_rng(seed)
+    rows = {0, M - 1}
+    for b in range(0, M, 256):
+        for h in (0, 128):
+            lo = b + h
+            if lo < M:
+                rows.add(lo + int(rng.integers(0, min(128, M - lo))))
+    return np.array(sorted(rows))
+
+
+# The round's other matrices at the chunk size, fewer tiles than compute units:
+# o and down (160 tiles) run stream-K, runs of 60 and 170 stages sharing tiles
+# two and three ways; qkv (224 tiles) runs its tiles whole, one per unit.
+@pytest.mark.parametrize("name,K,N,sk", [("qkv", 5120, 7168, False), ("o", 6144, 5120, True),
+                                         ("down", 17408, 5120, True)])
+def test_prefill_round_shapes_at_chunk_size(nv, name, K, N, sk):
+    import torch
+    M = 2048
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert _stream_k_shape(nv, M, K, N) == sk
+    codes, scales = synth.random_planes(K + 1, N + 2, N, K)
+    t = 2.5e-3
+    act = synth.activations(K + 3, N + 4, M, K)
+    pw = pack(nv, dev(codes), dev(scales), K, N, t)
+    out, _ = run(nv, pw, dev_bf16(act), nv.OUT_BF16)
+    rows, cols = _half_block_rows(M, K), _quarter_cols(N, N)
+    y, S = oracle.gemm(act[rows], codes[cols], scales[cols], t)
+    sub = out[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()]
+    check(sub, y, S, bf16=True, what="%s at M = 2048" % name)
 
 
 def test_prefill_stream_k_deterministic_and_pieces_schedule(nv):
