@@ -95,6 +95,19 @@ def round_bytes(M, layers=LAYERS):
     return sum(gemm_bytes(M, K, N) for _, K, N in ROUND_SHAPES) * layers
 
 
+def prefill_default_schedule(M, K, N):
+    """The schedule a default plan runs a prefill of M rows with on this
+    device: "stream-K" below one 256 x 256 tile per compute unit when at most
+    3/4 of the units hold a tile (and every run is at least half a tile),
+    else "pieces" (whole tiles, a last partial round cut along K)."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles = ((M + 255) // 256) * ((N + 255) // 256)
+    nk = (K + 63) // 64
+    applies = tiles % cus != 0 and tiles * nk // cus >= max(1, (nk + 1) // 2)
+    return "stream-K" if applies and tiles < cus and 4 * tiles <= 3 * cus else "pieces"
+
+
 def build_round(nv, seed=0, layers=LAYERS, max_M=8, log=None, shapes=ROUND_SHAPES):
     """Generate, quantise and pack every matrix of the round on the GPU (all
     packed planes in one arena, in round order).  Returns (round spec list,
@@ -424,20 +437,52 @@ def main():
         pact = synth.activations_device(0, 9001, PM, PK)
         pout = torch.empty((PM, PN), dtype=torch.bfloat16, device="cuda")
         pg = nv.Gemm(PM, PK, PN, nv.OUT_BF16)
-        # the other schedule, for comparison: whole tiles plus the last
-        # partial round's tiles cut along K and a sum kernel
+        # both schedules named, on the same data: whole tiles plus K pieces
+        # of a last partial round, and stream-K
         pg_pieces = nv.Gemm(PM, PK, PN, nv.OUT_BF16, prefill_schedule=nv.PREFILL_PIECES)
-    p_us = time_events(lambda: pg(ppw, pact, pout, stream=stream), max(3, args.steps // 4)) * 1e3
+        pg_sk = nv.Gemm(PM, PK, PN, nv.OUT_BF16, prefill_schedule=nv.PREFILL_STREAM_K)
+    reps = max(3, args.steps // 4)
+    p_us = time_events(lambda: pg(ppw, pact, pout, stream=stream), reps) * 1e3
     p_tflops = 2.0 * PM * PK * PN / (p_us * 1e-6) / 1e12
     log("prefill M=%d K=%d N=%d: %.1f us, %.1f TFLOP/s (%.1f%% of 2.5 PF bf16)"
         % (PM, PK, PN, p_us, p_tflops, 100 * p_tflops / BF16_MFMA_PEAK_TFLOPS))
-    pp_us = time_events(lambda: pg_pieces(ppw, pact, pout, stream=stream),
-                        max(3, args.steps // 4)) * 1e3
-    log("prefill, pieces schedule: %.1f us" % pp_us)
+    pp_us = time_events(lambda: pg_pieces(ppw, pact, pout, stream=stream), reps) * 1e3
+    ps_us = time_events(lambda: pg_sk(ppw, pact, pout, stream=stream), reps) * 1e3
+    log("prefill schedules: pieces %.1f us, stream-K %.1f us" % (pp_us, ps_us))
     prefill = {"M": PM, "K": PK, "N": PN, "us": round(p_us, 2), "TFLOP_s": round(p_tflops, 1),
                "frac_bf16_mfma_peak": round(p_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-               "schedule": "stream-K (default plan)", "pieces_schedule_us": round(pp_us, 2)}
-    del ppw, pact, pout, pg, pg_pieces
+               "default_schedule": prefill_default_schedule(PM, PK, PN),
+               "pieces_us": round(pp_us, 2), "stream_k_us": round(ps_us, 2)}
+    del ppw, pg, pg_pieces, pg_sk
+
+    # The round's four matrices at the chunk size (M = 2048, bf16 out): the
+    # default plan, and the pieces schedule beside it on the same data.
+    prefill_round = {}
+    for name, RK, RN in ROUND_SHAPES:
+        with torch.cuda.stream(stream):
+            wr = synth.weights_device(0, 9100 + RK + RN, RN, RK)
+            rpw = nv.PackedWeight.quantize(wr, stream=stream)
+            del wr
+            ract = pact[:, :RK] if RK <= PK else synth.activations_device(0, 9101, PM, RK)
+            ract = ract.contiguous()
+            rout = torch.empty((PM, RN), dtype=torch.bfloat16, device="cuda")
+            rg = nv.Gemm(PM, RK, RN, nv.OUT_BF16)
+            rgp = nv.Gemm(PM, RK, RN, nv.OUT_BF16, prefill_schedule=nv.PREFILL_PIECES)
+            rgs = nv.Gemm(PM, RK, RN, nv.OUT_BF16, prefill_schedule=nv.PREFILL_STREAM_K)
+        r_us = time_events(lambda: rg(rpw, ract, rout, stream=stream), reps) * 1e3
+        rp_us = time_events(lambda: rgp(rpw, ract, rout, stream=stream), reps) * 1e3
+        rs_us = time_events(lambda: rgs(rpw, ract, rout, stream=stream), reps) * 1e3
+        fl = 2.0 * PM * RK * RN
+        prefill_round[name] = {"K": RK, "N": RN, "us": round(r_us, 2),
+                               "frac_bf16_mfma_peak": round(fl / (r_us * 1e-6) / 1e12
+                                                            / BF16_MFMA_PEAK_TFLOPS, 4),
+                               "default_schedule": prefill_default_schedule(PM, RK, RN),
+                               "pieces_us": round(rp_us, 2), "stream_k_us": round(rs_us, 2)}
+        log("prefill M=%d %s (K=%d N=%d): %.1f us (pieces %.1f, stream-K %.1f)"
+            % (PM, name, RK, RN, r_us, rp_us, rs_us))
+        del rpw, ract, rout, rg, rgp, rgs
+    prefill["round_shapes"] = prefill_round
+    del pact, pout
 
     # Achievable: a plain streaming read of the same weight bytes, (a) as one
     # read of the whole arena and (b) as a graph of 256 reads, one per matrix

@@ -64,22 +64,36 @@ TILE = "nvfp4::decode_tile_kernel<"
 TOPK = "nvfp4::topk_"  # level and merge kernels
 CALIB_BYTES = 1 << 30
 DECODE = "nvfp4::decode_"  # decode_kernel< and decode_window_kernel<
-# The prefill chunk's kernels: the default plan's stream-K kernel (timed
-# first), then the pieces schedule's tile kernel and K-piece sum kernel.
+# The prefill chunk's kernels, in bench.py's order: the default plan (on a
+# 256-CU device whole tiles plus K pieces: tile kernel + K-piece sum kernel),
+# the pieces schedule again by name, the stream-K schedule; then the round's
+# four shapes at the chunk size, each under all three.
 PREFILL_SK = "nvfp4::prefill_sk_kernel<"
 PREFILL_PIECES = "nvfp4::prefill_kernel<"
 PREFILL_SUM = "nvfp4::prefill_reduce_kernel<"
 
 
-def default_prefill(names):
-    """Name prefix of the default plan's prefill kernel among the run's
-    kernel names: the stream-K kernel when the device ran it, else the
-    pieces schedule's tile kernel."""
-    return PREFILL_SK if any(PREFILL_SK in n for n in names) else PREFILL_PIECES
+def chunk_dispatches(rows, name_of):
+    """The prefill chunk's dispatches among `rows` (in time order; name_of(row)
+    gives the kernel name): (tile kernel, K-piece sum kernel, stream-K kernel)
+    lists.  The pieces dispatches are every one before the first stream-K
+    dispatch; the stream-K ones are that first unbroken run."""
+    pcs, psum, sk = [], [], []
+    state = 0  # 0: before any stream-K dispatch, 1: in the first run, 2: after it
+    for r in rows:
+        n = name_of(r)
+        if PREFILL_SK in n:
+            if state < 2:
+                state = 1
+                sk.append(r)
+        elif PREFILL_PIECES in n or PREFILL_SUM in n:
+            if state == 1:
+                state = 2
+            if state == 0:
+                (pcs if PREFILL_PIECES in n else psum).append(r)
+    return pcs, psum, sk
 
 
-def is_prefill(name, which):
-    return which in name
 COPY = "__amd_rocclr_copyBuffer"
 # The achievable leg's one read of the whole weight arena: non-temporal
 # 16-byte loads, the load type of the decode kernel's weight stream.
@@ -142,14 +156,10 @@ def summarize(out, dest):
     round_keys = {(r["Kernel_Name"], r["Grid_Size_X"]) for r in dec[:4]}
     head = [r for r in dec if (r["Kernel_Name"], r["Grid_Size_X"]) not in round_keys]
     dec = [r for r in dec if (r["Kernel_Name"], r["Grid_Size_X"]) in round_keys]
-    which = default_prefill([r["Kernel_Name"] for r in trace])
-    pre = [r for r in trace if is_prefill(r["Kernel_Name"], which)]
-    pcs = [r for r in trace if which != PREFILL_PIECES and PREFILL_PIECES in r["Kernel_Name"]]
     dur = lambda r: int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    avg_us = lambda rs: sum(map(dur, rs)) / len(rs) / 1e3 if rs else float("nan")
+    pcs, psum, sk = chunk_dispatches(trace, lambda r: r["Kernel_Name"])
     dec_avg_us = sum(map(dur, dec)) / len(dec) / 1e3
-    pre_avg_us = sum(map(dur, pre)) / len(pre) / 1e3 if pre else float("nan")
-    psum = [r for r in trace if PREFILL_SUM in r["Kernel_Name"]]
-    psum_avg_us = sum(map(dur, psum)) / len(psum) / 1e3 if psum else 0.0
     head_avg_us = sum(map(dur, head)) / len(head) / 1e3 if head else float("nan")
 
     # the first replay's first four launches are layer 0's qkv, o, gate_up, down
@@ -185,19 +195,19 @@ def summarize(out, dest):
               % (algo, roof["achieved"], algo / (dec_avg_us * 1e-6) / 1e9))
     md.append("| M = 8 round (ms) | %.4f | %.4f (sum of kernel durations / replays) |"
               % (line["ms_per_step"], sum(map(dur, dec)) / (len(dec) / per_round) / 1e6))
-    if which == PREFILL_PIECES:
-        md.append("| prefill chunk (us): tile kernel + K-piece sum kernel | %.2f | %.2f + %.2f "
-                  "= %.2f |" % (line["prefill_chunk"]["us"], pre_avg_us, psum_avg_us,
-                                pre_avg_us + psum_avg_us))
-    else:
-        md.append("| prefill chunk, default plan (us): stream-K kernel | %.2f | %.2f |"
-                  % (line["prefill_chunk"]["us"], pre_avg_us))
-        if pcs:
-            pcs_us = sum(map(dur, pcs)) / len(pcs) / 1e3
-            md.append("| prefill chunk, pieces schedule (us): tile kernel + K-piece sum kernel "
-                      "| %.2f | %.2f + %.2f = %.2f |"
-                      % (line["prefill_chunk"].get("pieces_schedule_us", float("nan")), pcs_us,
-                         psum_avg_us, pcs_us + psum_avg_us))
+    pc = line["prefill_chunk"]
+    md.append("| prefill chunk, default plan (%s) (us) | %.2f | |" % (pc.get("default_schedule", "?"),
+                                                                    pc["us"]))
+    md.append("| prefill chunk, pieces schedule (us): tile kernel + K-piece sum kernel | %.2f | "
+              "%.2f + %.2f = %.2f |" % (pc.get("pieces_us", float("nan")), avg_us(pcs),
+                                        avg_us(psum) if psum else 0.0,
+                                        avg_us(pcs) + (avg_us(psum) if psum else 0.0)))
+    md.append("| prefill chunk, stream-K schedule (us) | %.2f | %.2f |"
+              % (pc.get("stream_k_us", float("nan")), avg_us(sk)))
+    for name, rs in pc.get("round_shapes", {}).items():
+        md.append("| %s at M = 2048 (us): default (%s) / pieces / stream-K | %.2f / %.2f / %.2f "
+                  "| |" % (name, rs["default_schedule"], rs["us"], rs["pieces_us"],
+                           rs["stream_k_us"]))
     if "output_head" in line:
         md.append("| output head, M = 8, K = 5120, N = 152064, fp32 out (us) | %.2f | %.2f |"
                   % (line["output_head"]["us"], head_avg_us))
@@ -297,12 +307,11 @@ def summarize(out, dest):
         summarize_mfma(out, dest)
 
 
-def summarize_mfma(out, dest):
-    """prefill_m2048_mfma_counters.md: the prefill tile kernel's MFMA work from
-    SQ_INSTS_VALU_MFMA_MOPS_BF16 (units of 512 flops), checked against the
-    algorithmic 2 M K N, and its rate over the kernel-trace duration against
-    the 2.5 PFLOP/s bf16 peak; MFMA busy cycles as read."""
-    rows = list(csv.DictReader(open(find_csv(os.path.join(out, "mfma"),
+def counter_avgs(out, pass_name, counters):
+    """Per-dispatch counter sums (over the device) averaged over the prefill
+    chunk's pieces tile kernel and its stream-K kernel: ({counter: value},
+    {counter: value}, dispatch counts)."""
+    rows = list(csv.DictReader(open(find_csv(os.path.join(out, pass_name),
                                              "counter_collection.csv"))))
     per = collections.defaultdict(lambda: collections.defaultdict(float))
     name = {}
@@ -310,99 +319,116 @@ def summarize_mfma(out, dest):
         k = int(r["Dispatch_Id"])
         per[k][r["Counter_Name"]] += float(r["Counter_Value"])
         name[k] = r["Kernel_Name"]
-    which = default_prefill(name.values())
-    ids = sorted(k for k in per if is_prefill(name[k], which))
-    avg = {c: sum(per[k][c] for k in ids) / len(ids) for c in MFMA_COUNTERS}
+    pcs, _, sk = chunk_dispatches(sorted(name), lambda k: name[k])
+    avg = lambda ids: {c: sum(per[k][c] for k in ids) / len(ids) for c in counters} if ids \
+        else {c: float("nan") for c in counters}
+    return avg(pcs), avg(sk), (len(pcs), len(sk))
+
+
+def summarize_mfma(out, dest):
+    """prefill_m2048_mfma_counters.md: the prefill chunk's MFMA work, for its
+    pieces tile kernel (the default plan) and its stream-K kernel, from
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 (units of 512 flops) against the
+    algorithmic 2 M K N, the rate over the kernel-trace duration against the
+    2.5 PFLOP/s bf16 peak, the clock and the MFMA busy cycles; then the LDS
+    and VALU pass."""
+    a_pcs, a_sk, (n_pcs, n_sk) = counter_avgs(out, "mfma", MFMA_COUNTERS)
     trace = list(csv.DictReader(open(find_csv(os.path.join(out, "trace"), "kernel_trace.csv"))))
-    durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace
-            if is_prefill(r["Kernel_Name"], which)]
-    us = sum(durs) / len(durs) / 1e3
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+    pcs, psum, sk = chunk_dispatches(trace, lambda r: r["Kernel_Name"])
+    dur = lambda rs: sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rs) \
+        / len(rs) / 1e3 if rs else float("nan")
+    us = {"pcs": dur(pcs), "sk": dur(sk)}
     M, K, N = bench.PREFILL_SHAPE
     algo = 2.0 * M * K * N
-    flops = avg["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
-    md = ["# Prefill chunk (M = %d, K = %d, N = %d): MFMA counters\n" % (M, K, N)]
-    md.append("Commands (from the repository root, with `TMPDIR=/tmp`, run in /tmp), each a run "
-              "of its own via `python3 bench_profile.py --out OUT`:\n")
-    md.append("    " + shown(rocprof_cmd(PASSES[4][1], "OUT/mfma")))
-    md.append("    " + shown(rocprof_cmd(PASSES[0][1], "OUT/trace")) + "\n")
-    md.append("Counters per dispatch of the default plan's kernel (`%s...>`), summed over "
-              "the device, averaged over its %d dispatches:\n" % (which, len(ids)))
-    md.append("| counter | value |")
-    md.append("|---|---|")
-    for c in MFMA_COUNTERS:
-        md.append("| %s | %.0f |" % (c, avg[c]))
-    md.append("\n| figure | value |")
-    md.append("|---|---|")
-    md.append("| MFMA flops (MOPS_BF16 x 512) | %.4g |" % flops)
-    md.append("| algorithmic flops 2 M K N | %.4g |" % algo)
-    md.append("| counted / algorithmic | %.4f |" % (flops / algo))
-    md.append("| tile kernel, kernel-trace average (us) | %.2f |" % us)
-    md.append("| achieved bf16 MFMA rate (counted flops / duration, TFLOP/s) | %.1f |"
-              % (flops / us / 1e6))
-    md.append("| fraction of the 2.5 PFLOP/s dense bf16 peak | %.3f |" % (flops / us / 1e6 / 2500))
-    # device facts from the profiler's own agent table
     agent = [r for r in csv.DictReader(open(find_csv(os.path.join(out, "mfma"),
                                                      "agent_info.csv")))
              if r.get("Name", "").startswith("gfx")][0]
     xcc, simds = int(agent["Num_Xcc"]), int(agent["Simd_Count"])
-    clk_ghz = avg["GRBM_GUI_ACTIVE"] / xcc / (us * 1e3)
-    busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (avg["GRBM_GUI_ACTIVE"] / xcc * simds)
-    md.append("| clock while the kernel ran (GRBM_GUI_ACTIVE / %d XCDs / duration, GHz) | %.3f |"
-              % (xcc, clk_ghz))
+    cus = int(agent["Cu_Count"]) if "Cu_Count" in agent else simds // 4
+    md = ["# Prefill chunk (M = %d, K = %d, N = %d): MFMA, LDS and VALU counters\n" % (M, K, N)]
+    md.append("Commands (from the repository root, with `TMPDIR=/tmp`, run in /tmp), each a run "
+              "of its own via `python3 bench_profile.py --out OUT`:\n")
+    md.append("    " + shown(rocprof_cmd(PASSES[4][1], "OUT/mfma")))
+    md.append("    " + shown(rocprof_cmd(PASSES[5][1], "OUT/lds")))
+    md.append("    " + shown(rocprof_cmd(PASSES[0][1], "OUT/trace")) + "\n")
+    md.append("bench.py times the chunk with the default plan (whole tiles, the last round's "
+              "tiles in K pieces: `%s...>` and its sum `%s...>`), with that schedule again by "
+              "name, and with the stream-K schedule (`%s...>`). Counters per dispatch, summed "
+              "over the device, averaged over the chunk's %d tile-kernel and %d stream-K "
+              "dispatches of each run (the sum kernel issues no MFMA).\n"
+              % (PREFILL_PIECES, PREFILL_SUM, PREFILL_SK, n_pcs, n_sk))
+    md.append("| counter | pieces tile kernel | stream-K kernel |")
+    md.append("|---|---|---|")
+    for c in MFMA_COUNTERS:
+        md.append("| %s | %.0f | %.0f |" % (c, a_pcs[c], a_sk[c]))
+
+    def figs(a, t_us):
+        flops = a["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+        return {"flops": flops, "ratio": flops / algo, "us": t_us,
+                "tflops": flops / t_us / 1e6, "frac": flops / t_us / 1e6 / 2500,
+                "clk": a["GRBM_GUI_ACTIVE"] / xcc / (t_us * 1e3),
+                "busy": a["SQ_VALU_MFMA_BUSY_CYCLES"] / (a["GRBM_GUI_ACTIVE"] / xcc * simds)}
+    f_p, f_s = figs(a_pcs, us["pcs"]), figs(a_sk, us["sk"])
+    md.append("\n| figure | pieces tile kernel | stream-K kernel |")
+    md.append("|---|---|---|")
+    md.append("| MFMA flops (MOPS_BF16 x 512) | %.4g | %.4g |" % (f_p["flops"], f_s["flops"]))
+    md.append("| algorithmic flops 2 M K N | %.4g | %.4g |" % (algo, algo))
+    md.append("| counted / algorithmic | %.4f | %.4f |" % (f_p["ratio"], f_s["ratio"]))
+    md.append("| kernel-trace average (us) | %.2f | %.2f |" % (f_p["us"], f_s["us"]))
+    md.append("| achieved bf16 MFMA rate (TFLOP/s) | %.1f | %.1f |" % (f_p["tflops"], f_s["tflops"]))
+    md.append("| fraction of the 2.5 PFLOP/s dense bf16 peak | %.3f | %.3f |"
+              % (f_p["frac"], f_s["frac"]))
+    md.append("| clock while the kernel ran (GRBM_GUI_ACTIVE / %d XCDs / duration, GHz) "
+              "| %.3f | %.3f |" % (xcc, f_p["clk"], f_s["clk"]))
     md.append("| MFMA pipes busy: SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / %d x %d SIMDs) "
-              "| %.3f |\n" % (xcc, simds, busy))
-    md.append("SQ_VALU_MFMA_BUSY_CYCLES is the sum over SIMDs of cycles with an MFMA in "
-              "flight: here exactly 32 per `v_mfma_f32_32x32x16_bf16` (MOPS / 2). The peak "
-              "of 2.5 PFLOP/s assumes %d MHz; the clock counted during this kernel is lower, "
-              "so the busy fraction at the running clock exceeds the fraction of peak.\n"
-              % int(agent["Max_Engine_Clk_Fcompute"]))
-    md.append("The bench also times the pieces schedule (`%s...>` and its K-piece sum "
-              "`%s...>`) on the same data; its dispatches are not in these averages.\n"
-              % (PREFILL_PIECES, PREFILL_SUM))
+              "| %.3f | %.3f |\n" % (xcc, simds, f_p["busy"], f_s["busy"]))
+    md.append("The pieces schedule's figures are for its tile kernel alone (the K-piece sum "
+              "kernel takes %.2f us more per call in the trace). SQ_VALU_MFMA_BUSY_CYCLES is the "
+              "sum over SIMDs of cycles with an MFMA in flight: 32 per "
+              "`v_mfma_f32_32x32x16_bf16` (MOPS / 2). The peak of 2.5 PFLOP/s assumes %d MHz; "
+              "the clock counted during these kernels is lower, so the busy fraction at the "
+              "running clock exceeds the fraction of peak.\n"
+              % (dur(psum) if psum else 0.0, int(agent["Max_Engine_Clk_Fcompute"])))
     if os.path.isdir(os.path.join(out, "lds")):
-        md += lds_table(out, avg, xcc, simds, int(agent["Cu_Count"]) if "Cu_Count" in agent
-                        else simds // 4)
+        md += lds_table(out, a_pcs, a_sk, xcc, cus)
     with open(os.path.join(dest, "prefill_m2048_mfma_counters.md"), "w") as f:
         f.write("\n".join(md))
-    print("prefill: counted MFMA flops %.4g vs algorithmic %.4g; %.1f TFLOP/s over %.2f us"
-          % (flops, algo, flops / us / 1e6, us), flush=True)
+    print("prefill: counted MFMA flops %.4g / %.4g vs algorithmic %.4g; pieces %.2f us, "
+          "stream-K %.2f us" % (f_p["flops"], f_s["flops"], algo, f_p["us"], f_s["us"]),
+          flush=True)
 
 
-def lds_table(out, mfma_avg, xcc, simds, cus):
-    """LDS and VALU activity of the prefill tile kernel from the "lds" pass,
+def lds_table(out, m_pcs, m_sk, xcc, cus):
+    """LDS and VALU activity of the two chunk kernels from the "lds" pass,
     with the derived figures by the expressions rocprofv3 -L gives for them
     (LDSBankConflict, LdsBankConflict, VALUBusy)."""
-    rows = list(csv.DictReader(open(find_csv(os.path.join(out, "lds"),
-                                             "counter_collection.csv"))))
-    per = collections.defaultdict(lambda: collections.defaultdict(float))
-    name = {}
-    for r in rows:
-        k = int(r["Dispatch_Id"])
-        per[k][r["Counter_Name"]] += float(r["Counter_Value"])
-        name[k] = r["Kernel_Name"]
-    which = default_prefill(name.values())
-    ids = sorted(k for k in per if is_prefill(name[k], which))
-    avg = {c: sum(per[k][c] for k in ids) / len(ids) for c in LDS_COUNTERS}
-    gui = avg["GRBM_GUI_ACTIVE"] / xcc  # GRBM_GUI_ACTIVE of one XCD (the max over them)
-    md = ["## LDS and VALU activity (a counter pass of its own)\n",
-          "    " + shown(rocprof_cmd(PASSES[5][1], "OUT/lds")) + "\n",
-          "| counter | value |", "|---|---|"]
+    a_pcs, a_sk, _ = counter_avgs(out, "lds", LDS_COUNTERS)
+    md = ["## LDS and VALU activity\n", "| counter | pieces tile kernel | stream-K kernel |",
+          "|---|---|---|"]
     for c in LDS_COUNTERS:
-        md.append("| %s | %.0f |" % (c, avg[c]))
-    bank, idx = avg["SQ_LDS_BANK_CONFLICT"], avg["SQ_LDS_IDX_ACTIVE"]
-    md += ["\n| figure | value |", "|---|---|",
+        md.append("| %s | %.0f | %.0f |" % (c, a_pcs[c], a_sk[c]))
+
+    def figs(a, m):
+        gui = a["GRBM_GUI_ACTIVE"] / xcc  # GRBM_GUI_ACTIVE of one XCD (the max over them)
+        bank, idx = a["SQ_LDS_BANK_CONFLICT"], a["SQ_LDS_IDX_ACTIVE"]
+        return (bank / (idx - bank), 100.0 * bank / gui / cus, 100.0 * idx / gui / cus,
+                100.0 * a["SQ_ACTIVE_INST_VALU"] / cus / gui,
+                a["SQ_VALU_MFMA_COEXEC_CYCLES"] / m["SQ_VALU_MFMA_BUSY_CYCLES"])
+    p, k = figs(a_pcs, m_pcs), figs(a_sk, m_sk)
+    md += ["\n| figure | pieces tile kernel | stream-K kernel |", "|---|---|---|",
            "| LDS bank-conflict cycles per conflict-free LDS cycle (LdsBankConflict: "
-           "BANK_CONFLICT / (IDX_ACTIVE - BANK_CONFLICT)) | %.3f |" % (bank / (idx - bank)),
+           "BANK_CONFLICT / (IDX_ACTIVE - BANK_CONFLICT)) | %.3f | %.3f |" % (p[0], k[0]),
            "| share of the kernel's time the LDS is stalled by bank conflicts "
-           "(LDSBankConflict: 100 BANK_CONFLICT / GRBM_GUI_ACTIVE / %d CUs, %%) | %.1f |"
-           % (cus, 100.0 * bank / gui / cus),
-           "| VALUBusy (100 ACTIVE_INST_VALU / %d CUs / GRBM_GUI_ACTIVE, %%) | %.1f |"
-           % (cus, 100.0 * avg["SQ_ACTIVE_INST_VALU"] / cus / gui),
+           "(LDSBankConflict: 100 BANK_CONFLICT / GRBM_GUI_ACTIVE / %d CUs, %%) | %.1f | %.1f |"
+           % (cus, p[1], k[1]),
+           "| share of the kernel's time the LDS is active (100 IDX_ACTIVE / GRBM_GUI_ACTIVE / "
+           "%d CUs, %%) | %.1f | %.1f |" % (cus, p[2], k[2]),
+           "| VALUBusy (100 ACTIVE_INST_VALU / %d CUs / GRBM_GUI_ACTIVE, %%) | %.1f | %.1f |"
+           % (cus, p[3], k[3]),
            "| cycles an MFMA and a VALU instruction issued together, per MFMA-busy cycle "
-           "(VALU_MFMA_COEXEC / VALU_MFMA_BUSY of the MFMA pass) | %.3f |"
-           % (avg["SQ_VALU_MFMA_COEXEC_CYCLES"] / mfma_avg["SQ_VALU_MFMA_BUSY_CYCLES"])]
-    md.append("\nThe two passes are separate runs of the same command; each average is "
-              "over the default plan's kernel dispatches in its run.\n")
+           "(VALU_MFMA_COEXEC / VALU_MFMA_BUSY of the MFMA pass) | %.3f | %.3f |" % (p[4], k[4])]
+    md.append("\nThe two counter passes are separate runs of the same command.\n")
     return md
 
 

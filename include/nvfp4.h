@@ -69,14 +69,15 @@ enum nvfp4_out_dtype { NVFP4_OUT_F32 = 0, NVFP4_OUT_BF16 = 1 };
 /* Prefill schedules (nvfp4_gemm_config.prefill_schedule) for M > 64, whose
  * 256 x 256 output tiles are spread over the compute units: */
 enum nvfp4_prefill_schedule {
-    NVFP4_PREFILL_AUTO = 0,     /* stream-K where it applies (see nvfp4_gemm_run),
-                                   else pieces */
+    NVFP4_PREFILL_AUTO = 0,     /* stream-K below one tile per compute unit (see
+                                   nvfp4_gemm_run), else pieces */
     NVFP4_PREFILL_PIECES = 1,   /* whole tiles; the tiles of a last partial round cut
                                    along K into pieces, added by a second kernel */
-    NVFP4_PREFILL_STREAM_K = 2  /* (where it applies) every compute unit takes an
-                                   equal run of the tiles' K stages laid end to end; a
-                                   tile shared by two or three units is finished by the
-                                   last */
+    NVFP4_PREFILL_STREAM_K = 2  /* wherever it applies (tiles not a multiple of the
+                                   compute units, runs of at least half a tile): every
+                                   compute unit takes an equal run of the tiles' K
+                                   stages laid end to end; a tile shared by two or three
+                                   units is finished by the last */
 };
 
 /* Largest k of nvfp4_topk. */
@@ -196,15 +197,14 @@ void nvfp4_gemm_destroy(nvfp4_gemm plan);
  * (K, N) must equal the plan's, 1 <= M <= max_M.  M <= 8 uses the decode
  * kernel and 8 < M <= 64 the verify-width decode kernel (each one pass over
  * the weights for all M rows); larger M uses the bf16 MFMA prefill kernel.
- * When its 256 x 256 output tiles are not a multiple of the device's compute
- * units, it runs the stream-K schedule (one workgroup per compute unit,
- * equal runs of K stages; the fp32 partial sums of a tile shared by two or
- * three runs meet in the workspace and the last contributor adds them in run
- * order), provided each run holds at least half a tile and, below one tile
- * per unit, at most 3/4 of the units would hold a tile.  Otherwise whole
- * tiles, and a last partial round's tiles cut along K with a second kernel
- * adding their pieces (NVFP4_PREFILL_PIECES asks for that schedule in every
- * case).  The workspace holds, in this order, the
+ * With fewer 256 x 256 output tiles than the device's compute units, at
+ * most 3/4 of them, it runs the stream-K schedule (one workgroup per compute
+ * unit, equal runs of K stages of at least half a tile; the fp32 partial
+ * sums of a tile shared by two or three runs meet in the workspace and the
+ * last contributor adds them in run order).  Otherwise whole tiles, with a
+ * last partial round's tiles cut along K and a second kernel adding their
+ * pieces.  nvfp4_gemm_config.prefill_schedule can ask for either wherever it
+ * applies.  The workspace holds, in this order, the
  * decode, verify and prefill areas the plan's max_M needs.  For M > 8 and K not a
  * multiple of 512, every activation value must be finite: those kernels read
  * the tail of a row's last K window from the start of the next row and

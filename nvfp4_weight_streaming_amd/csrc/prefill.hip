@@ -700,11 +700,10 @@ __global__ __launch_bounds__(kPReduceThreads) void prefill_reduce_kernel(
         if (m + r < M) store_out<BF16>(out, (size_t)(m + r) * N + n, e[r] * ts);
 }
 
-// How a run of M rows is laid out over the compute units.  With tiles not a
-// multiple of the units, the stream-K schedule when each unit's run holds at
-// least half a tile's stages (unless the plan asks for pieces); otherwise the
-// tiles beyond whole rounds (one tile per compute unit at a time) are split
-// along K when at least two pieces each fit: n_tail tiles, S pieces each.
+// How a run of M rows is laid out over the compute units: the stream-K
+// schedule (below), or whole tiles with the tiles beyond whole rounds (one
+// tile per compute unit at a time) split along K when at least two pieces
+// each fit: n_tail tiles, S pieces each.
 struct PrefillSplit {
     int tiles, n_tail, splits;
     bool stream;
@@ -715,14 +714,17 @@ static PrefillSplit prefill_split(int M, int K, int N, int cus, int schedule) {
     const int nk = (K + kPBK - 1) / kPBK;
     PrefillSplit s{mblocks * nblocks, 0, 1, false};
     const int left = s.tiles % cus;
-    // stream-K when every run holds at least half a tile's stages (and one):
-    // then at most three runs share a tile.  Below one tile per unit only
-    // when at most 3/4 of the units would have a tile: with more, its hand-offs
-    // and part boundaries cost more than the idle units (measured at 224 of
-    // 256: 11% slower; at 160 of 256: 8-17% faster).
+    // Stream-K applies when every run holds at least half a tile's stages
+    // (and one): then at most three runs share a tile.  By default it is
+    // taken below one tile per unit when at most 3/4 of the units would have
+    // a tile (measured 8-20% faster at 160 and 136 of 256 tiles, 11% slower
+    // at 224); with more tiles than units the whole tiles plus K pieces of
+    // the last round measured 1-4% faster, so stream-K there only on request.
     const long long per_run = (long long)s.tiles * nk / cus;
-    const bool fills = s.tiles > cus || 4 * s.tiles <= 3 * cus;
-    if (schedule != NVFP4_PREFILL_PIECES && left && fills && per_run >= max(1, (nk + 1) / 2)) {
+    const bool applies = left && per_run >= max(1, (nk + 1) / 2);
+    const bool preferred = s.tiles < cus && 4 * s.tiles <= 3 * cus;
+    if (applies && (schedule == NVFP4_PREFILL_STREAM_K ||
+                    (schedule == NVFP4_PREFILL_AUTO && preferred))) {
         s.stream = true;
         return s;
     }

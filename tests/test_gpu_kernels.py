@@ -532,18 +532,21 @@ def test_prefill_and_decode_share_a_workspace(nv):
         check(out, y, S, bf16=False, what="M=%d after the other path" % m)
 
 
-# ---- prefill, stream-K schedule (more tiles than compute units) ----------------
+# ---- prefill, stream-K schedule ---------------------------------------------------
 
-def _stream_k_shape(nv, M, K, N):
-    """True when the device runs (M, K, N) with the stream-K schedule: tiles
-    not a multiple of the compute units, and every unit's run at least half
-    a tile's K stages (and one)."""
+def _stream_k_shape(nv, M, K, N, default=False):
+    """Whether stream-K applies to (M, K, N) on this device (tiles not a
+    multiple of the compute units, every unit's run at least half a tile's K
+    stages and one), or with default=True whether the default plan takes it
+    (also fewer tiles than units, at most 3/4 of them)."""
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     tiles = ((M + 255) // 256) * ((N + 255) // 256)
     nk = (K + 63) // 64
-    fills = tiles > cus or 4 * tiles <= 3 * cus
-    return tiles % cus != 0 and fills and tiles * nk // cus >= max(1, (nk + 1) // 2)
+    applies = tiles % cus != 0 and tiles * nk // cus >= max(1, (nk + 1) // 2)
+    if default:
+        return applies and tiles < cus and 4 * tiles <= 3 * cus
+    return applies
 
 
 def _quarter_cols(N, seed):
@@ -578,7 +581,8 @@ def test_prefill_stream_k_sampled(nv, M, K, N, bf16):
     import torch
     assert _stream_k_shape(nv, M, K, N)
     pw, a, cols, y, S = _sk_case(nv, M, K, N, M + K + N)
-    out, _ = run(nv, pw, a, nv.OUT_BF16 if bf16 else nv.OUT_F32)  # (canaries checked)
+    out, _ = run(nv, pw, a, nv.OUT_BF16 if bf16 else nv.OUT_F32,
+                 prefill_schedule=nv.PREFILL_STREAM_K)  # (canaries checked)
     check(out[:, torch.from_numpy(cols).cuda()], y, S, bf16=bf16,
           what="stream-K prefill %r" % ((M, K, N),))
 
@@ -605,7 +609,7 @@ def test_prefill_round_shapes_at_chunk_size(nv, name, K, N, sk):
     import torch
     M = 2048
     if torch.cuda.get_device_properties(0).multi_processor_count == 256:
-        assert _stream_k_shape(nv, M, K, N) == sk
+        assert _stream_k_shape(nv, M, K, N, default=True) == sk
     codes, scales = synth.random_planes(K + 1, N + 2, N, K)
     t = 2.5e-3
     act = synth.activations(K + 3, N + 4, M, K)
@@ -625,7 +629,7 @@ def test_prefill_stream_k_deterministic_and_pieces_schedule(nv):
     M, K, N = 300, 1040, 33000
     pw, a, cols, y, S = _sk_case(nv, M, K, N, 5)
     c = torch.from_numpy(cols).cuda()
-    g = nv.Gemm(M, K, N, nv.OUT_F32)
+    g = nv.Gemm(M, K, N, nv.OUT_F32, prefill_schedule=nv.PREFILL_STREAM_K)
     outs = []
     for _ in range(3):
         out = torch.full((M, N), float("nan"), device="cuda")
@@ -647,7 +651,7 @@ def test_prefill_stream_k_fresh_slots_and_shared_workspace(nv):
     import torch
     M, K, N = 600, 512, 30000
     cases = [_sk_case(nv, M, K, N, s) for s in (11, 12)]
-    g = nv.Gemm(M, K, N, nv.OUT_F32)
+    g = nv.Gemm(M, K, N, nv.OUT_F32, prefill_schedule=nv.PREFILL_STREAM_K)
     first = None
     for step, (ci, m) in enumerate([(0, M), (0, 8), (1, M), (0, M), (1, 5)]):
         pw, a, cols, y, S = cases[ci]
@@ -666,9 +670,10 @@ def test_prefill_stream_k_fresh_slots_and_shared_workspace(nv):
 
 def test_prefill_chunk_config_sampled(nv):
     """The prefill-chunk config: M = 2048, K = 5120, N = 17408, quantised
-    N(0, 0.02) weights, bf16 out; every row, sampled columns (544 tiles: the
-    stream-K schedule on a 256-CU device, 224 of the tiles shared between two
-    workgroups)."""
+    N(0, 0.02) weights, bf16 out; every row, sampled columns.  544 tiles on a
+    256-CU device: the default plan's whole tiles with the last round's 32
+    tiles in 8 K pieces each, and the stream-K schedule (224 of the tiles
+    shared between two workgroups)."""
     import torch
     M, K, N = 2048, 5120, 17408
     W = synth.weights(0, 300, N, K)
@@ -680,6 +685,8 @@ def test_prefill_chunk_config_sampled(nv):
     assert tg == t and np.array_equal(c[cols], c_ref) and np.array_equal(s[cols], s_ref)
     act = synth.activations(0, 300, M, K)
     pw = pack(nv, dev(c), dev(s), K, N, tg)
-    out, _ = run(nv, pw, dev_bf16(act), nv.OUT_BF16)
     y, S = oracle.gemm(act, c_ref, s_ref, t)
-    check(out[:, torch.from_numpy(cols).cuda()], y, S, bf16=True, what="prefill chunk")
+    for sch in (nv.PREFILL_AUTO, nv.PREFILL_STREAM_K):
+        out, _ = run(nv, pw, dev_bf16(act), nv.OUT_BF16, prefill_schedule=sch)
+        check(out[:, torch.from_numpy(cols).cuda()], y, S, bf16=True,
+              what="prefill chunk, schedule %d" % sch)
