@@ -481,11 +481,13 @@ __device__ __forceinline__ int sk_slot(int q, int t, long long W, int C, int nk)
 // Hand-off of a shared tile, wave by wave (wave w of every contributor owns
 // the same outputs): the wave stores its accumulators to its slot and, once
 // the stores have completed, increments the tile's counter.  The wave that
-// finds the other n - 1 increments already there adds the n slots in run
-// order, so the sum is the same float whichever contributor comes last,
-// zeroes the counter again and stores the outputs.  (The outputs are stored
-// here rather than by the caller: a store after the hand-off, reached from
-// both outcomes, would keep the accumulators alive through the loads.)  With every contributor on one XCD
+// finds the other n - 1 increments already there finishes the tile, with a
+// sum that is the same float whichever contributor comes last: with two
+// terms it adds the other's slot to its registers (own + other in either
+// order), with three it adds the three slots in run order, its own included.
+// It zeroes the counter again and stores the outputs itself (a store after
+// the hand-off, reached from both outcomes, would keep the accumulators
+// alive through the loads).  With every contributor on one XCD
 // (LOCAL) the slots and the counter live in that XCD's L2: plain stores and
 // loads, an agent-scope atomic.  Otherwise the stores and loads are
 // device-scope and the counter system-scope (coherent across XCDs).  Slots:
@@ -495,7 +497,7 @@ template <int BM, int BN, int NW, bool BF16, bool LOCAL>
 __device__ __forceinline__ void prefill_handoff(f32x16 (&acc)[ptiles_i(BM, NW)][ptiles_j(BN)],
                                                 float* __restrict__ slots,
                                                 unsigned int* __restrict__ counters, int ctr,
-                                                int mine, int n, const int (&slot)[kPMaxShare],
+                                                int me, int n, const int (&slot)[kPMaxShare],
                                                 void* __restrict__ out, float ts, int M, int N,
                                                 int m0, int n0) {
     constexpr int TI = PTiles<BM, BN, NW>::TI, TJ = PTiles<BM, BN, NW>::TJ;
@@ -508,7 +510,9 @@ __device__ __forceinline__ void prefill_handoff(f32x16 (&acc)[ptiles_i(BM, NW)][
     auto rsrc_of = [&](int s) {
         return prefill_rsrc(slots + ((size_t)s * NW + wave) * kF, (size_t)kF * 4);
     };
-    const __amdgpu_buffer_rsrc_t rm = rsrc_of(mine);
+    // (slot indices through scalar registers: the resources must be scalar)
+    const int own = __builtin_amdgcn_readfirstlane(me == 0 ? slot[0] : me == 1 ? slot[1] : slot[2]);
+    const __amdgpu_buffer_rsrc_t rm = rsrc_of(own);
     // float4 v of a slot at byte 16 lane + sk_soff(v / 64): the lane's part
     // in a vector register, the rest in the instruction's scalar offset (so
     // no per-float4 address registers are held)
@@ -535,7 +539,36 @@ __device__ __forceinline__ void prefill_handoff(f32x16 (&acc)[ptiles_i(BM, NW)][
     old = __builtin_amdgcn_readlane(old, 0);
     asm volatile("" ::: "memory");
     if (old != (unsigned int)(n - 1)) return;  // a later contributor finishes
-    // All n slots in run order, this wave's own included (stored and waited
+    if (n == 2) {
+        // Two terms: own + other is the same float in either order, so the
+        // other's slot is added to the registers.
+        const __amdgpu_buffer_rsrc_t ro =
+            rsrc_of(__builtin_amdgcn_readfirstlane(me == 0 ? slot[1] : slot[0]));
+        constexpr int kB2 = 2;
+#pragma unroll
+        for (int b0 = 0; b0 < TI * TJ; b0 += kB2) {
+            u32x4 x[kB2 * 4];
+#pragma unroll
+            for (int q = 0; q < kB2 * 4; ++q)
+                x[q] = __builtin_amdgcn_raw_buffer_load_b128(ro, voff, sk_soff(b0 * 4 + q), kAux);
+#pragma unroll
+            for (int q = 0; q < kB2 * 4; ++q) {
+                const int i = (b0 + q / 4) / TJ, j = (b0 + q / 4) % TJ, rq = q % 4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i][j][4 * rq + e] += __uint_as_float(x[q][e]);
+            }
+            asm volatile("" ::: "memory");
+        }
+        if (lane == 0) {
+            if (LOCAL)
+                __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else
+                __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+        prefill_store_tile<BM, BN, NW, BF16>(acc, out, ts, M, N, m0, n0);
+        return;
+    }
+    // Three terms: all slots in run order, this wave's own included (stored and waited
     // for above: the same values as its registers), so no term depends on
     // which contributor is adding; the sums go straight to the outputs, in
     // batches of kBatch MFMA tiles whose loads are in flight together.
@@ -641,14 +674,13 @@ __global__ __launch_bounds__(kPThreads) void prefill_sk_kernel(
             for (int i = 0; i < kPMaxShare; ++i)
                 slot[i] = __builtin_amdgcn_readfirstlane(i < n ? sk_slot(rf + i, t, W, C, nk)
                                                                : sk_slot(rf, t, W, C, nk));
-            const int mine = __builtin_amdgcn_readfirstlane(sk_slot(r, t, W, C, nk));
             const bool local = l2_local && rf / (C / 8) == (rf + n - 1) / (C / 8);
             if (local)
                 prefill_handoff<kPTile, kPTile, kPWaves, BF16, true>(
-                    acc, slots, counters, slot[0], mine, n, slot, out, ts, M, N, m0, n0);
+                    acc, slots, counters, slot[0], r - rf, n, slot, out, ts, M, N, m0, n0);
             else
                 prefill_handoff<kPTile, kPTile, kPWaves, BF16, false>(
-                    acc, slots, counters, slot[0], mine, n, slot, out, ts, M, N, m0, n0);
+                    acc, slots, counters, slot[0], r - rf, n, slot, out, ts, M, N, m0, n0);
         }
     }
 }
