@@ -248,12 +248,13 @@ int nvfp4_gemm_run_argmax(nvfp4_gemm plan, int M, int K, int N, const uint8_t* c
  * graph capture, tight serving loops, harnesses that forbid allocation): the
  * same kernels, with the split-K counters and partial sums in a static 16 MiB
  * device array per GPU (held until the process ends) instead of a caller
- * workspace.  Arguments as nvfp4_gemm_run, without the workspace.  A run that
- * needs more than 16 MiB of that state (a large prefill chunk; every
- * stream-K prefill run, whose hand-off slots take 512 KiB per compute unit:
- * a plan made with NVFP4_PREFILL_PIECES needs none where its tiles fill whole
- * rounds) returns NVFP4_EUNSUPPORTED and
- * launches nothing.  The first call on a device
+ * workspace.  Arguments as nvfp4_gemm_run, without the workspace.  Stream-K
+ * prefill runs do not fit (their hand-off slots take 512 KiB per compute
+ * unit): a default plan runs such an M with whole tiles and K pieces instead,
+ * whose sums can differ from nvfp4_gemm_run's in the last bits.  A run that
+ * still needs more than 16 MiB of that state (a large prefill chunk, or
+ * stream-K asked for by the plan) returns NVFP4_EUNSUPPORTED and launches
+ * nothing.  The first call on a device
  * zero-fills the array with one kernel on `stream`, so it must be made
  * outside stream capture (under capture it returns NVFP4_ESTATE and launches
  * nothing); later calls may be captured.  Every call on a GPU uses

@@ -281,11 +281,26 @@ static int scratch_for_current_device(hipStream_t s, void** ptr) {
     return NVFP4_OK;
 }
 
+static bool noalloc_fits(size_t counters, size_t partials) {
+    return counters <= kScratchCounters && partials <= kScratchBytes - kScratchCounters;
+}
+
+// The prefill schedule a run of M rows takes without a workspace: the plan's,
+// except that a default plan whose stream-K slots do not fit the scratch runs
+// whole tiles and K pieces instead where those fit.
+static int noalloc_prefill_schedule(const nvfp4_gemm_plan* p, int M) {
+    size_t c = 0, q = 0;
+    prefill_ws_need(p, M, p->pre.schedule, &c, &q);
+    if (noalloc_fits(c, q) || p->pre.schedule != NVFP4_PREFILL_AUTO) return p->pre.schedule;
+    prefill_ws_need(p, M, NVFP4_PREFILL_PIECES, &c, &q);
+    return noalloc_fits(c, q) ? NVFP4_PREFILL_PIECES : p->pre.schedule;
+}
+
 // Counter and partial-sum bytes a run of M rows needs in that layout.
 static void noalloc_need(const nvfp4_gemm_plan* p, int M, size_t* counters, size_t* partials) {
     *counters = *partials = 0;
     if (M > NVFP4_VERIFY_MAX_M && p->pre.enabled) {
-        prefill_ws_need(p, M, p->pre.schedule, counters, partials);
+        prefill_ws_need(p, M, noalloc_prefill_schedule(p, M), counters, partials);
     } else if (M > NVFP4_DECODE_MAX_M && p->ver.enabled) {
         *counters = p->ver.d.counter_bytes;
         *partials = p->ver.d.partial_bytes;
@@ -308,7 +323,7 @@ int nvfp4_gemm_run_noalloc(nvfp4_gemm plan, int M, int K, int N, const uint8_t* 
     if (st != NVFP4_OK) return st;
     size_t nc = 0, np = 0;
     noalloc_need(plan, M, &nc, &np);
-    if (nc > kScratchCounters || np > kScratchBytes - kScratchCounters)
+    if (!noalloc_fits(nc, np))
         return set_error(NVFP4_EUNSUPPORTED, "M: %d needs %zu bytes of split-K counters and %zu of "
                          "partial sums, above the static scratch (%zu and %zu bytes; use "
                          "nvfp4_gemm_run with a workspace)", M, nc, np, kScratchCounters,
@@ -317,6 +332,10 @@ int nvfp4_gemm_run_noalloc(nvfp4_gemm plan, int M, int K, int N, const uint8_t* 
     st = scratch_for_current_device((hipStream_t)stream, &ws);
     if (st) return st;
     const RunOffsets off{kScratchCounters, 0, kScratchCounters, 0, kScratchCounters};
+    if (M > NVFP4_VERIFY_MAX_M && plan->pre.enabled)
+        return launch_prefill(plan, M, codes_dev, scales_dev, tensor_scale, act_dev, out_dev, ws,
+                              off.pre_counters, off.pre_partial,
+                              noalloc_prefill_schedule(plan, M), (hipStream_t)stream);
     return run_gemm(plan, M, codes_dev, scales_dev, tensor_scale, act_dev, out_dev, ws, off,
                     (hipStream_t)stream);
 }

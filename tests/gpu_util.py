@@ -111,3 +111,25 @@ def check(out, y, S, bf16: bool, what=""):
         raise AssertionError("%s: %d of %d outside bound; first %s out=%r y=%r S=%r" % (
             what, int(bad.sum()), bad.size, tuple(i), o[tuple(i)], y[tuple(i)], S[tuple(i)]))
     return float(np.max(err / np.maximum(S, 1e-300)))
+
+
+def quarter_cols(N, seed):
+    """A random column in every 64-column quarter of each 256-column block:
+    with every row, that samples every wave's outputs of every tile (a wave
+    owns one quarter of a tile's columns), the shared tiles' included."""
+    rng = np.random.default_rng(seed)
+    cols = {q + int(rng.integers(0, min(64, N - q))) for q in range(0, N, 64)}
+    return np.array(sorted(cols | {0, N - 1}))
+
+
+def half_block_rows(M, seed):
+    """Two random rows of every 256-row block, one in each half (a wave owns
+    one half of a tile's rows), plus the first and last rows."""
+    rng = np.random.default_rng(seed)
+    rows = {0, M - 1}
+    for b in range(0, M, 256):
+        for h in (0, 128):
+            lo = b + h
+            if lo < M:
+                rows.add(lo + int(rng.integers(0, min(128, M - lo))))
+    return np.array(sorted(rows))

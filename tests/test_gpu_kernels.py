@@ -9,7 +9,8 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_util import canary_out, bf16_bits, check, dev, dev_bf16, host, pack, require_gpu, run
+from tests.gpu_util import (bf16_bits, canary_out, check, dev, dev_bf16, half_block_rows, host,
+                             pack, quarter_cols, require_gpu, run)
 
 pytestmark = pytest.mark.gpu
 
@@ -549,21 +550,12 @@ def _stream_k_shape(nv, M, K, N, default=False):
     return applies
 
 
-def _quarter_cols(N, seed):
-    """A random column in every 64-column quarter of each 256-column block:
-    with every row, that samples every wave's outputs of every tile (a wave
-    owns one quarter of a tile's columns), the shared tiles' included."""
-    rng = np.random.default_rng(seed)
-    cols = {q + int(rng.integers(0, min(64, N - q))) for q in range(0, N, 64)}
-    return np.array(sorted(cols | {0, N - 1}))
-
-
 def _sk_case(nv, M, K, N, seed):
     codes, scales = synth.random_planes(seed, M + N, N, K)
     t = float(np.float32(np.random.default_rng(seed).uniform(1e-4, 1e-2)))
     act = synth.activations(seed + 1, K + N, M, K)
     pw = pack(nv, dev(codes), dev(scales), K, N, t)
-    cols = _quarter_cols(N, seed)
+    cols = quarter_cols(N, seed)
     y, S = oracle.gemm(act, codes[cols], scales[cols], t)
     return pw, dev_bf16(act), cols, y, S
 
@@ -587,19 +579,6 @@ def test_prefill_stream_k_sampled(nv, M, K, N, bf16):
           what="stream-K prefill %r" % ((M, K, N),))
 
 
-def _half_block_rows(M, seed):
-    """Two random rows of every 256-row block, one in each half (a wave owns
-    one half of a tile's rows), plus the first and last rows."""
-    rng = np.random.default_rng(seed)
-    rows = {0, M - 1}
-    for b in range(0, M, 256):
-        for h in (0, 128):
-            lo = b + h
-            if lo < M:
-                rows.add(lo + int(rng.integers(0, min(128, M - lo))))
-    return np.array(sorted(rows))
-
-
 # The round's other matrices at the chunk size, fewer tiles than compute units:
 # o and down (160 tiles) run stream-K, runs of 60 and 170 stages sharing tiles
 # two and three ways; qkv (224 tiles) runs its tiles whole, one per unit.
@@ -615,7 +594,7 @@ def test_prefill_round_shapes_at_chunk_size(nv, name, K, N, sk):
     act = synth.activations(K + 3, N + 4, M, K)
     pw = pack(nv, dev(codes), dev(scales), K, N, t)
     out, _ = run(nv, pw, dev_bf16(act), nv.OUT_BF16)
-    rows, cols = _half_block_rows(M, K), _quarter_cols(N, N)
+    rows, cols = half_block_rows(M, K), quarter_cols(N, N)
     y, S = oracle.gemm(act[rows], codes[cols], scales[cols], t)
     sub = out[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()]
     check(sub, y, S, bf16=True, what="%s at M = 2048" % name)

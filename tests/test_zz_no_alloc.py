@@ -12,7 +12,8 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_util import bf16_bits, canary_out, check, dev, dev_bf16, host, pack, require_gpu
+from tests.gpu_util import (bf16_bits, canary_out, check, dev, dev_bf16, half_block_rows, host,
+                             pack, quarter_cols, require_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -73,6 +74,37 @@ def test_noalloc_refuses_a_run_beyond_the_scratch():
     assert st == nv.EUNSUPPORTED, (st, nv.last_error())
     assert "static scratch" in nv.last_error(), nv.last_error()
     assert torch.isnan(out).all().item()  # nothing ran
+
+
+def test_noalloc_prefill_default_plan_falls_back_to_pieces():
+    """o at M = 2048 (K = 6144, N = 5120: 160 tiles on 256 compute units): a
+    default plan runs it with stream-K, whose slots do not fit the static
+    scratch, so the no-allocation call runs whole tiles (no K split there):
+    bit-identical to a workspace run of a pieces plan, and within the bound
+    of the oracle on rows and columns that reach every wave of every tile."""
+    import torch
+    nv = require_gpu()
+    M, K, N = 2048, 6144, 5120
+    codes, scales = synth.random_planes(91, 92, N, K)
+    t = 3.0e-3
+    act = synth.activations(93, 94, M, K)
+    pw = pack(nv, dev(codes), dev(scales), K, N, t)
+    a = dev_bf16(act)
+    g = nv.Gemm(M, K, N, nv.OUT_BF16)
+    gp = nv.Gemm(M, K, N, nv.OUT_BF16, prefill_schedule=nv.PREFILL_PIECES)
+    ref, ref_canary = canary_out(M, N, torch.bfloat16)
+    gp(pw, a, ref)
+    got, got_canary = canary_out(M, N, torch.bfloat16)
+    st = _noalloc(nv, g.plan, M, pw, a, got)
+    assert st == nv.OK, (st, nv.last_error())
+    torch.cuda.synchronize()
+    ref_canary("pieces workspace run")
+    got_canary("noalloc run")
+    assert np.array_equal(bf16_bits(got), bf16_bits(ref))
+    rows, cols = half_block_rows(M, 5), quarter_cols(N, 6)
+    y, S = oracle.gemm(act[rows], codes[cols], scales[cols], t)
+    sub = got[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()]
+    check(sub, y, S, bf16=True, what="noalloc prefill fallback")
 
 
 _CAPTURE_CHILD = r'''
