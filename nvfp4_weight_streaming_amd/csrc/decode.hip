@@ -668,12 +668,11 @@ int make_decode_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, De
     // Column groups that alone give every compute unit 4 or more workgroups
     // (the output head: 2376) take no K split at all: one slice of the whole
     // K per workgroup, streamed window by window, and no hand-off (the head
-    // at M = 8: 72 us against 94 with 5 splits).  The round's matrices have
-    // 112..544 groups and keep their splits: two, of half of K each, when two
-    // workgroups per group nearly fill the chip (qkv: 8.46 us against 9.02
-    // with 5 splits, gate_up: 21.9 against 22.3, at M = 8 in 64-node
-    // graphs), else as above (o, 80 groups: 8.4 us with 6 splits against 8.8
-    // with 2).
+    // at M = 8: 72 us against 94 with 5 splits).  The round's other matrices
+    // keep their splits: two, of half of K each, when two workgroups per
+    // group nearly fill the chip (qkv, 112 groups: 8.46 us against 9.02 with
+    // 5 splits, gate_up, 544 groups: 21.9 against 22.3, at M = 8 in 64-node
+    // graphs); fewer groups take the slices below.
     const bool long_k = nsb >= 32;
     const bool defaults = !(cfg && (cfg->split_k || cfg->chunks || cfg->windows));
     int waves = (cfg && cfg->waves) ? cfg->waves : (long_k ? 8 : 4);
@@ -698,9 +697,15 @@ int make_decode_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, De
         chunks = 1;
     }
     const bool halves = !long_k && 8 * 2 * n_groups >= 7 * device_cus();
+    // Fewer groups: as many K slices as still give every workgroup a compute
+    // unit of its own, slices of at least 2 windows (o and the 5120 x 5120
+    // projection, 80 groups: 3 slices, 7.9 us at M = 8 against 8.4 with the
+    // 6 and 5 slices of 2 windows, and against 8.8 / 8.1 with 4 / 2 slices).
+    const int fill = device_cus() / ng8 > 1 ? device_cus() / ng8 : 1;
+    const int fill_windows = (nsb + fill - 1) / fill > 2 ? (nsb + fill - 1) / fill : 2;
     int windows = (cfg && cfg->windows) ? cfg->windows
-                  : defaults                 ? (wide ? nsb : long_k ? 6 : halves ? (nsb + 1) / 2 : 2)
-                                             : 1;
+                  : defaults ? (wide ? nsb : long_k ? 6 : halves ? (nsb + 1) / 2 : fill_windows)
+                             : 1;
     if (windows < 1) return set_error(NVFP4_EINVAL, "config.windows: %d < 1", windows);
     if ((long long)windows * chunks > nsb) windows = (nsb + chunks - 1) / chunks;
     const int splits = (nsb + chunks * windows - 1) / (chunks * windows);

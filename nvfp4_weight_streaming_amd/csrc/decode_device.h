@@ -122,10 +122,10 @@ __device__ __forceinline__ void kb_steps(float (&acc)[4], const uint4& cw, uint3
         const bf16x8 bv = e2m1x8_to_bf16(word(cw, s));
         r[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
     }
-    const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 0);
-    const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 1);
-    const float s2 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 2);
-    const float s3 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 3);
+    // the four E4M3 block scales, two per conversion
+    const f32x2v s01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)sw, false);
+    const f32x2v s23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)sw, true);
+    const float s0 = s01[0], s1 = s01[1], s2 = s23[0], s3 = s23[1];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         acc[j] = __builtin_fmaf(s0, r[0][j], acc[j]);

@@ -180,8 +180,8 @@ struct PStage {
             const int ls = u & 63;
             const int col = (u >> 6) * 16 + (ls & 15), g = ls >> 4;
             const int sw = (int)(s[i] >> (16 * h));
-            const float s0 = __builtin_amdgcn_cvt_f32_fp8(sw, 0);
-            const float s1 = __builtin_amdgcn_cvt_f32_fp8(sw, 1);
+            const f32x2v s01 = __builtin_amdgcn_cvt_pk_f32_fp8(sw, false);
+            const float s0 = s01[0], s1 = s01[1];
             // step 2h: k = 8 g .. 8 g + 7 of the stage; step 2h + 1: 32 further
             *(uint4*)(lb + swz(col, g)) = dequant8(c[i].x, s0);
             *(uint4*)(lb + swz(col, 4 + g)) = dequant8(c[i].y, s1);
