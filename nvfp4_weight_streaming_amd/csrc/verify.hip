@@ -549,10 +549,12 @@ static int verify_default_slice(int n_tiles, int nsb, int waves) {
 //  - 17..64 rows with more 4-tile column groups than compute units (gate_up):
 //    one 8-wave workgroup per unit over equal ranges (M = 32: 35.7 us
 //    against 38.7 with per-group slices; M = 64: 46.5 against 52.5);
-//  - otherwise per-group slices of the default length, 4 waves, except 8
-//    waves with slices of 6 superblocks for 17..48 rows of a long K (>= 32
-//    superblocks: down; M = 17: 18.2 us against 20.6, M = 32: 19.4 against
-//    21.4, M = 48: 24.4 against 25.0).
+//  - otherwise per-group slices of the default length, 4 waves, except for
+//    a long K (>= 32 superblocks: down): slices of 6 superblocks, with 8
+//    waves above 16 rows (M = 17: 18.2 us against 20.6, M = 32: 19.4
+//    against 21.4, M = 48: 24.4 against 25.0, M = 64: 25.4 against 27.3
+//    with 4 waves and 3 slices) and 4 waves up to 16 when the groups are
+//    fewer than the units (M = 16: 15.9 against 16.4 with 3 slices).
 // The launch configurations share one workspace area sized for the larger
 // of each part.
 int make_verify_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, VerifyConfig* v) {
@@ -586,11 +588,11 @@ int make_verify_config(int K, int N, int max_M, const nvfp4_gemm_config* cfg, Ve
             verify_ranges_config(n_tiles, nsb, forced ? forced : 8, G, v->rows,
                                  ranges ? ranges : 1, c);
         } else {
-            const bool long_mid = long_k && (G == 2 || G == 3);
-            const int waves = forced ? forced : long_mid ? 8 : 4;
-            const int sl = slice              ? slice
-                           : long_mid && !forced ? 6
-                                                 : verify_default_slice(n_tiles, nsb, waves);
+            const int waves = forced ? forced : long_k && G >= 2 ? 8 : 4;
+            // (up to 16 rows only where the groups are fewer than the units)
+            const bool few = round_up((n_tiles + waves - 1) / waves, 8) < device_cus();
+            int sl = slice ? slice : verify_default_slice(n_tiles, nsb, waves);
+            if (!slice && !forced && long_k && (G >= 2 || few)) sl = 6;
             verify_slices_config(n_tiles, nsb, waves, v->rows, sl, c);
         }
         d.counter_bytes = std::max(d.counter_bytes, c.counter_bytes);
