@@ -16,7 +16,8 @@
 // 64.  LDS holds three stages of 256 x 64 activations and two of 256 x 64
 // dequantised weights (160 KiB, one workgroup per compute unit).  8 waves as
 // 2 x 4, each owning 128 x 64 outputs as 4 x 2 MFMA tiles of 32 x 32 (128 fp32
-// accumulators per lane, in the accumulation registers).  Activations run two
+// accumulators per lane; two waves per SIMD, so 256 registers per lane in all).
+// Activations run two
 // stages ahead (direct-to-LDS copies); weights run two stages ahead in
 // registers and are dequantised into LDS one stage ahead, the conversion
 // interleaved with the multiplies; one barrier per stage.  LDS rows are 128
