@@ -432,6 +432,7 @@ __global__ __launch_bounds__(1024) void decode_tile_kernel(
     const uint4* __restrict__ codes, const uint4* __restrict__ scales,
     const uint16_t* __restrict__ act, void* __restrict__ out, float ts, int M, int K, int N,
     int nsb) {
+    static_assert(MR >= 1 && MR <= 4, "at most 4 staged rows (M <= MR)");
     constexpr int kRow = SBW * kSuperK + kLdsPad;  // bf16 elements per staged row
     extern __shared__ __attribute__((aligned(16))) __bf16 tile_lds[];
     const int waves = blockDim.x >> 6;
@@ -488,11 +489,11 @@ __global__ __launch_bounds__(1024) void decode_tile_kernel(
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < SBW; ++c)
-        if (c < ns) chunk_steps(acc, w[c], ap + c * kSuperK);
+        if (c < ns) chunk_steps<MR>(acc, w[c], ap + c * kSuperK);
 
     // Lanes g and g+2 hold the same (row, column) for the two block halves.
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] += __shfl_xor(acc[j], 32, 64);
+    for (int j = 0; j < MR; ++j) acc[j] += __shfl_xor(acc[j], 32, 64);
     if (lane < 32) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) red[(wave * 8 + 4 * g + j) * kTileN + col] = acc[j];

@@ -113,6 +113,10 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
 
 // 128 k: four independent MFMAs (one per 32-k step), then the block scales.
 // a: this lane's A-operand pointer for the first step of the 128.
+// J: output rows 0 .. J - 1 of each lane's four (4 g + j) are scaled and
+// accumulated; with at most J activation rows the others hold only the
+// zero rows' products and are never read.
+template <int J = 4>
 __device__ __forceinline__ void kb_steps(float (&acc)[4], const uint4& cw, uint32_t sw,
                                          const __bf16* a) {
     f32x4 r[4];
@@ -127,7 +131,7 @@ __device__ __forceinline__ void kb_steps(float (&acc)[4], const uint4& cw, uint3
     const f32x2v s23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)sw, true);
     const float s0 = s01[0], s1 = s01[1], s2 = s23[0], s3 = s23[1];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < J; ++j) {
         acc[j] = __builtin_fmaf(s0, r[0][j], acc[j]);
         acc[j] = __builtin_fmaf(s1, r[1][j], acc[j]);
         acc[j] = __builtin_fmaf(s2, r[2][j], acc[j]);
@@ -135,11 +139,12 @@ __device__ __forceinline__ void kb_steps(float (&acc)[4], const uint4& cw, uint3
     }
 }
 
+template <int J = 4>
 __device__ __forceinline__ void chunk_steps(float (&acc)[4], const Chunk& x, const __bf16* a) {
-    kb_steps(acc, x.c[0], x.s.x, a);
-    kb_steps(acc, x.c[1], x.s.y, a + 128);
-    kb_steps(acc, x.c[2], x.s.z, a + 256);
-    kb_steps(acc, x.c[3], x.s.w, a + 384);
+    kb_steps<J>(acc, x.c[0], x.s.x, a);
+    kb_steps<J>(acc, x.c[1], x.s.y, a + 128);
+    kb_steps<J>(acc, x.c[2], x.s.z, a + 256);
+    kb_steps<J>(acc, x.c[3], x.s.w, a + 384);
 }
 
 // Stage rows 0..7 of an activation K slice plus one zero row (row 8) into LDS
