@@ -279,7 +279,8 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
 // process against the earlier shape: 64-layer round 7% faster at M = 1 and at
 // M = 8, and the registers per lane fall from 122 to 76 (6 waves per SIMD
 // instead of 4).
-template <int WAVES, int NCH, bool BF16>
+// J: output rows scaled per lane (kb_steps); 1 or 2 when M is, else 4.
+template <int WAVES, int NCH, bool BF16, int J = 4>
 __global__ __launch_bounds__(WAVES * 64) void decode_window_kernel(
     const uint4* __restrict__ codes, const uint4* __restrict__ scales,
     const uint16_t* __restrict__ act, void* __restrict__ out, float* __restrict__ partial,
@@ -386,7 +387,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_window_kernel(
         const __bf16* ap = cur + (live ? m : 8) * kStride + 8 * g;
 #pragma unroll
         for (int c = 0; c < NCH; ++c)
-            if (c < nch) chunk_steps(acc, x[c], ap + c * kSuperK);
+            if (c < nch) chunk_steps<J>(acc, x[c], ap + c * kSuperK);
     };
     using Yes = std::integral_constant<bool, true>;
     using No = std::integral_constant<bool, false>;
@@ -740,7 +741,21 @@ static int launch_t(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const
     const DecodeConfig& d = p->dec;
     unsigned int* counters = (unsigned int*)ws;
     float* partial = ws ? (float*)((char*)ws + partial_off) : nullptr;
-    if (d.windows > 1)
+    if (NCH == 1 && d.windows > 1 && M <= 2) {
+        // one or two lanes: only the live output rows take their scales
+        if (M == 1)
+            hipLaunchKernelGGL((decode_window_kernel<WAVES, 1, BF16, 1>), dim3(d.grid),
+                               dim3(WAVES * 64), 0, s, (const uint4*)codes, (const uint4*)scales,
+                               act, out, partial, counters, ts, M, p->K, p->N, p->Kp / kSuperK,
+                               d.splits, d.n_groups, p->Np / kTileN, d.l2_local, d.windows,
+                               am.area);
+        else
+            hipLaunchKernelGGL((decode_window_kernel<WAVES, 1, BF16, 2>), dim3(d.grid),
+                               dim3(WAVES * 64), 0, s, (const uint4*)codes, (const uint4*)scales,
+                               act, out, partial, counters, ts, M, p->K, p->N, p->Kp / kSuperK,
+                               d.splits, d.n_groups, p->Np / kTileN, d.l2_local, d.windows,
+                               am.area);
+    } else if (d.windows > 1)
         hipLaunchKernelGGL((decode_window_kernel<WAVES, NCH, BF16>), dim3(d.grid),
                            dim3(WAVES * 64), 0, s, (const uint4*)codes, (const uint4*)scales, act,
                            out, partial, counters, ts, M, p->K, p->N, p->Kp / kSuperK, d.splits,
