@@ -159,12 +159,16 @@ def summarize(out, dest):
     dur = lambda r: int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
     avg_us = lambda rs: sum(map(dur, rs)) / len(rs) / 1e3 if rs else float("nan")
     pcs, psum, sk = chunk_dispatches(trace, lambda r: r["Kernel_Name"])
-    dec_avg_us = sum(map(dur, dec)) / len(dec) / 1e3
     head_avg_us = sum(map(dur, head)) / len(head) / 1e3 if head else float("nan")
 
     # the first replay's first four launches are layer 0's qkv, o, gate_up, down
     layers = bench.LAYERS
     per_round = 4 * layers
+    # bench.py's event time covers the timed replays only (after the warm-up
+    # ones, before the single-replay spread): the same launches here
+    t0 = line["warmup"] * per_round
+    timed = dec[t0:t0 + line["steps"] * per_round]
+    dec_avg_us = sum(map(dur, timed)) / len(timed) / 1e3
     names = {}
     for i, r in enumerate(dec[:4]):
         names[(r["Kernel_Name"], r["Grid_Size_X"])] = bench.ROUND_SHAPES[i]
@@ -194,7 +198,7 @@ def summarize(out, dest):
     md.append("| decode kernel, GB/s (algorithmic %d B per launch) | %.1f | %.1f |"
               % (algo, roof["achieved"], algo / (dec_avg_us * 1e-6) / 1e9))
     md.append("| M = 8 round (ms) | %.4f | %.4f (sum of kernel durations / replays) |"
-              % (line["ms_per_step"], sum(map(dur, dec)) / (len(dec) / per_round) / 1e6))
+              % (line["ms_per_step"], sum(map(dur, timed)) / (len(timed) / per_round) / 1e6))
     pc = line["prefill_chunk"]
     md.append("| prefill chunk, default plan (%s) (us) | %.2f | |" % (pc.get("default_schedule", "?"),
                                                                     pc["us"]))
@@ -214,7 +218,10 @@ def summarize(out, dest):
     md.append("")
     md.append("bench.py's average launch is the timed region's event time over the %d "
               "launches of a replay, so it includes the gaps between graph nodes; the "
-              "trace's figure is kernel time only.\n" % per_round)
+              "trace's figure is kernel time only, over the same %d timed replays (launches "
+              "%d .. %d of the %d decode launches in the trace; the per-shape table below "
+              "takes all of them).\n" % (per_round, line["steps"], t0, t0 + len(timed) - 1,
+                                          len(dec)))
     md.append("## Decode kernel per matrix shape\n")
     md.append("| matrix (K x N) | kernel | grid (threads) | launches | average (us) | "
               "algorithmic GB/s |")
