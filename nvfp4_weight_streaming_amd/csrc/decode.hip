@@ -20,7 +20,10 @@
 //     the two 16-value block sums separately: output rows 4g..4g+3 of lane l
 //     belong to block g/2, whose E4M3 scale the lane multiplies in with one
 //     fp32 FMA per row.  Products are exact (bf16 x E2M1 fits the MFMA's fp32
-//     product), block sums and the scaled accumulation are fp32.
+//     product), block sums and the scaled accumulation are fp32.  A row i
+//     (and i + 8) carries activation row 2 (i mod 4) + i / 4 (act_row), so
+//     output row 4g + j holds activation row 2j + g (g mod 2) and with M
+//     lanes only j < ceil(M / 2) need their FMAs (kLiveJ).
 //   The two row halves are added with one cross-lane exchange at the end.
 // K is split over workgroups when the column count alone cannot fill the
 // chip; partial sums go to a workspace and the last workgroup of a column
@@ -125,7 +128,7 @@ __device__ __forceinline__ void decode_finish(float (&acc)[4], void* __restrict_
             const int n = nt * kTileN + col;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int mm = 4 * g + j;
+                const int mm = 2 * j + g;
                 if (mm < M && n < N) emit(mm, n, acc[j] * ts);
             }
         }
@@ -144,7 +147,7 @@ __device__ __forceinline__ void decode_finish(float (&acc)[4], void* __restrict_
     if (mine) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int mm = 4 * g + j;
+            const int mm = 2 * j + g;
             if (mm < M) {
                 float* dst = pbase + mm * kCols + wave * kTileN + col;
                 if (l2_local)
@@ -243,7 +246,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
     // 4. MFMA over the slice.  A-operand row of this lane: activation row
     //    `col` for its block half (col < 8 pairs with octets 0,1; col >= 8
     //    with octets 2,3), else the zero row.
-    const int m = col & 7;
+    const int m = act_row(col & 7);
     const bool live = ((col >> 3) == (g >> 1)) && (m < M);
     const __bf16* ap = lds + (live ? m : 8) * kStride + 8 * g;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -350,7 +353,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_window_kernel(
         }
     };
 
-    const int m = col & 7;
+    const int m = act_row(col & 7);
     const bool live = ((col >> 3) == (g >> 1)) && (m < M);
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     // Window w: wait for its loads (not for the next window's), then compute.
@@ -484,20 +487,20 @@ __global__ __launch_bounds__(1024) void decode_tile_kernel(
     __syncthreads();  // the zero row is written
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's weights and rows have landed
 
-    const int m = col & 7;
+    const int m = act_row(col & 7);
     const bool live = ((col >> 3) == (g >> 1)) && (m < M);
     const __bf16* ap = live ? (rows + m * kRow + 8 * g) : (zero + 8 * g);
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < SBW; ++c)
-        if (c < ns) chunk_steps<MR>(acc, w[c], ap + c * kSuperK);
+        if (c < ns) chunk_steps<kLiveJ(MR)>(acc, w[c], ap + c * kSuperK);
 
     // Lanes g and g+2 hold the same (row, column) for the two block halves.
 #pragma unroll
-    for (int j = 0; j < MR; ++j) acc[j] += __shfl_xor(acc[j], 32, 64);
+    for (int j = 0; j < kLiveJ(MR); ++j) acc[j] += __shfl_xor(acc[j], 32, 64);
     if (lane < 32) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) red[(wave * 8 + 4 * g + j) * kTileN + col] = acc[j];
+        for (int j = 0; j < 4; ++j) red[(wave * 8 + 2 * j + g) * kTileN + col] = acc[j];
     }
     __syncthreads();
     if ((int)threadIdx.x < M * kTileN) {
@@ -741,20 +744,20 @@ static int launch_t(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const
     const DecodeConfig& d = p->dec;
     unsigned int* counters = (unsigned int*)ws;
     float* partial = ws ? (float*)((char*)ws + partial_off) : nullptr;
-    if (NCH == 1 && d.windows > 1 && M <= 2) {
-        // one or two lanes: only the live output rows take their scales
-        if (M == 1)
-            hipLaunchKernelGGL((decode_window_kernel<WAVES, 1, BF16, 1>), dim3(d.grid),
-                               dim3(WAVES * 64), 0, s, (const uint4*)codes, (const uint4*)scales,
-                               act, out, partial, counters, ts, M, p->K, p->N, p->Kp / kSuperK,
-                               d.splits, d.n_groups, p->Np / kTileN, d.l2_local, d.windows,
-                               am.area);
+    if (NCH == 1 && d.windows > 1 && M <= 6) {
+        // fewer than 7 lanes: only the live output rows take their scales
+#define NVFP4_WINDOW_J(JJ)                                                                     \
+    hipLaunchKernelGGL((decode_window_kernel<WAVES, 1, BF16, JJ>), dim3(d.grid),               \
+                       dim3(WAVES * 64), 0, s, (const uint4*)codes, (const uint4*)scales, act, \
+                       out, partial, counters, ts, M, p->K, p->N, p->Kp / kSuperK, d.splits,   \
+                       d.n_groups, p->Np / kTileN, d.l2_local, d.windows, am.area)
+        if (kLiveJ(M) == 1)
+            NVFP4_WINDOW_J(1);
+        else if (kLiveJ(M) == 2)
+            NVFP4_WINDOW_J(2);
         else
-            hipLaunchKernelGGL((decode_window_kernel<WAVES, 1, BF16, 2>), dim3(d.grid),
-                               dim3(WAVES * 64), 0, s, (const uint4*)codes, (const uint4*)scales,
-                               act, out, partial, counters, ts, M, p->K, p->N, p->Kp / kSuperK,
-                               d.splits, d.n_groups, p->Np / kTileN, d.l2_local, d.windows,
-                               am.area);
+            NVFP4_WINDOW_J(3);
+#undef NVFP4_WINDOW_J
     } else if (d.windows > 1)
         hipLaunchKernelGGL((decode_window_kernel<WAVES, NCH, BF16>), dim3(d.grid),
                            dim3(WAVES * 64), 0, s, (const uint4*)codes, (const uint4*)scales, act,

@@ -83,6 +83,13 @@ __device__ __forceinline__ bf16x8 e2m1x8_scaled_bf16(uint32_t w, float sc) {
     return v;
 }
 
+// Activation row carried by A-operand row i (and i + 8) of the split-A MFMA:
+// 2 (i mod 4) + i / 4.  Output row 4 g + j of a lane (g < 2) then belongs to
+// activation row 2 j + g, so with M rows only j < ceil(M / 2) are live in any
+// lane: kLiveJ(M) block-scale FMAs per MFMA instead of 4.
+__device__ __forceinline__ int act_row(int i) { return 2 * (i & 3) + (i >> 2); }
+__host__ __device__ constexpr int kLiveJ(int M) { return M >= 8 ? 4 : (M + 1) / 2; }
+
 // The packed bytes one wave streams per 512-k superblock: 4 code chunks (16 B
 // per lane each, 4 MFMA steps apiece) and one 16-byte scale word per lane.
 struct Chunk {
