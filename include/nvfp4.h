@@ -306,7 +306,11 @@ int nvfp4_round_workspace_bytes(const nvfp4_layer* layers, int n_layers, int max
  * decode kernel for M <= 8, the verify-width kernel for the widths of
  * speculative verification above 8: "Ignis" README, "Speculative decoding
  * (DFlash2)"), plus one SwiGLU launch before each matrix whose act_op asks for
- * it.  Launches are ordered on one stream, so matrix i+1 starts only once
+ * it -- except where the previous matrix (gate_up) runs the streamed-slice
+ * decode kernel with 4-wave column groups, bf16 outputs and N a multiple of 64:
+ * there its last epilogue per column group also writes the SwiGLU values (the
+ * same bits nvfp4_swiglu gives), with its column groups pairing gate tiles
+ * with the matching up tiles.  Launches are ordered on one stream, so matrix i+1 starts only once
  * every output of matrix i is written, the order of a forward pass in which
  * each matrix consumes the previous one's result.
  * The layer array is copied; the device buffers it names must stay valid

@@ -137,6 +137,12 @@ void prefill_ws_need(const nvfp4_gemm_plan* p, int M, int schedule, size_t* coun
                      size_t* partials);
 int launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 int launch_swiglu(const uint16_t* gate_up, uint16_t* out, int M, int F, hipStream_t s);
+// gate_up with the SwiGLU of its output written to h (round chaining); only
+// where decode_swiglu_fusable holds.
+bool decode_swiglu_fusable(const nvfp4_gemm_plan* p, int M);
+int launch_decode_swiglu(const nvfp4_gemm_plan* p, int M, const uint8_t* codes,
+                         const uint8_t* scales, float ts, const uint16_t* act, void* out,
+                         uint16_t* h, void* ws, size_t partial_off, hipStream_t s);
 
 // Shared validation of a GEMM run against its plan.
 int validate_run(const nvfp4_gemm_plan* p, int M, int K, int N, const void* codes,

@@ -31,6 +31,7 @@
 // deterministic.  Workgroups of one column group are placed on one XCD
 // (blockIdx % 8 selects the XCD), so their partials meet in one L2.
 #include "decode_device.h"
+#include "swiglu_device.h"
 #include <type_traits>
 
 namespace nvfp4 {
@@ -52,6 +53,17 @@ namespace nvfp4 {
 struct ArgmaxRef {
     unsigned long long* area;    // [groups][8] row keys; null: no argmax
     unsigned long long* s_keys;  // LDS, 8 words
+};
+
+// The gate_up epilogue that also computes SwiGLU for the next matrix (a round
+// whose down matrix takes the SwiGLU of gate_up's output): the column group
+// holds gate columns 32 ng .. 32 ng + 31 (waves 0, 1) and the up columns F
+// above them (waves 2, 3), so each output row's 32 h values can be formed from
+// the group's own bf16 outputs, exactly as the SwiGLU kernel forms them.
+struct SwigluRef {
+    uint16_t* h;     // [M][F] bf16 (the down matrix's activations)
+    int F;           // N / 2
+    uint16_t* s_gu;  // LDS, 8 rows x 64 group columns of bf16 outputs
 };
 
 __device__ __forceinline__ unsigned long long argmax_key(float v, int n) {
@@ -95,13 +107,15 @@ __global__ __launch_bounds__(256) void argmax_merge_kernel(const unsigned long l
 // The end of a workgroup: the two row halves of each lane's sums are added,
 // then the outputs (one slice) or the split-K hand-off (several), and the
 // argmax step when asked for.
-template <int WAVES, bool BF16>
+template <int WAVES, bool BF16, bool SW = false>
 __device__ __forceinline__ void decode_finish(float (&acc)[4], void* __restrict__ out,
                                               float* __restrict__ partial,
                                               unsigned int* __restrict__ counters, float ts,
                                               int M, int N, int splits, int n_tiles, int l2_local,
                                               int ng, int split, int nt, int* s_last,
-                                              const ArgmaxRef& am) {
+                                              const ArgmaxRef& am,
+                                              const SwigluRef& sw = SwigluRef{}) {
+    static_assert(!SW || (WAVES == 4 && BF16), "SwiGLU epilogue: 4 waves, bf16 outputs");
     constexpr int kThreads = WAVES * 64;
     constexpr int kCols = WAVES * kTileN;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -123,16 +137,32 @@ __device__ __forceinline__ void decode_finish(float (&acc)[4], void* __restrict_
                                    __HIP_MEMORY_SCOPE_WORKGROUP);
     };
 
+    // (SW) h for the group's 32 columns from its stashed bf16 outputs.
+    auto swiglu_tail = [&]() {
+        if constexpr (SW) {
+            __syncthreads();
+            for (int t = threadIdx.x; t < M * 32; t += kThreads) {
+                const int mm = t >> 5, jj = t & 31;
+                sw.h[(size_t)mm * sw.F + 32 * ng + jj] =
+                    swiglu_bf16(sw.s_gu[mm * 64 + jj], sw.s_gu[mm * 64 + 32 + jj]);
+            }
+        }
+    };
+
     if (splits == 1) {
         if (mine) {
             const int n = nt * kTileN + col;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int mm = 2 * j + g;
-                if (mm < M && n < N) emit(mm, n, acc[j] * ts);
+                if (mm < M && n < N) {
+                    emit(mm, n, acc[j] * ts);
+                    if constexpr (SW) sw.s_gu[mm * 64 + wave * kTileN + col] = f32_to_bf16_rne(acc[j] * ts);
+                }
             }
         }
         if (amax) argmax_group_done(am, ng);
+        swiglu_tail();
         return;
     }
 
@@ -183,8 +213,12 @@ __device__ __forceinline__ void decode_finish(float (&acc)[4], void* __restrict_
     for (int r = 0; r < kR; ++r) {
         const int idx = threadIdx.x + r * kThreads;
         const int mm = idx / kCols, c = idx - mm * kCols;
-        const int n = ng * kCols + c;
-        if (idx < M * kCols && n < N) emit(mm, n, sum[r] * ts);
+        int n = ng * kCols + c;
+        if constexpr (SW) n = c < 32 ? 32 * ng + c : sw.F + 32 * ng + (c - 32);
+        if (idx < M * kCols && n < N) {
+            emit(mm, n, sum[r] * ts);
+            if constexpr (SW) sw.s_gu[mm * 64 + c] = f32_to_bf16_rne(sum[r] * ts);
+        }
     }
     if (threadIdx.x == 0) {  // leave the counter zeroed for the next run
         if (l2_local)
@@ -193,6 +227,7 @@ __device__ __forceinline__ void decode_finish(float (&acc)[4], void* __restrict_
             __hip_atomic_store(&counters[ng], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
     if (amax) argmax_group_done(am, ng);
+    swiglu_tail();
 }
 
 // One workgroup = WAVES column tiles (one per wave) x one K slice of up to
@@ -282,14 +317,16 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
 // process against the earlier shape: 64-layer round 7% faster at M = 1 and at
 // M = 8, and the registers per lane fall from 122 to 76 (6 waves per SIMD
 // instead of 4).
-// J: output rows scaled per lane (kb_steps); 1 or 2 when M is, else 4.
-template <int WAVES, int NCH, bool BF16, int J = 4>
+// J: output rows scaled per lane (kb_steps, kLiveJ of the lanes).
+// SW: the gate_up epilogue with SwiGLU (SwigluRef): column group ng holds gate
+// tiles 2 ng, 2 ng + 1 and up tiles n_tiles / 2 + 2 ng, + 1.
+template <int WAVES, int NCH, bool BF16, int J = 4, bool SW = false>
 __global__ __launch_bounds__(WAVES * 64) void decode_window_kernel(
     const uint4* __restrict__ codes, const uint4* __restrict__ scales,
     const uint16_t* __restrict__ act, void* __restrict__ out, float* __restrict__ partial,
     unsigned int* __restrict__ counters, float ts, int M, int K, int N, int nsb, int splits,
     int n_groups, int n_tiles, int l2_local, int windows,
-    unsigned long long* __restrict__ amax_area) {
+    unsigned long long* __restrict__ amax_area, uint16_t* __restrict__ sw_h, int sw_F) {
     constexpr int kThreads = WAVES * 64;
     constexpr int kStride = NCH * kSuperK + kLdsPad;  // LDS row, bf16 elements
     constexpr int kSeg = 8 * NCH / WAVES;  // activation segments (1 KiB) per wave per window
@@ -302,6 +339,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_window_kernel(
     __shared__ __attribute__((aligned(16))) __bf16 lds1[9 * kStride];
     __shared__ int s_last;
     __shared__ unsigned long long s_keys[8];
+    __shared__ uint16_t s_gu[SW ? 8 * 64 : 1];
 
     const int b = blockIdx.x;
     const int xcd = b & 7, q = b >> 3;
@@ -315,7 +353,8 @@ __global__ __launch_bounds__(WAVES * 64) void decode_window_kernel(
     // The wave index is uniform; saying so keeps the activation resources scalar.
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
-    const int nt = min(ng * WAVES + wave, n_tiles - 1);
+    const int nt = SW ? (wave < 2 ? 2 * ng + wave : (n_tiles >> 1) + 2 * ng + (wave - 2))
+                      : min(ng * WAVES + wave, n_tiles - 1);
     const int col = lane & 15, g = lane >> 4;
     const uint4* cp = codes + ((size_t)nt * nsb + sb_begin) * 256 + lane;
     const uint4* sp = scales + ((size_t)nt * nsb + sb_begin) * 32 + col * 2 + (g >> 1);
@@ -407,9 +446,9 @@ __global__ __launch_bounds__(WAVES * 64) void decode_window_kernel(
     } else {
         step(w, No{}, wa, wb, lds0, lds1);
     }
-    decode_finish<WAVES, BF16>(acc, out, partial, counters, ts, M, N, splits, n_tiles, l2_local,
-                               ng, split, nt, &s_last,
-                               ArgmaxRef{amax_area, s_keys});
+    decode_finish<WAVES, BF16, SW>(acc, out, partial, counters, ts, M, N, splits, n_tiles,
+                                   l2_local, ng, split, nt, &s_last, ArgmaxRef{amax_area, s_keys},
+                                   SwigluRef{sw_h, sw_F, s_gu});
 }
 
 // ---- narrow widths: one workgroup per column tile ------------------------------------
@@ -750,7 +789,7 @@ static int launch_t(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const
     hipLaunchKernelGGL((decode_window_kernel<WAVES, 1, BF16, JJ>), dim3(d.grid),               \
                        dim3(WAVES * 64), 0, s, (const uint4*)codes, (const uint4*)scales, act, \
                        out, partial, counters, ts, M, p->K, p->N, p->Kp / kSuperK, d.splits,   \
-                       d.n_groups, p->Np / kTileN, d.l2_local, d.windows, am.area)
+                       d.n_groups, p->Np / kTileN, d.l2_local, d.windows, am.area, nullptr, 0)
         if (kLiveJ(M) == 1)
             NVFP4_WINDOW_J(1);
         else if (kLiveJ(M) == 2)
@@ -762,7 +801,7 @@ static int launch_t(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const
         hipLaunchKernelGGL((decode_window_kernel<WAVES, NCH, BF16>), dim3(d.grid),
                            dim3(WAVES * 64), 0, s, (const uint4*)codes, (const uint4*)scales, act,
                            out, partial, counters, ts, M, p->K, p->N, p->Kp / kSuperK, d.splits,
-                           d.n_groups, p->Np / kTileN, d.l2_local, d.windows, am.area);
+                           d.n_groups, p->Np / kTileN, d.l2_local, d.windows, am.area, nullptr, 0);
     else
         hipLaunchKernelGGL((decode_kernel<WAVES, NCH, BF16>), dim3(d.grid), dim3(WAVES * 64), 0,
                            s, (const uint4*)codes, (const uint4*)scales, act, out, partial,
@@ -808,6 +847,39 @@ int launch_decode(const nvfp4_gemm_plan* p, int M, const uint8_t* codes, const u
                      : launch_w<false>(p, mm, codes, scales, ts, a, o, ws, partial_off, none, s);
         if (st) return st;
     }
+    return NVFP4_OK;
+}
+
+// A gate_up run whose epilogue also writes h = SwiGLU(output) for the next
+// matrix (SwigluRef), in place of the separate SwiGLU kernel.  Applies when the
+// plan takes the streamed-slice decode kernel at this width with 4-wave groups
+// and bf16 outputs, and N is a multiple of 64 (whole gate/up group pairs).
+bool decode_swiglu_fusable(const nvfp4_gemm_plan* p, int M) {
+    const DecodeConfig& d = p->dec;
+    return M >= 1 && M <= NVFP4_DECODE_MAX_M && M > p->tile.max_m && d.windows > 1 &&
+           d.chunks == 1 && d.waves == 4 && p->out_dtype == NVFP4_OUT_BF16 && p->N % 64 == 0;
+}
+
+int launch_decode_swiglu(const nvfp4_gemm_plan* p, int M, const uint8_t* codes,
+                         const uint8_t* scales, float ts, const uint16_t* act, void* out,
+                         uint16_t* h, void* ws, size_t partial_off, hipStream_t s) {
+    const DecodeConfig& d = p->dec;
+    unsigned int* counters = (unsigned int*)ws;
+    float* partial = ws ? (float*)((char*)ws + partial_off) : nullptr;
+    const int F = p->N / 2;
+#define NVFP4_SWIGLU_J(JJ)                                                                   \
+    hipLaunchKernelGGL((decode_window_kernel<4, 1, true, JJ, true>), dim3(d.grid), dim3(256), 0, \
+                       s, (const uint4*)codes, (const uint4*)scales, act, out, partial,       \
+                       counters, ts, M, p->K, p->N, p->Kp / kSuperK, d.splits, d.n_groups,    \
+                       p->Np / kTileN, d.l2_local, d.windows, nullptr, h, F)
+    switch (kLiveJ(M)) {
+        case 1: NVFP4_SWIGLU_J(1); break;
+        case 2: NVFP4_SWIGLU_J(2); break;
+        case 3: NVFP4_SWIGLU_J(3); break;
+        default: NVFP4_SWIGLU_J(4); break;
+    }
+#undef NVFP4_SWIGLU_J
+    NVFP4_HIP(hipGetLastError());
     return NVFP4_OK;
 }
 

@@ -171,16 +171,28 @@ int nvfp4_round_create(nvfp4_round* plan, const nvfp4_layer* layers, int n_layer
             break;
         }
         int lst = NVFP4_OK;
+        bool fused = false;  // the previous matrix's epilogue wrote this one's SwiGLU
         for (int i = 0; i < n_layers && !lst; ++i) {
             const nvfp4_layer& l = r->layers[i];
-            if (l.act_op == NVFP4_ACT_SWIGLU_PREV)
+            if (l.act_op == NVFP4_ACT_SWIGLU_PREV && !fused)
                 lst = launch_swiglu((const uint16_t*)r->layers[i - 1].out_dev,
                                     const_cast<uint16_t*>(l.act_dev), M, l.K, cap);
             if (lst) break;
-            lst = run_gemm(r->plans[i], M, l.codes_dev, l.scales_dev, l.tensor_scale, l.act_dev,
-                           l.out_dev, workspace,
-                           RunOffsets{r->partial_off, 0, r->partial_off, 0, r->partial_off},
-                           cap);
+            // A gate_up whose output feeds the next matrix through SwiGLU writes
+            // that SwiGLU in its own epilogue where its plan allows, which saves
+            // the SwiGLU kernel's launch.
+            fused = i + 1 < n_layers && r->layers[i + 1].act_op == NVFP4_ACT_SWIGLU_PREV &&
+                    decode_swiglu_fusable(r->plans[i], M);
+            if (fused)
+                lst = launch_decode_swiglu(r->plans[i], M, l.codes_dev, l.scales_dev,
+                                           l.tensor_scale, l.act_dev, l.out_dev,
+                                           const_cast<uint16_t*>(r->layers[i + 1].act_dev),
+                                           workspace, r->partial_off, cap);
+            else
+                lst = run_gemm(r->plans[i], M, l.codes_dev, l.scales_dev, l.tensor_scale,
+                               l.act_dev, l.out_dev, workspace,
+                               RunOffsets{r->partial_off, 0, r->partial_off, 0, r->partial_off},
+                               cap);
         }
         hipGraph_t g = nullptr;
         e = hipStreamEndCapture(cap, &g);

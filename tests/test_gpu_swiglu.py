@@ -41,16 +41,26 @@ def test_swiglu_matches_oracle(nv, M, F):
     assert bad.size == 0, (bad[:3], got[tuple(bad[0])], want[tuple(bad[0])])
 
 
-def test_chained_mlp_round(nv):
+# (K, F, widths, widths whose gate_up epilogue writes the SwiGLU itself):
+# K = 512 (one superblock) keeps the SwiGLU kernel at every width; K = 2048
+# (two K slices: the last workgroup's epilogue) and K = 1024 (one slice: every
+# workgroup's epilogue) take the tile kernel up to 4 lanes and the fused
+# epilogue from 5 on.
+CHAINED = [(512, 1024, (1, 5, 8), ()), (2048, 1024, (1, 4, 5, 7, 8), (5, 7, 8)),
+           (1024, 1024, (2, 5, 8), (5, 8))]
+
+
+@pytest.mark.parametrize("K,F,widths,fused", CHAINED)
+def test_chained_mlp_round(nv, K, F, widths, fused):
     """Two layers of x -> gate_up -> SwiGLU -> down, the down matrices reading
-    the round-made SwiGLU of the gate_up outputs.  Every replay (widths 1, 5,
-    8) is checked against the oracle step by step: gate_up against
-    oracle.gemm, the round-made activations bit for bit against oracle.swiglu
-    of the gate_up output the round wrote, and down against oracle.gemm of
-    those activations (bf16 bound).  It must also equal the same steps run as
-    separate calls, bit for bit."""
+    the round-made SwiGLU of the gate_up outputs (made by the SwiGLU kernel, or
+    by gate_up's own epilogue where its plan allows).  Every replay is checked
+    against the oracle step by step: gate_up against oracle.gemm, the
+    round-made activations bit for bit against oracle.swiglu of the gate_up
+    output the round wrote, and down against oracle.gemm of those activations
+    (bf16 bound).  It must also equal the same steps run as separate calls,
+    bit for bit."""
     import torch
-    K, F = 512, 1024
     specs, mats, planes = [], [], []
     for layer in range(2):
         for j, (k, n) in enumerate(((K, 2 * F), (F, K))):
@@ -73,10 +83,13 @@ def test_chained_mlp_round(nv):
     ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     plan = nv.nvfp4_round_create(specs, 8, ws, ws_bytes)
     try:
-        for M in (1, 5, 8):
-            assert nv.nvfp4_round_graph_nodes(plan, M) == len(specs) + 2  # + two SwiGLU nodes
+        for M in widths:
+            # + two SwiGLU nodes where the gate_up epilogue does not make them
+            assert nv.nvfp4_round_graph_nodes(plan, M) == len(specs) + (0 if M in fused else 2)
             for s in specs:
                 s["out"].fill_(float("nan"))
+            for s in specs[1::2]:
+                s["act"].fill_(float("nan"))  # round-made: every value must be rewritten
             nv.nvfp4_round_run(plan, M)
             torch.cuda.synchronize()
             for layer in range(2):
