@@ -633,8 +633,9 @@ def main():
     del hpws, hact, hout, hg
 
     # Chained MLP: the same round with each down matrix reading the SwiGLU of
-    # its layer's gate_up output (one more graph node per layer), so the
-    # gate_up -> down pair is a dependent chain as in a forward pass.
+    # its layer's gate_up output (made by gate_up's epilogue where its plan
+    # allows, else by one more graph node per layer), so the gate_up -> down
+    # pair is a dependent chain as in a forward pass.
     chained = {}
     if not args.no_sweep:
         with torch.cuda.stream(stream):
